@@ -1,0 +1,212 @@
+/*
+ * oracle.c -- plain, slow CPU oracle for the BitNet b1.58 BitLinear path (W1.58A8).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark may load this library.  The GPU library never links, includes or
+ * calls it, and this file includes nothing from the GPU library.
+ *
+ * Sources (web pages; cited by page key and the page's own section numbers):
+ *   [P1] 2kiu.com, article on 1.58-bit quantization and hardware co-optimization
+ *        ("从显存焦虑说起 ... 1.58-bit量化：当权重只剩下-1、0、1").
+ *   [P2] nxmr.cn, tutorial "1.58 位大模型" (principles, NumPy simulation, memory estimate).
+ *   [P3] chenxutan.com, "1.58-bit 大模型极限量化实战：从 BitNet 三值权重到单颗 CPU
+ *        跑起 100B 模型".
+ *
+ * Every function is a direct, scalar transcription of the definition it cites.  There is
+ * no blocking, no vectorisation and no reordering beyond the definition.  Floating point:
+ *   - where the pages' code fixes fp32 (the divisions W/alpha and 127*x/beta, the
+ *     +1e-8 guard on beta, the final dequant multiply), this file computes in fp32;
+ *   - where the pages leave precision open (the mean of |W|, the scalar alpha*beta/127),
+ *     it computes in fp64 and rounds to fp32 once.
+ * Build: gcc -O2 -ffp-contract=off (no fast-math), so each C operation rounds once.
+ *
+ * Readings of points the pages leave open (each also listed in the design notes):
+ *   R1  alpha = mean|W| is accumulated in fp64 in plain row-major order, then rounded
+ *       to fp32 once.
+ *   R2  round() is round-half-to-even, as the pages' code uses torch.round / np.round.
+ *   R3  alpha == 0 (all-zero W): every code is 0 (the division 0/0 is not evaluated).
+ *   R4  beta carries the +1e-8 guard of the pages' code, added in fp32.
+ *   R5  beta is per token (per row of x); the pages' code takes one max over the
+ *       tensor, which is the same thing for a single token.
+ *   R6  packed code = w + 1 (00 -> -1, 01 -> 0, 10 -> +1; 11 never written), four
+ *       codes per byte, weight k = 4b + i at bits 2i..2i+1 of byte b, rows of W stored
+ *       one after another (row-major along K).
+ *   R7  s = fp32((double)alpha * (double)beta / 127.0), y = fp32((float)acc * s), then
+ *       + bias as a separate fp32 rounding.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#define ORACLE_OK 0
+#define ORACLE_EINVAL (-1)
+#define ORACLE_EBADCODE (-2)
+
+/* [P3 §2.3] alpha = mean(|W|) over all weights of the tensor (per-tensor scale).
+ * [P2 §3.1] the same formula; R1 fixes fp64 accumulation. */
+float oracle_absmean(const float* w, int64_t count) {
+    double s = 0.0;
+    for (int64_t i = 0; i < count; ++i) s += fabs((double)w[i]);
+    return (float)(s / (double)count);
+}
+
+/* [P2 §3.1, §4.2] per-output-row scale: alpha[n] = mean_k |W[n, k]|. */
+int oracle_absmean_rows(const float* w, int64_t n_rows, int64_t k, float* alpha) {
+    if (!w || !alpha || n_rows <= 0 || k <= 0) return ORACLE_EINVAL;
+    for (int64_t n = 0; n < n_rows; ++n) alpha[n] = oracle_absmean(w + n * k, k);
+    return ORACLE_OK;
+}
+
+/* [P3 §2.3, §4.1] W_hat = clip(round(W / alpha), -1, 1).
+ * The quotient is an fp32 division (weight / alpha in the page's code), rounded half to
+ * even (R2), clipped; -0.0 becomes code 0.  alpha == 0 gives code 0 (R3). */
+static int8_t ternary_code(float w, float alpha) {
+    if (alpha == 0.0f) return 0;
+    float q = w / alpha;
+    float r = rintf(q);
+    if (r > 1.0f) r = 1.0f;
+    if (r < -1.0f) r = -1.0f;
+    return (int8_t)r;
+}
+
+int oracle_ternarize(const float* w, int64_t count, float alpha, int8_t* codes) {
+    if (!w || !codes || count < 0) return ORACLE_EINVAL;
+    for (int64_t i = 0; i < count; ++i) codes[i] = ternary_code(w[i], alpha);
+    return ORACLE_OK;
+}
+
+/* Per-row variant: row n uses alpha[n]. */
+int oracle_ternarize_rows(const float* w, int64_t n_rows, int64_t k, const float* alpha,
+                          int8_t* codes) {
+    if (!w || !alpha || !codes || n_rows <= 0 || k <= 0) return ORACLE_EINVAL;
+    for (int64_t n = 0; n < n_rows; ++n)
+        for (int64_t j = 0; j < k; ++j) codes[n * k + j] = ternary_code(w[n * k + j], alpha[n]);
+    return ORACLE_OK;
+}
+
+/* [P3 §5.3] two bits per weight, 00/01/10 for -1/0/+1; layout R6. */
+int oracle_pack(const int8_t* codes, int64_t n_rows, int64_t k, uint8_t* packed) {
+    if (!codes || !packed || n_rows <= 0 || k <= 0 || k % 4 != 0) return ORACLE_EINVAL;
+    int64_t row_bytes = k / 4;
+    for (int64_t n = 0; n < n_rows; ++n) {
+        for (int64_t b = 0; b < row_bytes; ++b) {
+            unsigned byte = 0;
+            for (int i = 0; i < 4; ++i) {
+                int w = codes[n * k + 4 * b + i];
+                if (w < -1 || w > 1) return ORACLE_EBADCODE;
+                byte |= (unsigned)(w + 1) << (2 * i);
+            }
+            packed[n * row_bytes + b] = (uint8_t)byte;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* Inverse of oracle_pack.  The pattern 11 is never written; meeting it is an error. */
+int oracle_unpack(const uint8_t* packed, int64_t n_rows, int64_t k, int8_t* codes) {
+    if (!codes || !packed || n_rows <= 0 || k <= 0 || k % 4 != 0) return ORACLE_EINVAL;
+    int64_t row_bytes = k / 4;
+    for (int64_t n = 0; n < n_rows; ++n) {
+        for (int64_t b = 0; b < row_bytes; ++b) {
+            unsigned byte = packed[n * row_bytes + b];
+            for (int i = 0; i < 4; ++i) {
+                unsigned c = (byte >> (2 * i)) & 3u;
+                if (c == 3u) return ORACLE_EBADCODE;
+                codes[n * k + 4 * b + i] = (int8_t)((int)c - 1);
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* [P3 §2.3, §4.1, §5.3] weight quantization as one call: per-tensor alpha, codes, packing.
+ * codes (nullable) receives the unpacked ternary values as well. */
+int oracle_quantize_weights(const float* w, int64_t n_rows, int64_t k, int8_t* codes,
+                            uint8_t* packed, float* alpha) {
+    if (!w || !packed || !alpha || n_rows <= 0 || k <= 0 || k % 4 != 0) return ORACLE_EINVAL;
+    float a = oracle_absmean(w, n_rows * k);
+    int64_t row_bytes = k / 4;
+    for (int64_t n = 0; n < n_rows; ++n) {
+        for (int64_t b = 0; b < row_bytes; ++b) {
+            unsigned byte = 0;
+            for (int i = 0; i < 4; ++i) {
+                int8_t c = ternary_code(w[n * k + 4 * b + i], a);
+                if (codes) codes[n * k + 4 * b + i] = c;
+                byte |= (unsigned)(c + 1) << (2 * i);
+            }
+            packed[n * row_bytes + b] = (uint8_t)byte;
+        }
+    }
+    *alpha = a;
+    return ORACLE_OK;
+}
+
+/* [P3 §2.4, §4.1] beta = max|x| (+1e-8, R4), x_q = clip(round(127 * x / beta), -127, 127).
+ * Per token (R5): row m of x has its own beta[m].  127*x is an fp32 product and the
+ * quotient an fp32 division, in the order the page's code writes them. */
+int oracle_quantize_act(const float* x, int64_t m_rows, int64_t k, int8_t* xq, float* beta) {
+    if (!x || !xq || !beta || m_rows <= 0 || k <= 0) return ORACLE_EINVAL;
+    for (int64_t m = 0; m < m_rows; ++m) {
+        const float* row = x + m * k;
+        float mx = 0.0f;
+        for (int64_t j = 0; j < k; ++j) {
+            float a = fabsf(row[j]);
+            if (a > mx) mx = a;
+        }
+        float b = mx + 1e-8f;
+        beta[m] = b;
+        for (int64_t j = 0; j < k; ++j) {
+            float t = (row[j] * 127.0f) / b;
+            float r = rintf(t);
+            if (r > 127.0f) r = 127.0f;
+            if (r < -127.0f) r = -127.0f;
+            xq[m * k + j] = (int8_t)r;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* [P2 §3.3] Y[m][n] = sum over k with W=+1 of X[m][k] minus sum over k with W=-1 of
+ * X[m][k]; zero weights are skipped.  Integer accumulation (int32 holds 127*K for any
+ * K below 16.9 million).  Output rows n in [n0, n1) only, so a caller can split work. */
+int oracle_ternary_matmul(const int8_t* xq, int64_t m_rows, int64_t k, const int8_t* codes,
+                          int64_t n_rows, int32_t* acc, int64_t n0, int64_t n1) {
+    if (!xq || !codes || !acc || m_rows <= 0 || k <= 0 || n_rows <= 0) return ORACLE_EINVAL;
+    if (n0 < 0 || n1 > n_rows || n0 > n1) return ORACLE_EINVAL;
+    for (int64_t m = 0; m < m_rows; ++m) {
+        for (int64_t n = n0; n < n1; ++n) {
+            int32_t s = 0;
+            for (int64_t j = 0; j < k; ++j) {
+                int8_t c = codes[n * k + j];
+                if (c == 1) s += xq[m * k + j];
+                else if (c == -1) s -= xq[m * k + j];
+            }
+            acc[m * n_rows + n] = s;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* [P3 §2.4, §2.5, §4.2] dequantisation scale alpha*beta/127, reading R7. */
+float oracle_dequant_scale(float alpha, float beta) {
+    return (float)((double)alpha * (double)beta / 127.0);
+}
+
+/* [P3 §2.4, §3.2 step 4] y = acc * (alpha*beta/127) + bias.  alpha_rows (nullable)
+ * selects the per-row alpha variant [P2 §3.1]: then column n uses alpha_rows[n]. */
+int oracle_dequant(const int32_t* acc, const float* beta, float alpha, const float* alpha_rows,
+                   int64_t m_rows, int64_t n_rows, const float* bias, float* y, int64_t n0,
+                   int64_t n1) {
+    if (!acc || !beta || !y || m_rows <= 0 || n_rows <= 0) return ORACLE_EINVAL;
+    if (n0 < 0 || n1 > n_rows || n0 > n1) return ORACLE_EINVAL;
+    for (int64_t m = 0; m < m_rows; ++m) {
+        for (int64_t n = n0; n < n1; ++n) {
+            float a = alpha_rows ? alpha_rows[n] : alpha;
+            float s = oracle_dequant_scale(a, beta[m]);
+            float v = (float)acc[m * n_rows + n] * s;
+            if (bias) v = v + bias[n];
+            y[m * n_rows + n] = v;
+        }
+    }
+    return ORACLE_OK;
+}

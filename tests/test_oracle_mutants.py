@@ -1,0 +1,54 @@
+"""Plant plausible mistakes in a copy of the oracle and check that the pins catch each one.
+
+Each mutant is one textual change to oracle.c (a dropped term, a wrong sign or index, a
+transposed operand, another rounding), compiled to a temporary library and run against
+test_oracle_pins.py in a child process.  A mutant that every pin lets through would mean
+the pins do not constrain that part of the oracle."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(os.path.dirname(HERE), "oracle", "oracle.c")
+
+MUTANTS = [
+    ("half-away rounding of W/alpha", "float r = rintf(q);", "float r = roundf(q);"),
+    ("dropped abs in absmean", "s += fabs((double)w[i]);", "s += (double)w[i];"),
+    ("mean divides by count-1", "return (float)(s / (double)count);", "return (float)(s / (double)(count - 1));"),
+    ("transposed division W/alpha", "float q = w / alpha;", "float q = alpha / w;"),
+    ("dropped upper clip of codes", "if (r > 1.0f) r = 1.0f;", ""),
+    ("reversed bit order in quantize_weights", "byte |= (unsigned)(c + 1) << (2 * i);",
+     "byte |= (unsigned)(c + 1) << (6 - 2 * i);"),
+    ("reversed bit order in pack", "byte |= (unsigned)(w + 1) << (2 * i);",
+     "byte |= (unsigned)(w + 1) << (6 - 2 * i);"),
+    ("wrong code offset in unpack", "codes[n * k + 4 * b + i] = (int8_t)((int)c - 1);",
+     "codes[n * k + 4 * b + i] = (int8_t)((int)c);"),
+    ("dropped abs in activation max", "if (a > mx) mx = a;", "if (a > mx) mx = row[j];"),
+    ("dropped 1e-8 guard", "float b = mx + 1e-8f;", "float b = mx;"),
+    ("reciprocal instead of division", "float t = (row[j] * 127.0f) / b;", "float t = row[j] * (127.0f / b);"),
+    ("reciprocal in ternarization", "float q = w / alpha;", "float q = w * (1.0f / alpha);"),
+    ("half-away rounding of activations", "float r = rintf(t);", "float r = roundf(t);"),
+    ("sign flip on +1 weights", "if (c == 1) s += xq[m * k + j];", "if (c == 1) s -= xq[m * k + j];"),
+    ("dropped token index", "else if (c == -1) s -= xq[m * k + j];", "else if (c == -1) s -= xq[j];"),
+    ("fp32 dequant scale", "return (float)((double)alpha * (double)beta / 127.0);",
+     "return alpha * beta / 127.0f;"),
+    ("transposed acc in dequant", "float v = (float)acc[m * n_rows + n] * s;",
+     "float v = (float)acc[n * m_rows + m] * s;"),
+    ("bias subtracted", "if (bias) v = v + bias[n];", "if (bias) v = v - bias[n];"),
+    ("per-row alpha indexed by token", "float a = alpha_rows ? alpha_rows[n] : alpha;",
+     "float a = alpha_rows ? alpha_rows[m] : alpha;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_kill_mutant(name, old, new, tmp_path):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site not unique/found: {old!r}"
+    mut = tmp_path / "oracle_mutant.c"
+    mut.write_text(src.replace(old, new))
+    so = tmp_path / "liboracle_mutant.so"
+    r = subprocess.run([sys.executable, os.path.join(HERE, "_mutant_runner.py"), str(mut), str(so)],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"mutant '{name}' survived every pin:\n{r.stdout[-2000:]}"
