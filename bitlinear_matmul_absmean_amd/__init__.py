@@ -1,0 +1,183 @@
+"""Python binding of the MI355X BitNet b1.58 BitLinear library (W1.58A8).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels of
+``libbitlinear.so`` behind the C ABI of ``include/bitlinear.h``.  PyTorch provides device
+memory (tensors) and the current HIP stream; nothing here computes on the host.  If the
+library has not been built, importing this package raises -- there is no fallback.
+
+The functions carry the C names.  ``lib`` exposes the raw C entry points (ctypes) for
+callers that manage pointers themselves.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libbitlinear.so")
+
+BITLINEAR_OK = 0
+BITLINEAR_ERR_INVALID_ARG = -1
+BITLINEAR_ERR_SHAPE = -2
+BITLINEAR_ERR_ALIGNMENT = -3
+BITLINEAR_ERR_WORKSPACE = -4
+BITLINEAR_ERR_HIP = -5
+BITLINEAR_MAX_K = 16909320
+
+# Every symbol the header declares, with (restype, argtypes).
+_P, _I64, _SZ, _INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+SIGNATURES = {
+    "bitlinear_abi_version": (_INT, []),
+    "bitlinear_status_string": (ctypes.c_char_p, [_INT]),
+    "bitlinear_last_hip_error": (_INT, []),
+    "bitlinear_quantize_weights_workspace_size": (_SZ, [_I64, _I64]),
+    "bitlinear_quantize_weights": (_INT, [_P, _I64, _I64, _P, _P, _P, _SZ, _P]),
+    "bitlinear_quantize_weights_rows": (_INT, [_P, _I64, _I64, _P, _P, _P]),
+    "bitlinear_quantize_act": (_INT, [_P, _I64, _I64, _P, _P, _P]),
+    "bitlinear_forward": (_INT, [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P]),
+    "bitlinear_forward_rows": (_INT, [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P]),
+    "bitlinear_forward_kernel": (ctypes.c_char_p, [_I64, _I64, _I64, _P, _P]),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m bitlinear_matmul_absmean_amd.build` "
+            "(hipcc --offload-arch=gfx950). There is no CPU fallback.")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+class BitLinearError(RuntimeError):
+    def __init__(self, what: str, status: int):
+        msg = lib.bitlinear_status_string(status).decode()
+        if status == BITLINEAR_ERR_HIP:
+            msg += f" (hipError {lib.bitlinear_last_hip_error()})"
+        super().__init__(f"{what}: {msg} [status {status}]")
+        self.status = status
+
+
+def _check(what: str, status: int):
+    if status != BITLINEAR_OK:
+        raise BitLinearError(what, status)
+
+
+def abi_version() -> int:
+    return lib.bitlinear_abi_version()
+
+
+# ------------------------------------------------------------------ torch marshalling
+def _torch():
+    import torch  # imported lazily: the C entry points above need no torch
+    return torch
+
+
+def _dev(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def bitlinear_quantize_weights(W, W_packed=None, alpha=None, workspace=None, stream=None):
+    """W [N, K] fp32 -> (W_packed uint8 [N, K/4], alpha fp32 [1]) on the device."""
+    torch = _torch()
+    N, K = W.shape
+    if W_packed is None:
+        W_packed = torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
+    if alpha is None:
+        alpha = torch.empty(1, dtype=torch.float32, device=W.device)
+    need = lib.bitlinear_quantize_weights_workspace_size(N, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=W.device)
+    _check("bitlinear_quantize_weights", lib.bitlinear_quantize_weights(
+        _dev(W, torch.float32, "W"), N, K, _dev(W_packed, torch.uint8, "W_packed"),
+        _dev(alpha, torch.float32, "alpha"), _dev(workspace, torch.uint8, "workspace"),
+        workspace.numel(), _stream(stream)))
+    return W_packed, alpha
+
+
+def bitlinear_quantize_weights_rows(W, W_packed=None, alpha_rows=None, stream=None):
+    """W [N, K] fp32 -> (W_packed uint8 [N, K/4], alpha_rows fp32 [N])."""
+    torch = _torch()
+    N, K = W.shape
+    if W_packed is None:
+        W_packed = torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
+    if alpha_rows is None:
+        alpha_rows = torch.empty(N, dtype=torch.float32, device=W.device)
+    _check("bitlinear_quantize_weights_rows", lib.bitlinear_quantize_weights_rows(
+        _dev(W, torch.float32, "W"), N, K, _dev(W_packed, torch.uint8, "W_packed"),
+        _dev(alpha_rows, torch.float32, "alpha_rows"), _stream(stream)))
+    return W_packed, alpha_rows
+
+
+def bitlinear_quantize_act(x, x_q=None, beta=None, stream=None):
+    """x [M, K] fp32 -> (x_q int8 [M, K], beta fp32 [M])."""
+    torch = _torch()
+    M, K = x.shape
+    if x_q is None:
+        x_q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if beta is None:
+        beta = torch.empty(M, dtype=torch.float32, device=x.device)
+    _check("bitlinear_quantize_act", lib.bitlinear_quantize_act(
+        _dev(x, torch.float32, "x"), M, K, _dev(x_q, torch.int8, "x_q"),
+        _dev(beta, torch.float32, "beta"), _stream(stream)))
+    return x_q, beta
+
+
+def _forward(fn, what, x_q, beta, W_packed, alpha, bias, y, acc, stream):
+    torch = _torch()
+    M, K = x_q.shape
+    N = W_packed.shape[0]
+    if W_packed.shape[1] * 4 != K:
+        raise ValueError("W_packed must be [N, K/4]")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x_q.device)
+    if acc is True:
+        acc = torch.empty((M, N), dtype=torch.int32, device=x_q.device)
+    acc_ptr = _dev(acc, torch.int32, "acc") if acc is not None and acc is not False else None
+    bias_ptr = _dev(bias, torch.float32, "bias") if bias is not None else None
+    _check(what, fn(
+        _dev(x_q, torch.int8, "x_q"), _dev(beta, torch.float32, "beta"), M, K,
+        _dev(W_packed, torch.uint8, "W_packed"), _dev(alpha, torch.float32, "alpha"), N,
+        bias_ptr, _dev(y, torch.float32, "y"), acc_ptr, _stream(stream)))
+    return (y, acc) if acc_ptr is not None else y
+
+
+def bitlinear_forward(x_q, beta, W_packed, alpha, bias=None, y=None, acc=None, stream=None):
+    """y [M, N] = (x_q . W_hat^T) * alpha*beta/127 (+ bias).  acc=True (or an int32 [M, N]
+    tensor) also returns the exact integer sums: (y, acc)."""
+    return _forward(lib.bitlinear_forward, "bitlinear_forward", x_q, beta, W_packed, alpha,
+                    bias, y, acc, stream)
+
+
+def bitlinear_forward_rows(x_q, beta, W_packed, alpha_rows, bias=None, y=None, acc=None, stream=None):
+    """bitlinear_forward with one alpha per output row."""
+    return _forward(lib.bitlinear_forward_rows, "bitlinear_forward_rows", x_q, beta, W_packed,
+                    alpha_rows, bias, y, acc, stream)
+
+
+def bitlinear_forward_kernel(M, K, N, x_q=None, W_packed=None) -> str:
+    """Name of the kernel bitlinear_forward selects (pointers decide alignment; None
+    stands for a 256-byte aligned allocation)."""
+    xp = x_q.data_ptr() if x_q is not None else 256
+    wp = W_packed.data_ptr() if W_packed is not None else 256
+    return lib.bitlinear_forward_kernel(M, K, N, xp, wp).decode()

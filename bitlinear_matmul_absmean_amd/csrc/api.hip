@@ -1,0 +1,147 @@
+// api.hip -- the C ABI declared in include/bitlinear.h: host-side validation, then kernel
+// selection by shape and launch on the caller's stream.  No allocation, no sync, no state.
+#include "bitlinear.h"
+
+#include <limits.h>
+
+#include "common.hpp"
+
+using namespace bitlinear;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+inline int hip_status(hipError_t e) {
+    if (e == hipSuccess) return BITLINEAR_OK;
+    g_last_hip_error = (int)e;
+    return BITLINEAR_ERR_HIP;
+}
+
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// a*b without overflow into a signed 64-bit result
+inline bool mul_ok(int64_t a, int64_t b) { return a > 0 && b > 0 && a <= INT64_MAX / b; }
+
+// The fast forward kernels read 16-byte rows of x_q and W_packed.
+inline bool fast_forward_ok(int64_t K, const int8_t* xq, const uint8_t* wp) {
+    return K % 64 == 0 && aligned(xq, 16) && aligned(wp, 16);
+}
+
+int check_forward(const int8_t* x_q, const float* beta, int64_t M, int64_t K, const uint8_t* W_packed,
+                  const float* alpha, int64_t N, float* y) {
+    if (!x_q || !beta || !W_packed || !alpha || !y) return BITLINEAR_ERR_INVALID_ARG;
+    if (M <= 0 || K <= 0 || N <= 0) return BITLINEAR_ERR_INVALID_ARG;
+    if (K % 4 != 0 || K > BITLINEAR_MAX_K) return BITLINEAR_ERR_SHAPE;
+    if (!mul_ok(M, K) || !mul_ok(N, K) || !mul_ok(M, N)) return BITLINEAR_ERR_SHAPE;
+    if (N > (int64_t)UINT_MAX || M > (int64_t)65535 * 128) return BITLINEAR_ERR_SHAPE;
+    return BITLINEAR_OK;
+}
+
+enum class Path { Gemv, Gemm, Generic };
+
+Path choose_path(int64_t M, int64_t K, const int8_t* xq, const uint8_t* wp) {
+    if (!fast_forward_ok(K, xq, wp)) return Path::Generic;
+    return M <= 4 ? Path::Gemv : Path::Gemm;
+}
+
+int run_forward(const ForwardArgs& a, hipStream_t stream) {
+    switch (choose_path(a.M, a.K, a.xq, a.wp)) {
+        case Path::Gemv: return hip_status(launch_gemv_dot4(a, stream));
+        case Path::Gemm: return hip_status(launch_gemm_mfma(a, stream));
+        default: return hip_status(launch_forward_generic(a, stream));
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+int bitlinear_abi_version(void) { return BITLINEAR_ABI_VERSION; }
+
+const char* bitlinear_status_string(int status) {
+    switch (status) {
+        case BITLINEAR_OK: return "ok";
+        case BITLINEAR_ERR_INVALID_ARG: return "invalid argument (null pointer or non-positive size)";
+        case BITLINEAR_ERR_SHAPE: return "unsupported shape (K % 4 != 0, K too large or size overflow)";
+        case BITLINEAR_ERR_ALIGNMENT: return "pointer alignment";
+        case BITLINEAR_ERR_WORKSPACE: return "workspace missing or too small";
+        case BITLINEAR_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int bitlinear_last_hip_error(void) { return g_last_hip_error; }
+
+size_t bitlinear_quantize_weights_workspace_size(int64_t N, int64_t K) {
+    if (N <= 0 || K <= 0) return 0;
+    return (size_t)N * sizeof(double);
+}
+
+int bitlinear_quantize_weights(const float* W, int64_t N, int64_t K, uint8_t* W_packed, float* alpha,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!W || !W_packed || !alpha) return BITLINEAR_ERR_INVALID_ARG;
+    if (N <= 0 || K <= 0) return BITLINEAR_ERR_INVALID_ARG;
+    if (K % 4 != 0 || K > BITLINEAR_MAX_K || !mul_ok(N, K) || N > (int64_t)INT_MAX * 4)
+        return BITLINEAR_ERR_SHAPE;
+    if (!aligned(W, 16) || !aligned(W_packed, 4)) return BITLINEAR_ERR_ALIGNMENT;
+    if (!workspace || workspace_bytes < bitlinear_quantize_weights_workspace_size(N, K))
+        return BITLINEAR_ERR_WORKSPACE;
+    if (!aligned(workspace, 8)) return BITLINEAR_ERR_ALIGNMENT;
+    double* rows = static_cast<double*>(workspace);
+    int st = hip_status(launch_row_abs_sums(W, N, K, rows, stream));
+    if (st) return st;
+    st = hip_status(launch_alpha_from_rows(rows, N, K, alpha, stream));
+    if (st) return st;
+    return hip_status(launch_ternary_pack(W, N, K, alpha, false, W_packed, stream));
+}
+
+int bitlinear_quantize_weights_rows(const float* W, int64_t N, int64_t K, uint8_t* W_packed,
+                                    float* alpha_rows, hipStream_t stream) {
+    if (!W || !W_packed || !alpha_rows) return BITLINEAR_ERR_INVALID_ARG;
+    if (N <= 0 || K <= 0) return BITLINEAR_ERR_INVALID_ARG;
+    if (K % 4 != 0 || K > BITLINEAR_MAX_K || !mul_ok(N, K) || N > (int64_t)INT_MAX * 4)
+        return BITLINEAR_ERR_SHAPE;
+    if (!aligned(W, 16) || !aligned(W_packed, 4)) return BITLINEAR_ERR_ALIGNMENT;
+    int st = hip_status(launch_alpha_rows(W, N, K, alpha_rows, stream));
+    if (st) return st;
+    return hip_status(launch_ternary_pack(W, N, K, alpha_rows, true, W_packed, stream));
+}
+
+int bitlinear_quantize_act(const float* x, int64_t M, int64_t K, int8_t* x_q, float* beta,
+                           hipStream_t stream) {
+    if (!x || !x_q || !beta) return BITLINEAR_ERR_INVALID_ARG;
+    if (M <= 0 || K <= 0) return BITLINEAR_ERR_INVALID_ARG;
+    if (!mul_ok(M, K) || M > (int64_t)INT_MAX) return BITLINEAR_ERR_SHAPE;
+    return hip_status(launch_quantize_act(x, M, K, x_q, beta, stream));
+}
+
+int bitlinear_forward(const int8_t* x_q, const float* beta, int64_t M, int64_t K, const uint8_t* W_packed,
+                      const float* alpha, int64_t N, const float* bias, float* y, int32_t* acc,
+                      hipStream_t stream) {
+    int st = check_forward(x_q, beta, M, K, W_packed, alpha, N, y);
+    if (st) return st;
+    ForwardArgs a{x_q, beta, M, K, N, W_packed, alpha, false, bias, y, acc};
+    return run_forward(a, stream);
+}
+
+int bitlinear_forward_rows(const int8_t* x_q, const float* beta, int64_t M, int64_t K,
+                           const uint8_t* W_packed, const float* alpha_rows, int64_t N, const float* bias,
+                           float* y, int32_t* acc, hipStream_t stream) {
+    int st = check_forward(x_q, beta, M, K, W_packed, alpha_rows, N, y);
+    if (st) return st;
+    ForwardArgs a{x_q, beta, M, K, N, W_packed, alpha_rows, true, bias, y, acc};
+    return run_forward(a, stream);
+}
+
+const char* bitlinear_forward_kernel(int64_t M, int64_t K, int64_t N, const int8_t* x_q,
+                                     const uint8_t* W_packed) {
+    (void)N;
+    switch (choose_path(M, K, x_q, W_packed)) {
+        case Path::Gemv: return "gemv_dot4";
+        case Path::Gemm: return "gemm_mfma_i8";
+        default: return "generic";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+// common.hpp -- shared device helpers and launch declarations for the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bitlinear {
+
+constexpr int kWave = 64;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Launch with `lds` bytes of dynamic LDS; above 64 KiB the kernel must first be allowed
+// the larger allocation (gfx950 has 160 KiB of LDS per workgroup).
+template <typename Kernel, typename... Args>
+static inline hipError_t launch_with_lds(Kernel k, dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                                         Args... args) {
+    if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k, grid, block, lds, s, args...);
+    return hipGetLastError();
+}
+
+// Wave-wide reductions.  Integer sums and float maxima are exact in any order.
+__device__ __forceinline__ int wave_sum_i32(int v) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) v = fmaxf(v, __shfl_xor(v, s, kWave));
+    return v;
+}
+
+// Butterfly sum in fp64; every lane ends with the same value, and the order of the
+// additions depends only on the lane count, so the result is reproducible.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s, kWave);
+    return v;
+}
+
+// Dequantization scale alpha*beta/127: fp64 product and quotient, one fp32 rounding.
+__device__ __forceinline__ float dequant_scale(float alpha, float beta) {
+    return (float)((double)alpha * (double)beta / 127.0);
+}
+
+// y = fp32(acc) * s (+ bias) with separate roundings (the library builds with
+// -ffp-contract=off, so no multiply-add is fused).
+__device__ __forceinline__ float dequant(int acc, float s, const float* __restrict__ bias, int64_t n) {
+    float v = (float)acc * s;
+    if (bias) v = v + bias[n];
+    return v;
+}
+
+// Signed 4 x int8 dot product with int32 accumulate (v_dot4_i32_i8).
+__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
+    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+// 4x4 byte transpose of 16 bytes: byte j of output dword i = byte i of input dword j.
+__device__ __forceinline__ u32x4 transpose4x4_bytes(u32x4 s) {
+    u32x4 o;
+    o.x = (s.x & 0xFFu) | ((s.y & 0xFFu) << 8) | ((s.z & 0xFFu) << 16) | ((s.w & 0xFFu) << 24);
+    o.y = ((s.x >> 8) & 0xFFu) | (((s.y >> 8) & 0xFFu) << 8) | (((s.z >> 8) & 0xFFu) << 16) |
+          (((s.w >> 8) & 0xFFu) << 24);
+    o.z = ((s.x >> 16) & 0xFFu) | (((s.y >> 16) & 0xFFu) << 8) | (((s.z >> 16) & 0xFFu) << 16) |
+          (((s.w >> 16) & 0xFFu) << 24);
+    o.w = (s.x >> 24) | ((s.y >> 24) << 8) | ((s.z >> 24) << 16) | ((s.w >> 24) << 24);
+    return o;
+}
+
+// Sum of the four signed bytes of a dword.
+__device__ __forceinline__ int byte_sum(uint32_t v) { return dot4(v, 0x01010101u, 0); }
+
+// ---- launch wrappers (one per kernel family), defined in the .hip files -------------------
+hipError_t launch_row_abs_sums(const float* W, int64_t N, int64_t K, double* rowsum, hipStream_t s);
+hipError_t launch_alpha_from_rows(const double* rowsum, int64_t N, int64_t K, float* alpha, hipStream_t s);
+hipError_t launch_alpha_rows(const float* W, int64_t N, int64_t K, float* alpha_rows, hipStream_t s);
+hipError_t launch_ternary_pack(const float* W, int64_t N, int64_t K, const float* alpha, bool per_row,
+                               uint8_t* packed, hipStream_t s);
+hipError_t launch_quantize_act(const float* x, int64_t M, int64_t K, int8_t* xq, float* beta, hipStream_t s);
+
+struct ForwardArgs {
+    const int8_t* xq;
+    const float* beta;
+    int64_t M, K, N;
+    const uint8_t* wp;
+    const float* alpha;   // [1] or [N]
+    bool alpha_per_row;
+    const float* bias;
+    float* y;
+    int32_t* acc;
+};
+
+hipError_t launch_gemv_dot4(const ForwardArgs& a, hipStream_t s);
+hipError_t launch_gemm_mfma(const ForwardArgs& a, hipStream_t s);
+hipError_t launch_forward_generic(const ForwardArgs& a, hipStream_t s);
+
+}  // namespace bitlinear

@@ -1,0 +1,158 @@
+/*
+ * bitlinear.h -- C ABI of the MI355X (gfx950) BitNet b1.58 BitLinear library (W1.58A8).
+ *
+ * Page keys used in the citations below:
+ *   [P2] nxmr.cn tutorial "1.58 位大模型" (per-row absmean, add/sub form of the matmul).
+ *   [P3] chenxutan.com, "1.58-bit 大模型极限量化实战：从 BitNet 三值权重到单颗 CPU 跑起 100B 模型"
+ *        (absmean / absmax formulas, BitLinear forward, 2-bit packing).
+ *
+ * The layer is split the way [P3 §3.2] describes BitLinear: weights are quantized once and
+ * cached (bitlinear_quantize_weights); every call quantizes the activations
+ * (bitlinear_quantize_act), runs the ternary x int8 integer matmul and applies the
+ * alpha*beta/127 dequantization (bitlinear_forward).
+ *
+ * Conventions shared by every entry point
+ *   - Memory: every array argument is DEVICE memory on the current HIP device, allocated and
+ *     owned by the caller.  The library never allocates, frees or retains caller memory and
+ *     keeps no state between calls; calls are reentrant.
+ *   - Execution: every call validates its arguments on the host, enqueues its kernels on
+ *     `stream` (0 = the null stream) and returns without synchronising.  Results are
+ *     visible to later work on the same stream.
+ *   - Errors: 0 (BITLINEAR_OK) or a negative bitlinear_status.  Argument validation happens
+ *     before any HIP call, so an invalid call enqueues nothing.  BITLINEAR_ERR_HIP reports a
+ *     launch error from the HIP runtime (hipGetLastError after the launch).
+ *   - Layouts: row-major.  W is [N, K] (out_features x in_features, the nn.Linear
+ *     convention [P3 §4.2]); x is [M, K] (M tokens); y = x W^T is [M, N].
+ *   - Packed ternary weights: uint8 [N, K/4].  Weight W[n, k] is stored as the 2-bit code
+ *     W_hat + 1 (00 -> -1, 01 -> 0, 10 -> +1; 11 is never written) [P3 §5.3], at bits
+ *     2*(k%4) .. 2*(k%4)+1 of byte n*K/4 + k/4.  K must be a multiple of 4.
+ *   - Non-finite inputs (NaN, Inf) give unspecified codes and outputs.
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BITLINEAR_ABI_VERSION 1
+
+/* Largest K for which |acc| <= 127*K still fits int32. */
+#define BITLINEAR_MAX_K 16909320
+
+typedef enum bitlinear_status {
+    BITLINEAR_OK = 0,
+    BITLINEAR_ERR_INVALID_ARG = -1, /* null required pointer, size <= 0 */
+    BITLINEAR_ERR_SHAPE = -2,       /* K % 4 != 0, K > BITLINEAR_MAX_K, size overflow */
+    BITLINEAR_ERR_ALIGNMENT = -3,   /* a pointer lacks the alignment the call documents */
+    BITLINEAR_ERR_WORKSPACE = -4,   /* workspace null or smaller than required */
+    BITLINEAR_ERR_HIP = -5          /* the HIP runtime reported an error at launch */
+} bitlinear_status;
+
+/* Returns BITLINEAR_ABI_VERSION of the built library. */
+int bitlinear_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* bitlinear_status_string(int status);
+
+/* The hipError_t of the last BITLINEAR_ERR_HIP returned on the calling thread (0 if none). */
+int bitlinear_last_hip_error(void);
+
+/*
+ * Bytes of device workspace bitlinear_quantize_weights needs for an [N, K] tensor:
+ * N fp64 row partial sums (0 for invalid sizes).
+ */
+size_t bitlinear_quantize_weights_workspace_size(int64_t N, int64_t K);
+
+/*
+ * Absmean ternary weight quantization with one scale per tensor [P3 §2.3, §4.1]:
+ *     alpha = mean(|W|),  W_hat = clip(round(W / alpha), -1, 1),  packed 2 bits/weight.
+ * |W| is summed in fp64 (fixed order: per-row partials, then a fixed tree over rows) and
+ * alpha is rounded to fp32 once; W / alpha is an IEEE fp32 division; round() is
+ * round-half-to-even.  An all-zero W gives alpha = 0 and every code 0 (weight 0).
+ *
+ *   W          [N, K] fp32, 16-byte aligned.                                (in)
+ *   W_packed   [N, K/4] uint8 in the packed layout above, 4-byte aligned.   (out)
+ *   alpha      [1] fp32.                                                    (out)
+ *   workspace  >= bitlinear_quantize_weights_workspace_size(N, K) bytes,
+ *              8-byte aligned; scratch, contents undefined on return.
+ * Errors: INVALID_ARG (null pointer, N or K <= 0), SHAPE (K % 4, K too large, N*K
+ * overflow), ALIGNMENT, WORKSPACE, HIP.
+ */
+int bitlinear_quantize_weights(const float* W, int64_t N, int64_t K, uint8_t* W_packed,
+                               float* alpha, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/*
+ * Per-output-row variant [P2 §3.1, §4.2]: alpha_rows[n] = mean_k |W[n, k]| (fp64 sum of
+ * the row, one fp32 rounding); row n is ternarized with alpha_rows[n].  Needs no workspace.
+ *   alpha_rows [N] fp32 (out).  Other arguments and errors as bitlinear_quantize_weights.
+ */
+int bitlinear_quantize_weights_rows(const float* W, int64_t N, int64_t K, uint8_t* W_packed,
+                                    float* alpha_rows, hipStream_t stream);
+
+/*
+ * Per-token absmax int8 activation quantization [P3 §2.4, §4.1]:
+ *     beta[m] = max_k |x[m, k]| + 1e-8 (fp32 add, as the page's code guards the division),
+ *     x_q[m, k] = clip(round(fp32(127 * x[m, k]) / beta[m]), -127, 127),
+ * with an IEEE fp32 division and round-half-to-even.  An all-zero token gives
+ * beta = 1e-8 and x_q = 0.
+ *
+ *   x     [M, K] fp32.       (in)     x_q  [M, K] int8.   (out)
+ *   beta  [M] fp32.          (out)
+ * Any K >= 1 is accepted; K % 4 == 0 with 16-byte aligned x and 4-byte aligned x_q takes
+ * the vector path.  Errors: INVALID_ARG, SHAPE (M*K overflow), HIP.
+ */
+int bitlinear_quantize_act(const float* x, int64_t M, int64_t K, int8_t* x_q, float* beta,
+                           hipStream_t stream);
+
+/*
+ * Ternary x int8 matmul with the dequantization epilogue [P3 §2.4, §2.5, §3.2; P2 §3.3]:
+ *     acc[m, n] = sum_k x_q[m, k] * W_hat[n, k]
+ *               = sum_{W_hat=+1} x_q - sum_{W_hat=-1} x_q      (int32, exact)
+ *     y[m, n]   = fp32(acc[m, n]) * fp32(alpha * beta[m] / 127)  (+ bias[n])
+ * where alpha*beta/127 is evaluated in fp64 and rounded to fp32 once, the product is one
+ * fp32 rounding and the bias a separate fp32 addition.
+ *
+ *   x_q       [M, K] int8 (from bitlinear_quantize_act).   (in)
+ *   beta      [M] fp32.                                     (in)
+ *   W_packed  [N, K/4] uint8, packed layout above.          (in)
+ *   alpha     [1] fp32 (from bitlinear_quantize_weights).   (in)
+ *   bias      [N] fp32 or NULL.                             (in)
+ *   y         [M, N] fp32.                                  (out)
+ *   acc       [M, N] int32 or NULL; when given, receives the exact integer sums.  (out)
+ * The kernel is chosen by shape: M <= 4 runs a VALU GEMV (dot4 on unpacked codes), larger M
+ * an int8 MFMA GEMM that unpacks the ternary tiles on chip.  Both fast paths need
+ * K % 64 == 0 and 16-byte aligned x_q and W_packed; other inputs run a generic kernel
+ * with identical results.
+ * Errors: INVALID_ARG, SHAPE (K % 4, K > BITLINEAR_MAX_K, size overflow), HIP.
+ */
+int bitlinear_forward(const int8_t* x_q, const float* beta, int64_t M, int64_t K,
+                      const uint8_t* W_packed, const float* alpha, int64_t N, const float* bias,
+                      float* y, int32_t* acc, hipStream_t stream);
+
+/*
+ * bitlinear_forward with one alpha per output row [P2 §3.1]: column n of y uses
+ * alpha_rows[n] ([N] fp32, from bitlinear_quantize_weights_rows).  Same contract otherwise.
+ */
+int bitlinear_forward_rows(const int8_t* x_q, const float* beta, int64_t M, int64_t K,
+                           const uint8_t* W_packed, const float* alpha_rows, int64_t N,
+                           const float* bias, float* y, int32_t* acc, hipStream_t stream);
+
+/*
+ * Name of the kernel bitlinear_forward launches for these arguments ("gemv_dot4",
+ * "gemm_mfma_i8", "generic"); a static string, for profiling and reports.
+ */
+const char* bitlinear_forward_kernel(int64_t M, int64_t K, int64_t N, const int8_t* x_q,
+                                     const uint8_t* W_packed);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITLINEAR_H */

@@ -1,0 +1,133 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports every symbol
+include/bitlinear.h declares, and rejects invalid arguments before any HIP call.
+
+Every call below is invalid on purpose, so nothing is ever enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+
+
+@pytest.fixture(scope="module")
+def bl():
+    pkg = os.path.join(ROOT, "bitlinear_matmul_absmean_amd", "libbitlinear.so")
+    if not os.path.exists(pkg):
+        from bitlinear_matmul_absmean_amd import build as b
+        b.build()
+    import bitlinear_matmul_absmean_amd as m
+    return m
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bitlinear_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_symbols_are_exported(bl):
+    names = _declared()
+    assert "bitlinear_forward" in names and "bitlinear_quantize_act" in names
+    lib = ctypes.CDLL(bl.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in bitlinear.h but not exported"
+    # and the binding knows each of them
+    assert set(names) <= set(bl.SIGNATURES)
+
+
+def test_abi_version_and_status_strings(bl):
+    assert bl.abi_version() == 1
+    for st in (0, -1, -2, -3, -4, -5):
+        s = bl.lib.bitlinear_status_string(st).decode()
+        assert s and s != "unknown status"
+    assert bl.lib.bitlinear_status_string(-99).decode() == "unknown status"
+    assert bl.lib.bitlinear_last_hip_error() == 0
+
+
+def test_workspace_size(bl):
+    assert bl.lib.bitlinear_quantize_weights_workspace_size(4096, 11008) == 4096 * 8
+    assert bl.lib.bitlinear_quantize_weights_workspace_size(0, 16) == 0
+    assert bl.lib.bitlinear_quantize_weights_workspace_size(4, -1) == 0
+
+
+A = 4096  # a fake, 4096-aligned "device address"; never dereferenced (calls are invalid)
+
+
+def test_quantize_weights_validation(bl):
+    f = bl.lib.bitlinear_quantize_weights
+    ws = 1 << 20
+    assert f(None, 4, 8, A, A, A, ws, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert f(A, 4, 8, None, A, A, ws, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert f(A, 4, 8, A, None, A, ws, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert f(A, 0, 8, A, A, A, ws, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert f(A, 4, -8, A, A, A, ws, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert f(A, 4, 6, A, A, A, ws, None) == bl.BITLINEAR_ERR_SHAPE
+    assert f(A, 4, bl.BITLINEAR_MAX_K + 4, A, A, A, ws, None) == bl.BITLINEAR_ERR_SHAPE
+    assert f(A, 1 << 62, 1 << 20, A, A, A, ws, None) == bl.BITLINEAR_ERR_SHAPE
+    assert f(A + 4, 4, 8, A, A, A, ws, None) == bl.BITLINEAR_ERR_ALIGNMENT
+    assert f(A, 4, 8, A + 2, A, A, ws, None) == bl.BITLINEAR_ERR_ALIGNMENT
+    assert f(A, 4, 8, A, A, None, ws, None) == bl.BITLINEAR_ERR_WORKSPACE
+    assert f(A, 4, 8, A, A, A, 31, None) == bl.BITLINEAR_ERR_WORKSPACE
+    assert f(A, 4, 8, A, A, A + 4, ws, None) == bl.BITLINEAR_ERR_ALIGNMENT
+
+
+def test_quantize_weights_rows_validation(bl):
+    f = bl.lib.bitlinear_quantize_weights_rows
+    assert f(None, 4, 8, A, A, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert f(A, 4, 8, A, None, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert f(A, 4, 10, A, A, None) == bl.BITLINEAR_ERR_SHAPE
+    assert f(A + 8, 4, 8, A, A, None) == bl.BITLINEAR_ERR_ALIGNMENT
+
+
+def test_quantize_act_validation(bl):
+    f = bl.lib.bitlinear_quantize_act
+    assert f(None, 1, 8, A, A, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert f(A, 1, 8, None, A, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert f(A, 1, 8, A, None, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert f(A, 0, 8, A, A, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert f(A, 1, 0, A, A, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert f(A, 1 << 40, 1 << 30, A, A, None) == bl.BITLINEAR_ERR_SHAPE
+
+
+@pytest.mark.parametrize("name", ["bitlinear_forward", "bitlinear_forward_rows"])
+def test_forward_validation(bl, name):
+    f = getattr(bl.lib, name)
+    ok = dict(xq=A, beta=A, M=1, K=64, wp=A, alpha=A, N=8, bias=None, y=A, acc=None, s=None)
+
+    def call(**kw):
+        d = dict(ok)
+        d.update(kw)
+        return f(d["xq"], d["beta"], d["M"], d["K"], d["wp"], d["alpha"], d["N"], d["bias"], d["y"],
+                 d["acc"], d["s"])
+
+    for k in ("xq", "beta", "wp", "alpha", "y"):
+        assert call(**{k: None}) == bl.BITLINEAR_ERR_INVALID_ARG
+    for k in ("M", "K", "N"):
+        assert call(**{k: 0}) == bl.BITLINEAR_ERR_INVALID_ARG
+        assert call(**{k: -4}) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert call(K=66) == bl.BITLINEAR_ERR_SHAPE
+    assert call(K=bl.BITLINEAR_MAX_K + 4) == bl.BITLINEAR_ERR_SHAPE
+    assert call(M=1 << 40, K=1 << 24 - 4) == bl.BITLINEAR_ERR_SHAPE
+    assert call(N=1 << 33) == bl.BITLINEAR_ERR_SHAPE
+
+
+def test_kernel_selection(bl):
+    sel = bl.lib.bitlinear_forward_kernel
+    assert sel(1, 4096, 4096, A, A).decode() == "gemv_dot4"
+    assert sel(4, 4096, 4096, A, A).decode() == "gemv_dot4"
+    assert sel(5, 4096, 4096, A, A).decode() == "gemm_mfma_i8"
+    assert sel(2048, 4096, 11008, A, A).decode() == "gemm_mfma_i8"
+    assert sel(1, 4100, 4096, A, A).decode() == "generic"        # K % 64 != 0
+    assert sel(1, 4096, 4096, A + 4, A).decode() == "generic"    # unaligned x_q
+    assert sel(64, 4096, 4096, A, A + 8).decode() == "generic"   # unaligned W_packed
+
+
+def test_binding_has_no_host_fallback():
+    src = open(os.path.join(ROOT, "bitlinear_matmul_absmean_amd", "__init__.py")).read()
+    assert "import oracle" not in src and "from oracle" not in src
+    for f in os.listdir(os.path.join(ROOT, "bitlinear_matmul_absmean_amd", "csrc")):
+        text = open(os.path.join(ROOT, "bitlinear_matmul_absmean_amd", "csrc", f)).read()
+        assert "oracle" not in text.lower(), f

@@ -1,0 +1,283 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element by element.
+
+Bar: packed bytes, x_q, beta and int32 acc bit-exact; alpha within 1e-6 relative (bit-exact
+expected) with zero code flips; y within 1e-5 relative (bit-exact expected).  Shapes span
+several tiles with ragged tails; the full-size workloads are checked on sampled output
+rows in the launch configuration the benchmark times.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bitlinear_matmul_absmean_amd as bl
+    return torch, bl
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _to(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _rel_ok(y, ref, tol=1e-5):
+    y = y.astype(np.float64)
+    ref = ref.astype(np.float64)
+    return np.all(np.abs(y - ref) <= tol * np.abs(ref))
+
+
+# ------------------------------------------------------------------ activation quantization
+ACT_CASES = [(1, 1024), (1, 4096), (1, 11008), (3, 28672), (64, 4096), (17, 1000), (2, 6), (5, 4100)]
+
+
+@pytest.mark.parametrize("m,k", ACT_CASES)
+def test_quantize_act_parity(dev, m, k):
+    torch, bl = dev
+    _say(f"quantize_act M={m} K={k}")
+    x = workloads.activations_with_outliers(4, m, k)
+    xq_o, beta_o = oracle.quantize_act(x)
+    xq, beta = bl.bitlinear_quantize_act(_to(torch, x))
+    torch.cuda.synchronize()
+    assert np.array_equal(beta.cpu().numpy().view(np.uint32), beta_o.view(np.uint32))
+    assert np.array_equal(xq.cpu().numpy(), xq_o)
+
+
+def test_quantize_act_prefill_full_size(dev):
+    torch, bl = dev
+    _say("quantize_act prefill M=2048 K=4096 with outliers")
+    x = workloads.activations_with_outliers(4, 2048, 4096)
+    xq_o, beta_o = oracle.quantize_act(x)
+    xq, beta = bl.bitlinear_quantize_act(_to(torch, x))
+    torch.cuda.synchronize()
+    assert np.array_equal(beta.cpu().numpy(), beta_o)
+    assert np.array_equal(xq.cpu().numpy(), xq_o)
+
+
+def test_quantize_act_ties_and_zero_rows(dev):
+    torch, bl = dev
+    x = np.zeros((3, 8), np.float32)
+    x[0, :6] = [127.0, 0.5, 1.5, -2.5, 2.5, -127.0]
+    x[2] = np.linspace(-3, 3, 8, dtype=np.float32)
+    xq_o, beta_o = oracle.quantize_act(x)
+    xq, beta = bl.bitlinear_quantize_act(_to(torch, x))
+    torch.cuda.synchronize()
+    assert np.array_equal(beta.cpu().numpy(), beta_o)
+    assert np.array_equal(xq.cpu().numpy(), xq_o)
+    assert xq.cpu().numpy()[0, :6].tolist() == [127, 0, 2, -2, 2, -127]
+
+
+# ------------------------------------------------------------------ weight quantization
+W_CASES = [(1024, 1024), (4096, 4096), (11008, 4096), (4096, 11008), (1000, 1028), (3, 4), (7, 12), (65, 64)]
+
+
+def _flips(w, alpha_gpu, alpha_o, packed_gpu, packed_o, k):
+    """Count code mismatches and those that sit within 2 ulp of a rounding boundary."""
+    cg = oracle.unpack(packed_gpu, k)
+    co = oracle.unpack(packed_o, k)
+    bad = np.argwhere(cg != co)
+    boundary = 0
+    for n, j in bad[:1000]:
+        q = np.float32(w[n, j]) / np.float32(alpha_o)
+        frac = abs(abs(float(q)) - 0.5)
+        if frac <= 2 * np.spacing(np.float32(0.5)) or abs(abs(float(q)) - 1.5) <= 2 * np.spacing(np.float32(1.5)):
+            boundary += 1
+    return len(bad), boundary
+
+
+@pytest.mark.parametrize("n,k", W_CASES)
+def test_quantize_weights_parity(dev, n, k):
+    torch, bl = dev
+    _say(f"quantize_weights N={n} K={k}")
+    w = workloads.weights(2, n, k)
+    _, packed_o, alpha_o = oracle.quantize_weights(w)
+    packed, alpha = bl.bitlinear_quantize_weights(_to(torch, w))
+    torch.cuda.synchronize()
+    a = float(alpha.cpu().numpy()[0])
+    assert abs(a - float(alpha_o)) <= 1e-6 * abs(float(alpha_o))
+    pg = packed.cpu().numpy()
+    flips, boundary = _flips(w, a, alpha_o, pg, packed_o, k)
+    assert flips == 0 and boundary == 0, (flips, boundary)
+    assert np.array_equal(pg, packed_o)
+    assert np.float32(a).view(np.uint32) == np.float32(alpha_o).view(np.uint32)
+
+
+def test_quantize_weights_special_cases(dev):
+    torch, bl = dev
+    cases = [np.array([[0.9, -0.3, 0.05, -1.2]], np.float32),           # worked example
+             np.array([[3.0, 0.5, -0.5, 0.0]], np.float32),             # ties at .5
+             np.zeros((5, 8), np.float32),                              # alpha = 0
+             np.full((4, 16), -0.02, np.float32)]                       # constant magnitude
+    for w in cases:
+        n, k = w.shape
+        _, packed_o, alpha_o = oracle.quantize_weights(w)
+        packed, alpha = bl.bitlinear_quantize_weights(_to(torch, w))
+        torch.cuda.synchronize()
+        assert np.array_equal(packed.cpu().numpy(), packed_o), w
+        assert alpha.cpu().numpy()[0] == alpha_o
+    assert packed_o is not None
+
+
+@pytest.mark.parametrize("n,k", [(1024, 1024), (11008, 4096), (33, 68)])
+def test_quantize_weights_rows_parity(dev, n, k):
+    torch, bl = dev
+    w = workloads.weights(2, n, k, index=1)
+    ar_o = oracle.absmean_rows(w)
+    packed_o = oracle.pack(oracle.ternarize_rows(w, ar_o))
+    packed, ar = bl.bitlinear_quantize_weights_rows(_to(torch, w))
+    torch.cuda.synchronize()
+    assert np.array_equal(ar.cpu().numpy(), ar_o)
+    assert np.array_equal(packed.cpu().numpy(), packed_o)
+
+
+# ------------------------------------------------------------------ forward
+def _random_operands(m, k, n, seed):
+    rs = np.random.default_rng(seed)
+    xq = rs.integers(-127, 128, size=(m, k)).astype(np.int8)
+    codes = rs.choice(np.array([-1, 0, 1], np.int8), size=(n, k), p=[0.345, 0.31, 0.345])
+    beta = rs.uniform(2.0, 60.0, size=m).astype(np.float32)
+    alpha = np.float32(rs.uniform(0.015, 0.017))
+    return xq, codes, oracle.pack(codes), beta, alpha
+
+
+FWD_CASES = [
+    (1, 64, 1), (1, 1024, 1024), (1, 4096, 100), (2, 4096, 257), (3, 11008, 130), (4, 128, 4096),
+    (5, 64, 7), (8, 4096, 300), (16, 1024, 64), (17, 4096, 129), (33, 192, 65), (64, 11008, 70),
+    (65, 1024, 130), (128, 256, 256), (130, 4096, 200), (300, 128, 257),
+    (1, 100, 33), (6, 4100, 65), (70, 12, 9),      # K % 64 != 0: generic kernel
+]
+
+
+@pytest.mark.parametrize("m,k,n", FWD_CASES)
+def test_forward_parity(dev, m, k, n):
+    torch, bl = dev
+    kern = bl.bitlinear_forward_kernel(m, k, n)
+    _say(f"forward M={m} K={k} N={n} kernel={kern}")
+    xq, codes, packed, beta, alpha = _random_operands(m, k, n, seed=m * 7919 + k * 31 + n)
+    acc_o = oracle.ternary_matmul(xq, codes)
+    y_o = oracle.dequant(acc_o, beta, alpha)
+    y, acc = bl.bitlinear_forward(_to(torch, xq), _to(torch, beta), _to(torch, packed),
+                                  _to(torch, np.array([alpha], np.float32)), acc=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), acc_o)
+    yg = y.cpu().numpy()
+    assert _rel_ok(yg, y_o)
+    assert np.array_equal(yg, y_o)
+
+
+@pytest.mark.parametrize("m,k,n", [(1, 4096, 64), (12, 1024, 96), (200, 128, 70)])
+def test_forward_bias_and_rows(dev, m, k, n):
+    torch, bl = dev
+    xq, codes, packed, beta, alpha = _random_operands(m, k, n, seed=5)
+    rs = np.random.default_rng(9)
+    bias = rs.standard_normal(n).astype(np.float32)
+    ar = rs.uniform(0.01, 0.02, size=n).astype(np.float32)
+    acc_o = oracle.ternary_matmul(xq, codes)
+    y_o = oracle.dequant(acc_o, beta, alpha, bias=bias)
+    yr_o = oracle.dequant(acc_o, beta, alpha_rows=ar, bias=bias)
+    args = (_to(torch, xq), _to(torch, beta), _to(torch, packed))
+    y = bl.bitlinear_forward(*args, _to(torch, np.array([alpha], np.float32)), bias=_to(torch, bias))
+    yr = bl.bitlinear_forward_rows(*args, _to(torch, ar), bias=_to(torch, bias))
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy(), y_o)
+    assert np.array_equal(yr.cpu().numpy(), yr_o)
+
+
+def test_forward_extreme_values(dev):
+    """|acc| = 127*K at the largest workload K, and every weight pattern."""
+    torch, bl = dev
+    k = 28672
+    xq = np.full((5, k), 127, np.int8)
+    xq[1] = -127
+    xq[2, ::2] = -127
+    codes = np.ones((6, k), np.int8)
+    codes[1] = -1
+    codes[2] = 0
+    codes[3, 1::2] = -1
+    codes[4, ::3] = 0
+    codes[5] = np.random.default_rng(1).integers(-1, 2, size=k)
+    beta = np.full(5, 127.0, np.float32)
+    alpha = np.float32(1.0)
+    acc_o = oracle.ternary_matmul(xq, codes)
+    for m in (1, 4, 5):
+        y, acc = bl.bitlinear_forward(_to(torch, xq[:m]), _to(torch, beta[:m]), _to(torch, oracle.pack(codes)),
+                                      _to(torch, np.array([alpha], np.float32)), acc=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(acc.cpu().numpy(), acc_o[:m])
+    assert acc_o[0, 0] == 127 * k
+
+
+def test_end_to_end_single_bitlinear(dev):
+    """Workload 1: x [1, 1024], W [1024, 1024]: quantize_weights -> quantize_act -> forward."""
+    torch, bl = dev
+    w = workloads.weights(1, 1024, 1024)
+    x = workloads.activations(1, 1, 1024)
+    r = oracle.bitlinear(x, w)
+    packed, alpha = bl.bitlinear_quantize_weights(_to(torch, w))
+    xq, beta = bl.bitlinear_quantize_act(_to(torch, x))
+    y, acc = bl.bitlinear_forward(xq, beta, packed, alpha, acc=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(packed.cpu().numpy(), r["packed"])
+    assert np.array_equal(xq.cpu().numpy(), r["xq"])
+    assert np.array_equal(acc.cpu().numpy(), r["acc"])
+    assert np.array_equal(y.cpu().numpy(), r["y"])
+
+
+# ------------------------------------------------------------------ full-size workloads, sampled
+FULL = [(1, 4096, 4096), (1, 4096, 11008), (1, 11008, 4096),
+        (8, 4096, 11008), (16, 11008, 4096), (64, 4096, 11008), (64, 11008, 4096),
+        (2048, 4096, 4096), (2048, 4096, 11008)]
+
+
+@pytest.mark.parametrize("m,k,n", FULL)
+def test_full_size_sampled(dev, m, k, n):
+    torch, bl = dev
+    _say(f"full-size M={m} K={k} N={n}")
+    w = workloads.weights(3, n, k)
+    x = workloads.activations_with_outliers(3, m, k) if m >= 512 else workloads.activations(3, m, k)
+    packed, alpha = bl.bitlinear_quantize_weights(_to(torch, w))
+    xq, beta = bl.bitlinear_quantize_act(_to(torch, x))
+    y, acc = bl.bitlinear_forward(xq, beta, packed, alpha, acc=True)
+    torch.cuda.synchronize()
+    codes_o, packed_o, alpha_o = oracle.quantize_weights(w)
+    xq_o, beta_o = oracle.quantize_act(x)
+    assert alpha.cpu().numpy()[0] == alpha_o
+    assert np.array_equal(packed.cpu().numpy(), packed_o)
+    assert np.array_equal(xq.cpu().numpy(), xq_o)
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(n - 8, n),
+                                     np.random.default_rng(n + m).choice(n, 48, replace=False)]))
+    acc_g = acc.cpu().numpy()
+    y_g = y.cpu().numpy()
+    for r in rows:
+        a_o = oracle.ternary_matmul(xq_o, codes_o[r:r + 1])
+        assert np.array_equal(acc_g[:, r:r + 1], a_o), r
+        assert np.array_equal(y_g[:, r:r + 1], oracle.dequant(a_o, beta_o, alpha_o))
+
+
+def test_repeatable_bitwise(dev):
+    torch, bl = dev
+    w = workloads.weights(3, 4096, 4096)
+    x = workloads.activations(3, 64, 4096)
+    wt, xt = _to(torch, w), _to(torch, x)
+    outs = []
+    for _ in range(3):
+        packed, alpha = bl.bitlinear_quantize_weights(wt)
+        xq, beta = bl.bitlinear_quantize_act(xt)
+        outs.append([t.cpu().numpy().copy() for t in (packed, alpha, xq, beta,
+                                                      bl.bitlinear_forward(xq, beta, packed, alpha))])
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert np.array_equal(a, b)

@@ -119,3 +119,27 @@ def stream_alpha(layer: int, proj: int) -> np.float32:
 def stream_activation(layer: int, proj: int, k: int) -> np.ndarray:
     """x [1, K] ~ N(0, 1) for one (layer, projection) of the 70B-class stream."""
     return activations(5, 1, k, layer * 16 + proj)
+
+
+_synth = None
+
+
+def device_stream_packed(out, layer: int, proj: int, stream=None):
+    """Fill the uint8 device tensor ``out`` ([N, K/4]) with the packed codes of one
+    70B-class projection, on the device (libsynth.so, same definition as above)."""
+    global _synth
+    import ctypes
+    import os
+
+    import torch
+    if _synth is None:
+        path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsynth.so")
+        lib = ctypes.CDLL(path)
+        lib.synth_ternary_packed.restype = ctypes.c_int
+        lib.synth_ternary_packed.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p]
+        _synth = lib
+    s = torch.cuda.current_stream() if stream is None else stream
+    rc = _synth.synth_ternary_packed(out.data_ptr(), out.numel(), stream_state(layer, proj), s.cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"synth_ternary_packed failed: hipError {rc}")
+    return out
