@@ -1,0 +1,286 @@
+"""Benchmark of the BitLinear W1.58A8 hot path on one MI355X.
+
+Workload (the headline): 7B-class decode, M = 1 token, the three projection shapes
+(K, N) = (4096, 4096), (4096, 11008), (11008, 4096).  One step = for each shape,
+bitlinear_quantize_act (x fp32 -> x_q, beta) then bitlinear_forward (x_q -> y fp32), i.e. every
+per-token step of the path; the weights are quantized once beforehand (the pages cache them)
+and bitlinear_quantize_weights is timed separately.  Weights rotate through a pool of distinct
+copies (> 1 GiB) so that no step finds its weights in the 256 MiB Infinity Cache or the L2.
+
+The K timed steps are captured into one HIP graph (decode steps are replayed, not re-issued
+from Python) and timed with HIP events on the capture stream, bracketed by device syncs.
+`value` = packed weight bytes streamed per step * K / elapsed (GB/s).
+
+Extra objects on the same JSON line: `roofline` for the dominant kernel (the decode GEMV on the
+(4096, 11008) shape, timed in isolation the same way), `prefill` (M = 2048 int8-MFMA TOPS),
+`batched` (M = 8/16/64), `chain70b` (one decode step of the 70B-class stream) and
+`cpu_baseline` (the CPU oracle on a bounded sample of the same workload).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+INT8_MFMA_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA, 5.0 POPS
+METRIC = "decode GEMV weight GB/s (% HBM peak); prefill int8 TOPS (% MFMA peak)"
+DECODE_SHAPES = [(4096, 4096), (4096, 11008), (11008, 4096)]   # (K, N)
+POOL_BYTES = 1 << 31
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _graph_time(torch, fn, reps: int, warm_fn=None):
+    """Capture `fn(i)` for i < reps into one graph, replay once; return ms per rep."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(min(reps, 3)):
+            (warm_fn or fn)(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(reps):
+            fn(i)
+    g.replay()                         # untimed replay (first-launch costs)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps, g
+
+
+def decode_setup(torch, bl, workloads, dev):
+    """Quantize the three decode weights once, then fill rotation pools of packed copies."""
+    per_step = sum(n * k // 4 for k, n in DECODE_SHAPES)
+    copies = max(2, POOL_BYTES // per_step)
+    shapes = []
+    for idx, (k, n) in enumerate(DECODE_SHAPES):
+        w = torch.from_numpy(workloads.weights(2, n, k, index=idx)).to(dev)
+        packed, alpha = bl.bitlinear_quantize_weights(w)
+        del w
+        pool = [packed] + [packed.clone() for _ in range(copies - 1)]
+        x = [torch.from_numpy(workloads.activations(2, 1, k, index=100 * idx + j)).to(dev) for j in range(8)]
+        xq = torch.empty((1, k), dtype=torch.int8, device=dev)
+        beta = torch.empty(1, dtype=torch.float32, device=dev)
+        y = torch.empty((1, n), dtype=torch.float32, device=dev)
+        shapes.append(dict(k=k, n=n, pool=pool, alpha=alpha, x=x, xq=xq, beta=beta, y=y))
+    torch.cuda.synchronize()
+    return shapes, per_step, copies
+
+
+def decode_step(bl, shapes, copies, i):
+    for sh in shapes:
+        bl.bitlinear_quantize_act(sh["x"][i % 8], sh["xq"], sh["beta"])
+        bl.bitlinear_forward(sh["xq"], sh["beta"], sh["pool"][i % copies], sh["alpha"], y=sh["y"])
+
+
+def roofline_gemv(torch, bl, sh, copies, reps=480):
+    """Dominant kernel: the decode GEMV on (K, N) = (4096, 11008), back to back in a graph."""
+    k, n = sh["k"], sh["n"]
+    bl.bitlinear_quantize_act(sh["x"][0], sh["xq"], sh["beta"])
+    ms, _ = _graph_time(torch, lambda i: bl.bitlinear_forward(sh["xq"], sh["beta"], sh["pool"][i % copies],
+                                                              sh["alpha"], y=sh["y"]), reps)
+    # algorithmic bytes of one launch: packed weights + x_q + beta + alpha + y
+    alg = n * k // 4 + k + 4 + 4 + 4 * n
+    achieved = alg / (ms * 1e-3) / 1e9
+    return dict(kernel=bl.bitlinear_forward_kernel(1, k, n, sh["xq"], sh["pool"][0]), shape=dict(M=1, K=k, N=n),
+                bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None, us_per_launch=round(ms * 1e3, 3),
+                bytes_per_launch=alg)
+
+
+def prefill_bench(torch, bl, workloads, dev, k=4096, n=11008, m=2048, reps=20):
+    w = torch.from_numpy(workloads.weights(4, n, k)).to(dev)
+    packed, alpha = bl.bitlinear_quantize_weights(w)
+    del w
+    x = torch.from_numpy(workloads.activations_with_outliers(4, m, k)).to(dev)
+    xq, beta = bl.bitlinear_quantize_act(x)
+    y = torch.empty((m, n), dtype=torch.float32, device=dev)
+    ms, _ = _graph_time(torch, lambda i: bl.bitlinear_forward(xq, beta, packed, alpha, y=y), reps)
+    msq, _ = _graph_time(torch, lambda i: bl.bitlinear_quantize_act(x, xq, beta), reps)
+    tops = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+    return dict(shape=dict(M=m, K=k, N=n), kernel=bl.bitlinear_forward_kernel(m, k, n, xq, packed),
+                us=round(ms * 1e3, 2), tops=round(tops, 1), pct_mfma_peak=round(100 * tops / INT8_MFMA_PEAK_TOPS, 2),
+                quantize_act_us=round(msq * 1e3, 2),
+                end_to_end_tops=round(2.0 * m * n * k / ((ms + msq) * 1e-3) / 1e12, 1))
+
+
+def batched_bench(torch, bl, workloads, dev, reps=96):
+    out = []
+    for (k, n) in [(4096, 11008), (11008, 4096)]:
+        w = torch.from_numpy(workloads.weights(3, n, k)).to(dev)
+        packed, alpha = bl.bitlinear_quantize_weights(w)
+        del w
+        copies = max(2, (1 << 30) // (n * k // 4))
+        pool = [packed] + [packed.clone() for _ in range(copies - 1)]
+        for m in (8, 16, 64):
+            x = torch.from_numpy(workloads.activations(3, m, k)).to(dev)
+            xq, beta = bl.bitlinear_quantize_act(x)
+            y = torch.empty((m, n), dtype=torch.float32, device=dev)
+            ms, _ = _graph_time(torch, lambda i: bl.bitlinear_forward(xq, beta, pool[i % copies], alpha, y=y), reps)
+            gbs = n * k / 4 / (ms * 1e-3) / 1e9
+            out.append(dict(M=m, K=k, N=n, kernel=bl.bitlinear_forward_kernel(m, k, n, xq, packed),
+                            us=round(ms * 1e3, 2), weight_gbs=round(gbs, 1),
+                            pct_hbm=round(100 * gbs / HBM_PEAK_GBS, 2)))
+        del pool
+        torch.cuda.empty_cache()
+    return out
+
+
+def chain70b_bench(torch, bl, workloads, dev, layers=80, reps=3):
+    """One decode step of the 70B-class stream: 80 layers x 7 projections, each
+    quantize_act + forward, weights generated on the device (17.1 GB resident)."""
+    projs = []
+    total = 0
+    for layer in range(layers):
+        for p, (name, k, n) in enumerate(workloads.W5_PROJ):
+            wp = torch.empty((n, k // 4), dtype=torch.uint8, device=dev)
+            workloads.device_stream_packed(wp, layer, p)
+            total += wp.numel()
+            projs.append((k, n, wp, torch.tensor([workloads.stream_alpha(layer, p)], device=dev)))
+    xs = {k: torch.from_numpy(workloads.activations(5, 1, k)).to(dev) for k in (8192, 28672)}
+    xq = {k: torch.empty((1, k), dtype=torch.int8, device=dev) for k in (8192, 28672)}
+    beta = torch.empty(1, dtype=torch.float32, device=dev)
+    ys = {n: torch.empty((1, n), dtype=torch.float32, device=dev) for n in (1024, 8192, 28672)}
+    torch.cuda.synchronize()
+
+    def step(i):
+        for (k, n, wp, alpha) in projs:
+            bl.bitlinear_quantize_act(xs[k], xq[k], beta)
+            bl.bitlinear_forward(xq[k], beta, wp, alpha, y=ys[n])
+    ms, _ = _graph_time(torch, step, reps)
+    gbs = total / (ms * 1e-3) / 1e9
+    res = dict(layers=layers, weight_bytes=total, ms_per_step=round(ms, 3), weight_gbs=round(gbs, 1),
+               pct_hbm=round(100 * gbs / HBM_PEAK_GBS, 2), tokens_per_s=round(1e3 / ms, 1))
+    del projs
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(workloads, budget_s=12.0):
+    """The CPU oracle (as it stands) on a bounded sample of the decode workload: whole steps
+    (quantize_act + unpack + integer matmul + dequant for the three shapes), output rows
+    split over threads.  Returns weight GB/s like the GPU value."""
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(16, cores))
+    data = []
+    for idx, (k, n) in enumerate(DECODE_SHAPES):
+        w = workloads.weights(2, n, k, index=idx)
+        codes, packed, alpha = oracle.quantize_weights(w)
+        data.append((k, n, packed, alpha, workloads.activations(2, 1, k, index=100 * idx)))
+    per_step = sum(n * k // 4 for k, n in DECODE_SHAPES)
+    pool = ThreadPoolExecutor(cores)
+
+    def one_step():
+        for (k, n, packed, alpha, x) in data:
+            xq, beta = oracle.quantize_act(x)
+            acc = np.zeros((1, n), np.int32)
+            y = np.zeros((1, n), np.float32)
+            bounds = np.linspace(0, n, cores + 1).astype(int)
+
+            def part(t):
+                n0, n1 = bounds[t], bounds[t + 1]
+                if n1 <= n0:
+                    return
+                codes = oracle.unpack(packed[n0:n1], k)
+                acc[:, n0:n1] = oracle.ternary_matmul(xq, codes)
+                oracle.dequant(acc, beta, alpha, n0=n0, n1=n1, out=y)
+            list(pool.map(part, range(cores)))
+
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        one_step()
+        steps += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    pool.shutdown()
+    return dict(value=round(per_step * steps / dt / 1e9, 3), unit="GB/s", cores=cores, kind="oracle",
+                sample=f"{steps} whole decode steps (M=1; K,N = 4096x4096, 4096x11008, 11008x4096), "
+                       f"{dt:.1f} s wall, output rows split over {cores} threads")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extras", action="store_true", help="headline workload and roofline only")
+    ap.add_argument("--no-chain", action="store_true", help="skip the 70B-class chain")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (see DESIGN.md, sharding). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bitlinear_matmul_absmean_amd as bl
+    import workloads
+
+    dev = torch.device("cuda:0")
+    log(f"device {torch.cuda.get_device_name(0)}; building decode pools")
+    shapes, per_step, copies = decode_setup(torch, bl, workloads, dev)
+    log(f"pool: {copies} copies x {per_step} B")
+
+    # warmup (untimed), then exactly K steps in one graph
+    wms, _ = _graph_time(torch, lambda i: decode_step(bl, shapes, copies, i), max(1, args.warmup))
+    torch.cuda.synchronize()
+    ms_step, g = _graph_time(torch, lambda i: decode_step(bl, shapes, copies, i), args.steps)
+    value = per_step / (ms_step * 1e-3) / 1e9
+    log(f"decode step {ms_step * 1e3:.2f} us -> {value:.1f} GB/s")
+
+    roof = roofline_gemv(torch, bl, shapes[1], copies)
+    log(f"roofline {roof}")
+    extras = {}
+    if not args.no_extras:
+        extras["prefill"] = prefill_bench(torch, bl, workloads, dev)
+        log(f"prefill {extras['prefill']}")
+        extras["batched"] = batched_bench(torch, bl, workloads, dev)
+        log(f"batched {extras['batched']}")
+    del shapes
+    torch.cuda.empty_cache()
+    if not args.no_extras and not args.no_chain:
+        extras["chain70b"] = chain70b_bench(torch, bl, workloads, dev)
+        log(f"chain70b {extras['chain70b']}")
+    cpu = None if args.no_cpu else cpu_baseline(workloads)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "7B-class decode GEMV, M=1: quantize_act + forward on (K,N) = "
+                               "(4096,4096), (4096,11008), (11008,4096); W ~ N(0,0.02) ternarized, 2-bit packed; "
+                               "x ~ N(0,1)", "M": 1, "shapes_KN": DECODE_SHAPES,
+                   "weight_bytes_per_step": per_step, "rotation_copies": copies, "timing": "one HIP graph of K steps"},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    line.update(extras)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
