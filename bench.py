@@ -2,9 +2,10 @@
 
 Workload (the headline): 7B-class decode, M = 1 token, the three projection shapes
 (K, N) = (4096, 4096), (4096, 11008), (11008, 4096).  One step = for each shape,
-bitlinear_quantize_act (x fp32 -> x_q, beta) then bitlinear_forward (x_q -> y fp32), i.e. every
-per-token step of the path; the weights are quantized once beforehand (the pages cache them)
-and bitlinear_quantize_weights is timed separately.  Weights rotate through a pool of distinct
+bitlinear_forward_fused (x fp32 -> y fp32: activation quantization, ternary matmul, dequant in
+one kernel), i.e. every per-token step of the path; the weights are quantized once beforehand
+(the pages cache them).  The same step through the two-call ABI (bitlinear_quantize_act, then
+bitlinear_forward) is reported beside it.  Weights rotate through a pool of distinct
 copies (> 1 GiB) so that no step finds its weights in the 256 MiB Infinity Cache or the L2.
 
 The K timed steps are captured into one HIP graph (decode steps are replayed, not re-issued
@@ -83,24 +84,38 @@ def decode_setup(torch, bl, workloads, dev):
 
 
 def decode_step(bl, shapes, copies, i):
+    """One decode step: x fp32 -> y fp32 for each shape, one fused call each
+    (activation quantization, ternary matmul and dequantization in one kernel)."""
+    for sh in shapes:
+        bl.bitlinear_forward_fused(sh["x"][i % 8], sh["pool"][i % copies], sh["alpha"], y=sh["y"])
+
+
+def decode_step_two_call(bl, shapes, copies, i):
+    """The same step through the two-call ABI: quantize_act, then forward."""
     for sh in shapes:
         bl.bitlinear_quantize_act(sh["x"][i % 8], sh["xq"], sh["beta"])
         bl.bitlinear_forward(sh["xq"], sh["beta"], sh["pool"][i % copies], sh["alpha"], y=sh["y"])
 
 
 def roofline_gemv(torch, bl, sh, copies, reps=480):
-    """Dominant kernel: the decode GEMV on (K, N) = (4096, 11008), back to back in a graph."""
+    """Dominant kernel: the fused decode GEMV on (K, N) = (4096, 11008), back to back in a
+    graph on one stream, weights rotating through the pool."""
     k, n = sh["k"], sh["n"]
-    bl.bitlinear_quantize_act(sh["x"][0], sh["xq"], sh["beta"])
-    ms, _ = _graph_time(torch, lambda i: bl.bitlinear_forward(sh["xq"], sh["beta"], sh["pool"][i % copies],
-                                                              sh["alpha"], y=sh["y"]), reps)
-    # algorithmic bytes of one launch: packed weights + x_q + beta + alpha + y
-    alg = n * k // 4 + k + 4 + 4 + 4 * n
+    ms, _ = _graph_time(torch, lambda i: bl.bitlinear_forward_fused(sh["x"][i % 8], sh["pool"][i % copies],
+                                                                    sh["alpha"], y=sh["y"]), reps)
+    # algorithmic bytes of one launch: packed weights + x (fp32) + alpha + y (fp32)
+    alg = n * k // 4 + 4 * k + 4 + 4 * n
     achieved = alg / (ms * 1e-3) / 1e9
-    return dict(kernel=bl.bitlinear_forward_kernel(1, k, n, sh["xq"], sh["pool"][0]), shape=dict(M=1, K=k, N=n),
-                bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None, us_per_launch=round(ms * 1e3, 3),
-                bytes_per_launch=alg)
+    # the unfused forward kernel alone (x_q in), for reference
+    bl.bitlinear_quantize_act(sh["x"][0], sh["xq"], sh["beta"])
+    ms_f, _ = _graph_time(torch, lambda i: bl.bitlinear_forward(sh["xq"], sh["beta"], sh["pool"][i % copies],
+                                                                sh["alpha"], y=sh["y"]), reps)
+    return dict(kernel=bl.bitlinear_forward_fused_kernel(1, k, n, sh["x"][0], sh["pool"][0]),
+                shape=dict(M=1, K=k, N=n), bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
+                unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                us_per_launch=round(ms * 1e3, 3), bytes_per_launch=alg,
+                forward_only=dict(kernel="gemv_dot4", us_per_launch=round(ms_f * 1e3, 3),
+                                  gbs=round((n * k // 4 + k + 4 * n) / (ms_f * 1e-3) / 1e9, 1)))
 
 
 def prefill_bench(torch, bl, workloads, dev, k=4096, n=11008, m=2048, reps=20):
@@ -142,8 +157,9 @@ def batched_bench(torch, bl, workloads, dev, reps=96):
 
 
 def chain70b_bench(torch, bl, workloads, dev, layers=80, reps=3):
-    """One decode step of the 70B-class stream: 80 layers x 7 projections, each
-    quantize_act + forward, weights generated on the device (17.1 GB resident)."""
+    """One decode step of the 70B-class stream: 80 layers x 7 projections, one fused call
+    each (the two-call ABI reported beside it), weights generated on the device (17.1 GB
+    resident), one stream, in order."""
     projs = []
     total = 0
     for layer in range(layers):
@@ -160,12 +176,18 @@ def chain70b_bench(torch, bl, workloads, dev, layers=80, reps=3):
 
     def step(i):
         for (k, n, wp, alpha) in projs:
+            bl.bitlinear_forward_fused(xs[k], wp, alpha, y=ys[n])
+
+    def step_two_call(i):
+        for (k, n, wp, alpha) in projs:
             bl.bitlinear_quantize_act(xs[k], xq[k], beta)
             bl.bitlinear_forward(xq[k], beta, wp, alpha, y=ys[n])
     ms, _ = _graph_time(torch, step, reps)
+    ms2, _ = _graph_time(torch, step_two_call, reps)
     gbs = total / (ms * 1e-3) / 1e9
     res = dict(layers=layers, weight_bytes=total, ms_per_step=round(ms, 3), weight_gbs=round(gbs, 1),
-               pct_hbm=round(100 * gbs / HBM_PEAK_GBS, 2), tokens_per_s=round(1e3 / ms, 1))
+               pct_hbm=round(100 * gbs / HBM_PEAK_GBS, 2), tokens_per_s=round(1e3 / ms, 1),
+               two_call_ms_per_step=round(ms2, 3))
     del projs
     torch.cuda.empty_cache()
     return res
@@ -249,6 +271,8 @@ def main():
     ms_step, g = _graph_time(torch, lambda i: decode_step(bl, shapes, copies, i), args.steps)
     value = per_step / (ms_step * 1e-3) / 1e9
     log(f"decode step {ms_step * 1e3:.2f} us -> {value:.1f} GB/s")
+    ms_two, _ = _graph_time(torch, lambda i: decode_step_two_call(bl, shapes, copies, i), args.steps)
+    log(f"decode step, two-call ABI {ms_two * 1e3:.2f} us")
 
     roof = roofline_gemv(torch, bl, shapes[1], copies)
     log(f"roofline {roof}")
@@ -270,11 +294,13 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": "7B-class decode GEMV, M=1: quantize_act + forward on (K,N) = "
+        "config": {"workload": "7B-class decode GEMV, M=1: fused quantize_act + forward on (K,N) = "
                                "(4096,4096), (4096,11008), (11008,4096); W ~ N(0,0.02) ternarized, 2-bit packed; "
                                "x ~ N(0,1)", "M": 1, "shapes_KN": DECODE_SHAPES,
                    "weight_bytes_per_step": per_step, "rotation_copies": copies, "timing": "one HIP graph of K steps"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "decode_two_call": {"us_per_step": round(ms_two * 1e3, 2),
+                            "weight_gbs": round(per_step / (ms_two * 1e-3) / 1e9, 1)},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

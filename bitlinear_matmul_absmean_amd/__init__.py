@@ -37,6 +37,8 @@ SIGNATURES = {
     "bitlinear_forward": (_INT, [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P]),
     "bitlinear_forward_rows": (_INT, [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P]),
     "bitlinear_forward_kernel": (ctypes.c_char_p, [_I64, _I64, _I64, _P, _P]),
+    "bitlinear_forward_fused": (_INT, [_P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P, _P, _P]),
+    "bitlinear_forward_fused_kernel": (ctypes.c_char_p, [_I64, _I64, _I64, _P, _P, _P]),
 }
 
 
@@ -173,6 +175,37 @@ def bitlinear_forward_rows(x_q, beta, W_packed, alpha_rows, bias=None, y=None, a
     """bitlinear_forward with one alpha per output row."""
     return _forward(lib.bitlinear_forward_rows, "bitlinear_forward_rows", x_q, beta, W_packed,
                     alpha_rows, bias, y, acc, stream)
+
+
+def bitlinear_forward_fused(x, W_packed, alpha, bias=None, y=None, x_q=None, beta=None, acc=None,
+                            stream=None):
+    """y [M, N] from fp32 x [M, K] in one call (activation quantization + forward).
+    x_q / beta (tensors) receive the quantized activations if given; acc as bitlinear_forward.
+    Returns y, or (y, acc) when acc is requested."""
+    torch = _torch()
+    M, K = x.shape
+    N = W_packed.shape[0]
+    if W_packed.shape[1] * 4 != K:
+        raise ValueError("W_packed must be [N, K/4]")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    if acc is True:
+        acc = torch.empty((M, N), dtype=torch.int32, device=x.device)
+    acc_ptr = _dev(acc, torch.int32, "acc") if acc is not None and acc is not False else None
+    _check("bitlinear_forward_fused", lib.bitlinear_forward_fused(
+        _dev(x, torch.float32, "x"), M, K, _dev(W_packed, torch.uint8, "W_packed"),
+        _dev(alpha, torch.float32, "alpha"), N,
+        _dev(bias, torch.float32, "bias") if bias is not None else None, _dev(y, torch.float32, "y"),
+        _dev(x_q, torch.int8, "x_q") if x_q is not None else None,
+        _dev(beta, torch.float32, "beta") if beta is not None else None, acc_ptr, _stream(stream)))
+    return (y, acc) if acc_ptr is not None else y
+
+
+def bitlinear_forward_fused_kernel(M, K, N, x=None, W_packed=None, x_q=None) -> str:
+    xp = x.data_ptr() if x is not None else 256
+    wp = W_packed.data_ptr() if W_packed is not None else 256
+    qp = x_q.data_ptr() if x_q is not None else None
+    return lib.bitlinear_forward_fused_kernel(M, K, N, xp, wp, qp).decode()
 
 
 def bitlinear_forward_kernel(M, K, N, x_q=None, W_packed=None) -> str:

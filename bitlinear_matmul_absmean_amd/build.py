@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libbitlinear.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["api.hip", "quantize.hip", "gemv.hip", "gemm.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemv.hip", "decode.hip", "gemm.hip"]
 ARCH = os.environ.get("BITLINEAR_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -38,16 +38,24 @@ int check_forward(const int8_t* x_q, const float* beta, int64_t M, int64_t K, co
     return BITLINEAR_OK;
 }
 
-enum class Path { Gemv, Gemm, Generic };
+enum class Path { Gemv, Decode, Gemm, Generic };
 
+// M <= 4: VALU GEMV; up to 64 tokens: weight-streaming MFMA decode kernel; more: MFMA GEMM.
 Path choose_path(int64_t M, int64_t K, const int8_t* xq, const uint8_t* wp) {
     if (!fast_forward_ok(K, xq, wp)) return Path::Generic;
-    return M <= 4 ? Path::Gemv : Path::Gemm;
+    if (gemv_supports(M, K)) return Path::Gemv;
+    if (decode_mfma_supports(M, K)) return Path::Decode;
+    return Path::Gemm;
+}
+
+bool fused_fast_ok(int64_t M, int64_t K, const float* x, const uint8_t* wp, const int8_t* xq_out) {
+    return gemv_supports(M, K) && aligned(x, 16) && aligned(wp, 16) && (!xq_out || aligned(xq_out, 16));
 }
 
 int run_forward(const ForwardArgs& a, hipStream_t stream) {
     switch (choose_path(a.M, a.K, a.xq, a.wp)) {
         case Path::Gemv: return hip_status(launch_gemv_dot4(a, stream));
+        case Path::Decode: return hip_status(launch_decode_mfma(a, stream));
         case Path::Gemm: return hip_status(launch_gemm_mfma(a, stream));
         default: return hip_status(launch_forward_generic(a, stream));
     }
@@ -134,11 +142,36 @@ int bitlinear_forward_rows(const int8_t* x_q, const float* beta, int64_t M, int6
     return run_forward(a, stream);
 }
 
+int bitlinear_forward_fused(const float* x, int64_t M, int64_t K, const uint8_t* W_packed, const float* alpha,
+                            int64_t N, const float* bias, float* y, int8_t* x_q, float* beta, int32_t* acc,
+                            hipStream_t stream) {
+    if (!x) return BITLINEAR_ERR_INVALID_ARG;
+    int st = check_forward(reinterpret_cast<const int8_t*>(x), reinterpret_cast<const float*>(x), M, K, W_packed,
+                           alpha, N, y);
+    if (st) return st;
+    if (fused_fast_ok(M, K, x, W_packed, x_q)) {
+        ForwardArgs a{nullptr, nullptr, M, K, N, W_packed, alpha, false, bias, y, acc};
+        return hip_status(launch_gemv_fused(a, x, x_q, beta, stream));
+    }
+    // other shapes: the two-call path, which needs x_q and beta as its intermediate
+    if (!x_q || !beta) return BITLINEAR_ERR_INVALID_ARG;
+    st = bitlinear_quantize_act(x, M, K, x_q, beta, stream);
+    if (st) return st;
+    return bitlinear_forward(x_q, beta, M, K, W_packed, alpha, N, bias, y, acc, stream);
+}
+
+const char* bitlinear_forward_fused_kernel(int64_t M, int64_t K, int64_t N, const float* x, const uint8_t* W_packed,
+                                           const int8_t* x_q) {
+    (void)N;
+    return fused_fast_ok(M, K, x, W_packed, x_q) ? "gemv_fused" : "quantize_act+forward";
+}
+
 const char* bitlinear_forward_kernel(int64_t M, int64_t K, int64_t N, const int8_t* x_q,
                                      const uint8_t* W_packed) {
     (void)N;
     switch (choose_path(M, K, x_q, W_packed)) {
         case Path::Gemv: return "gemv_dot4";
+        case Path::Decode: return "decode_mfma_i8";
         case Path::Gemm: return "gemm_mfma_i8";
         default: return "generic";
     }

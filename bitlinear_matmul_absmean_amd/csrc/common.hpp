@@ -99,8 +99,12 @@ struct ForwardArgs {
     int32_t* acc;
 };
 
+bool gemv_supports(int64_t M, int64_t K);
 hipError_t launch_gemv_dot4(const ForwardArgs& a, hipStream_t s);
+hipError_t launch_gemv_fused(const ForwardArgs& a, const float* x, int8_t* xq_out, float* beta_out, hipStream_t s);
 hipError_t launch_gemm_mfma(const ForwardArgs& a, hipStream_t s);
+bool decode_mfma_supports(int64_t M, int64_t K);
+hipError_t launch_decode_mfma(const ForwardArgs& a, hipStream_t s);
 hipError_t launch_forward_generic(const ForwardArgs& a, hipStream_t s);
 
 }  // namespace bitlinear

@@ -2,55 +2,220 @@
 //
 // What is computed ([P2] nxmr.cn "1.58 位大模型" §3.3; [P3] chenxutan.com "1.58-bit 大模型极限量化实战"
 // §2.4-§2.5, §3.2): acc[m,n] = sum_{W=+1} x_q[m,k] - sum_{W=-1} x_q[m,k], then
-// y = fp32(acc) * fp32(alpha*beta[m]/127) (+ bias).
+// y = fp32(acc) * fp32(alpha*beta[m]/127) (+ bias).  The fused variant also performs the
+// per-token absmax quantization of x [P3 §2.4] inside the same launch.
 //
-// How: the weight stream is the only large operand, so each wave streams whole packed
-// rows with 16-byte loads (one wave load = 1 KiB of one row = 4096 weights) and keeps
-// several rows in flight.  A 16-byte load holds 64 codes c = W+1 in {0,1,2}; the four
-// masks (v >> 2i) & 0x03030303 turn each dword into four dwords of byte codes, and
-// v_dot4_i32_i8 adds c*x_q four weights at a time.  Because c - 1 = W, the per-row sum is
-// acc = sum c*x_q - sum x_q: a +1 weight adds x_q once, a 0 weight adds nothing and a -1
-// weight subtracts it -- the add/sub with zero skipping of the pages, four lanes of bytes
-// per instruction.  sum x_q is one per-token constant computed while staging x_q.
-//
-// x_q is staged once per workgroup in LDS, pre-transposed so that byte j of mask dword i
-// meets x_q[k] with k = 4j + i inside each 16-weight group, and laid out so that the 64
-// lanes of a wave read 1 KiB of consecutive LDS per ds_read_b128 (no bank conflicts).
+// Decode streams every weight once, so the kernel is built around the weight stream:
+//   * Each wave owns a contiguous range of rows and walks it R rows at a time with two
+//     register buffers: the 16-byte loads of the next R rows are in flight while the current
+//     R rows are reduced.  A wave load is 1 KiB of one packed row (4096 weights), fully
+//     coalesced; row bases are wave-uniform (scalar) so a load costs one VGPR offset.
+//   * Activations are staged once per workgroup into LDS after the first weight loads are
+//     issued, so their latency hides under the weight latency.
+//   * A 16-byte load holds 64 codes c = W+1 in {0,1,2}, four per byte (weight 4b+i at bits
+//     2i).  Fields i = 0,1,2 are isolated with one AND each (the byte then holds c * 4^i),
+//     field 3 with a shift and an AND; v_dot4_i32_i8 multiplies each by four x_q bytes into
+//     four accumulators, recombined as a0 + a1/4 + a2/16 + a3 (exact).  Because c - 1 = W,
+//     acc = sum c*x_q - sum x_q: a +1 weight adds x_q, a 0 weight adds nothing, a -1 weight
+//     subtracts it -- the add/sub with zero skipping, four bytes per instruction.
+//   * x_q sits in LDS transposed within every 16-byte group (byte j of field dword i holds
+//     x_q[k = 4j + i]) and ordered so that the 64 lanes of a wave read 1 KiB of consecutive
+//     LDS per ds_read_b128.  Wave reductions use DPP inside 16-lane rows and readlane
+//     across rows.
+//   * The fused variant quantizes x with the quotient fp32(127x)/beta formed as q = a*y,
+//     y = RN(1/beta), then q + (a - q*beta)*y with two FMAs: by Markstein's theorem (the
+//     reciprocal within half an ulp, the first quotient within one ulp, the remainder exact
+//     through the FMA) this is the correctly rounded IEEE quotient, bit for bit what a
+//     division gives, at a third of the instructions.
 #include "common.hpp"
 
 namespace bitlinear {
 
-template <int MT, int R>
-__global__ __launch_bounds__(256) void k_gemv_dot4(ForwardArgs a, int C, int CPL) {
-    extern __shared__ u32x4 xs[];          // [MT][CPL][4][64] units of 16 bytes
-    __shared__ int tsum[4][4];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t K = a.K, N = a.N, rowb = K >> 2;
+struct GemvArgs {
+    ForwardArgs f;        // f.xq / f.beta are inputs of the unfused kernel
+    const float* x;       // fused: fp32 activations [M, K]
+    int8_t* xq_out;       // fused: optional export of x_q [M, K]
+    float* beta_out;      // fused: optional export of beta [M]
+    int C;                // K / 64 (chunks of 64 weights per row)
+    int64_t rows_per_wave;
+};
 
-    // ---- stage x_q (transposed per 16-byte group) and per-token sum of x_q ----------
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) { return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false); }
+
+// Sum over each 16-lane row (every lane of the row ends with the row sum).
+__device__ __forceinline__ int row16_sum(int v) {
+    v += dpp_i<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp_i<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp_i<0x141>(v);   // row_half_mirror
+    v += dpp_i<0x140>(v);   // row_mirror
+    return v;
+}
+
+// Wave total, uniform (scalar) result.
+__device__ __forceinline__ int wave_total(int v) {
+    v = row16_sum(v);
+    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+           __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
+
+__device__ __forceinline__ float wave_max_dpp(float f) {
+    int v = __float_as_int(f);
+    v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(dpp_i<0xB1>(v))));
+    v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(dpp_i<0x4E>(v))));
+    v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(dpp_i<0x141>(v))));
+    v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(dpp_i<0x140>(v))));
+    const float a = __int_as_float(__builtin_amdgcn_readlane(v, 0));
+    const float b = __int_as_float(__builtin_amdgcn_readlane(v, 16));
+    const float c = __int_as_float(__builtin_amdgcn_readlane(v, 32));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(v, 48));
+    return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+// int8 code of one activation [P3 §2.4]: clip(rne(fp32(127 x) / beta), -127, 127), with
+// the correctly rounded quotient from the reciprocal y = RN(1/beta) (see the file header).
+__device__ __forceinline__ uint32_t act_byte(float x, float beta, float y) {
+    const float a = x * 127.0f;
+    const float q = a * y;
+    const float r = __builtin_fmaf(-q, beta, a);
+    const float t = __builtin_fmaf(r, y, q);
+    const float c = __builtin_amdgcn_fmed3f(rintf(t), -127.0f, 127.0f);
+    return (uint32_t)((int)c) & 0xFFu;
+}
+
+__device__ __forceinline__ u32x4 act_bytes16(const float4 (&v)[4], float beta, float y) {
+    uint32_t d[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        d[i] = act_byte(v[i].x, beta, y) | (act_byte(v[i].y, beta, y) << 8) | (act_byte(v[i].z, beta, y) << 16) |
+               (act_byte(v[i].w, beta, y) << 24);
+    return u32x4{d[0], d[1], d[2], d[3]};
+}
+
+// MT tokens (the kernel masks tokens >= M), CPL chunks of 64 weights per lane and row,
+// R rows per wave step, FUSED = quantize x inside.
+template <int MT, int CPL, int R, bool FUSED>
+__global__ __launch_bounds__(256) void k_gemv(GemvArgs g) {
+    extern __shared__ u32x4 xs[];          // [MT][CPL][4][64] units of 16 bytes
+    __shared__ float red_f[MT][4];
+    __shared__ int red_i[MT][4];
+    const ForwardArgs& a = g.f;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int M = (int)a.M, C = g.C;
+    const int64_t K = a.K, N = a.N, rowb = K >> 2;
+    const int64_t rb = ((int64_t)blockIdx.x * 4 + wave) * g.rows_per_wave;
+    const int64_t re = rb + g.rows_per_wave < N ? rb + g.rows_per_wave : N;
+    const bool tail_lane = lane + 64 * (CPL - 1) < C;   // the last chunk may be partial
+
+    // ---- weight loads: rows r0 .. r0+R-1 (those < re) into a register buffer ----------
+    auto load_rows = [&](u32x4 (&w)[R][CPL], int64_t r0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t row = r0 + r;
+            if (row < re) {
+                const uint8_t* base = a.wp + row * rowb;     // wave-uniform
+#pragma unroll
+                for (int j = 0; j < CPL; ++j) {
+                    if (j < CPL - 1 || tail_lane)
+                        w[r][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + 16 * (lane + 64 * j)));
+                    else
+                        w[r][j] = u32x4{0u, 0u, 0u, 0u};
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < CPL; ++j) w[r][j] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    u32x4 wa[R][CPL], wb[R][CPL];
+    if (rb < re) load_rows(wa, rb);
+
+    // ---- stage x_q: this thread's units are (t = i / CPL, j = i % CPL, q = wave, l = lane)
     int part[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) part[t] = 0;
-    const int units = MT * CPL * 256;
-    for (int u = tid; u < units; u += 256) {
-        const int l = u & 63, q = (u >> 6) & 3, jt = u >> 8;
-        const int j = jt % CPL, t = jt / CPL;
-        const int c = l + 64 * j;
-        u32x4 o = {0u, 0u, 0u, 0u};
-        if (c < C) {
-            const u32x4 s = *reinterpret_cast<const u32x4*>(a.xq + t * K + 64 * c + 16 * q);
-            o = transpose4x4_bytes(s);
-            int bs = byte_sum(s.x) + byte_sum(s.y) + byte_sum(s.z) + byte_sum(s.w);
+    float beta_t[MT];
+    if constexpr (FUSED) {
+        constexpr bool KEEP = MT * CPL <= 4;       // keep x in registers between the two passes
+        float4 xv[KEEP ? MT * CPL : 1][4];
+        float mx[MT];
 #pragma unroll
-            for (int tt = 0; tt < MT; ++tt)
-                if (tt == t) part[tt] += bs;
+        for (int t = 0; t < MT; ++t) mx[t] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < MT * CPL; ++i) {
+            const int t = i / CPL, j = i % CPL, c = lane + 64 * j;
+            if (c < C && t < M) {
+                const float4* src = reinterpret_cast<const float4*>(g.x + t * K + 64 * c + 16 * wave);
+                float4 v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = src[e];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    mx[t] = fmaxf(mx[t], fmaxf(fmaxf(fabsf(v[e].x), fabsf(v[e].y)), fmaxf(fabsf(v[e].z), fabsf(v[e].w))));
+                    if constexpr (KEEP) xv[i][e] = v[e];
+                }
+            }
         }
-        xs[u] = o;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            const float m = wave_max_dpp(mx[t]);
+            if (lane == 0) red_f[t][wave] = m;
+        }
+        __syncthreads();
+        float rcp[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            beta_t[t] = fmaxf(fmaxf(red_f[t][0], red_f[t][1]), fmaxf(red_f[t][2], red_f[t][3])) + 1e-8f;
+            rcp[t] = 1.0f / beta_t[t];
+        }
+        const bool exporter = blockIdx.x == 0;
+#pragma unroll
+        for (int i = 0; i < MT * CPL; ++i) {
+            const int t = i / CPL, j = i % CPL, c = lane + 64 * j;
+            u32x4 o = {0u, 0u, 0u, 0u};
+            if (c < C && t < M) {
+                float4 v[4];
+                if constexpr (KEEP) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = xv[i][e];
+                } else {
+                    const float4* src = reinterpret_cast<const float4*>(g.x + t * K + 64 * c + 16 * wave);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = src[e];
+                }
+                const u32x4 s = act_bytes16(v, beta_t[t], rcp[t]);
+                if (exporter && g.xq_out)
+                    *reinterpret_cast<u32x4*>(g.xq_out + t * K + 64 * c + 16 * wave) = s;
+                o = transpose4x4_bytes(s);
+                part[t] += byte_sum(s.x) + byte_sum(s.y) + byte_sum(s.z) + byte_sum(s.w);
+            }
+            xs[i * 256 + tid] = o;
+        }
+        if (exporter && g.beta_out && tid < M) {
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+                if (t == tid) g.beta_out[t] = beta_t[t];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < MT * CPL; ++i) {
+            const int t = i / CPL, j = i % CPL, c = lane + 64 * j;
+            u32x4 o = {0u, 0u, 0u, 0u};
+            if (c < C && t < M) {
+                const u32x4 s = *reinterpret_cast<const u32x4*>(a.xq + t * K + 64 * c + 16 * wave);
+                o = transpose4x4_bytes(s);
+                part[t] += byte_sum(s.x) + byte_sum(s.y) + byte_sum(s.z) + byte_sum(s.w);
+            }
+            xs[i * 256 + tid] = o;
+        }
+#pragma unroll
+        for (int t = 0; t < MT; ++t) beta_t[t] = t < M ? a.beta[t] : 0.0f;
     }
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-        int v = wave_sum_i32(part[t]);
-        if (lane == 0) tsum[wave][t] = v;
+        const int v = wave_total(part[t]);
+        if (lane == 0) red_i[t][wave] = v;
     }
     __syncthreads();
     int xsum[MT];
@@ -58,35 +223,19 @@ __global__ __launch_bounds__(256) void k_gemv_dot4(ForwardArgs a, int C, int CPL
     const float alpha0 = a.alpha_per_row ? 0.0f : a.alpha[0];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-        xsum[t] = tsum[0][t] + tsum[1][t] + tsum[2][t] + tsum[3][t];
-        sc[t] = dequant_scale(alpha0, a.beta[t]);
+        xsum[t] = red_i[t][0] + red_i[t][1] + red_i[t][2] + red_i[t][3];
+        sc[t] = dequant_scale(alpha0, beta_t[t]);
     }
 
-    // ---- stream rows: wave gw owns row groups gw*R, (gw + TW)*R, ... -------------------
-    const int64_t TW = (int64_t)gridDim.x * 4;
-    for (int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * R; row0 < N; row0 += TW * R) {
-        int acc[R][MT];
+    // ---- reduce R rows held in w, finish them ------------------------------------------
+    auto finish_rows = [&](const u32x4 (&w)[R][CPL], int64_t r0) {
+        int s0[R][MT], s1[R][MT], s2[R][MT], s3[R][MT];
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int t = 0; t < MT; ++t) acc[r][t] = 0;
-
-        u32x4 cur[R], nxt[R];
-        auto load = [&](u32x4 (&dst)[R], int j) {
-            const int c = lane + 64 * j;
+            for (int t = 0; t < MT; ++t) s0[r][t] = s1[r][t] = s2[r][t] = s3[r][t] = 0;
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const int64_t row = row0 + r;
-                if (c < C && row < N)
-                    dst[r] = __builtin_nontemporal_load(
-                        reinterpret_cast<const u32x4*>(a.wp + row * rowb + 16 * (int64_t)c));
-                else
-                    dst[r] = u32x4{0u, 0u, 0u, 0u};
-            }
-        };
-        load(cur, 0);
-        for (int j = 0; j < CPL; ++j) {
-            if (j + 1 < CPL) load(nxt, j + 1);
+        for (int j = 0; j < CPL; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 u32x4 X[MT];
@@ -94,82 +243,126 @@ __global__ __launch_bounds__(256) void k_gemv_dot4(ForwardArgs a, int C, int CPL
                 for (int t = 0; t < MT; ++t) X[t] = xs[((t * CPL + j) * 4 + q) * 64 + lane];
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    const uint32_t v = q == 0 ? cur[r].x : q == 1 ? cur[r].y : q == 2 ? cur[r].z : cur[r].w;
-                    const uint32_t d0 = v & 0x03030303u;
-                    const uint32_t d1 = (v >> 2) & 0x03030303u;
-                    const uint32_t d2 = (v >> 4) & 0x03030303u;
-                    const uint32_t d3 = (v >> 6) & 0x03030303u;
+                    const uint32_t v = q == 0 ? w[r][j].x : q == 1 ? w[r][j].y : q == 2 ? w[r][j].z : w[r][j].w;
+                    const uint32_t d0 = v & 0x03030303u;          // c
+                    const uint32_t d1 = v & 0x0C0C0C0Cu;          // 4c
+                    const uint32_t d2 = v & 0x30303030u;          // 16c
+                    const uint32_t d3 = (v >> 6) & 0x03030303u;   // c
 #pragma unroll
                     for (int t = 0; t < MT; ++t) {
-                        int s = acc[r][t];
-                        s = dot4(d0, X[t].x, s);
-                        s = dot4(d1, X[t].y, s);
-                        s = dot4(d2, X[t].z, s);
-                        s = dot4(d3, X[t].w, s);
-                        acc[r][t] = s;
+                        s0[r][t] = dot4(d0, X[t].x, s0[r][t]);
+                        s1[r][t] = dot4(d1, X[t].y, s1[r][t]);
+                        s2[r][t] = dot4(d2, X[t].z, s2[r][t]);
+                        s3[r][t] = dot4(d3, X[t].w, s3[r][t]);
                     }
                 }
             }
-            if (j + 1 < CPL) {
-#pragma unroll
-                for (int r = 0; r < R; ++r) cur[r] = nxt[r];
-            }
-        }
-
-        // ---- reduce over the wave; lane r*MT + t finishes (row0 + r, token t) --------
-        int mine = 0, my_xsum = 0;
-        float my_sc = 0.0f;
+        // lane r*MT + t finishes (r0 + r, token t)
+        int mine = 0, my_xsum = 0, my_t = 0, my_r = 0;
+        float my_sc = 0.0f, my_beta = 0.0f;
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
-                int v = wave_sum_i32(acc[r][t]);
+                const int v = wave_total(s0[r][t] + (s1[r][t] >> 2) + (s2[r][t] >> 4) + s3[r][t]);
                 if (lane == r * MT + t) {
                     mine = v;
                     my_xsum = xsum[t];
                     my_sc = sc[t];
+                    my_beta = beta_t[t];
+                    my_t = t;
+                    my_r = r;
                 }
             }
         if (lane < R * MT) {
-            const int r = lane / MT, t = lane % MT;
-            const int64_t n = row0 + r;
-            if (n < N) {
+            const int64_t n = r0 + my_r;
+            if (n < re && my_t < M) {
                 const int total = mine - my_xsum;
-                const float s = a.alpha_per_row ? dequant_scale(a.alpha[n], a.beta[t]) : my_sc;
-                a.y[t * N + n] = dequant(total, s, a.bias, n);
-                if (a.acc) a.acc[t * N + n] = total;
+                const float s = a.alpha_per_row ? dequant_scale(a.alpha[n], my_beta) : my_sc;
+                a.y[my_t * N + n] = dequant(total, s, a.bias, n);
+                if (a.acc) a.acc[my_t * N + n] = total;
             }
         }
+    };
+
+    // ---- walk the row range, two register buffers in turn -------------------------------
+    for (int64_t r0 = rb; r0 < re; r0 += 2 * R) {
+        if (r0 + R < re) load_rows(wb, r0 + R);
+        finish_rows(wa, r0);
+        if (r0 + R >= re) break;
+        if (r0 + 2 * R < re) load_rows(wa, r0 + 2 * R);
+        finish_rows(wb, r0 + R);
     }
 }
 
-template <int MT>
-static hipError_t launch_mt(const ForwardArgs& a, hipStream_t s) {
-    const int C = (int)(a.K / 64);
-    const int CPL = (C + 63) / 64;
-    // rows per wave per pass: enough waves to cover the chip, at most 16 loads in flight
-    int64_t want = a.N / 2048;
-    int R = want >= 8 ? 8 : want >= 4 ? 4 : want >= 2 ? 2 : 1;
-    while (R > 1 && R * CPL > 16) R >>= 1;
-    const int64_t groups = (a.N + R - 1) / R;
-    const int64_t blocks = (groups + 3) / 4;
+// ---------------------------------------------------------------------------------------
+// Launch shape.  The chip runs up to kWavesTarget waves of this kernel at once; each wave
+// gets ceil(N / waves) contiguous rows, walked R rows at a time.  R keeps R * CPL loads of
+// 16 bytes per lane per buffer (two buffers) within LMAX.
+constexpr int64_t kWavesTarget = 2048;
+
+template <int MT, int CPL, bool FUSED>
+static hipError_t launch_cpl(const GemvArgs& g0, hipStream_t s) {
+    constexpr int LMAX = MT == 1 ? 8 : 4;
+    GemvArgs g = g0;
+    const int64_t N = g.f.N;
+    int64_t rpw = (N + kWavesTarget - 1) / kWavesTarget;
+    int R = 1;
+    while (R < 8 && R * 2 * CPL <= LMAX && R < rpw) R *= 2;
+    if (rpw < R) rpw = R;
+    g.rows_per_wave = rpw;
+    const int64_t waves = (N + rpw - 1) / rpw;
+    const int64_t blocks = (waves + 3) / 4;
     const size_t lds = (size_t)MT * CPL * 256 * 16;
-    dim3 g((unsigned)blocks), b(256);
-    switch (R) {
-        case 8: return launch_with_lds(k_gemv_dot4<MT, 8>, g, b, lds, s, a, C, CPL);
-        case 4: return launch_with_lds(k_gemv_dot4<MT, 4>, g, b, lds, s, a, C, CPL);
-        case 2: return launch_with_lds(k_gemv_dot4<MT, 2>, g, b, lds, s, a, C, CPL);
-        default: return launch_with_lds(k_gemv_dot4<MT, 1>, g, b, lds, s, a, C, CPL);
+    const dim3 grid((unsigned)blocks), block(256);
+    if constexpr (8 * CPL <= LMAX)
+        if (R == 8) return launch_with_lds(k_gemv<MT, CPL, 8, FUSED>, grid, block, lds, s, g);
+    if constexpr (4 * CPL <= LMAX)
+        if (R == 4) return launch_with_lds(k_gemv<MT, CPL, 4, FUSED>, grid, block, lds, s, g);
+    if constexpr (2 * CPL <= LMAX)
+        if (R == 2) return launch_with_lds(k_gemv<MT, CPL, 2, FUSED>, grid, block, lds, s, g);
+    return launch_with_lds(k_gemv<MT, CPL, 1, FUSED>, grid, block, lds, s, g);
+}
+
+template <bool FUSED>
+static hipError_t launch_m1(const GemvArgs& g, hipStream_t s) {
+    switch ((g.C + 63) / 64) {
+        case 1: return launch_cpl<1, 1, FUSED>(g, s);
+        case 2: return launch_cpl<1, 2, FUSED>(g, s);
+        case 3: return launch_cpl<1, 3, FUSED>(g, s);
+        case 4: return launch_cpl<1, 4, FUSED>(g, s);
+        case 5: return launch_cpl<1, 5, FUSED>(g, s);
+        case 6: return launch_cpl<1, 6, FUSED>(g, s);
+        case 7: return launch_cpl<1, 7, FUSED>(g, s);
+        default: return launch_cpl<1, 8, FUSED>(g, s);
     }
+}
+
+template <bool FUSED>
+static hipError_t launch_m4(const GemvArgs& g, hipStream_t s) {
+    switch ((g.C + 63) / 64) {
+        case 1: return launch_cpl<4, 1, FUSED>(g, s);
+        case 2: return launch_cpl<4, 2, FUSED>(g, s);
+        case 3: return launch_cpl<4, 3, FUSED>(g, s);
+        default: return launch_cpl<4, 4, FUSED>(g, s);
+    }
+}
+
+// One token: up to 8 chunks of 64 weights per lane (K <= 32768); two to four tokens: up
+// to 4 (K <= 16384).  Other shapes go to the MFMA kernel.
+bool gemv_supports(int64_t M, int64_t K) {
+    if (K % 64 != 0 || M < 1 || M > 4) return false;
+    return M == 1 ? K <= 32768 : K <= 16384;
 }
 
 hipError_t launch_gemv_dot4(const ForwardArgs& a, hipStream_t s) {
-    switch (a.M) {
-        case 1: return launch_mt<1>(a, s);
-        case 2: return launch_mt<2>(a, s);
-        case 3: return launch_mt<3>(a, s);
-        default: return launch_mt<4>(a, s);
-    }
+    GemvArgs g{a, nullptr, nullptr, nullptr, (int)(a.K / 64), 0};
+    return a.M == 1 ? launch_m1<false>(g, s) : launch_m4<false>(g, s);
+}
+
+hipError_t launch_gemv_fused(const ForwardArgs& a, const float* x, int8_t* xq_out, float* beta_out, hipStream_t s) {
+    GemvArgs g{a, x, xq_out, beta_out, (int)(a.K / 64), 0};
+    return a.M == 1 ? launch_m1<true>(g, s) : launch_m4<true>(g, s);
 }
 
 }  // namespace bitlinear

@@ -129,11 +129,17 @@ __device__ __forceinline__ float block_max_256(float v, float* red) {
     return r;
 }
 
-__device__ __forceinline__ uint32_t act_code(float x, float beta) {
-    float t = (x * 127.0f) / beta;        // fp32 product, then IEEE fp32 division
-    float r = rintf(t);
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (uint32_t)((int)r) & 0xFFu;
+// fp32(127 x) / beta rounded to nearest-even as an IEEE division would, formed from the
+// reciprocal y = RN(1/beta): q = RN(a*y), r = a - q*beta (exact through the FMA),
+// t = RN(q + r*y).  Markstein's theorem (reciprocal within half an ulp, first quotient within
+// one ulp) makes t the correctly rounded quotient.
+__device__ __forceinline__ uint32_t act_code(float x, float beta, float y) {
+    const float a = x * 127.0f;
+    const float q = a * y;
+    const float r = __builtin_fmaf(-q, beta, a);
+    const float t = __builtin_fmaf(r, y, q);
+    const float c = __builtin_amdgcn_fmed3f(rintf(t), -127.0f, 127.0f);
+    return (uint32_t)((int)c) & 0xFFu;
 }
 
 template <bool VEC>
@@ -154,17 +160,18 @@ __global__ __launch_bounds__(256) void k_quantize_act(const float* __restrict__ 
     }
     mx = block_max_256(mx, red);
     const float b = mx + 1e-8f;
+    const float y = 1.0f / b;
     if (threadIdx.x == 0) beta[m] = b;
     if (VEC) {
         const float4* r4 = reinterpret_cast<const float4*>(row);
         uint32_t* out = reinterpret_cast<uint32_t*>(xq + m * K);
         for (int64_t c = threadIdx.x; c < (K >> 2); c += 256) {
             float4 v = r4[c];
-            out[c] = act_code(v.x, b) | (act_code(v.y, b) << 8) | (act_code(v.z, b) << 16) |
-                     (act_code(v.w, b) << 24);
+            out[c] = act_code(v.x, b, y) | (act_code(v.y, b, y) << 8) | (act_code(v.z, b, y) << 16) |
+                     (act_code(v.w, b, y) << 24);
         }
     } else {
-        for (int64_t c = threadIdx.x; c < K; c += 256) xq[m * K + c] = (int8_t)act_code(row[c], b);
+        for (int64_t c = threadIdx.x; c < K; c += 256) xq[m * K + c] = (int8_t)act_code(row[c], b, y);
     }
 }
 

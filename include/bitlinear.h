@@ -126,9 +126,9 @@ int bitlinear_quantize_act(const float* x, int64_t M, int64_t K, int8_t* x_q, fl
  *   bias      [N] fp32 or NULL.                             (in)
  *   y         [M, N] fp32.                                  (out)
  *   acc       [M, N] int32 or NULL; when given, receives the exact integer sums.  (out)
- * The kernel is chosen by shape: M <= 4 runs a VALU GEMV (dot4 on unpacked codes), larger M
- * an int8 MFMA GEMM that unpacks the ternary tiles on chip.  Both fast paths need
- * K % 64 == 0 and 16-byte aligned x_q and W_packed; other inputs run a generic kernel
+ * The kernel is chosen by shape: M <= 4 and K <= 32768 run a VALU GEMV (dot4 on unpacked
+ * codes), other M an int8 MFMA GEMM that unpacks the ternary tiles on chip.  Both fast paths
+ * need K % 64 == 0 and 16-byte aligned x_q and W_packed; other inputs run a generic kernel
  * with identical results.
  * Errors: INVALID_ARG, SHAPE (K % 4, K > BITLINEAR_MAX_K, size overflow), HIP.
  */
@@ -143,6 +143,28 @@ int bitlinear_forward(const int8_t* x_q, const float* beta, int64_t M, int64_t K
 int bitlinear_forward_rows(const int8_t* x_q, const float* beta, int64_t M, int64_t K,
                            const uint8_t* W_packed, const float* alpha_rows, int64_t N,
                            const float* bias, float* y, int32_t* acc, hipStream_t stream);
+
+/*
+ * Activation quantization and forward in one call [P3 §3.2 steps 2-4]: y from fp32 x,
+ * with results identical to bitlinear_quantize_act followed by bitlinear_forward.
+ * For M <= 4, K % 64 == 0, K <= 32768 and 16-byte aligned x, W_packed (and x_q if given)
+ * it is one kernel that quantizes x on chip; otherwise it makes the two calls.
+ *
+ *   x      [M, K] fp32.                                               (in)
+ *   x_q    [M, K] int8 or NULL; receives the quantized activations.   (out)
+ *   beta   [M] fp32 or NULL; receives the per-token scales.           (out)
+ *   W_packed, alpha, N, bias, y, acc: as bitlinear_forward.
+ * x_q and beta may be NULL only on the one-kernel path (else INVALID_ARG).
+ * Errors: as bitlinear_forward.
+ */
+int bitlinear_forward_fused(const float* x, int64_t M, int64_t K, const uint8_t* W_packed,
+                            const float* alpha, int64_t N, const float* bias, float* y,
+                            int8_t* x_q, float* beta, int32_t* acc, hipStream_t stream);
+
+/* Kernel(s) bitlinear_forward_fused launches for these arguments ("gemv_fused" or
+ * "quantize_act+forward"); a static string. */
+const char* bitlinear_forward_fused_kernel(int64_t M, int64_t K, int64_t N, const float* x,
+                                           const uint8_t* W_packed, const int8_t* x_q);
 
 /*
  * Name of the kernel bitlinear_forward launches for these arguments ("gemv_dot4",

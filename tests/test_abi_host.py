@@ -114,15 +114,38 @@ def test_forward_validation(bl, name):
     assert call(N=1 << 33) == bl.BITLINEAR_ERR_SHAPE
 
 
+def test_forward_fused_validation(bl):
+    f = bl.lib.bitlinear_forward_fused
+    assert f(None, 1, 64, A, A, 8, None, A, None, None, None, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert f(A, 1, 64, None, A, 8, None, A, None, None, None, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert f(A, 1, 64, A, None, 8, None, A, None, None, None, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert f(A, 1, 64, A, A, 8, None, None, None, None, None, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert f(A, 0, 64, A, A, 8, None, A, None, None, None, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert f(A, 1, 66, A, A, 8, None, A, None, None, None, None) == bl.BITLINEAR_ERR_SHAPE
+    # two-call path without x_q / beta buffers
+    assert f(A, 5, 64, A, A, 8, None, A, None, None, None, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert f(A + 4, 1, 64, A, A, 8, None, A, None, None, None, None) == bl.BITLINEAR_ERR_INVALID_ARG
+
+
 def test_kernel_selection(bl):
     sel = bl.lib.bitlinear_forward_kernel
     assert sel(1, 4096, 4096, A, A).decode() == "gemv_dot4"
     assert sel(4, 4096, 4096, A, A).decode() == "gemv_dot4"
-    assert sel(5, 4096, 4096, A, A).decode() == "gemm_mfma_i8"
+    assert sel(5, 4096, 4096, A, A).decode() == "decode_mfma_i8"
+    assert sel(64, 11008, 4096, A, A).decode() == "decode_mfma_i8"
+    assert sel(65, 4096, 4096, A, A).decode() == "gemm_mfma_i8"
     assert sel(2048, 4096, 11008, A, A).decode() == "gemm_mfma_i8"
     assert sel(1, 4100, 4096, A, A).decode() == "generic"        # K % 64 != 0
     assert sel(1, 4096, 4096, A + 4, A).decode() == "generic"    # unaligned x_q
     assert sel(64, 4096, 4096, A, A + 8).decode() == "generic"   # unaligned W_packed
+    assert sel(1, 32768, 64, A, A).decode() == "gemv_dot4"
+    assert sel(1, 32832, 64, A, A).decode() == "decode_mfma_i8"   # K beyond the GEMV's registers
+    assert sel(4, 16384, 64, A, A).decode() == "gemv_dot4"
+    assert sel(4, 16448, 64, A, A).decode() == "decode_mfma_i8"
+    fsel = bl.lib.bitlinear_forward_fused_kernel
+    assert fsel(1, 4096, 4096, A, A, None).decode() == "gemv_fused"
+    assert fsel(1, 4096, 4096, A, A, A + 4).decode() == "quantize_act+forward"  # x_q export unaligned
+    assert fsel(5, 4096, 4096, A, A, A).decode() == "quantize_act+forward"
 
 
 def test_binding_has_no_host_fallback():

@@ -157,6 +157,7 @@ FWD_CASES = [
     (1, 64, 1), (1, 1024, 1024), (1, 4096, 100), (2, 4096, 257), (3, 11008, 130), (4, 128, 4096),
     (5, 64, 7), (8, 4096, 300), (16, 1024, 64), (17, 4096, 129), (33, 192, 65), (64, 11008, 70),
     (65, 1024, 130), (128, 256, 256), (130, 4096, 200), (300, 128, 257),
+    (64, 4160, 33), (7, 28672, 20), (40, 2048, 300), (16, 16448, 65), (2, 32832, 17), (63, 320, 1000),
     (1, 100, 33), (6, 4100, 65), (70, 12, 9),      # K % 64 != 0: generic kernel
 ]
 
@@ -281,3 +282,53 @@ def test_repeatable_bitwise(dev):
     for o in outs[1:]:
         for a, b in zip(outs[0], o):
             assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------------ fused quantize + forward
+FUSED_CASES = [(1, 64, 5), (1, 1024, 1024), (1, 4096, 4096), (1, 4096, 11008), (1, 11008, 4096),
+               (1, 28672, 1100), (1, 8192, 3000), (1, 32768, 70), (2, 4096, 300), (3, 11008, 130),
+               (4, 16384, 257), (4, 192, 4096)]
+
+
+@pytest.mark.parametrize("m,k,n", FUSED_CASES)
+def test_forward_fused_parity(dev, m, k, n):
+    torch, bl = dev
+    _say(f"forward_fused M={m} K={k} N={n}")
+    w = workloads.weights(6, n, k)
+    x = workloads.activations_with_outliers(6, m, k)
+    codes_o, packed_o, alpha_o = oracle.quantize_weights(w)
+    xq_o, beta_o = oracle.quantize_act(x)
+    acc_o = oracle.ternary_matmul(xq_o, codes_o)
+    y_o = oracle.dequant(acc_o, beta_o, alpha_o)
+    xt = _to(torch, x)
+    xq = torch.empty((m, k), dtype=torch.int8, device="cuda")
+    beta = torch.empty(m, dtype=torch.float32, device="cuda")
+    pk, al = _to(torch, packed_o), _to(torch, np.array([alpha_o], np.float32))
+    assert bl.bitlinear_forward_fused_kernel(m, k, n, xt, pk, xq) == "gemv_fused"
+    y, acc = bl.bitlinear_forward_fused(xt, pk, al, x_q=xq, beta=beta, acc=True)
+    y2 = bl.bitlinear_forward_fused(xt, pk, al)          # no exports
+    torch.cuda.synchronize()
+    assert np.array_equal(xq.cpu().numpy(), xq_o)
+    assert np.array_equal(beta.cpu().numpy(), beta_o)
+    assert np.array_equal(acc.cpu().numpy(), acc_o)
+    assert np.array_equal(y.cpu().numpy(), y_o)
+    assert np.array_equal(y2.cpu().numpy(), y_o)
+
+
+@pytest.mark.parametrize("m,k,n", [(5, 4096, 130), (64, 1024, 64), (2, 100, 33), (3, 28672, 40)])
+def test_forward_fused_two_call_path(dev, m, k, n):
+    torch, bl = dev
+    w = workloads.weights(6, n, k, index=2)
+    x = workloads.activations(6, m, k, index=2)
+    r = oracle.bitlinear(x, w)
+    xt = _to(torch, x)
+    xq = torch.empty((m, k), dtype=torch.int8, device="cuda")
+    beta = torch.empty(m, dtype=torch.float32, device="cuda")
+    pk, al = _to(torch, r["packed"]), _to(torch, np.array([r["alpha"]], np.float32))
+    assert bl.bitlinear_forward_fused_kernel(m, k, n, xt, pk, xq) == "quantize_act+forward"
+    y = bl.bitlinear_forward_fused(xt, pk, al, x_q=xq, beta=beta, bias=None)
+    torch.cuda.synchronize()
+    assert np.array_equal(xq.cpu().numpy(), r["xq"])
+    assert np.array_equal(y.cpu().numpy(), r["y"])
+    with pytest.raises(bl.BitLinearError):
+        bl.bitlinear_forward_fused(xt, pk, al)            # needs x_q and beta on this path
