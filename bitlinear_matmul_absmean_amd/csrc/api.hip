@@ -38,14 +38,30 @@ int check_forward(const int8_t* x_q, const float* beta, int64_t M, int64_t K, co
     return BITLINEAR_OK;
 }
 
-enum class Path { Gemv, Decode, Gemm, Generic };
+enum class Path { Gemv, Decode, Gemm, DecodeSliced, Generic };
 
-// M <= 4: VALU GEMV; up to 64 tokens: weight-streaming MFMA decode kernel; more: MFMA GEMM.
+// M <= 4: VALU GEMV; up to 64 tokens: weight-streaming MFMA decode kernel; more: MFMA GEMM
+// (K % 128 == 0), else the decode kernel over 64-token slices.
 Path choose_path(int64_t M, int64_t K, const int8_t* xq, const uint8_t* wp) {
     if (!fast_forward_ok(K, xq, wp)) return Path::Generic;
     if (gemv_supports(M, K)) return Path::Gemv;
     if (decode_mfma_supports(M, K)) return Path::Decode;
-    return Path::Gemm;
+    if (gemm_supports_k(K)) return Path::Gemm;
+    return Path::DecodeSliced;
+}
+
+hipError_t launch_decode_sliced(const ForwardArgs& a, hipStream_t stream) {
+    for (int64_t m0 = 0; m0 < a.M; m0 += 64) {
+        ForwardArgs s = a;
+        s.M = a.M - m0 < 64 ? a.M - m0 : 64;
+        s.xq = a.xq + m0 * a.K;
+        s.beta = a.beta + m0;
+        s.y = a.y + m0 * a.N;
+        s.acc = a.acc ? a.acc + m0 * a.N : nullptr;
+        hipError_t e = launch_decode_mfma(s, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 bool fused_fast_ok(int64_t M, int64_t K, const float* x, const uint8_t* wp, const int8_t* xq_out) {
@@ -57,6 +73,7 @@ int run_forward(const ForwardArgs& a, hipStream_t stream) {
         case Path::Gemv: return hip_status(launch_gemv_dot4(a, stream));
         case Path::Decode: return hip_status(launch_decode_mfma(a, stream));
         case Path::Gemm: return hip_status(launch_gemm_mfma(a, stream));
+        case Path::DecodeSliced: return hip_status(launch_decode_sliced(a, stream));
         default: return hip_status(launch_forward_generic(a, stream));
     }
 }
@@ -173,6 +190,7 @@ const char* bitlinear_forward_kernel(int64_t M, int64_t K, int64_t N, const int8
         case Path::Gemv: return "gemv_dot4";
         case Path::Decode: return "decode_mfma_i8";
         case Path::Gemm: return "gemm_mfma_i8";
+        case Path::DecodeSliced: return "decode_mfma_i8_sliced";
         default: return "generic";
     }
 }

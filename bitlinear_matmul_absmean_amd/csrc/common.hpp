@@ -10,6 +10,7 @@ constexpr int kWave = 64;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 
 // Launch with `lds` bytes of dynamic LDS; above 64 KiB the kernel must first be allowed
 // the larger allocation (gfx950 has 160 KiB of LDS per workgroup).
@@ -102,6 +103,7 @@ struct ForwardArgs {
 bool gemv_supports(int64_t M, int64_t K);
 hipError_t launch_gemv_dot4(const ForwardArgs& a, hipStream_t s);
 hipError_t launch_gemv_fused(const ForwardArgs& a, const float* x, int8_t* xq_out, float* beta_out, hipStream_t s);
+bool gemm_supports_k(int64_t K);
 hipError_t launch_gemm_mfma(const ForwardArgs& a, hipStream_t s);
 bool decode_mfma_supports(int64_t M, int64_t K);
 hipError_t launch_decode_mfma(const ForwardArgs& a, hipStream_t s);

@@ -134,6 +134,7 @@ def test_kernel_selection(bl):
     assert sel(5, 4096, 4096, A, A).decode() == "decode_mfma_i8"
     assert sel(64, 11008, 4096, A, A).decode() == "decode_mfma_i8"
     assert sel(65, 4096, 4096, A, A).decode() == "gemm_mfma_i8"
+    assert sel(65, 4160, 4096, A, A).decode() == "gemm_mfma_i8"
     assert sel(2048, 4096, 11008, A, A).decode() == "gemm_mfma_i8"
     assert sel(1, 4100, 4096, A, A).decode() == "generic"        # K % 64 != 0
     assert sel(1, 4096, 4096, A + 4, A).decode() == "generic"    # unaligned x_q

@@ -158,6 +158,7 @@ FWD_CASES = [
     (5, 64, 7), (8, 4096, 300), (16, 1024, 64), (17, 4096, 129), (33, 192, 65), (64, 11008, 70),
     (65, 1024, 130), (128, 256, 256), (130, 4096, 200), (300, 128, 257),
     (64, 4160, 33), (7, 28672, 20), (40, 2048, 300), (16, 16448, 65), (2, 32832, 17), (63, 320, 1000),
+    (200, 4160, 130), (129, 192, 300), (1000, 128, 70), (96, 11008, 514),
     (1, 100, 33), (6, 4100, 65), (70, 12, 9),      # K % 64 != 0: generic kernel
 ]
 
