@@ -6,15 +6,23 @@
 // fp32(alpha*beta[m]/127) (+ bias).  With many tokens (prefill) this is a dense contraction
 // and the compute peak is what matters [P3 §5.5], so it runs on MFMA.
 //
-// Tiles: a workgroup computes BM tokens x BN weight rows, four waves in a WGM x WGN grid, K in
-// steps of BK with double-buffered LDS (one barrier per step).  Per step:
-//   * A (x_q): BM x BK bytes from global, every 16-byte group transposed 4x4 with v_perm so that
-//     operand byte 4i+j holds x_q[k = 4j+i], written to LDS (rows padded against bank
-//     conflicts).  The same pass accumulates the per-token sum of x_q.
-//   * B (weights): BN rows x BK/4 bytes of packed codes, to LDS as they are (4x less traffic
-//     than int8); the lane feeding column n reads one packed dword (16 codes) and expands it
-//     with four masks (v >> 2i) & 0x03030303 into its 16-byte operand: byte 4i+j = c of weight
-//     4j+i.  c = W+1, so acc = sum c*x_q - sum x_q.
+// Tiles: a workgroup computes 128 tokens x 256 weight rows; its four waves sit side by side in
+// N (wave tile 128 x 64: four 32-row A blocks against two 32-column B blocks, 8 accumulators of
+// 16 registers).  K advances in steps of 64 with double-buffered LDS, one barrier per step.
+//   * A (x_q): 128 x 64 bytes per step from global, every 16-byte group transposed 4x4 with
+//     v_perm so that operand byte 4i+j holds x_q[k = 4j+i], written to LDS (rows padded by one
+//     16-byte unit against bank conflicts).  The same pass accumulates the per-token sum of x_q.
+//   * B (weights): 256 rows x 16 bytes of packed codes per step, to LDS as they are (4x less
+//     traffic than int8), dword p of column c stored at p ^ 2((c >> 4) & 1) so that columns c
+//     and c + 16 fall in different banks.  The lane feeding column n reads one packed dword (16
+//     codes) and expands it with four masks (v >> 2i) & 0x03030303 into its 16-byte operand:
+//     byte 4i+j = c of weight 4j+i.  c = W+1, so acc = sum c*x_q - sum x_q.
+// Each step first reads every operand it needs from LDS and issues the global loads of the step
+// after next (two register stages), then issues its 16 MFMAs one at a time with a slice of VALU
+// work (the second half's B expansion, the next step's transposes, sums and LDS stores) after
+// each, fixed in place with scheduling barriers: a wave then keeps issuing VALU while its
+// previous MFMA occupies the matrix core.  Without the barriers the compiler bunches the VALU
+// work and the MFMAs apart.
 // The 32x32x32 int8 MFMA does twice the work of the 16x16x64 one in the same issue time on
 // gfx950 (measured: 4.9 vs 2.7 POPS over the chip), so the waves tile in 32x32 blocks.  Its
 // lane layout (checked on the device): A/B lane l holds row/column l%32, k = 16*(l/32)+j;
@@ -39,93 +47,72 @@ __device__ __forceinline__ u32x4 transpose4x4_v(u32x4 s) {
     return o;
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN>
-__global__ __launch_bounds__(256, 2) void k_gemm_mfma(ForwardArgs a, int tiles_m, int tiles_n) {
-    static_assert(WGM * WGN == 4, "four waves per workgroup");
-    constexpr int WM = BM / WGM, WN = BN / WGN;       // wave tile
-    constexpr int FM = WM / 32, FN = WN / 32;         // 32x32 MFMA blocks per wave
-    constexpr int GK = BK / 16;                       // 16-byte groups per row and step
-    constexpr int AU = BM * GK;                       // A units per step
-    constexpr int APT = AU / 256;                     // A units per thread
-    constexpr int ASTR = GK + 1;                      // LDS units per A row (one of padding)
-    constexpr int BPR = BK / 64;                      // 16-byte packed units per B row and step
-    constexpr int BU = BN * BPR;
-    constexpr int BTB = BN * BK / 4 / 256;            // bytes of the B tile each thread moves
-    static_assert(AU % 256 == 0 && FM >= 1 && FN >= 1, "tile shape");
-    static_assert(BTB == 8 || BTB == 16, "B staging granularity");
+__device__ __forceinline__ i32x4 unpack16(uint32_t v) {
+    return i32x4{(int)(v & 0x03030303u), (int)((v >> 2) & 0x03030303u), (int)((v >> 4) & 0x03030303u),
+                 (int)((v >> 6) & 0x03030303u)};
+}
+#define SB() __builtin_amdgcn_sched_barrier(0)
+#define MF(i, j, av, bv) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, acc[i][j], 0, 0, 0)
 
+constexpr int GEMM_BM = 128, GEMM_BN = 256, GEMM_BK = 64;
+
+__global__ __launch_bounds__(256, 2) void k_gemm_mfma(ForwardArgs a, int tiles_m, int tiles_n) {
+    constexpr int BM = GEMM_BM, BN = GEMM_BN, BK = GEMM_BK;
+    constexpr int WN = BN / 4;                 // wave tile 128 x 64
+    constexpr int FM = 4, FN = 2;
+    constexpr int GK = BK / 16, APT = BM * GK / 256, ASTR = GK + 1;
     __shared__ u32x4 As[2][BM * ASTR];
-    __shared__ u32x4 Bs[2][BU];
+    __shared__ u32x4 Bs[2][BN];
     __shared__ int rsum[BM];
     __shared__ float ssc[BM];
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / WGN, wn = wave % WGN;
+    const int wn = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t M = a.M, N = a.N, K = a.K, rowb = K >> 2;
-
-    // XCD-aware tile order: hardware id h runs on XCD h % 8; give XCD x the contiguous logical
-    // tiles [x * T/8, (x+1) * T/8) when T % 8 == 0 (else keep the hardware order).
     const int T = tiles_m * tiles_n;
     int t = blockIdx.x;
     if (T % 8 == 0) t = (t % 8) * (T / 8) + t / 8;
-    const int tm = t / tiles_n, tn = t % tiles_n;       // token block major
+    const int tm = t / tiles_n, tn = t % tiles_n;
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const int KS = (int)(K / BK);
-
     for (int i = tid; i < BM; i += 256) {
         const int64_t m = m0 + i;
         ssc[i] = (!a.alpha_per_row && m < M) ? dequant_scale(a.alpha[0], a.beta[m]) : 0.0f;
     }
 
-    // Two register stages: the global loads of step ks+2 are issued while step ks computes,
-    // so about two steps of MFMA work cover their L2 / Infinity Cache latency.
-    // B staging words (BTB bytes per thread): dwords 0..BTB/4-1 used
-    u32x4 ra0[APT], rb0[1], ra1[APT], rb1[1];
+    // Staging: thread tid moves A units u = tid + 256 i (token row u / GK, 16 bytes at k = 16 (u % GK))
+    // and the 16 packed bytes of weight row (column) tid.  Rows past M or N are clamped to the last
+    // row, so every load is unconditional and the compiler counts outstanding loads exactly
+    // (partial vmcnt waits instead of draining); the results of such rows are never written.
+    const int8_t* ap[APT];
+#pragma unroll
+    for (int i = 0; i < APT; ++i) {
+        const int u = tid + 256 * i;
+        ap[i] = a.xq + min(m0 + u / GK, M - 1) * K + 16 * (u % GK);
+    }
+    const uint8_t* bp = a.wp + min(n0 + tid, N - 1) * rowb;
+    const bool bsw = (tid >> 4) & 1;
+    u32x4 ra0[APT], ra1[APT], rb0, rb1;
     int rs[APT];
 #pragma unroll
     for (int i = 0; i < APT; ++i) rs[i] = 0;
-
-    // Branch-free loads (rows past M or N are clamped to the last row: their results are
-    // never written), so the compiler can count outstanding loads exactly.
-    auto gload = [&](u32x4 (&ra)[APT], u32x4 (&rb)[1], int ks) {
+    auto gload = [&](u32x4 (&ra)[APT], u32x4& rb, int ks) {
 #pragma unroll
-        for (int i = 0; i < APT; ++i) {
-            const int u = tid + 256 * i;
-            const int64_t m = min(m0 + u / GK, M - 1);
-            ra[i] = *reinterpret_cast<const u32x4*>(a.xq + m * K + (int64_t)ks * BK + 16 * (u % GK));
-        }
-        {
-            const int byte = tid * BTB;                   // offset inside the BN x BK/4 tile
-            const int64_t n = min(n0 + byte / (BK / 4), N - 1);
-            const uint8_t* src = a.wp + n * rowb + (int64_t)ks * (BK / 4) + byte % (BK / 4);
-            if constexpr (BTB == 16) {
-                rb[0] = *reinterpret_cast<const u32x4*>(src);
-            } else {
-                const uint2 v = *reinterpret_cast<const uint2*>(src);
-                rb[0] = u32x4{v.x, v.y, 0u, 0u};
-            }
-        }
+        for (int i = 0; i < APT; ++i) ra[i] = *reinterpret_cast<const u32x4*>(ap[i] + (int64_t)ks * BK);
+        rb = *reinterpret_cast<const u32x4*>(bp + (int64_t)ks * (BK / 4));
     };
-    auto sstore = [&](const u32x4 (&ra)[APT], const u32x4 (&rb)[1], int buf, bool count) {
-#pragma unroll
-        for (int i = 0; i < APT; ++i) {
-            const int u = tid + 256 * i;
-            As[buf][(u / GK) * ASTR + u % GK] = transpose4x4_v(ra[i]);
-            const int bs = byte_sum(ra[i].x) + byte_sum(ra[i].y) + byte_sum(ra[i].z) + byte_sum(ra[i].w);
-            rs[i] += count ? bs : 0;
-        }
-        uint8_t* bdst = reinterpret_cast<uint8_t*>(&Bs[buf][0]) + tid * BTB;
-        // dword p of column c is stored at p ^ (2 * ((c >> 4) & 1)) (see the reads)
-        const bool sw = ((tid * BTB / (BK / 4)) >> 4) & 1;
-        if constexpr (BTB == 16) {
-            *reinterpret_cast<u32x4*>(bdst) = sw ? u32x4{rb[0].z, rb[0].w, rb[0].x, rb[0].y} : rb[0];
-        } else {
-            // 8 bytes = dwords (2h, 2h+1) of the column: they move to (2h^2, 2h^2+1)
-            const int h = (tid * BTB % (BK / 4)) / 8;
-            uint8_t* col = bdst - (tid * BTB % (BK / 4));
-            *reinterpret_cast<uint2*>(col + 8 * (sw ? (h ^ 1) : h)) = make_uint2(rb[0].x, rb[0].y);
-        }
+    auto stage_a = [&](const u32x4& r, int i, int buf, bool count) {
+        const int u = tid + 256 * i;
+        As[buf][(u / GK) * ASTR + u % GK] = transpose4x4_v(r);
+        int v = rs[i];
+        v = __builtin_amdgcn_sdot4((int)r.x, 0x01010101, v, false);
+        v = __builtin_amdgcn_sdot4((int)r.y, 0x01010101, v, false);
+        v = __builtin_amdgcn_sdot4((int)r.z, 0x01010101, v, false);
+        v = __builtin_amdgcn_sdot4((int)r.w, 0x01010101, v, false);
+        rs[i] = count ? v : rs[i];
+    };
+    auto stage_b = [&](const u32x4& r, int buf) {
+        Bs[buf][tid] = bsw ? u32x4{r.z, r.w, r.x, r.y} : r;
     };
 
     i32x16 acc[FM][FN];
@@ -135,53 +122,69 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(ForwardArgs a, int tiles_m
         for (int j = 0; j < FN; ++j) acc[i][j] = i32x16{};
 
     const int lr = lane & 31, lg = lane >> 5;
-    auto compute = [&](int buf) {
+    int boff[2][FN];
 #pragma unroll
-        for (int kk = 0; kk < BK / 32; ++kk) {          // 32 weights per MFMA step
-            i32x4 bop[FN];
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int col = wn * WN + j * 32 + lr;
-                // packed dword 2*kk + lg of this column's BK/4-byte slice = its 16 codes
-                // (stored XOR-swizzled by column so that columns c and c+16 use other banks)
-                const int pos = (2 * kk + lg) ^ (((col >> 4) & 1) << 1);
-                const uint32_t v = reinterpret_cast<const uint32_t*>(&Bs[buf][col * BPR])[pos];
-                bop[j] = i32x4{(int)(v & 0x03030303u), (int)((v >> 2) & 0x03030303u),
-                               (int)((v >> 4) & 0x03030303u), (int)((v >> 6) & 0x03030303u)};
-            }
-#pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int row = wm * WM + i * 32 + lr;
-                const i32x4 aop = (i32x4)As[buf][row * ASTR + kk * 2 + lg];
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop, bop[j], acc[i][j], 0, 0, 0);
-            }
+        for (int j = 0; j < FN; ++j) {
+            const int col = wn * WN + j * 32 + lr;
+            boff[kk][j] = col * 4 + ((2 * kk + lg) ^ (((col >> 4) & 1) << 1));
         }
+
+    // One K step: read every operand of the step from LDS, issue the global loads two steps
+    // ahead, then run the 16 MFMAs with the staging of the next step (transpose, sums, LDS
+    // stores) and the second half's B expansion placed one piece after each MFMA.
+    auto step = [&](int buf, const u32x4 (&rc)[APT], const u32x4& rbc, u32x4 (&rn)[APT], u32x4& rbn, int ksl, bool count) {
+        uint32_t bw[2][FN];
+        i32x4 av[2][FM];
+        const uint32_t* b32 = reinterpret_cast<const uint32_t*>(&Bs[buf][0]);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) bw[kk][j] = b32[boff[kk][j]];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int i = 0; i < FM; ++i) av[kk][i] = (i32x4)As[buf][(i * 32 + lr) * ASTR + kk * 2 + lg];
+        SB();
+        gload(rn, rbn, ksl);
+        SB();
+        i32x4 b0[FN], b1[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) b0[j] = unpack16(bw[0][j]);
+        SB();
+        MF(0, 0, av[0][0], b0[0]); b1[0] = unpack16(bw[1][0]); SB();
+        MF(0, 1, av[0][0], b0[1]); b1[1] = unpack16(bw[1][1]); SB();
+        MF(1, 0, av[0][1], b0[0]); stage_a(rc[0], 0, buf ^ 1, count); SB();
+        MF(1, 1, av[0][1], b0[1]); stage_a(rc[1], 1, buf ^ 1, count); SB();
+        MF(2, 0, av[0][2], b0[0]); stage_b(rbc, buf ^ 1); SB();
+        MF(2, 1, av[0][2], b0[1]); SB();
+        MF(3, 0, av[0][3], b0[0]); SB();
+        MF(3, 1, av[0][3], b0[1]); SB();
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) MF(i, j, av[1][i], b1[j]);
     };
 
-    // Steady state: the loads are unconditional (past the end they re-read the last step,
-    // whose data is then not used), so the compiler can wait for the older stage only
-    // (vmcnt of the newer stage's count) instead of draining every load.
+    // Two register stages: at the top of an iteration LDS buffer 0 holds step ks and ra1/rb1 hold
+    // step ks+1.  Past the end the loads re-read the last step; `count` keeps those out of the sums.
     const int last = KS - 1;
     gload(ra0, rb0, 0);
     gload(ra1, rb1, KS > 1 ? 1 : 0);
-    sstore(ra0, rb0, 0, true);
+#pragma unroll
+    for (int i = 0; i < APT; ++i) stage_a(ra0[i], i, 0, true);
+    stage_b(rb0, 0);
     __syncthreads();
     int ks = 0;
     for (; ks + 2 <= KS; ks += 2) {
-        gload(ra0, rb0, min(ks + 2, last));
-        compute(0);
-        sstore(ra1, rb1, 1, true);
+        step(0, ra1, rb1, ra0, rb0, min(ks + 2, last), ks + 1 < KS);
         __syncthreads();
-        gload(ra1, rb1, min(ks + 3, last));
-        compute(1);
-        sstore(ra0, rb0, 0, ks + 2 < KS);
+        step(1, ra0, rb0, ra1, rb1, min(ks + 3, last), ks + 2 < KS);
         __syncthreads();
     }
-    if (ks < KS) compute(0);               // odd number of steps: the last one sits in buffer 0
+    if (ks < KS) step(0, ra1, rb1, ra0, rb0, last, false);
 
-    // per-token sums of x_q: the GK consecutive threads that staged a row hold its parts
 #pragma unroll
     for (int i = 0; i < APT; ++i) {
         int v = rs[i];
@@ -191,13 +194,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(ForwardArgs a, int tiles_m
         if (u % GK == 0) rsum[u / GK] = v;
     }
     __syncthreads();
-
-    // 32x32 MFMA result layout: lane l, element r -> row 8*(r/4) + 4*(l/32) + r%4, column l%32.
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int mr = wm * WM + i * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
+            const int mr = i * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
             const int64_t m = m0 + mr;
             if (m >= M) continue;
             const int xs = rsum[mr];
@@ -215,17 +216,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(ForwardArgs a, int tiles_m
         }
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN>
-static hipError_t launch_tile(const ForwardArgs& a, hipStream_t s) {
-    const int tm = (int)((a.M + BM - 1) / BM), tn = (int)((a.N + BN - 1) / BN);
-    hipLaunchKernelGGL((k_gemm_mfma<BM, BN, BK, WGM, WGN>), dim3((unsigned)(tm * tn)), dim3(256), 0, s, a, tm, tn);
-    return hipGetLastError();
-}
-
-bool gemm_supports_k(int64_t K) { return K % 64 == 0; }
+bool gemm_supports_k(int64_t K) { return K % GEMM_BK == 0; }
 
 hipError_t launch_gemm_mfma(const ForwardArgs& a, hipStream_t s) {
-    return launch_tile<128, 256, 64, 2, 2>(a, s);
+    const int tm = (int)((a.M + GEMM_BM - 1) / GEMM_BM), tn = (int)((a.N + GEMM_BN - 1) / GEMM_BN);
+    hipLaunchKernelGGL(k_gemm_mfma, dim3((unsigned)(tm * tn)), dim3(256), 0, s, a, tm, tn);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------------
