@@ -101,6 +101,11 @@ struct ForwardArgs {
 };
 
 bool gemv_supports(int64_t M, int64_t K);
+struct GemvShape {
+    int waves_per_wg;         // 4 or 16
+    int64_t waves_target;     // waves the grid aims at
+};
+GemvShape gemv_shape(int64_t M, int64_t K, int64_t N);
 hipError_t launch_gemv_dot4(const ForwardArgs& a, hipStream_t s);
 hipError_t launch_gemv_fused(const ForwardArgs& a, const float* x, int8_t* xq_out, float* beta_out, hipStream_t s);
 bool gemm_supports_k(int64_t K);

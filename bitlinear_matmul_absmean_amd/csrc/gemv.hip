@@ -93,69 +93,103 @@ __device__ __forceinline__ u32x4 act_bytes16(const float4 (&v)[4], float beta, f
 }
 
 // MT tokens (the kernel masks tokens >= M), CPL chunks of 64 weights per lane and row,
-// R rows per wave step, FUSED = quantize x inside.
-template <int MT, int CPL, int R, bool FUSED>
-__global__ __launch_bounds__(256) void k_gemv(GemvArgs g) {
+// R rows per wave step, FUSED = quantize x inside, WAVES waves per workgroup.
+template <int MT, int CPL, int R, bool FUSED, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_gemv(GemvArgs g) {
+    constexpr int NT = 64 * WAVES;            // threads per workgroup
+    constexpr int UNITS = MT * CPL * 256;     // 16-byte units of x_q staged per workgroup
+    constexpr int UPT = (UNITS + NT - 1) / NT;
     extern __shared__ u32x4 xs[];          // [MT][CPL][4][64] units of 16 bytes
-    __shared__ float red_f[MT][4];
-    __shared__ int red_i[MT][4];
+    __shared__ float red_f[MT][WAVES];
+    __shared__ int red_i[MT][WAVES];
     const ForwardArgs& a = g.f;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int M = (int)a.M, C = g.C;
     const int64_t K = a.K, N = a.N, rowb = K >> 2;
-    const int64_t rb = ((int64_t)blockIdx.x * 4 + wave) * g.rows_per_wave;
-    const int64_t re = rb + g.rows_per_wave < N ? rb + g.rows_per_wave : N;
+    const int64_t rb = ((int64_t)blockIdx.x * WAVES + wave) * g.rows_per_wave;
+    const int64_t re = rb + g.rows_per_wave < N ? rb + g.rows_per_wave : N;   // may be <= rb: no rows
     const bool tail_lane = lane + 64 * (CPL - 1) < C;   // the last chunk may be partial
 
-    // ---- weight loads: rows r0 .. r0+R-1 (those < re) into a register buffer ----------
+    // ---- weight loads: rows r0 .. r0+R-1 into a register buffer -------------------------
+    // Branch-free, so that the compiler can wait for exactly the loads it needs: rows past
+    // this wave's range re-read its last row (never written back), and lanes past the last
+    // 64-weight chunk of a row re-read chunk 0: the x_q staged for those lanes is zero, so
+    // their products vanish.
     auto load_rows = [&](u32x4 (&w)[R][CPL], int64_t r0) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int64_t row = r0 + r;
-            if (row < re) {
-                const uint8_t* base = a.wp + row * rowb;     // wave-uniform
+            const int64_t row = r0 + r < re ? r0 + r : re - 1;
+            const uint8_t* base = a.wp + row * rowb;     // wave-uniform
 #pragma unroll
-                for (int j = 0; j < CPL; ++j) {
-                    if (j < CPL - 1 || tail_lane)
-                        w[r][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + 16 * (lane + 64 * j)));
-                    else
-                        w[r][j] = u32x4{0u, 0u, 0u, 0u};
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < CPL; ++j) w[r][j] = u32x4{0u, 0u, 0u, 0u};
+            for (int j = 0; j < CPL; ++j) {
+                const int cj = (j < CPL - 1 || tail_lane) ? lane + 64 * j : 0;
+                w[r][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + 16 * cj));
             }
         }
     };
-    u32x4 wa[R][CPL], wb[R][CPL];
-    if (rb < re) load_rows(wa, rb);
-
-    // ---- stage x_q: this thread's units are (t = i / CPL, j = i % CPL, q = wave, l = lane)
+    // ---- stage x_q.  Unit u of the LDS image holds the 16 weights' worth of x_q at
+    // k = 64 c + 16 q for token t, with i = u / 256 = t * CPL + j, q = (u / 64) % 4, lane
+    // l = u % 64 and c = l + 64 j: the lane that reads weight chunk c of a row finds its four
+    // x_q dwords at units (i, q = 0..3, l).  Thread tid stages units tid, tid + NT, ...
+    // The (small, cache-resident) activation loads are issued before the weight loads: a
+    // wave's loads complete in order, so activations queued behind the weights would hold the
+    // staging back until all of this wave's weights had arrived.  Out-of-range units load
+    // element 0 and are masked afterwards, so the loads are unconditional.
     int part[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) part[t] = 0;
+    auto unit_at = [&](int u, int& t, int& c, int& q) {
+        const int i = u >> 8;
+        t = i / CPL;
+        c = (u & 63) + 64 * (i % CPL);
+        q = (u >> 6) & 3;
+        return u < UNITS && c < C && t < M;
+    };
+    auto add_part = [&](int t, int v) {
+#pragma unroll
+        for (int tt = 0; tt < MT; ++tt)
+            if (tt == t) part[tt] += v;
+    };
+    u32x4 wa[R][CPL], wb[R][CPL];
     float beta_t[MT];
     if constexpr (FUSED) {
-        constexpr bool KEEP = MT * CPL <= 4;       // keep x in registers between the two passes
-        float4 xv[KEEP ? MT * CPL : 1][4];
+        constexpr bool KEEP = UPT <= 4;       // keep x in registers between the two passes
+        float4 xv[KEEP ? UPT : 1][4];
+        bool ok[UPT];
+        if constexpr (KEEP) {
+#pragma unroll
+            for (int k = 0; k < UPT; ++k) {
+                int t, c, q;
+                ok[k] = unit_at(tid + NT * k, t, c, q);
+                const float4* src = reinterpret_cast<const float4*>(g.x + (ok[k] ? t * K + 64 * c + 16 * q : 0));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) xv[k][e] = src[e];
+            }
+        }
+        load_rows(wa, rb);
         float mx[MT];
 #pragma unroll
         for (int t = 0; t < MT; ++t) mx[t] = 0.0f;
 #pragma unroll
-        for (int i = 0; i < MT * CPL; ++i) {
-            const int t = i / CPL, j = i % CPL, c = lane + 64 * j;
-            if (c < C && t < M) {
-                const float4* src = reinterpret_cast<const float4*>(g.x + t * K + 64 * c + 16 * wave);
-                float4 v[4];
+        for (int k = 0; k < UPT; ++k) {
+            int t, c, q;
+            const bool valid = unit_at(tid + NT * k, t, c, q);
+            float4 v[4];
+            if constexpr (KEEP) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = xv[k][e];
+            } else {
+                const float4* src = reinterpret_cast<const float4*>(g.x + (valid ? t * K + 64 * c + 16 * q : 0));
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = src[e];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    mx[t] = fmaxf(mx[t], fmaxf(fmaxf(fabsf(v[e].x), fabsf(v[e].y)), fmaxf(fabsf(v[e].z), fabsf(v[e].w))));
-                    if constexpr (KEEP) xv[i][e] = v[e];
-                }
             }
+            float m = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m = fmaxf(m, fmaxf(fmaxf(fabsf(v[e].x), fabsf(v[e].y)), fmaxf(fabsf(v[e].z), fabsf(v[e].w))));
+#pragma unroll
+            for (int tt = 0; tt < MT; ++tt)
+                if (valid && tt == t) mx[tt] = fmaxf(mx[tt], m);
         }
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
@@ -166,31 +200,39 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs g) {
         float rcp[MT];
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-            beta_t[t] = fmaxf(fmaxf(red_f[t][0], red_f[t][1]), fmaxf(red_f[t][2], red_f[t][3])) + 1e-8f;
+            float m = red_f[t][0];
+#pragma unroll
+            for (int w = 1; w < WAVES; ++w) m = fmaxf(m, red_f[t][w]);
+            beta_t[t] = m + 1e-8f;
             rcp[t] = 1.0f / beta_t[t];
         }
         const bool exporter = blockIdx.x == 0;
 #pragma unroll
-        for (int i = 0; i < MT * CPL; ++i) {
-            const int t = i / CPL, j = i % CPL, c = lane + 64 * j;
+        for (int k = 0; k < UPT; ++k) {
+            const int u = tid + NT * k;
+            int t, c, q;
             u32x4 o = {0u, 0u, 0u, 0u};
-            if (c < C && t < M) {
+            if (unit_at(u, t, c, q)) {
+                float bt = beta_t[0], rt = rcp[0];
+#pragma unroll
+                for (int tt = 1; tt < MT; ++tt)
+                    if (tt == t) { bt = beta_t[tt]; rt = rcp[tt]; }
                 float4 v[4];
                 if constexpr (KEEP) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = xv[i][e];
+                    for (int e = 0; e < 4; ++e) v[e] = xv[k][e];
                 } else {
-                    const float4* src = reinterpret_cast<const float4*>(g.x + t * K + 64 * c + 16 * wave);
+                    const float4* src = reinterpret_cast<const float4*>(g.x + t * K + 64 * c + 16 * q);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) v[e] = src[e];
                 }
-                const u32x4 s = act_bytes16(v, beta_t[t], rcp[t]);
+                const u32x4 sb = act_bytes16(v, bt, rt);
                 if (exporter && g.xq_out)
-                    *reinterpret_cast<u32x4*>(g.xq_out + t * K + 64 * c + 16 * wave) = s;
-                o = transpose4x4_bytes(s);
-                part[t] += byte_sum(s.x) + byte_sum(s.y) + byte_sum(s.z) + byte_sum(s.w);
+                    *reinterpret_cast<u32x4*>(g.xq_out + t * K + 64 * c + 16 * q) = sb;
+                o = transpose4x4_bytes(sb);
+                add_part(t, byte_sum(sb.x) + byte_sum(sb.y) + byte_sum(sb.z) + byte_sum(sb.w));
             }
-            xs[i * 256 + tid] = o;
+            if (u < UNITS) xs[u] = o;
         }
         if (exporter && g.beta_out && tid < M) {
 #pragma unroll
@@ -198,16 +240,24 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs g) {
                 if (t == tid) g.beta_out[t] = beta_t[t];
         }
     } else {
+        u32x4 xr[UPT];
 #pragma unroll
-        for (int i = 0; i < MT * CPL; ++i) {
-            const int t = i / CPL, j = i % CPL, c = lane + 64 * j;
+        for (int k = 0; k < UPT; ++k) {
+            int t, c, q;
+            const bool valid = unit_at(tid + NT * k, t, c, q);
+            xr[k] = *reinterpret_cast<const u32x4*>(a.xq + (valid ? t * K + 64 * c + 16 * q : 0));
+        }
+        load_rows(wa, rb);
+#pragma unroll
+        for (int k = 0; k < UPT; ++k) {
+            const int u = tid + NT * k;
+            int t, c, q;
             u32x4 o = {0u, 0u, 0u, 0u};
-            if (c < C && t < M) {
-                const u32x4 s = *reinterpret_cast<const u32x4*>(a.xq + t * K + 64 * c + 16 * wave);
-                o = transpose4x4_bytes(s);
-                part[t] += byte_sum(s.x) + byte_sum(s.y) + byte_sum(s.z) + byte_sum(s.w);
+            if (unit_at(u, t, c, q)) {
+                o = transpose4x4_bytes(xr[k]);
+                add_part(t, byte_sum(xr[k].x) + byte_sum(xr[k].y) + byte_sum(xr[k].z) + byte_sum(xr[k].w));
             }
-            xs[i * 256 + tid] = o;
+            if (u < UNITS) xs[u] = o;
         }
 #pragma unroll
         for (int t = 0; t < MT; ++t) beta_t[t] = t < M ? a.beta[t] : 0.0f;
@@ -223,7 +273,9 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs g) {
     const float alpha0 = a.alpha_per_row ? 0.0f : a.alpha[0];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-        xsum[t] = red_i[t][0] + red_i[t][1] + red_i[t][2] + red_i[t][3];
+        xsum[t] = 0;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) xsum[t] += red_i[t][w];
         sc[t] = dequant_scale(alpha0, beta_t[t]);
     }
 
@@ -287,41 +339,61 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs g) {
 
     // ---- walk the row range, two register buffers in turn -------------------------------
     for (int64_t r0 = rb; r0 < re; r0 += 2 * R) {
-        if (r0 + R < re) load_rows(wb, r0 + R);
+        load_rows(wb, r0 + R);
         finish_rows(wa, r0);
         if (r0 + R >= re) break;
-        if (r0 + 2 * R < re) load_rows(wa, r0 + 2 * R);
+        load_rows(wa, r0 + 2 * R);
         finish_rows(wb, r0 + R);
     }
 }
 
 // ---------------------------------------------------------------------------------------
-// Launch shape.  The chip runs up to kWavesTarget waves of this kernel at once; each wave
-// gets ceil(N / waves) contiguous rows, walked R rows at a time.  R keeps R * CPL loads of
-// 16 bytes per lane per buffer (two buffers) within LMAX.
-constexpr int64_t kWavesTarget = 2048;
+// Launch shape.  With one token and at least 16 rows per CU, workgroups are 16 waves (one per
+// CU): the staging of x (read, and in the fused kernel absmax and quantization) is then done
+// once per CU instead of once per four waves.  Otherwise workgroups are four waves.  The grid
+// aims at `waves_target` waves; each wave gets ceil(N / waves) contiguous rows, walked R rows
+// at a time, R a power of two not above that count, with R * CPL loads of 16 bytes per lane
+// per buffer (two buffers) within LMAX.
+GemvShape gemv_shape(int64_t M, int64_t K, int64_t N) {
+    GemvShape sh{4, 2048};
+    if (M != 1) return sh;
+    const int64_t cpl = (K / 64 + 63) / 64;
+    // 16 waves need at most 128 VGPRs: rows of up to 3 chunks per lane; longer rows take 8
+    const int w = cpl <= 3 ? 16 : 8;
+    if (N >= (int64_t)w * 256) sh = GemvShape{w, (int64_t)w * 256};
+    return sh;
+}
 
-template <int MT, int CPL, bool FUSED>
-static hipError_t launch_cpl(const GemvArgs& g0, hipStream_t s) {
+template <int MT, int CPL, bool FUSED, int WAVES>
+static hipError_t launch_shape(const GemvArgs& g0, int64_t waves_target, hipStream_t s) {
     constexpr int LMAX = MT == 1 ? 8 : 4;
     GemvArgs g = g0;
     const int64_t N = g.f.N;
-    int64_t rpw = (N + kWavesTarget - 1) / kWavesTarget;
+    const int64_t rpw = (N + waves_target - 1) / waves_target;
     int R = 1;
-    while (R < 8 && R * 2 * CPL <= LMAX && R < rpw) R *= 2;
-    if (rpw < R) rpw = R;
+    while (R < 8 && R * 2 * CPL <= LMAX && 2 * R <= rpw) R *= 2;
     g.rows_per_wave = rpw;
     const int64_t waves = (N + rpw - 1) / rpw;
-    const int64_t blocks = (waves + 3) / 4;
+    const int64_t blocks = (waves + WAVES - 1) / WAVES;
     const size_t lds = (size_t)MT * CPL * 256 * 16;
-    const dim3 grid((unsigned)blocks), block(256);
+    const dim3 grid((unsigned)blocks), block(64 * WAVES);
     if constexpr (8 * CPL <= LMAX)
-        if (R == 8) return launch_with_lds(k_gemv<MT, CPL, 8, FUSED>, grid, block, lds, s, g);
+        if (R == 8) return launch_with_lds(k_gemv<MT, CPL, 8, FUSED, WAVES>, grid, block, lds, s, g);
     if constexpr (4 * CPL <= LMAX)
-        if (R == 4) return launch_with_lds(k_gemv<MT, CPL, 4, FUSED>, grid, block, lds, s, g);
+        if (R == 4) return launch_with_lds(k_gemv<MT, CPL, 4, FUSED, WAVES>, grid, block, lds, s, g);
     if constexpr (2 * CPL <= LMAX)
-        if (R == 2) return launch_with_lds(k_gemv<MT, CPL, 2, FUSED>, grid, block, lds, s, g);
-    return launch_with_lds(k_gemv<MT, CPL, 1, FUSED>, grid, block, lds, s, g);
+        if (R == 2) return launch_with_lds(k_gemv<MT, CPL, 2, FUSED, WAVES>, grid, block, lds, s, g);
+    return launch_with_lds(k_gemv<MT, CPL, 1, FUSED, WAVES>, grid, block, lds, s, g);
+}
+
+template <int MT, int CPL, bool FUSED>
+static hipError_t launch_cpl(const GemvArgs& g, hipStream_t s) {
+    const GemvShape sh = gemv_shape(g.f.M, g.f.K, g.f.N);
+    if constexpr (MT == 1 && CPL <= 3)
+        if (sh.waves_per_wg == 16) return launch_shape<MT, CPL, FUSED, 16>(g, sh.waves_target, s);
+    if constexpr (MT == 1 && CPL >= 4)
+        if (sh.waves_per_wg == 8) return launch_shape<MT, CPL, FUSED, 8>(g, sh.waves_target, s);
+    return launch_shape<MT, CPL, FUSED, 4>(g, sh.waves_target, s);
 }
 
 template <bool FUSED>

@@ -160,6 +160,10 @@ FWD_CASES = [
     (64, 4160, 33), (7, 28672, 20), (40, 2048, 300), (16, 16448, 65), (2, 32832, 17), (63, 320, 1000),
     (200, 4160, 130), (129, 192, 300), (1000, 128, 70), (96, 11008, 514),
     (1, 100, 33), (6, 4100, 65), (70, 12, 9),      # K % 64 != 0: generic kernel
+    # one token, the launch shapes of the decode GEMV: 16-wave workgroups (rows of <= 3 chunks per
+    # lane, N >= 4096) with 1, 3 and 4 rows per wave; 8-wave workgroups for longer rows; ragged N
+    (1, 4096, 4096), (1, 4096, 11008), (1, 12288, 4097), (1, 4096, 16385), (1, 16384, 2048),
+    (1, 28672, 2100), (1, 8192, 2048),
 ]
 
 
@@ -288,7 +292,8 @@ def test_repeatable_bitwise(dev):
 # ------------------------------------------------------------------ fused quantize + forward
 FUSED_CASES = [(1, 64, 5), (1, 1024, 1024), (1, 4096, 4096), (1, 4096, 11008), (1, 11008, 4096),
                (1, 28672, 1100), (1, 8192, 3000), (1, 32768, 70), (2, 4096, 300), (3, 11008, 130),
-               (4, 16384, 257), (4, 192, 4096)]
+               (4, 16384, 257), (4, 192, 4096),
+               (1, 12288, 4097), (1, 16384, 2048), (1, 28672, 2100), (1, 4096, 16385)]
 
 
 @pytest.mark.parametrize("m,k,n", FUSED_CASES)
