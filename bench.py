@@ -97,6 +97,42 @@ def decode_step_two_call(bl, shapes, copies, i):
         bl.bitlinear_forward(sh["xq"], sh["beta"], sh["pool"][i % copies], sh["alpha"], y=sh["y"])
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemv_fused_decode7b_hbm_traffic.md")
+KERNEL_SOURCES = ["gemv.hip", "common.hpp"]
+
+
+def kernel_source_sha():
+    """sha256 over the sources of the decode GEMV kernel (the traffic figure is void once they change)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "bitlinear_matmul_absmean_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def committed_traffic():
+    """HBM bytes per launch of the roofline kernel from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for a copy of known size),
+    or None when the summary is missing or the kernel sources have changed since it was taken."""
+    try:
+        with open(TRAFFIC_PROFILE) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].split(": ", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("source_sha256") != kernel_source_sha():
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
 def roofline_gemv(torch, bl, sh, copies, reps=480):
     """Dominant kernel: the fused decode GEMV on (K, N) = (4096, 11008), back to back in a
     graph on one stream, weights rotating through the pool."""
@@ -112,7 +148,7 @@ def roofline_gemv(torch, bl, sh, copies, reps=480):
                                                                 sh["alpha"], y=sh["y"]), reps)
     return dict(kernel=bl.bitlinear_forward_fused_kernel(1, k, n, sh["x"][0], sh["pool"][0]),
                 shape=dict(M=1, K=k, N=n), bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
-                unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=committed_traffic(),
                 us_per_launch=round(ms * 1e3, 3), bytes_per_launch=alg,
                 forward_only=dict(kernel="gemv_dot4", us_per_launch=round(ms_f * 1e3, 3),
                                   gbs=round((n * k // 4 + k + 4 * n) / (ms_f * 1e-3) / 1e9, 1)))
@@ -242,6 +278,107 @@ def cpu_baseline(workloads, budget_s=12.0):
                        f"{dt:.1f} s wall, output rows split over {cores} threads")
 
 
+def kernel_only(kind: str, launches: int):
+    """Run only one kernel, `launches` times, for counter collection under rocprofv3:
+    gemv_fused = the roofline kernel (decode GEMV, K=4096, N=11008, weights rotating through
+    64 copies so every launch reads HBM); copy = a plain 256 MiB device copy (calibrates
+    FETCH_SIZE / WRITE_SIZE); gemm = the prefill GEMM (M=2048, K=4096, N=11008)."""
+    import torch
+    import bitlinear_matmul_absmean_amd as bl
+    import workloads
+    dev = torch.device("cuda:0")
+    if kind == "copy":
+        nbytes = 256 << 20
+        a = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(launches):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copy: {launches} x {nbytes} B")
+        return
+    if kind == "gemv_fused":
+        k, n = DECODE_SHAPES[1]
+        w = torch.from_numpy(workloads.weights(2, n, k, index=1)).to(dev)
+        packed, alpha = bl.bitlinear_quantize_weights(w)
+        del w
+        pool = [packed] + [packed.clone() for _ in range(63)]
+        x = torch.from_numpy(workloads.activations(2, 1, k, index=100)).to(dev)
+        y = torch.empty((1, n), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        for i in range(launches):
+            bl.bitlinear_forward_fused(x, pool[i % len(pool)], alpha, y=y)
+        torch.cuda.synchronize()
+        log(f"gemv_fused: {launches} launches of {bl.bitlinear_forward_fused_kernel(1, k, n, x, packed)}")
+        return
+    if kind == "gemm":
+        m, k, n = 2048, 4096, 11008
+        w = torch.from_numpy(workloads.weights(4, n, k)).to(dev)
+        packed, alpha = bl.bitlinear_quantize_weights(w)
+        del w
+        x = torch.from_numpy(workloads.activations_with_outliers(4, m, k)).to(dev)
+        xq, beta = bl.bitlinear_quantize_act(x)
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(launches):
+            bl.bitlinear_forward(xq, beta, packed, alpha, y=y)
+        torch.cuda.synchronize()
+        log(f"gemm: {launches} launches")
+        return
+    raise SystemExit(f"unknown --kernel-only {kind}")
+
+
+def _pmc_means(d: str):
+    """{kernel name: {counter: mean value per dispatch}} from a rocprofv3 --pmc csv directory."""
+    import csv
+    import glob
+    from collections import defaultdict
+    acc = defaultdict(lambda: defaultdict(list))
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                acc[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return {k: {c: sum(v) / len(v) for c, v in cs.items()} | {"_n": max(len(v) for v in cs.values())}
+            for k, cs in acc.items()}
+
+
+def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, commands):
+    """Turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE, for the roofline kernel and
+    for the 256 MiB calibration copy) into the traffic summary kept under profiles/."""
+    def pick(means, key, counter):
+        cands = [(v["_n"], k, v[counter]) for k, v in means.items() if key in k and counter in v]
+        if not cands:
+            raise SystemExit(f"no kernel matching {key!r} with {counter} in the counter runs")
+        return max(cands)
+    nbytes = 256 << 20
+    _, gname, fetch_kib = pick(_pmc_means(fetch_dir), "k_gemv", "FETCH_SIZE")
+    _, _, write_kib = pick(_pmc_means(write_dir), "k_gemv", "WRITE_SIZE")
+    _, cname, cfetch_kib = pick(_pmc_means(cfetch_dir), "copy", "FETCH_SIZE")
+    _, _, cwrite_kib = pick(_pmc_means(cwrite_dir), "copy", "WRITE_SIZE")
+    ff = nbytes / (cfetch_kib * 1024.0)
+    fw = nbytes / (cwrite_kib * 1024.0)
+    k, n = DECODE_SHAPES[1]
+    alg = n * k // 4 + 4 * k + 4 + 4 * n
+    hbm = fetch_kib * 1024.0 * ff + write_kib * 1024.0 * fw
+    out = ["# HBM traffic of the decode GEMV (fused, M=1, K=4096, N=11008), from rocprofv3 counters", "",
+           "Commands (repository root, one MI355X):", "", "```"] + commands + ["```", "",
+           "FETCH_SIZE and WRITE_SIZE are read per dispatch in KiB and scaled by what they read for a "
+           f"plain device copy of {nbytes} bytes (`{cname}`): the copy fetches and writes exactly that many "
+           "bytes, so factor = bytes / (counter KiB * 1024).", "",
+           f"- kernel: `{gname}`",
+           f"- source_sha256: `{kernel_source_sha()}`",
+           f"- fetch_kib_per_launch: {fetch_kib:.1f}",
+           f"- write_kib_per_launch: {write_kib:.1f}",
+           f"- copy_fetch_kib: {cfetch_kib:.1f}",
+           f"- copy_write_kib: {cwrite_kib:.1f}",
+           f"- fetch_factor: {ff:.4f}",
+           f"- write_factor: {fw:.4f}",
+           f"- hbm_bytes_per_launch: {hbm:.0f}",
+           f"- algorithmic_bytes_per_launch: {alg}",
+           f"- traffic_over_algorithmic: {hbm / alg:.4f}", ""]
+    return "\n".join(out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -250,11 +387,24 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extras", action="store_true", help="headline workload and roofline only")
     ap.add_argument("--no-chain", action="store_true", help="skip the 70B-class chain")
+    ap.add_argument("--kernel-only", choices=["gemv_fused", "copy", "gemm"],
+                    help="run only this kernel (for rocprofv3 counter runs)")
+    ap.add_argument("--launches", type=int, default=50)
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("GEMV_FETCH", "GEMV_WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="write the traffic summary from four rocprofv3 --pmc output directories")
+    ap.add_argument("--pmc-commands", default="", help="';'-separated commands recorded in the summary")
     args = ap.parse_args()
+    if args.pmc_summary:
+        print(pmc_summary(*args.pmc_summary, [c.strip() for c in args.pmc_commands.split(";") if c.strip()]))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (see DESIGN.md, sharding). "
+        print("bench.py measures one GPU: the library has no multi-GPU path. "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.kernel_only:
+        kernel_only(args.kernel_only, args.launches)
+        return
 
     import torch
     import bitlinear_matmul_absmean_amd as bl

@@ -105,7 +105,7 @@ struct GemvShape {
     int waves_per_wg;         // 4 or 16
     int64_t waves_target;     // waves the grid aims at
 };
-GemvShape gemv_shape(int64_t M, int64_t K, int64_t N);
+GemvShape gemv_shape(int64_t M, int64_t K, int64_t N, bool fused);
 hipError_t launch_gemv_dot4(const ForwardArgs& a, hipStream_t s);
 hipError_t launch_gemv_fused(const ForwardArgs& a, const float* x, int8_t* xq_out, float* beta_out, hipStream_t s);
 bool gemm_supports_k(int64_t K);

@@ -131,9 +131,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(ForwardArgs a, int tiles_m
             boff[kk][j] = col * 4 + ((2 * kk + lg) ^ (((col >> 4) & 1) << 1));
         }
 
-    // One K step: read every operand of the step from LDS, issue the global loads two steps
-    // ahead, then run the 16 MFMAs with the staging of the next step (transpose, sums, LDS
-    // stores) and the second half's B expansion placed one piece after each MFMA.
+    // One K step with every piece of non-MFMA work cut into slices of about three VALU
+    // instructions, one slice after each MFMA.
     auto step = [&](int buf, const u32x4 (&rc)[APT], const u32x4& rbc, u32x4 (&rn)[APT], u32x4& rbn, int ksl, bool count) {
         uint32_t bw[2][FN];
         i32x4 av[2][FM];
@@ -153,18 +152,47 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(ForwardArgs a, int tiles_m
 #pragma unroll
         for (int j = 0; j < FN; ++j) b0[j] = unpack16(bw[0][j]);
         SB();
-        MF(0, 0, av[0][0], b0[0]); b1[0] = unpack16(bw[1][0]); SB();
-        MF(0, 1, av[0][0], b0[1]); b1[1] = unpack16(bw[1][1]); SB();
-        MF(1, 0, av[0][1], b0[0]); stage_a(rc[0], 0, buf ^ 1, count); SB();
-        MF(1, 1, av[0][1], b0[1]); stage_a(rc[1], 1, buf ^ 1, count); SB();
-        MF(2, 0, av[0][2], b0[0]); stage_b(rbc, buf ^ 1); SB();
-        MF(2, 1, av[0][2], b0[1]); SB();
-        MF(3, 0, av[0][3], b0[0]); SB();
-        MF(3, 1, av[0][3], b0[1]); SB();
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) MF(i, j, av[1][i], b1[j]);
+        const int ob = buf ^ 1;
+        // first half: B expansion of kk = 1 and the transposes of both A units
+        MF(0, 0, av[0][0], b0[0]);
+        b1[0].x = (int)(bw[1][0] & 0x03030303u); b1[0].y = (int)((bw[1][0] >> 2) & 0x03030303u); SB();
+        MF(0, 1, av[0][0], b0[1]);
+        b1[0].z = (int)((bw[1][0] >> 4) & 0x03030303u); b1[0].w = (int)((bw[1][0] >> 6) & 0x03030303u); SB();
+        MF(1, 0, av[0][1], b0[0]);
+        b1[1].x = (int)(bw[1][1] & 0x03030303u); b1[1].y = (int)((bw[1][1] >> 2) & 0x03030303u); SB();
+        MF(1, 1, av[0][1], b0[1]);
+        b1[1].z = (int)((bw[1][1] >> 4) & 0x03030303u); b1[1].w = (int)((bw[1][1] >> 6) & 0x03030303u); SB();
+        uint32_t q[2][4];
+        MF(2, 0, av[0][2], b0[0]);
+        q[0][0] = __builtin_amdgcn_perm(rc[0].y, rc[0].x, 0x05010400u); q[0][1] = __builtin_amdgcn_perm(rc[0].y, rc[0].x, 0x07030602u);
+        q[0][2] = __builtin_amdgcn_perm(rc[0].w, rc[0].z, 0x05010400u); q[0][3] = __builtin_amdgcn_perm(rc[0].w, rc[0].z, 0x07030602u); SB();
+        MF(2, 1, av[0][2], b0[1]);
+        As[ob][(tid / GK) * ASTR + tid % GK] = u32x4{__builtin_amdgcn_perm(q[0][2], q[0][0], 0x05040100u), __builtin_amdgcn_perm(q[0][2], q[0][0], 0x07060302u),
+                                                     __builtin_amdgcn_perm(q[0][3], q[0][1], 0x05040100u), __builtin_amdgcn_perm(q[0][3], q[0][1], 0x07060302u)};
+        SB();
+        MF(3, 0, av[0][3], b0[0]);
+        q[1][0] = __builtin_amdgcn_perm(rc[1].y, rc[1].x, 0x05010400u); q[1][1] = __builtin_amdgcn_perm(rc[1].y, rc[1].x, 0x07030602u);
+        q[1][2] = __builtin_amdgcn_perm(rc[1].w, rc[1].z, 0x05010400u); q[1][3] = __builtin_amdgcn_perm(rc[1].w, rc[1].z, 0x07030602u); SB();
+        MF(3, 1, av[0][3], b0[1]);
+        As[ob][((tid + 256) / GK) * ASTR + tid % GK] = u32x4{__builtin_amdgcn_perm(q[1][2], q[1][0], 0x05040100u), __builtin_amdgcn_perm(q[1][2], q[1][0], 0x07060302u),
+                                                             __builtin_amdgcn_perm(q[1][3], q[1][1], 0x05040100u), __builtin_amdgcn_perm(q[1][3], q[1][1], 0x07060302u)};
+        SB();
+        // second half: sums and the B store
+        int v0 = rs[0], v1 = rs[1];
+        MF(0, 0, av[1][0], b1[0]);
+        v0 = __builtin_amdgcn_sdot4((int)rc[0].x, 0x01010101, v0, false); v0 = __builtin_amdgcn_sdot4((int)rc[0].y, 0x01010101, v0, false); SB();
+        MF(0, 1, av[1][0], b1[1]);
+        v0 = __builtin_amdgcn_sdot4((int)rc[0].z, 0x01010101, v0, false); v0 = __builtin_amdgcn_sdot4((int)rc[0].w, 0x01010101, v0, false); SB();
+        MF(1, 0, av[1][1], b1[0]);
+        v1 = __builtin_amdgcn_sdot4((int)rc[1].x, 0x01010101, v1, false); v1 = __builtin_amdgcn_sdot4((int)rc[1].y, 0x01010101, v1, false); SB();
+        MF(1, 1, av[1][1], b1[1]);
+        v1 = __builtin_amdgcn_sdot4((int)rc[1].z, 0x01010101, v1, false); v1 = __builtin_amdgcn_sdot4((int)rc[1].w, 0x01010101, v1, false); SB();
+        MF(2, 0, av[1][2], b1[0]);
+        rs[0] = count ? v0 : rs[0]; rs[1] = count ? v1 : rs[1]; SB();
+        MF(2, 1, av[1][2], b1[1]);
+        stage_b(rbc, ob); SB();
+        MF(3, 0, av[1][3], b1[0]); SB();
+        MF(3, 1, av[1][3], b1[1]); SB();
     };
 
     // Two register stages: at the top of an iteration LDS buffer 0 holds step ks and ra1/rb1 hold

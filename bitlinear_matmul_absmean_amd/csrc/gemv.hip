@@ -348,19 +348,27 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(GemvArgs g) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Launch shape.  With one token and at least 16 rows per CU, workgroups are 16 waves (one per
-// CU): the staging of x (read, and in the fused kernel absmax and quantization) is then done
-// once per CU instead of once per four waves.  Otherwise workgroups are four waves.  The grid
-// aims at `waves_target` waves; each wave gets ceil(N / waves) contiguous rows, walked R rows
-// at a time, R a power of two not above that count, with R * CPL loads of 16 bytes per lane
-// per buffer (two buffers) within LMAX.
-GemvShape gemv_shape(int64_t M, int64_t K, int64_t N) {
+// Launch shape: waves per workgroup and the number of waves the grid aims at; each wave gets
+// ceil(N / waves) contiguous rows, walked R rows at a time (R a power of two not above that
+// count, R * CPL loads of 16 bytes per lane per buffer, two buffers, within LMAX).
+// Measured on MI355X over the decode shapes (one token):
+//  * forward (x_q given): with rows of one 64-weight chunk per lane (K <= 4096) many small
+//    workgroups win (4 waves, 8192 waves in all, 1-2 rows each: loads of many waves overlap
+//    the short compute of each); longer rows want about 2048 waves;
+//  * fused (x fp32 given): every workgroup reads all of x to find its absmax, so fewer, larger
+//    workgroups win: 8 waves and 2048 in all, or 16 waves and 4096 in all for rows of two or
+//    three chunks per lane (their registers fit the 128 that 16-wave workgroups allow).
+// Shapes with too few rows for that many waves per CU fall back to 4-wave workgroups.
+GemvShape gemv_shape(int64_t M, int64_t K, int64_t N, bool fused) {
     GemvShape sh{4, 2048};
     if (M != 1) return sh;
     const int64_t cpl = (K / 64 + 63) / 64;
-    // 16 waves need at most 128 VGPRs: rows of up to 3 chunks per lane; longer rows take 8
-    const int w = cpl <= 3 ? 16 : 8;
-    if (N >= (int64_t)w * 256) sh = GemvShape{w, (int64_t)w * 256};
+    GemvShape want;
+    if (!fused)
+        want = cpl == 1 ? GemvShape{4, N >= 8192 ? 8192 : 2048} : GemvShape{cpl <= 3 ? 4 : 8, 2048};
+    else
+        want = (cpl == 2 || cpl == 3) ? GemvShape{16, 4096} : GemvShape{8, 2048};
+    if (N >= (int64_t)want.waves_per_wg * 256) sh = want;
     return sh;
 }
 
@@ -388,10 +396,10 @@ static hipError_t launch_shape(const GemvArgs& g0, int64_t waves_target, hipStre
 
 template <int MT, int CPL, bool FUSED>
 static hipError_t launch_cpl(const GemvArgs& g, hipStream_t s) {
-    const GemvShape sh = gemv_shape(g.f.M, g.f.K, g.f.N);
+    const GemvShape sh = gemv_shape(g.f.M, g.f.K, g.f.N, FUSED);
     if constexpr (MT == 1 && CPL <= 3)
         if (sh.waves_per_wg == 16) return launch_shape<MT, CPL, FUSED, 16>(g, sh.waves_target, s);
-    if constexpr (MT == 1 && CPL >= 4)
+    if constexpr (MT == 1)
         if (sh.waves_per_wg == 8) return launch_shape<MT, CPL, FUSED, 8>(g, sh.waves_target, s);
     return launch_shape<MT, CPL, FUSED, 4>(g, sh.waves_target, s);
 }
