@@ -1,24 +1,30 @@
-// decode.hip -- batched-decode ternary x int8 matmul (a few to 64 tokens) on the int8 matrix
-// cores (v_mfma_i32_16x16x64_i8), gfx950.
+// decode.hip -- batched-decode ternary x int8 matmul (5 to 64 tokens) on the int8 matrix
+// cores (v_mfma_i32_32x32x32_i8 and v_mfma_i32_16x16x64_i8), gfx950.
 //
 // What is computed ([P3] chenxutan.com "1.58-bit 大模型极限量化实战" §2.4-§2.5, §3.2;
 // [P2] nxmr.cn "1.58 位大模型" §3.3): acc = x_q . W_hat^T (int32), y = fp32(acc) *
 // fp32(alpha*beta[m]/127) (+ bias).
 //
-// With up to 64 tokens the product is still bound by the weight stream (the ridge of int8
-// MFMA against HBM is near 78 tokens), so the weights are read exactly once, straight from
-// HBM into registers, 16 bytes (64 codes) per lane: lane (n, g) of a wave holds bytes
-// [16g, 16g+16) of a 64-byte block of row n, i.e. one wave load covers 16 rows x 256
-// weights.  Dword d of the lane's 16 bytes (16 codes) is expanded by four masks
-// (v >> 2i) & 0x03030303 into the lane's 16-byte B operand of MFMA number d, so byte 4i+j of
-// the operand is the code c = W+1 of weight k = 4j + i of that 16-weight group.
-//
-// Work split: a workgroup owns 16*RB rows and all tokens; its waves split K in 256-weight
-// chunks, round robin.  x_q is staged per K-phase into LDS with every 16-byte group
-// transposed 4x4 (byte 4i+j = x_q[k = 4j+i]), which is the A operand of the MFMA, so A and B
-// meet on the same k.  The per-token sum of x_q is accumulated while staging; since
-// c - 1 = W, acc = sum c*x_q - sum x_q.  The waves' partial 16x16 tiles are added in LDS at
-// the end (integer sums: order-free, exact).
+// With up to 64 tokens the product is bound by memory, not by the matrix cores (the ridge of
+// int8 MFMA against HBM is near 78 tokens), so the layout is chosen for bytes:
+//   * a workgroup of eight waves owns RB blocks of 32 weight rows, and the grid has about one
+//     workgroup per CU, so every workgroup reads its weight rows once and the activations
+//     x_q (M x K bytes) once;
+//   * the eight waves split K: wave w walks its own range of 128-weight sub-steps, loading
+//     its slice of x_q straight from global memory (cache-resident after the first
+//     workgroup) into MFMA A registers, with no LDS staging and no barrier in the main loop;
+//     only the eight partial 32 x 32 tiles per (row block, token block) are added through LDS
+//     at the end (integer sums: exact in any order);
+//   * inside a 128-weight sub-step, lane group g (lanes 32g..32g+31) takes the four 16-weight
+//     groups 4g..4g+3, so each lane reads 64 contiguous bytes of x_q per token block and 16
+//     contiguous bytes (64 codes) per weight row: A and B operands of one MFMA then sit at the
+//     same k, and every load covers whole 64-byte runs of a row;
+//   * a packed dword (16 codes, weight 4b+i at bits 2i of byte b) expands with four masks
+//     (v >> 2i) & 0x03030303 into the 16-byte B operand: byte 4i+j = c of weight 4j+i, with
+//     c = W + 1; the matching x_q bytes are transposed 4x4 with v_perm; acc = sum c*x_q -
+//     sum x_q, the per-token sum of x_q accumulated on the way.
+// MFMA 32x32x32 i8 lane layout (checked on the device): A/B lane l holds row/column l%32,
+// k = 16*(l/32)+j; accumulator r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
 #include "common.hpp"
 
 namespace bitlinear {
@@ -37,144 +43,320 @@ __device__ __forceinline__ u32x4 transpose4x4_perm(u32x4 s) {
     return o;
 }
 
-// MB: 16-token column blocks (tokens <= 16*MB); RB: 16-row blocks per workgroup;
-// WAVES: waves per workgroup (K split); KP: K-phase length staged in LDS (multiple of 256).
-template <int MB, int RB, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void k_decode_mfma(ForwardArgs a, int KP) {
-    extern __shared__ u32x4 lds[];
-    __shared__ int tsum[64];
+constexpr int BD_WAVES = 8;
+
+// MT: 32-token blocks (tokens <= 32*MT); RB: 32-row blocks per workgroup.
+template <int MT, int RB>
+__global__ __launch_bounds__(BD_WAVES * 64) void k_bdec(ForwardArgs a) {
+    extern __shared__ i32x4 red[];                 // [wave][RB*MT tiles][4][64] partial tiles
+    __shared__ int tsum_w[BD_WAVES][MT * 32];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int M = (int)a.M;
+    const int64_t K = a.K, N = a.N, rowb = K >> 2;
+    const int64_t n0 = (int64_t)blockIdx.x * (32 * RB);
+    const int lr = lane & 31, lg = lane >> 5;
+
+    // sub-steps of 128 weights; wave w takes [s0, s1)
+    const int SP = (int)((K + 127) / 128);
+    const int s0 = (int)((int64_t)SP * wave / BD_WAVES), s1 = (int)((int64_t)SP * (wave + 1) / BD_WAVES);
+
+    // operand sources (rows past M or N are clamped: their results are never written)
+    const int8_t* xrow[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) xrow[t] = a.xq + (int64_t)min(32 * t + lr, M - 1) * K;
+    const uint8_t* wrow[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) wrow[r] = a.wp + min(n0 + 32 * r + lr, N - 1) * rowb;
+
+    // loads of one sub-step; a lane group whose 64 weights lie past K (the last sub-step when
+    // K % 128 == 64) re-reads the first 64 weights of its rows and its x_q is zeroed, so the
+    // products vanish
+    u32x4 xa[3][MT][4], wb[3][RB];
+    auto load = [&](int st, int s) {
+        const int64_t k0 = (int64_t)s * 128 + 64 * lg;
+        const int64_t kx = k0 < K ? k0 : 0;
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) xa[st][t][q] = *reinterpret_cast<const u32x4*>(xrow[t] + kx + 16 * q);
+#pragma unroll
+        for (int r = 0; r < RB; ++r) wb[st][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[r] + kx / 4));
+    };
+
+    i32x16 acc[RB][MT];
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[r][t] = i32x16{};
+    int ts[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) ts[t] = 0;
+
+    auto compute = [&](int st, int s) {
+        const bool live = (int64_t)s * 128 + 64 * lg < K;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            i32x4 av[MT];
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const u32x4 v = live ? xa[st][t][q] : u32x4{0u, 0u, 0u, 0u};
+                av[t] = (i32x4)transpose4x4_perm(v);
+                int z = ts[t];
+                z = __builtin_amdgcn_sdot4((int)v.x, 0x01010101, z, false);
+                z = __builtin_amdgcn_sdot4((int)v.y, 0x01010101, z, false);
+                z = __builtin_amdgcn_sdot4((int)v.z, 0x01010101, z, false);
+                ts[t] = __builtin_amdgcn_sdot4((int)v.w, 0x01010101, z, false);
+            }
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const uint32_t w = q == 0 ? wb[st][r].x : q == 1 ? wb[st][r].y : q == 2 ? wb[st][r].z : wb[st][r].w;
+                const i32x4 bv = {(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u),
+                                  (int)((w >> 4) & 0x03030303u), (int)((w >> 6) & 0x03030303u)};
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+                    acc[r][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[t], bv, acc[r][t], 0, 0, 0);
+            }
+        }
+    };
+
+    // three register stages, loop unrolled by three: the loads of sub-steps s+1 and s+2 are in
+    // flight while s is computed (past the wave's range they re-read its last sub-step, whose
+    // data is then not used), so the compiler waits for one stage at a time
+    if (s0 < s1) {
+        const int last = s1 - 1;
+        load(0, s0);
+        load(1, min(s0 + 1, last));
+        load(2, min(s0 + 2, last));
+        int s = s0;
+        for (; s + 3 <= s1; s += 3) {
+            // scheduling barriers keep each load group where it is (the compiler would
+            // otherwise sink them and wait for nearly every load at the top of the loop)
+            compute(0, s);
+            __builtin_amdgcn_sched_barrier(0);
+            load(0, min(s + 3, last));
+            __builtin_amdgcn_sched_barrier(0);
+            compute(1, s + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            load(1, min(s + 4, last));
+            __builtin_amdgcn_sched_barrier(0);
+            compute(2, s + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            load(2, min(s + 5, last));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (s < s1) compute(0, s);
+        if (s + 1 < s1) compute(1, s + 1);
+    }
+
+    // per-token sums of x_q: lanes l and l+32 hold the two halves of token l%32's k range
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        const int v = ts[t] + __shfl_xor(ts[t], 32, 64);
+        if (lg == 0) tsum_w[wave][32 * t + lr] = v;
+    }
+    // partial tiles to LDS: tile (r, t) of wave w at red[((w * RB * MT + r * MT + t) * 4 + c) * 64 + lane]
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                red[((wave * RB * MT + r * MT + t) * 4 + c) * 64 + lane] =
+                    i32x4{acc[r][t][4 * c], acc[r][t][4 * c + 1], acc[r][t][4 * c + 2], acc[r][t][4 * c + 3]};
+    __syncthreads();
+
+    // epilogue: element e = (tile, c, lane) -> accumulator regs 4c..4c+3 of that lane:
+    // token 32 t + 8 c + 4 (lane / 32) + i, weight row n0 + 32 r + lane % 32
+    const float alpha0 = a.alpha_per_row ? 0.0f : a.alpha[0];
+    for (int e = tid; e < RB * MT * 4 * 64; e += BD_WAVES * 64) {
+        const int l = e & 63, c = (e >> 6) & 3, tile = e >> 8;
+        const int r = tile / MT, t = tile % MT;
+        i32x4 s = {0, 0, 0, 0};
+#pragma unroll
+        for (int w = 0; w < BD_WAVES; ++w) s += red[((w * RB * MT + tile) * 4 + c) * 64 + l];
+        const int64_t n = n0 + 32 * r + (l & 31);
+        if (n >= N) continue;
+        const float al = a.alpha_per_row ? a.alpha[n] : alpha0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = 32 * t + 8 * c + 4 * (l >> 5) + i;
+            if (m >= M) continue;
+            int xs = 0;
+#pragma unroll
+            for (int w = 0; w < BD_WAVES; ++w) xs += tsum_w[w][m];
+            const int total = s[i] - xs;
+            a.y[(int64_t)m * N + n] = dequant(total, dequant_scale(al, a.beta[m]), a.bias, n);
+            if (a.acc) a.acc[(int64_t)m * N + n] = total;
+        }
+    }
+}
+
+// The same scheme on 16 x 16 x 64 tiles for up to 16 tokens: four lanes share a weight row
+// (lane group g = l / 16 holds 64 contiguous weights of it), so a load instruction covers 16
+// rows x 64 bytes instead of 32 rows x 32 bytes, and x_q is loaded for 16 token rows instead
+// of 32.  Sub-steps of 256 weights; in MFMA q of a sub-step lane group g takes the 16-weight
+// group 4g + q.  16x16x64 lane layout (checked on the device): A/B lane l holds row/column
+// l%16, k = 16*(l/16)+j; accumulator r of lane l is row 4*(l/16) + r, column l%16.
+template <int MT, int RB>
+__global__ __launch_bounds__(BD_WAVES * 64) void k_bdec16(ForwardArgs a) {
+    extern __shared__ i32x4 red[];                 // [wave][RB * MT tiles][64]
+    __shared__ int tsum_w[BD_WAVES][16 * MT];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int M = (int)a.M;
     const int64_t K = a.K, N = a.N, rowb = K >> 2;
     const int64_t n0 = (int64_t)blockIdx.x * (16 * RB);
     const int lr = lane & 15, lg = lane >> 4;
-    const int ustride = KP / 16 + 1;           // LDS units per token row (one unit of padding)
+    const int SP = (int)((K + 255) / 256);
+    const int s0 = (int)((int64_t)SP * wave / BD_WAVES), s1 = (int)((int64_t)SP * (wave + 1) / BD_WAVES);
+    const int8_t* xrow[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) xrow[t] = a.xq + (int64_t)min(16 * t + lr, M - 1) * K;
+    const uint8_t* wrow[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) wrow[r] = a.wp + min(n0 + 16 * r + lr, N - 1) * rowb;
 
-    for (int i = tid; i < 64; i += WAVES * 64) tsum[i] = 0;
-
-    i32x4 acc[RB][MB];
+    // a lane group whose 64 weights lie past K (K % 256 != 0) re-reads the first 64 weights of
+    // its rows and its x_q is zeroed, so the products vanish
+    u32x4 xa[3][MT][4], wb[3][RB];
+    auto load = [&](int st, int s) {
+        const int64_t k0 = (int64_t)s * 256 + 64 * lg;
+        const int64_t kx = k0 < K ? k0 : 0;
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) xa[st][t][q] = *reinterpret_cast<const u32x4*>(xrow[t] + kx + 16 * q);
+#pragma unroll
+        for (int r = 0; r < RB; ++r) wb[st][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[r] + kx / 4));
+    };
+    i32x4 acc[RB][MT];
 #pragma unroll
     for (int r = 0; r < RB; ++r)
 #pragma unroll
-        for (int b = 0; b < MB; ++b) acc[r][b] = i32x4{0, 0, 0, 0};
-
-    // token row each lane feeds as A (rows past M repeat the last token; their results are dropped)
-    int arow[MB];
+        for (int t = 0; t < MT; ++t) acc[r][t] = i32x4{0, 0, 0, 0};
+    int ts[MT];
 #pragma unroll
-    for (int b = 0; b < MB; ++b) arow[b] = min(16 * b + lr, M - 1) * ustride;
-
-    for (int64_t p0 = 0; p0 < K; p0 += KP) {
-        const int kp = (int)(K - p0 < KP ? K - p0 : KP);
-        const int c0 = (int)(p0 / 256), c1 = (int)((p0 + kp + 255) / 256);
-
-        // 1. this wave's weight chunks of the phase: issue every load first
-        constexpr int CMAX = 8 / RB;           // chunks per wave per phase (host keeps KP small enough)
-        u32x4 w[CMAX][RB];
+    for (int t = 0; t < MT; ++t) ts[t] = 0;
+    auto compute = [&](int st, int s) {
+        const bool live = (int64_t)s * 256 + 64 * lg < K;
 #pragma unroll
-        for (int i = 0; i < CMAX; ++i) {
-            const int c = c0 + wave + WAVES * i;
-            const bool cv = c < c1 && (int64_t)c * 256 + 64 * lg < K;
+        for (int q = 0; q < 4; ++q) {
+            i32x4 av[MT];
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const u32x4 v = live ? xa[st][t][q] : u32x4{0u, 0u, 0u, 0u};
+                av[t] = (i32x4)transpose4x4_perm(v);
+                int z = ts[t];
+                z = __builtin_amdgcn_sdot4((int)v.x, 0x01010101, z, false);
+                z = __builtin_amdgcn_sdot4((int)v.y, 0x01010101, z, false);
+                z = __builtin_amdgcn_sdot4((int)v.z, 0x01010101, z, false);
+                ts[t] = __builtin_amdgcn_sdot4((int)v.w, 0x01010101, z, false);
+            }
 #pragma unroll
             for (int r = 0; r < RB; ++r) {
-                const int64_t n = n0 + 16 * r + lr;
-                w[i][r] = (cv && n < N)
-                              ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.wp + n * rowb + 64 * (int64_t)c + 16 * lg))
-                              : u32x4{0u, 0u, 0u, 0u};
+                const uint32_t w = q == 0 ? wb[st][r].x : q == 1 ? wb[st][r].y : q == 2 ? wb[st][r].z : wb[st][r].w;
+                const i32x4 bv = {(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u),
+                                  (int)((w >> 4) & 0x03030303u), (int)((w >> 6) & 0x03030303u)};
+#pragma unroll
+                for (int t = 0; t < MT; ++t) acc[r][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[t], bv, acc[r][t], 0, 0, 0);
             }
         }
-
-        // 2. stage x_q[:, p0 : p0 + kp] transposed; sum x_q per token
-        __syncthreads();                       // previous phase's readers are done
-        const int units = M * (kp / 16);
-        for (int u = tid; u < units; u += WAVES * 64) {
-            const int m = u / (kp / 16), gidx = u - m * (kp / 16);
-            const u32x4 s = *reinterpret_cast<const u32x4*>(a.xq + m * K + p0 + 16 * gidx);
-            lds[m * ustride + gidx] = transpose4x4_perm(s);
-            atomicAdd(&tsum[m], byte_sum(s.x) + byte_sum(s.y) + byte_sum(s.z) + byte_sum(s.w));
+    };
+    if (s0 < s1) {
+        const int last = s1 - 1;
+        load(0, s0);
+        load(1, min(s0 + 1, last));
+        load(2, min(s0 + 2, last));
+        int s = s0;
+        for (; s + 3 <= s1; s += 3) {
+            compute(0, s);
+            __builtin_amdgcn_sched_barrier(0);
+            load(0, min(s + 3, last));
+            __builtin_amdgcn_sched_barrier(0);
+            compute(1, s + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            load(1, min(s + 4, last));
+            __builtin_amdgcn_sched_barrier(0);
+            compute(2, s + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            load(2, min(s + 5, last));
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __syncthreads();
-
-        // 3. MFMAs
-#pragma unroll
-        for (int i = 0; i < CMAX; ++i) {
-            const int c = c0 + wave + WAVES * i;
-            if (c >= c1) break;
-            const int gbase = (int)((int64_t)c * 256 - p0) / 16 + 4 * lg;   // this lane group's first unit
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                i32x4 aop[MB];
-#pragma unroll
-                for (int b = 0; b < MB; ++b) aop[b] = (i32x4)lds[arow[b] + gbase + d];
-#pragma unroll
-                for (int r = 0; r < RB; ++r) {
-                    const uint32_t v = d == 0 ? w[i][r].x : d == 1 ? w[i][r].y : d == 2 ? w[i][r].z : w[i][r].w;
-                    const i32x4 bop = {(int)(v & 0x03030303u), (int)((v >> 2) & 0x03030303u),
-                                       (int)((v >> 4) & 0x03030303u), (int)((v >> 6) & 0x03030303u)};
-#pragma unroll
-                    for (int b = 0; b < MB; ++b)
-                        acc[r][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[b], bop, acc[r][b], 0, 0, 0);
-                }
-            }
-        }
+        if (s < s1) compute(0, s);
+        if (s + 1 < s1) compute(1, s + 1);
     }
-
-    // 4. add the waves' partial tiles (LDS reused), then the epilogue
-    __syncthreads();
+    // token sums: the four lane groups of token l%16 hold disjoint parts of its k range
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        int v = ts[t] + __shfl_xor(ts[t], 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        if (lg == 0) tsum_w[wave][16 * t + lr] = v;
+    }
 #pragma unroll
     for (int r = 0; r < RB; ++r)
 #pragma unroll
-        for (int b = 0; b < MB; ++b) lds[((r * MB + b) * WAVES + wave) * 64 + lane] = (u32x4)acc[r][b];
+        for (int t = 0; t < MT; ++t) red[(wave * RB * MT + r * MT + t) * 64 + lane] = acc[r][t];
     __syncthreads();
     const float alpha0 = a.alpha_per_row ? 0.0f : a.alpha[0];
-    for (int t = wave; t < RB * MB; t += WAVES) {
-        const int r = t / MB, b = t % MB;
-        i32x4 s = {0, 0, 0, 0};
-        for (int wv = 0; wv < WAVES; ++wv) s += (i32x4)lds[(t * WAVES + wv) * 64 + lane];
-        const int64_t n = n0 + 16 * r + lr;
+    for (int e = tid; e < RB * MT * 64; e += BD_WAVES * 64) {
+        const int l = e & 63, tile = e >> 6;
+        const int r = tile / MT, t = tile % MT;
+        i32x4 sum = {0, 0, 0, 0};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int m = 16 * b + 4 * lg + e;        // 16x16 result: lane l, element e -> row 4*(l/16)+e, col l%16
-            if (m < M && n < N) {
-                const int total = s[e] - tsum[m];
-                const float al = a.alpha_per_row ? a.alpha[n] : alpha0;
-                a.y[m * N + n] = dequant(total, dequant_scale(al, a.beta[m]), a.bias, n);
-                if (a.acc) a.acc[m * N + n] = total;
-            }
+        for (int w = 0; w < BD_WAVES; ++w) sum += red[(w * RB * MT + tile) * 64 + l];
+        const int64_t n = n0 + 16 * r + (l & 15);
+        if (n >= N) continue;
+        const float al = a.alpha_per_row ? a.alpha[n] : alpha0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = 16 * t + 4 * (l >> 4) + i;
+            if (m >= M) continue;
+            int xs = 0;
+#pragma unroll
+            for (int w = 0; w < BD_WAVES; ++w) xs += tsum_w[w][m];
+            const int total = sum[i] - xs;
+            a.y[(int64_t)m * N + n] = dequant(total, dequant_scale(al, a.beta[m]), a.bias, n);
+            if (a.acc) a.acc[(int64_t)m * N + n] = total;
         }
     }
 }
 
-template <int MB, int RB, int WAVES>
-static hipError_t launch_cfg(const ForwardArgs& a, hipStream_t s) {
-    // K-phase: each wave gets at most 8/RB chunks of 256 weights per phase, and the staged
-    // x_q phase must fit the LDS budget.
-    int kp = WAVES * (8 / RB) * 256;
-    const int64_t budget = 144 * 1024;
-    while (kp > 256 && ((int64_t)a.M * (kp / 16 + 1) + 16) * 16 > budget) kp /= 2;
-    const int64_t red = (int64_t)RB * MB * WAVES * 64 * 16;
-    // 16 spare units: a partial last chunk's idle lane groups address up to 11 units past a row
-    const int64_t stage = ((int64_t)a.M * (kp / 16 + 1) + 16) * 16;
-    const size_t lds = (size_t)(stage > red ? stage : red);
-    const dim3 grid((unsigned)((a.N + 16 * RB - 1) / (16 * RB))), block(WAVES * 64);
-    return launch_with_lds(k_decode_mfma<MB, RB, WAVES>, grid, block, lds, s, a, kp);
+template <int MT, int RB>
+static hipError_t launch_bdec16(const ForwardArgs& a, hipStream_t s) {
+    const int64_t blocks = (a.N + 16 * RB - 1) / (16 * RB);
+    const size_t lds = (size_t)BD_WAVES * RB * MT * 64 * sizeof(i32x4);
+    return launch_with_lds(k_bdec16<MT, RB>, dim3((unsigned)blocks), dim3(BD_WAVES * 64), lds, s, a);
+}
+
+template <int MT, int RB>
+static hipError_t launch_bdec(const ForwardArgs& a, hipStream_t s) {
+    const int64_t blocks = (a.N + 32 * RB - 1) / (32 * RB);
+    const size_t lds = (size_t)BD_WAVES * RB * MT * 4 * 64 * sizeof(i32x4);
+    return launch_with_lds(k_bdec<MT, RB>, dim3((unsigned)blocks), dim3(BD_WAVES * 64), lds, s, a);
 }
 
 bool decode_mfma_supports(int64_t M, int64_t K) { return M >= 1 && M <= 64 && K % 64 == 0; }
 
+// Tile shape by token count: 16 x 16 x 64 tiles up to 32 tokens (better weight loads, fewer
+// token rows of x_q), 32 x 32 x 32 tiles up to 64.  Row blocks per workgroup: the fewest that
+// keep the grid within about one workgroup per CU (256), so that x_q is read as few times as
+// possible, within the registers (no spills) and the LDS of the final reduction.
 hipError_t launch_decode_mfma(const ForwardArgs& a, hipStream_t s) {
-    // enough workgroups to cover the chip with 16*RB rows each
-    const int64_t N = a.N;
+    const int64_t nb16 = (a.N + 15) / 16;
     if (a.M <= 16) {
-        if (N >= 8192) return launch_cfg<1, 2, 4>(a, s);
-        return launch_cfg<1, 1, 4>(a, s);
+        if (nb16 <= 256) return launch_bdec16<1, 1>(a, s);
+        if (nb16 <= 512) return launch_bdec16<1, 2>(a, s);
+        if (nb16 <= 1024) return launch_bdec16<1, 4>(a, s);
+        return launch_bdec16<1, 8>(a, s);
     }
     if (a.M <= 32) {
-        if (N >= 8192) return launch_cfg<2, 2, 4>(a, s);
-        return launch_cfg<2, 1, 4>(a, s);
+        if (nb16 <= 256) return launch_bdec16<2, 1>(a, s);
+        return launch_bdec16<2, 2>(a, s);
     }
-    if (N >= 8192) return launch_cfg<4, 2, 8>(a, s);
-    return launch_cfg<4, 1, 8>(a, s);
+    const int64_t nb = (a.N + 31) / 32;
+    if (nb <= 256) return launch_bdec<2, 1>(a, s);
+    return launch_bdec<2, 2>(a, s);
 }
 
 }  // namespace bitlinear

@@ -164,6 +164,10 @@ FWD_CASES = [
     # lane, N >= 4096) with 1, 3 and 4 rows per wave; 8-wave workgroups for longer rows; ragged N
     (1, 4096, 4096), (1, 4096, 11008), (1, 12288, 4097), (1, 4096, 16385), (1, 16384, 2048),
     (1, 28672, 2100), (1, 8192, 2048),
+    # batched decode launch shapes: 16x16x64 tiles with 1/2/4/8 row blocks per workgroup and one or
+    # two token blocks, 32x32x32 tiles with 1/2; K % 256 = 64 and K % 128 = 64 tails; ragged N
+    (8, 256, 9000), (12, 128, 17000), (16, 192, 5000), (9, 4160, 700), (24, 320, 4100),
+    (32, 64, 8300), (20, 4352, 300), (48, 192, 8200), (64, 4160, 600), (41, 128, 33),
 ]
 
 
