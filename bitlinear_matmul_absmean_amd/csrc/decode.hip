@@ -46,42 +46,51 @@ __device__ __forceinline__ u32x4 transpose4x4_perm(u32x4 s) {
 constexpr int BD_WAVES = 8;
 
 // MT: 32-token blocks (tokens <= 32*MT); RB: 32-row blocks per workgroup.
+// x_q goes through a wave-private LDS region: eight lanes read one token's 128 bytes of a
+// sub-step (whole cache lines; a load instruction covers 8 tokens), transpose each 16-byte
+// group 4x4 and store it; the MFMA A operands are then read back from LDS.  Reading x_q
+// straight into the operand layout would touch 16 bytes of each of 32 token rows per load
+// instruction, which the texture path serves one cache line at a time.
 template <int MT, int RB>
 __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec(ForwardArgs a) {
-    extern __shared__ i32x4 red[];                 // [wave][RB*MT tiles][4][64] partial tiles
+    // first the x_q staging ([wave][MT * 32 token rows][XU units]), then the partial tiles
+    extern __shared__ i32x4 red[];
     __shared__ int tsum_w[BD_WAVES][MT * 32];
+    constexpr int XU = 9;                          // 16-byte units per token row (8 + 1 of padding)
+    constexpr int XR = MT * 32 * XU;               // units of one wave's region
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int M = (int)a.M;
     const int64_t K = a.K, N = a.N, rowb = K >> 2;
     const int64_t n0 = (int64_t)blockIdx.x * (32 * RB);
     const int lr = lane & 31, lg = lane >> 5;
+    i32x4* xs = red + wave * XR;
 
     // sub-steps of 128 weights; wave w takes [s0, s1)
     const int SP = (int)((K + 127) / 128);
     const int s0 = (int)((int64_t)SP * wave / BD_WAVES), s1 = (int)((int64_t)SP * (wave + 1) / BD_WAVES);
 
-    // operand sources (rows past M or N are clamped: their results are never written)
-    const int8_t* xrow[MT];
+    // x_q loads: instruction i covers tokens 8i + lane/8, unit u = lane % 8 (16 bytes at k0 + 16u);
+    // weight loads: lane (lr, lg) reads 16 bytes (64 codes at k0 + 64 lg) of row n0 + 32r + lr.
+    // Rows past M or N are clamped (never written); past K (the last sub-step when
+    // K % 128 == 64) the loads re-read the row start and the staged x_q is zeroed.
+    const int xu = lane & 7, xt = lane >> 3;
+    const int8_t* xrow[MT * 4];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) xrow[t] = a.xq + (int64_t)min(32 * t + lr, M - 1) * K;
+    for (int i = 0; i < MT * 4; ++i) xrow[i] = a.xq + (int64_t)min(8 * i + xt, M - 1) * K + 16 * xu;
     const uint8_t* wrow[RB];
 #pragma unroll
     for (int r = 0; r < RB; ++r) wrow[r] = a.wp + min(n0 + 32 * r + lr, N - 1) * rowb;
 
-    // loads of one sub-step; a lane group whose 64 weights lie past K (the last sub-step when
-    // K % 128 == 64) re-reads the first 64 weights of its rows and its x_q is zeroed, so the
-    // products vanish
-    u32x4 xa[3][MT][4], wb[3][RB];
+    u32x4 xa[2][MT * 4], wb[2][RB];
     auto load = [&](int st, int s) {
-        const int64_t k0 = (int64_t)s * 128 + 64 * lg;
-        const int64_t kx = k0 < K ? k0 : 0;
+        const int64_t kx = (int64_t)s * 128 + 16 * xu < K ? (int64_t)s * 128 : 0;
 #pragma unroll
-        for (int t = 0; t < MT; ++t)
+        for (int i = 0; i < MT * 4; ++i) xa[st][i] = *reinterpret_cast<const u32x4*>(xrow[i] + kx);
+        const int64_t kw = (int64_t)s * 128 + 64 * lg;
+        const int64_t kwx = kw < K ? kw : 0;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) xa[st][t][q] = *reinterpret_cast<const u32x4*>(xrow[t] + kx + 16 * q);
-#pragma unroll
-        for (int r = 0; r < RB; ++r) wb[st][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[r] + kx / 4));
+        for (int r = 0; r < RB; ++r) wb[st][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[r] + kwx / 4));
     };
 
     i32x16 acc[RB][MT];
@@ -89,72 +98,76 @@ __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec(ForwardArgs a) {
     for (int r = 0; r < RB; ++r)
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[r][t] = i32x16{};
-    int ts[MT];
+    int ts[MT * 4];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) ts[t] = 0;
+    for (int i = 0; i < MT * 4; ++i) ts[i] = 0;
 
     auto compute = [&](int st, int s) {
-        const bool live = (int64_t)s * 128 + 64 * lg < K;
+        // stage x_q (transposed) and expand the weights of this sub-step
+        const bool xlive = (int64_t)s * 128 + 16 * xu < K;
+#pragma unroll
+        for (int i = 0; i < MT * 4; ++i) {
+            const u32x4 v = xlive ? xa[st][i] : u32x4{0u, 0u, 0u, 0u};
+            xs[(8 * i + xt) * XU + xu] = (i32x4)transpose4x4_perm(v);
+            int z = ts[i];
+            z = __builtin_amdgcn_sdot4((int)v.x, 0x01010101, z, false);
+            z = __builtin_amdgcn_sdot4((int)v.y, 0x01010101, z, false);
+            z = __builtin_amdgcn_sdot4((int)v.z, 0x01010101, z, false);
+            ts[i] = __builtin_amdgcn_sdot4((int)v.w, 0x01010101, z, false);
+        }
+        i32x4 bv[RB][4];
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t w = q == 0 ? wb[st][r].x : q == 1 ? wb[st][r].y : q == 2 ? wb[st][r].z : wb[st][r].w;
+                bv[r][q] = i32x4{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u),
+                                 (int)((w >> 4) & 0x03030303u), (int)((w >> 6) & 0x03030303u)};
+            }
+        // in MFMA q, lane group g takes the 16-weight group 4g + q of the sub-step
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             i32x4 av[MT];
 #pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                const u32x4 v = live ? xa[st][t][q] : u32x4{0u, 0u, 0u, 0u};
-                av[t] = (i32x4)transpose4x4_perm(v);
-                int z = ts[t];
-                z = __builtin_amdgcn_sdot4((int)v.x, 0x01010101, z, false);
-                z = __builtin_amdgcn_sdot4((int)v.y, 0x01010101, z, false);
-                z = __builtin_amdgcn_sdot4((int)v.z, 0x01010101, z, false);
-                ts[t] = __builtin_amdgcn_sdot4((int)v.w, 0x01010101, z, false);
-            }
+            for (int t = 0; t < MT; ++t) av[t] = xs[(32 * t + lr) * XU + 4 * lg + q];
 #pragma unroll
-            for (int r = 0; r < RB; ++r) {
-                const uint32_t w = q == 0 ? wb[st][r].x : q == 1 ? wb[st][r].y : q == 2 ? wb[st][r].z : wb[st][r].w;
-                const i32x4 bv = {(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u),
-                                  (int)((w >> 4) & 0x03030303u), (int)((w >> 6) & 0x03030303u)};
+            for (int r = 0; r < RB; ++r)
 #pragma unroll
                 for (int t = 0; t < MT; ++t)
-                    acc[r][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[t], bv, acc[r][t], 0, 0, 0);
-            }
+                    acc[r][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[t], bv[r][q], acc[r][t], 0, 0, 0);
         }
     };
 
-    // three register stages, loop unrolled by three: the loads of sub-steps s+1 and s+2 are in
-    // flight while s is computed (past the wave's range they re-read its last sub-step, whose
-    // data is then not used), so the compiler waits for one stage at a time
+    // two register stages; each sub-step first consumes its stage (LDS store, weight expansion),
+    // then the stage is refilled with the sub-step after next
     if (s0 < s1) {
         const int last = s1 - 1;
         load(0, s0);
         load(1, min(s0 + 1, last));
-        load(2, min(s0 + 2, last));
         int s = s0;
-        for (; s + 3 <= s1; s += 3) {
-            // scheduling barriers keep each load group where it is (the compiler would
-            // otherwise sink them and wait for nearly every load at the top of the loop)
+        for (; s + 2 <= s1; s += 2) {
             compute(0, s);
             __builtin_amdgcn_sched_barrier(0);
-            load(0, min(s + 3, last));
+            load(0, min(s + 2, last));
             __builtin_amdgcn_sched_barrier(0);
             compute(1, s + 1);
             __builtin_amdgcn_sched_barrier(0);
-            load(1, min(s + 4, last));
-            __builtin_amdgcn_sched_barrier(0);
-            compute(2, s + 2);
-            __builtin_amdgcn_sched_barrier(0);
-            load(2, min(s + 5, last));
+            load(1, min(s + 3, last));
             __builtin_amdgcn_sched_barrier(0);
         }
         if (s < s1) compute(0, s);
-        if (s + 1 < s1) compute(1, s + 1);
     }
 
-    // per-token sums of x_q: lanes l and l+32 hold the two halves of token l%32's k range
+    // per-token sums of x_q: the eight lanes xt of a token hold its eight 16-byte groups
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-        const int v = ts[t] + __shfl_xor(ts[t], 32, 64);
-        if (lg == 0) tsum_w[wave][32 * t + lr] = v;
+    for (int i = 0; i < MT * 4; ++i) {
+        int v = ts[i];
+        v += __shfl_xor(v, 1, 64);
+        v += __shfl_xor(v, 2, 64);
+        v += __shfl_xor(v, 4, 64);
+        if (xu == 0) tsum_w[wave][8 * i + xt] = v;
     }
+    __syncthreads();                               // every wave is done with its staging region
     // partial tiles to LDS: tile (r, t) of wave w at red[((w * RB * MT + r * MT + t) * 4 + c) * 64 + lane]
 #pragma unroll
     for (int r = 0; r < RB; ++r)
@@ -172,9 +185,9 @@ __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec(ForwardArgs a) {
     for (int e = tid; e < RB * MT * 4 * 64; e += BD_WAVES * 64) {
         const int l = e & 63, c = (e >> 6) & 3, tile = e >> 8;
         const int r = tile / MT, t = tile % MT;
-        i32x4 s = {0, 0, 0, 0};
+        i32x4 sum = {0, 0, 0, 0};
 #pragma unroll
-        for (int w = 0; w < BD_WAVES; ++w) s += red[((w * RB * MT + tile) * 4 + c) * 64 + l];
+        for (int w = 0; w < BD_WAVES; ++w) sum += red[((w * RB * MT + tile) * 4 + c) * 64 + l];
         const int64_t n = n0 + 32 * r + (l & 31);
         if (n >= N) continue;
         const float al = a.alpha_per_row ? a.alpha[n] : alpha0;
@@ -182,14 +195,22 @@ __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec(ForwardArgs a) {
         for (int i = 0; i < 4; ++i) {
             const int m = 32 * t + 8 * c + 4 * (l >> 5) + i;
             if (m >= M) continue;
-            int xs = 0;
+            int xs_ = 0;
 #pragma unroll
-            for (int w = 0; w < BD_WAVES; ++w) xs += tsum_w[w][m];
-            const int total = s[i] - xs;
+            for (int w = 0; w < BD_WAVES; ++w) xs_ += tsum_w[w][m];
+            const int total = sum[i] - xs_;
             a.y[(int64_t)m * N + n] = dequant(total, dequant_scale(al, a.beta[m]), a.bias, n);
             if (a.acc) a.acc[(int64_t)m * N + n] = total;
         }
     }
+}
+
+template <int MT, int RB>
+static hipError_t launch_bdec(const ForwardArgs& a, hipStream_t s) {
+    const int64_t blocks = (a.N + 32 * RB - 1) / (32 * RB);
+    const size_t stage = (size_t)BD_WAVES * MT * 32 * 9 * sizeof(i32x4);
+    const size_t tiles = (size_t)BD_WAVES * RB * MT * 4 * 64 * sizeof(i32x4);
+    return launch_with_lds(k_bdec<MT, RB>, dim3((unsigned)blocks), dim3(BD_WAVES * 64), stage > tiles ? stage : tiles, s, a);
 }
 
 // The same scheme on 16 x 16 x 64 tiles for up to 16 tokens: four lanes share a weight row
@@ -329,12 +350,6 @@ static hipError_t launch_bdec16(const ForwardArgs& a, hipStream_t s) {
     return launch_with_lds(k_bdec16<MT, RB>, dim3((unsigned)blocks), dim3(BD_WAVES * 64), lds, s, a);
 }
 
-template <int MT, int RB>
-static hipError_t launch_bdec(const ForwardArgs& a, hipStream_t s) {
-    const int64_t blocks = (a.N + 32 * RB - 1) / (32 * RB);
-    const size_t lds = (size_t)BD_WAVES * RB * MT * 4 * 64 * sizeof(i32x4);
-    return launch_with_lds(k_bdec<MT, RB>, dim3((unsigned)blocks), dim3(BD_WAVES * 64), lds, s, a);
-}
 
 bool decode_mfma_supports(int64_t M, int64_t K) { return M >= 1 && M <= 64 && K % 64 == 0; }
 
