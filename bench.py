@@ -154,6 +154,62 @@ def roofline_gemv(torch, bl, sh, copies, reps=480):
                                   gbs=round((n * k // 4 + k + 4 * n) / (ms_f * 1e-3) / 1e9, 1)))
 
 
+def ceilings(torch, dev, read_sizes):
+    """Measured ceilings on this GPU, timed like the path's kernels: a streaming read
+    (bitlinear_ceiling_read) at each size in `read_sizes`, rotating through 2 GiB of distinct
+    data, and an MFMA-only loop of v_mfma_i32_32x32x32_i8 with random and with constant operands."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "bitlinear_matmul_absmean_amd", "libbitlinear_ceiling.so"))
+    lib.bitlinear_ceiling_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    lib.bitlinear_ceiling_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p]
+    pool_bytes = 2 << 30
+    pool = torch.ones(pool_bytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+    out = {"hbm_read_gbs": {}, "mfma_i8_tops": {}}
+    for size in read_sizes:
+        size = (size + 4095) // 4096 * 4096
+        copies = max(1, pool_bytes // size)
+        reps = 200 if size < (64 << 20) else 10
+
+        def rd(i, size=size, copies=copies):
+            st = torch.cuda.current_stream().cuda_stream
+            rc = lib.bitlinear_ceiling_read(ctypes.c_void_p(pool.data_ptr() + (i % copies) * size), size,
+                                            ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(st))
+            if rc != 0:
+                raise RuntimeError(f"bitlinear_ceiling_read failed ({rc})")
+        ms, _ = _graph_time(torch, rd, reps)
+        out["hbm_read_gbs"][str(size)] = round(size / (ms * 1e-3) / 1e9, 1)
+    del pool
+    g = torch.Generator(device="cpu").manual_seed(1580)
+    for kind in ("random", "constant"):
+        if kind == "random":
+            ops_h = torch.randint(-2**31, 2**31 - 1, (65536,), dtype=torch.int64, generator=g).to(torch.int32)
+        else:
+            ops_h = torch.full((65536,), 0x03030303, dtype=torch.int32)
+        ops_d = ops_h.to(dev)
+        nops = ctypes.c_int64(0)
+        st = torch.cuda.current_stream().cuda_stream
+        blocks, iters = 512, 2000
+        for _ in range(2):
+            lib.bitlinear_ceiling_mfma(blocks, iters, ctypes.c_void_p(ops_d.data_ptr()), ctypes.c_void_p(sink.data_ptr()),
+                                       ctypes.byref(nops), ctypes.c_void_p(st))
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            rc = lib.bitlinear_ceiling_mfma(blocks, iters, ctypes.c_void_p(ops_d.data_ptr()), ctypes.c_void_p(sink.data_ptr()),
+                                            ctypes.byref(nops), ctypes.c_void_p(st))
+            if rc != 0:
+                raise RuntimeError(f"bitlinear_ceiling_mfma failed ({rc})")
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        out["mfma_i8_tops"][kind] = round(nops.value / (ms * 1e-3) / 1e12, 1)
+    torch.cuda.empty_cache()
+    return out
+
+
 def prefill_bench(torch, bl, workloads, dev, k=4096, n=11008, m=2048, reps=20):
     w = torch.from_numpy(workloads.weights(4, n, k)).to(dev)
     packed, alpha = bl.bitlinear_quantize_weights(w)
@@ -426,17 +482,26 @@ def main():
 
     roof = roofline_gemv(torch, bl, shapes[1], copies)
     log(f"roofline {roof}")
+    del shapes
+    torch.cuda.empty_cache()
     extras = {}
     if not args.no_extras:
         extras["prefill"] = prefill_bench(torch, bl, workloads, dev)
         log(f"prefill {extras['prefill']}")
         extras["batched"] = batched_bench(torch, bl, workloads, dev)
         log(f"batched {extras['batched']}")
-    del shapes
-    torch.cuda.empty_cache()
     if not args.no_extras and not args.no_chain:
         extras["chain70b"] = chain70b_bench(torch, bl, workloads, dev)
         log(f"chain70b {extras['chain70b']}")
+    # measured ceilings last: the MFMA loop heats the chip, which would slow what follows it
+    ceil = ceilings(torch, dev, [roof["bytes_per_launch"], 1 << 30])
+    log(f"ceilings {ceil}")
+    read_ceiling = list(ceil["hbm_read_gbs"].values())[0]
+    roof["measured_ceiling"] = {"gbs": read_ceiling, "what": "streaming read of the same byte count, same timing",
+                                "frac": round(roof["achieved"] / read_ceiling, 4)}
+    if "prefill" in extras:
+        extras["prefill"]["pct_measured_mfma_random"] = round(
+            100 * extras["prefill"]["tops"] / ceil["mfma_i8_tops"]["random"], 2)
     cpu = None if args.no_cpu else cpu_baseline(workloads)
 
     line = {
@@ -452,6 +517,7 @@ def main():
         "decode_two_call": {"us_per_step": round(ms_two * 1e3, 2),
                             "weight_gbs": round(per_step / (ms_two * 1e-3) / 1e9, 1)},
         "roofline": roof,
+        "ceilings": ceil,
         "cpu_baseline": cpu,
     }
     line.update(extras)

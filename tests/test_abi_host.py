@@ -22,8 +22,8 @@ def bl():
     return m
 
 
-def _declared():
-    src = open(HEADER).read()
+def _declared(header=HEADER):
+    src = open(header).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(bitlinear_[a-z0-9_]+)\s*\(", src)))
 
@@ -36,6 +36,22 @@ def test_header_symbols_are_exported(bl):
         assert hasattr(lib, n), f"{n} declared in bitlinear.h but not exported"
     # and the binding knows each of them
     assert set(names) <= set(bl.SIGNATURES)
+
+
+def test_ceiling_library_exports_its_header(bl):
+    """The measurement kernels live in their own library, declared by bitlinear_ceiling.h."""
+    names = _declared(os.path.join(ROOT, "include", "bitlinear_ceiling.h"))
+    assert names == ["bitlinear_ceiling_mfma", "bitlinear_ceiling_read"]
+    lib = ctypes.CDLL(os.path.join(ROOT, "bitlinear_matmul_absmean_amd", "libbitlinear_ceiling.so"))
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in bitlinear_ceiling.h but not exported"
+    # invalid arguments are rejected before any HIP call
+    lib.bitlinear_ceiling_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.bitlinear_ceiling_read(None, 16, None, None) == -1
+    assert lib.bitlinear_ceiling_read(ctypes.c_void_p(16), 15, ctypes.c_void_p(16), None) == -1
+    lib.bitlinear_ceiling_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.bitlinear_ceiling_mfma(0, 1, ctypes.c_void_p(16), ctypes.c_void_p(16), None, None) == -1
 
 
 def test_abi_version_and_status_strings(bl):
