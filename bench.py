@@ -226,6 +226,41 @@ def prefill_bench(torch, bl, workloads, dev, k=4096, n=11008, m=2048, reps=20):
                 end_to_end_tops=round(2.0 * m * n * k / ((ms + msq) * 1e-3) / 1e12, 1))
 
 
+def quantize_bench(torch, bl, workloads, dev, reps=20):
+    """a1 and a2 against the HBM roofline.  Weight quantization (offline, once per layer) reads W
+    twice (absmean first, then the codes) and writes the packed bytes: 8NK + NK/4 bytes for
+    W [11008, 4096].  Activation quantization reads x and writes x_q and beta: 5MK + 4M bytes,
+    for the prefill batch (M = 2048, K = 4096) and one decode token (M = 1, K = 4096)."""
+    n, k = 11008, 4096
+    w = torch.from_numpy(workloads.weights(4, n, k)).to(dev)
+    packed = torch.empty((n, k // 4), dtype=torch.uint8, device=dev)
+    alpha = torch.empty(1, dtype=torch.float32, device=dev)
+    alpha_rows = torch.empty(n, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(8, bl.lib.bitlinear_quantize_weights_workspace_size(n, k)), dtype=torch.uint8, device=dev)
+    ms_w, _ = _graph_time(torch, lambda i: bl.bitlinear_quantize_weights(w, packed, alpha, ws), reps)
+    ms_r, _ = _graph_time(torch, lambda i: bl.bitlinear_quantize_weights_rows(w, packed, alpha_rows), reps)
+    del w
+    bw = 8 * n * k + n * k // 4
+    out = {"quantize_weights": {"shape": dict(N=n, K=k), "alg_bytes": bw, "us": round(ms_w * 1e3, 2),
+                                "gbs": round(bw / (ms_w * 1e-3) / 1e9, 1),
+                                "pct_hbm": round(100 * bw / (ms_w * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                                "per_row_alpha_us": round(ms_r * 1e3, 2)}}
+    acts = []
+    for m in (2048, 1):
+        x = torch.from_numpy(workloads.activations_with_outliers(4, m, k) if m > 1 else
+                             workloads.activations(2, 1, k)).to(dev)
+        xq = torch.empty((m, k), dtype=torch.int8, device=dev)
+        beta = torch.empty(m, dtype=torch.float32, device=dev)
+        ms, _ = _graph_time(torch, lambda i: bl.bitlinear_quantize_act(x, xq, beta), 200 if m == 1 else reps)
+        ba = 5 * m * k + 4 * m
+        acts.append({"M": m, "K": k, "alg_bytes": ba, "us": round(ms * 1e3, 2),
+                     "gbs": round(ba / (ms * 1e-3) / 1e9, 1),
+                     "pct_hbm": round(100 * ba / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)})
+    out["quantize_act"] = acts
+    torch.cuda.empty_cache()
+    return out
+
+
 def batched_bench(torch, bl, workloads, dev, reps=96):
     out = []
     for (k, n) in [(4096, 11008), (11008, 4096)]:
@@ -490,6 +525,9 @@ def main():
         log(f"prefill {extras['prefill']}")
         extras["batched"] = batched_bench(torch, bl, workloads, dev)
         log(f"batched {extras['batched']}")
+        extras.update(quantize_bench(torch, bl, workloads, dev))
+        log(f"quantize_weights {extras['quantize_weights']}")
+        log(f"quantize_act {extras['quantize_act']}")
     if not args.no_extras and not args.no_chain:
         extras["chain70b"] = chain70b_bench(torch, bl, workloads, dev)
         log(f"chain70b {extras['chain70b']}")
