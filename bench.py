@@ -286,19 +286,36 @@ def batched_bench(torch, bl, workloads, dev, reps=96):
 def chain70b_bench(torch, bl, workloads, dev, layers=80, reps=3):
     """One decode step of the 70B-class stream: 80 layers x 7 projections, one fused call
     each (the two-call ABI reported beside it), weights generated on the device (17.1 GB
-    resident), one stream, in order."""
-    projs = []
+    resident), one stream, in order.  The grouped variant makes 4 calls per layer: q, k and v
+    (which read the same x) as one bitlinear_forward_fused_rows call over their stacked rows,
+    gate and up likewise, o and down alone -- the same bytes and, bit for bit, the same outputs.
+    Each layer's q/k/v and gate/up rows are allocated adjacent, so the grouped calls take views."""
+    projs, groups = [], []
     total = 0
+    P = workloads.W5_PROJ
     for layer in range(layers):
-        for p, (name, k, n) in enumerate(workloads.W5_PROJ):
-            wp = torch.empty((n, k // 4), dtype=torch.uint8, device=dev)
-            workloads.device_stream_packed(wp, layer, p)
-            total += wp.numel()
-            projs.append((k, n, wp, torch.tensor([workloads.stream_alpha(layer, p)], device=dev)))
+        alphas = [workloads.stream_alpha(layer, p) for p in range(len(P))]
+        bufs = {}
+        for members in ((0, 1, 2), (3,), (4, 5), (6,)):
+            k = P[members[0]][1]
+            rows = sum(P[p][2] for p in members)
+            buf = torch.empty((rows, k // 4), dtype=torch.uint8, device=dev)
+            r0 = 0
+            for p in members:
+                n = P[p][2]
+                view = buf[r0:r0 + n]
+                workloads.device_stream_packed(view, layer, p)
+                bufs[p] = view
+                r0 += n
+            total += buf.numel()
+            ar = np.concatenate([np.full(P[p][2], alphas[p], np.float32) for p in members])
+            groups.append((k, rows, buf, torch.from_numpy(ar).to(dev)))
+        for p, (name, k, n) in enumerate(P):
+            projs.append((k, n, bufs[p], torch.tensor([alphas[p]], device=dev)))
     xs = {k: torch.from_numpy(workloads.activations(5, 1, k)).to(dev) for k in (8192, 28672)}
     xq = {k: torch.empty((1, k), dtype=torch.int8, device=dev) for k in (8192, 28672)}
     beta = torch.empty(1, dtype=torch.float32, device=dev)
-    ys = {n: torch.empty((1, n), dtype=torch.float32, device=dev) for n in (1024, 8192, 28672)}
+    ys = {n: torch.empty((1, n), dtype=torch.float32, device=dev) for n in (1024, 8192, 10240, 28672, 57344)}
     torch.cuda.synchronize()
 
     def step(i):
@@ -309,13 +326,22 @@ def chain70b_bench(torch, bl, workloads, dev, layers=80, reps=3):
         for (k, n, wp, alpha) in projs:
             bl.bitlinear_quantize_act(xs[k], xq[k], beta)
             bl.bitlinear_forward(xq[k], beta, wp, alpha, y=ys[n])
+
+    def step_grouped(i):
+        for (k, n, wp, alpha_rows) in groups:
+            bl.bitlinear_forward_fused_rows(xs[k], wp, alpha_rows, y=ys[n])
     ms, _ = _graph_time(torch, step, reps)
     ms2, _ = _graph_time(torch, step_two_call, reps)
+    ms3, _ = _graph_time(torch, step_grouped, reps)
     gbs = total / (ms * 1e-3) / 1e9
     res = dict(layers=layers, weight_bytes=total, ms_per_step=round(ms, 3), weight_gbs=round(gbs, 1),
                pct_hbm=round(100 * gbs / HBM_PEAK_GBS, 2), tokens_per_s=round(1e3 / ms, 1),
-               two_call_ms_per_step=round(ms2, 3))
-    del projs
+               two_call_ms_per_step=round(ms2, 3),
+               grouped=dict(calls_per_layer=4, ms_per_step=round(ms3, 3),
+                            weight_gbs=round(total / (ms3 * 1e-3) / 1e9, 1),
+                            pct_hbm=round(100 * total / (ms3 * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                            tokens_per_s=round(1e3 / ms3, 1)))
+    del projs, groups
     torch.cuda.empty_cache()
     return res
 

@@ -38,6 +38,7 @@ SIGNATURES = {
     "bitlinear_forward_rows": (_INT, [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P]),
     "bitlinear_forward_kernel": (ctypes.c_char_p, [_I64, _I64, _I64, _P, _P]),
     "bitlinear_forward_fused": (_INT, [_P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P, _P, _P]),
+    "bitlinear_forward_fused_rows": (_INT, [_P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P, _P, _P]),
     "bitlinear_forward_fused_kernel": (ctypes.c_char_p, [_I64, _I64, _I64, _P, _P, _P]),
 }
 
@@ -177,11 +178,7 @@ def bitlinear_forward_rows(x_q, beta, W_packed, alpha_rows, bias=None, y=None, a
                     alpha_rows, bias, y, acc, stream)
 
 
-def bitlinear_forward_fused(x, W_packed, alpha, bias=None, y=None, x_q=None, beta=None, acc=None,
-                            stream=None):
-    """y [M, N] from fp32 x [M, K] in one call (activation quantization + forward).
-    x_q / beta (tensors) receive the quantized activations if given; acc as bitlinear_forward.
-    Returns y, or (y, acc) when acc is requested."""
+def _forward_fused(name, x, W_packed, alpha, bias, y, x_q, beta, acc, stream):
     torch = _torch()
     M, K = x.shape
     N = W_packed.shape[0]
@@ -192,13 +189,28 @@ def bitlinear_forward_fused(x, W_packed, alpha, bias=None, y=None, x_q=None, bet
     if acc is True:
         acc = torch.empty((M, N), dtype=torch.int32, device=x.device)
     acc_ptr = _dev(acc, torch.int32, "acc") if acc is not None and acc is not False else None
-    _check("bitlinear_forward_fused", lib.bitlinear_forward_fused(
+    _check(name, getattr(lib, name)(
         _dev(x, torch.float32, "x"), M, K, _dev(W_packed, torch.uint8, "W_packed"),
         _dev(alpha, torch.float32, "alpha"), N,
         _dev(bias, torch.float32, "bias") if bias is not None else None, _dev(y, torch.float32, "y"),
         _dev(x_q, torch.int8, "x_q") if x_q is not None else None,
         _dev(beta, torch.float32, "beta") if beta is not None else None, acc_ptr, _stream(stream)))
     return (y, acc) if acc_ptr is not None else y
+
+
+def bitlinear_forward_fused(x, W_packed, alpha, bias=None, y=None, x_q=None, beta=None, acc=None,
+                            stream=None):
+    """y [M, N] from fp32 x [M, K] in one call (activation quantization + forward).
+    x_q / beta (tensors) receive the quantized activations if given; acc as bitlinear_forward.
+    Returns y, or (y, acc) when acc is requested."""
+    return _forward_fused("bitlinear_forward_fused", x, W_packed, alpha, bias, y, x_q, beta, acc, stream)
+
+
+def bitlinear_forward_fused_rows(x, W_packed, alpha_rows, bias=None, y=None, x_q=None, beta=None, acc=None,
+                                 stream=None):
+    """bitlinear_forward_fused with alpha_rows [N] fp32 (one alpha per output row); also the
+    call for grouped projections (stacked packed rows, each projection's alpha repeated)."""
+    return _forward_fused("bitlinear_forward_fused_rows", x, W_packed, alpha_rows, bias, y, x_q, beta, acc, stream)
 
 
 def bitlinear_forward_fused_kernel(M, K, N, x=None, W_packed=None, x_q=None) -> str:

@@ -159,22 +159,35 @@ int bitlinear_forward_rows(const int8_t* x_q, const float* beta, int64_t M, int6
     return run_forward(a, stream);
 }
 
-int bitlinear_forward_fused(const float* x, int64_t M, int64_t K, const uint8_t* W_packed, const float* alpha,
-                            int64_t N, const float* bias, float* y, int8_t* x_q, float* beta, int32_t* acc,
-                            hipStream_t stream) {
+static int forward_fused(const float* x, int64_t M, int64_t K, const uint8_t* W_packed, const float* alpha,
+                         bool per_row, int64_t N, const float* bias, float* y, int8_t* x_q, float* beta, int32_t* acc,
+                         hipStream_t stream) {
     if (!x) return BITLINEAR_ERR_INVALID_ARG;
     int st = check_forward(reinterpret_cast<const int8_t*>(x), reinterpret_cast<const float*>(x), M, K, W_packed,
                            alpha, N, y);
     if (st) return st;
     if (fused_fast_ok(M, K, x, W_packed, x_q)) {
-        ForwardArgs a{nullptr, nullptr, M, K, N, W_packed, alpha, false, bias, y, acc};
+        ForwardArgs a{nullptr, nullptr, M, K, N, W_packed, alpha, per_row, bias, y, acc};
         return hip_status(launch_gemv_fused(a, x, x_q, beta, stream));
     }
     // other shapes: the two-call path, which needs x_q and beta as its intermediate
     if (!x_q || !beta) return BITLINEAR_ERR_INVALID_ARG;
     st = bitlinear_quantize_act(x, M, K, x_q, beta, stream);
     if (st) return st;
-    return bitlinear_forward(x_q, beta, M, K, W_packed, alpha, N, bias, y, acc, stream);
+    return per_row ? bitlinear_forward_rows(x_q, beta, M, K, W_packed, alpha, N, bias, y, acc, stream)
+                   : bitlinear_forward(x_q, beta, M, K, W_packed, alpha, N, bias, y, acc, stream);
+}
+
+int bitlinear_forward_fused(const float* x, int64_t M, int64_t K, const uint8_t* W_packed, const float* alpha,
+                            int64_t N, const float* bias, float* y, int8_t* x_q, float* beta, int32_t* acc,
+                            hipStream_t stream) {
+    return forward_fused(x, M, K, W_packed, alpha, false, N, bias, y, x_q, beta, acc, stream);
+}
+
+int bitlinear_forward_fused_rows(const float* x, int64_t M, int64_t K, const uint8_t* W_packed,
+                                 const float* alpha_rows, int64_t N, const float* bias, float* y, int8_t* x_q,
+                                 float* beta, int32_t* acc, hipStream_t stream) {
+    return forward_fused(x, M, K, W_packed, alpha_rows, true, N, bias, y, x_q, beta, acc, stream);
 }
 
 const char* bitlinear_forward_fused_kernel(int64_t M, int64_t K, int64_t N, const float* x, const uint8_t* W_packed,

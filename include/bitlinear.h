@@ -161,6 +161,18 @@ int bitlinear_forward_fused(const float* x, int64_t M, int64_t K, const uint8_t*
                             const float* alpha, int64_t N, const float* bias, float* y,
                             int8_t* x_q, float* beta, int32_t* acc, hipStream_t stream);
 
+/*
+ * bitlinear_forward_fused with one alpha per output row [P2 §3.1]: column n of y uses
+ * alpha_rows[n] ([N] fp32).  Besides per-row quantized weights this serves grouped
+ * projections: the packed rows of several projections that read the same x (the q, k and v
+ * of an attention block, or gate and up of an MLP) stacked into one [N1 + N2 + ..., K/4]
+ * matrix, each projection's per-tensor alpha repeated over its rows, give in one launch the
+ * outputs of the separate calls, bit for bit.  Same contract as bitlinear_forward_fused.
+ */
+int bitlinear_forward_fused_rows(const float* x, int64_t M, int64_t K, const uint8_t* W_packed,
+                                 const float* alpha_rows, int64_t N, const float* bias, float* y,
+                                 int8_t* x_q, float* beta, int32_t* acc, hipStream_t stream);
+
 /* Kernel(s) bitlinear_forward_fused launches for these arguments ("gemv_fused" or
  * "quantize_act+forward"); a static string. */
 const char* bitlinear_forward_fused_kernel(int64_t M, int64_t K, int64_t N, const float* x,

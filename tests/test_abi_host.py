@@ -16,7 +16,11 @@ HEADER = os.path.join(ROOT, "include", "bitlinear.h")
 def bl():
     pkg = os.path.join(ROOT, "bitlinear_matmul_absmean_amd", "libbitlinear.so")
     if not os.path.exists(pkg):
-        from bitlinear_matmul_absmean_amd import build as b
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "bitlinear_hip_build", os.path.join(ROOT, "bitlinear_matmul_absmean_amd", "build.py"))
+        b = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(b)
         b.build()
     import bitlinear_matmul_absmean_amd as m
     return m
@@ -128,6 +132,21 @@ def test_forward_validation(bl, name):
     assert call(K=bl.BITLINEAR_MAX_K + 4) == bl.BITLINEAR_ERR_SHAPE
     assert call(M=1 << 40, K=1 << 24 - 4) == bl.BITLINEAR_ERR_SHAPE
     assert call(N=1 << 33) == bl.BITLINEAR_ERR_SHAPE
+
+
+def test_forward_fused_rows_validation(bl):
+    """The per-row (grouped) fused call validates like the per-tensor one, before any HIP call."""
+    f = bl.lib.bitlinear_forward_fused_rows
+    good = 4096
+    # null x, null alpha_rows, null y
+    assert f(None, 1, 64, good, good, 8, None, good, None, None, None, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert f(good, 1, 64, good, None, 8, None, good, None, None, None, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert f(good, 1, 64, good, good, 8, None, None, None, None, None, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    # K % 4, sizes
+    assert f(good, 1, 66, good, good, 8, None, good, None, None, None, None) == bl.BITLINEAR_ERR_SHAPE
+    assert f(good, 0, 64, good, good, 8, None, good, None, None, None, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    # the two-call path (M > 4) needs x_q and beta
+    assert f(good, 8, 64, good, good, 8, None, good, None, None, None, None) == bl.BITLINEAR_ERR_INVALID_ARG
 
 
 def test_forward_fused_validation(bl):

@@ -342,3 +342,59 @@ def test_forward_fused_two_call_path(dev, m, k, n):
     assert np.array_equal(y.cpu().numpy(), r["y"])
     with pytest.raises(bl.BitLinearError):
         bl.bitlinear_forward_fused(xt, pk, al)            # needs x_q and beta on this path
+
+
+# Grouped projections through bitlinear_forward_fused_rows: the packed rows of projections that
+# read the same x stacked into one matrix, each projection's own per-tensor alpha repeated over
+# its rows.  One launch must give, bit for bit, what the oracle gives for each projection alone.
+GROUP_CASES = [
+    (1, 4096, (4096, 1024, 1024)),       # q, k, v of an attention block (one kernel)
+    (1, 8192, (2816, 2816)),             # gate, up of an MLP
+    (1, 1024, (200, 57, 300)),           # ragged groups
+    (3, 4096, (1000, 300)),              # M = 3: still one kernel
+    (9, 2048, (400, 129)),               # M = 9: the two-call path (forward_rows)
+]
+
+
+@pytest.mark.parametrize("m,k,ns", GROUP_CASES)
+def test_forward_fused_rows_grouped(dev, m, k, ns):
+    torch, bl = dev
+    _say(f"forward_fused_rows grouped M={m} K={k} N={ns}")
+    x = workloads.activations(7, m, k)
+    xq_o, beta_o = oracle.quantize_act(x)
+    packed, alpha_rows, y_ref = [], [], []
+    for g, n in enumerate(ns):
+        w = workloads.weights(7, n, k, index=g)
+        codes_o, packed_o, alpha_o = oracle.quantize_weights(w)
+        packed.append(packed_o)
+        alpha_rows.append(np.full(n, alpha_o, np.float32))
+        y_ref.append(oracle.dequant(oracle.ternary_matmul(xq_o, codes_o), beta_o, alpha_o))
+    pk = _to(torch, np.concatenate(packed, axis=0))
+    ar = _to(torch, np.concatenate(alpha_rows))
+    y_ref = np.concatenate(y_ref, axis=1)
+    xt = _to(torch, x)
+    xq = torch.empty((m, k), dtype=torch.int8, device="cuda")
+    beta = torch.empty(m, dtype=torch.float32, device="cuda")
+    y = bl.bitlinear_forward_fused_rows(xt, pk, ar, x_q=xq, beta=beta)
+    torch.cuda.synchronize()
+    assert np.array_equal(xq.cpu().numpy(), xq_o)
+    yg = y.cpu().numpy()
+    assert _rel_ok(yg, y_ref)
+    assert np.array_equal(yg, y_ref)
+
+
+@pytest.mark.parametrize("m,k,n", [(1, 4096, 4096), (1, 11008, 300), (2, 1024, 777)])
+def test_forward_fused_rows_per_row_alpha(dev, m, k, n):
+    """Per-row alpha [P2 §3.1] quantization followed by the fused per-row forward."""
+    torch, bl = dev
+    w = workloads.weights(7, n, k, index=9)
+    x = workloads.activations(7, m, k, index=9)
+    alpha_rows_o = oracle.absmean_rows(w)
+    codes_o = oracle.ternarize_rows(w, alpha_rows_o)
+    packed_o = oracle.pack(codes_o)
+    xq_o, beta_o = oracle.quantize_act(x)
+    acc_o = oracle.ternary_matmul(xq_o, codes_o)
+    y_o = oracle.dequant(acc_o, beta_o, 0.0, alpha_rows=alpha_rows_o)
+    y = bl.bitlinear_forward_fused_rows(_to(torch, x), _to(torch, packed_o), _to(torch, alpha_rows_o))
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy(), y_o)
