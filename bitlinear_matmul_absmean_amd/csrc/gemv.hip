@@ -93,8 +93,9 @@ __device__ __forceinline__ u32x4 act_bytes16(const float4 (&v)[4], float beta, f
 }
 
 // MT tokens (the kernel masks tokens >= M), CPL chunks of 64 weights per lane and row,
-// R rows per wave step, FUSED = quantize x inside, WAVES waves per workgroup.
-template <int MT, int CPL, int R, bool FUSED, int WAVES>
+// R rows per wave step, FUSED = quantize x inside, WAVES waves per workgroup, SINGLE = the
+// wave's rows all fit one step (one register buffer, every weight load issued up front).
+template <int MT, int CPL, int R, bool FUSED, int WAVES, bool SINGLE>
 __global__ __launch_bounds__(64 * WAVES) void k_gemv(GemvArgs g) {
     constexpr int NT = 64 * WAVES;            // threads per workgroup
     constexpr int UNITS = MT * CPL * 256;     // 16-byte units of x_q staged per workgroup
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(GemvArgs g) {
         for (int tt = 0; tt < MT; ++tt)
             if (tt == t) part[tt] += v;
     };
-    u32x4 wa[R][CPL], wb[R][CPL];
+    u32x4 wa[R][CPL], wb[SINGLE ? 1 : R][SINGLE ? 1 : CPL];
     float beta_t[MT];
     if constexpr (FUSED) {
         constexpr bool KEEP = UPT <= 4;       // keep x in registers between the two passes
@@ -338,19 +339,24 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(GemvArgs g) {
     };
 
     // ---- walk the row range, two register buffers in turn -------------------------------
-    for (int64_t r0 = rb; r0 < re; r0 += 2 * R) {
-        load_rows(wb, r0 + R);
-        finish_rows(wa, r0);
-        if (r0 + R >= re) break;
-        load_rows(wa, r0 + 2 * R);
-        finish_rows(wb, r0 + R);
+    if constexpr (SINGLE) {
+        (void)wb;
+        if (rb < re) finish_rows(wa, rb);
+    } else {
+        for (int64_t r0 = rb; r0 < re; r0 += 2 * R) {
+            load_rows(wb, r0 + R);
+            finish_rows(wa, r0);
+            if (r0 + R >= re) break;
+            load_rows(wa, r0 + 2 * R);
+            finish_rows(wb, r0 + R);
+        }
     }
 }
 
 // ---------------------------------------------------------------------------------------
 // Launch shape: waves per workgroup and the number of waves the grid aims at; each wave gets
-// ceil(N / waves) contiguous rows, walked R rows at a time (R a power of two not above that
-// count, R * CPL loads of 16 bytes per lane per buffer, two buffers, within LMAX).
+// ceil(N / waves) contiguous rows: one step holding all of them when they fit the registers,
+// else steps of R rows with two buffers.
 // Measured on MI355X over the decode shapes (one token):
 //  * forward (x_q given): with rows of one 64-weight chunk per lane (K <= 4096) many small
 //    workgroups win (4 waves, 8192 waves in all, 1-2 rows each: loads of many waves overlap
@@ -359,6 +365,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(GemvArgs g) {
 //    workgroups win: 8 waves and 2048 in all, or 16 waves and 4096 in all for rows of two or
 //    three chunks per lane (their registers fit the 128 that 16-wave workgroups allow).
 // Shapes with too few rows for that many waves per CU fall back to 4-wave workgroups.
+static int64_t rows_per_step(int64_t rpw) {      // the single-step row counts instantiated
+    return rpw <= 4 ? rpw : rpw <= 6 ? 6 : rpw <= 8 ? 8 : 9;
+}
+
 GemvShape gemv_shape(int64_t M, int64_t K, int64_t N, bool fused) {
     GemvShape sh{4, 2048};
     if (M != 1) return sh;
@@ -366,38 +376,59 @@ GemvShape gemv_shape(int64_t M, int64_t K, int64_t N, bool fused) {
     GemvShape want;
     if (!fused)
         want = cpl == 1 ? GemvShape{4, N >= 8192 ? 8192 : 2048} : GemvShape{cpl <= 3 ? 4 : 8, 2048};
+    else if (cpl >= 2 && rows_per_step((N + 4095) / 4096) * cpl <= 8)
+        want = GemvShape{16, 4096};    // one short step per wave within the 128 VGPRs of 16 waves
     else
-        want = (cpl == 2 || cpl == 3) ? GemvShape{16, 4096} : GemvShape{8, 2048};
+        want = GemvShape{8, 2048};
     if (N >= (int64_t)want.waves_per_wg * 256) sh = want;
     return sh;
 }
 
+// single step: R from {1, 2, 3, 4, 6, 8}, the smallest not below the rows per wave, within
+// single_loads(WAVES, CPL) loads of 16 bytes per lane: 8 in 16-wave workgroups (their 128
+// VGPRs; more rows there measured slower than two-buffer steps), 20 with 4 or 8 waves (256)
+constexpr int single_loads(int waves, int /*cpl*/) { return waves == 16 ? 8 : 20; }
+constexpr int next_rows(int r) { return r == 1 ? 2 : r == 2 ? 3 : r == 3 ? 4 : r == 4 ? 6 : 8; }
+
+template <int MT, int CPL, bool FUSED, int WAVES, int R>
+static hipError_t launch_single(const GemvArgs& g, dim3 grid, dim3 block, size_t lds, int64_t rpw, hipStream_t s) {
+    if constexpr (R < 8 && next_rows(R) * CPL <= single_loads(WAVES, CPL))
+        if (rpw > R) return launch_single<MT, CPL, FUSED, WAVES, next_rows(R)>(g, grid, block, lds, rpw, s);
+    return launch_with_lds(k_gemv<MT, CPL, R, FUSED, WAVES, true>, grid, block, lds, s, g);
+}
+
 template <int MT, int CPL, bool FUSED, int WAVES>
 static hipError_t launch_shape(const GemvArgs& g0, int64_t waves_target, hipStream_t s) {
+    // One token: when a wave's rows fit the registers, one step with every weight load issued
+    // before the activation staging.  Otherwise (and for 2-4 tokens, whose
+    // accumulators take more registers) double-buffered steps of R rows, R * CPL <= LMAX.
     constexpr int LMAX = MT == 1 ? 8 : 4;
+    constexpr int R = (LMAX / CPL) < 1 ? 1 : (LMAX / CPL);
     GemvArgs g = g0;
     const int64_t N = g.f.N;
     const int64_t rpw = (N + waves_target - 1) / waves_target;
-    int R = 1;
-    while (R < 8 && R * 2 * CPL <= LMAX && 2 * R <= rpw) R *= 2;
     g.rows_per_wave = rpw;
     const int64_t waves = (N + rpw - 1) / rpw;
     const int64_t blocks = (waves + WAVES - 1) / WAVES;
     const size_t lds = (size_t)MT * CPL * 256 * 16;
     const dim3 grid((unsigned)blocks), block(64 * WAVES);
-    if constexpr (8 * CPL <= LMAX)
-        if (R == 8) return launch_with_lds(k_gemv<MT, CPL, 8, FUSED, WAVES>, grid, block, lds, s, g);
-    if constexpr (4 * CPL <= LMAX)
-        if (R == 4) return launch_with_lds(k_gemv<MT, CPL, 4, FUSED, WAVES>, grid, block, lds, s, g);
-    if constexpr (2 * CPL <= LMAX)
-        if (R == 2) return launch_with_lds(k_gemv<MT, CPL, 2, FUSED, WAVES>, grid, block, lds, s, g);
-    return launch_with_lds(k_gemv<MT, CPL, 1, FUSED, WAVES>, grid, block, lds, s, g);
+    if constexpr (MT == 1) {
+        int rs = 1;
+        while (rs < rpw && rs < 8) rs = next_rows(rs);
+        if (rs >= rpw && rs * CPL <= single_loads(WAVES, CPL))
+            return launch_single<MT, CPL, FUSED, WAVES, 1>(g, grid, block, lds, rpw, s);
+    }
+    if constexpr (WAVES == 16 && CPL > 3) {
+        return hipErrorInvalidConfiguration;   // not chosen by gemv_shape (it would spill)
+    } else {
+        return launch_with_lds(k_gemv<MT, CPL, R, FUSED, WAVES, false>, grid, block, lds, s, g);
+    }
 }
 
 template <int MT, int CPL, bool FUSED>
 static hipError_t launch_cpl(const GemvArgs& g, hipStream_t s) {
     const GemvShape sh = gemv_shape(g.f.M, g.f.K, g.f.N, FUSED);
-    if constexpr (MT == 1 && CPL <= 3)
+    if constexpr (MT == 1)
         if (sh.waves_per_wg == 16) return launch_shape<MT, CPL, FUSED, 16>(g, sh.waves_target, s);
     if constexpr (MT == 1)
         if (sh.waves_per_wg == 8) return launch_shape<MT, CPL, FUSED, 8>(g, sh.waves_target, s);
