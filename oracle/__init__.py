@@ -9,7 +9,8 @@ this module only marshals NumPy arrays through ctypes.  Page keys used in citati
 
 * [P2] nxmr.cn tutorial "1.58 位大模型" (per-row absmean, add/sub derivation, memory estimate).
 * [P3] chenxutan.com, "1.58-bit 大模型极限量化实战：从 BitNet 三值权重到单颗 CPU 跑起 100B 模型"
-  (absmean / absmax formulas, worked example, BitLinear forward, 2-bit packing).
+  (absmean / absmax formulas, worked example, BitLinear forward, 2-bit packing, §6.2 the
+  rotation before absmax).
 """
 from __future__ import annotations
 
@@ -56,6 +57,7 @@ def _load():
         "oracle_ternary_matmul": (ctypes.c_int, [p, i64, i64, p, i64, p, i64, i64]),
         "oracle_dequant_scale": (f32, [f32, f32]),
         "oracle_dequant": (ctypes.c_int, [p, p, f32, p, i64, i64, p, p, i64, i64]),
+        "oracle_hadamard_rows": (ctypes.c_int, [p, i64, i64, i64, p, p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -212,3 +214,32 @@ def bitlinear(x: np.ndarray, w: np.ndarray, bias: np.ndarray | None = None):
     acc = ternary_matmul(xq, codes)
     y = dequant(acc, beta, alpha, bias=bias)
     return dict(codes=codes, packed=packed, alpha=alpha, xq=xq, beta=beta, acc=acc, y=y)
+
+
+def hadamard_rows(x: np.ndarray, block: int, signs: np.ndarray | None = None) -> np.ndarray:
+    """[P3 §6.2] randomized Hadamard rotation along K in blocks of ``block`` (readings R10,
+    R11 of ``oracle.c``): sign flip by ``signs`` (int8, negative = flip), Sylvester
+    butterflies with stride 1, 2, ..., block/2 in fp32, then a multiply by fp32(1/sqrt(block))."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim == 1:
+        x = x[None, :]
+    m, k = x.shape
+    d = None if signs is None else np.ascontiguousarray(signs, dtype=np.int8)
+    if d is not None:
+        assert d.shape == (k,)
+    out = np.empty((m, k), np.float32)
+    _check(_load().oracle_hadamard_rows(_ptr(x), m, k, int(block), _ptr(d), _ptr(out)), "hadamard_rows")
+    return out
+
+
+def quantize_act_hadamard(x: np.ndarray, block: int, signs: np.ndarray | None = None):
+    """[P3 §6.2 then §2.4] rotate each token (:func:`hadamard_rows`), then per-token absmax
+    int8 of the rotated row.  Returns (x_q int8 [M,K], beta fp32 [M])."""
+    return quantize_act(hadamard_rows(x, block, signs))
+
+
+def bitlinear_hadamard(x: np.ndarray, w: np.ndarray, block: int, signs: np.ndarray | None = None,
+                       bias: np.ndarray | None = None):
+    """BitLinear forward with the rotation of [P3 §6.2] on both operands: W and x are rotated
+    by the same R, then quantized and multiplied as in :func:`bitlinear`."""
+    return bitlinear(hadamard_rows(x, block, signs), hadamard_rows(w, block, signs), bias=bias)

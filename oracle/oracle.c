@@ -33,6 +33,14 @@
  *       one after another (row-major along K).
  *   R7  s = fp32((double)alpha * (double)beta / 127.0), y = fp32((float)acc * s), then
  *       + bias as a separate fp32 rounding.
+ *   R10 the rotation before absmax [P3 §6.2] is a randomized Walsh-Hadamard transform
+ *       applied to each row along K in blocks of B (a power of two dividing K): a sign
+ *       flip by d[k] in {+1, -1} (the random part; an input, negative int8 = flip), then
+ *       the Sylvester Hadamard matrix of order B scaled by 1/sqrt(B).  The same rotation
+ *       of the rows of W keeps x . W^T unchanged in exact arithmetic (R R^T = I).
+ *   R11 the rotation is evaluated in fp32 as butterflies (a, b) -> (a + b, a - b) on
+ *       pairs (j, j + h), with h = 1, 2, 4, ..., B/2 in that order, then one fp32
+ *       multiply of every result by fp32(1/sqrt(B)) (exact when B is a power of 4).
  */
 #include <math.h>
 #include <stddef.h>
@@ -206,6 +214,34 @@ int oracle_dequant(const int32_t* acc, const float* beta, float alpha, const flo
             float v = (float)acc[m * n_rows + n] * s;
             if (bias) v = v + bias[n];
             y[m * n_rows + n] = v;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* [P3 §6.2] randomized Hadamard rotation of each row of x [m_rows, k], readings R10, R11.
+ * signs (nullable = all +1) holds d[0..k-1]; block is B.  out may equal x. */
+int oracle_hadamard_rows(const float* x, int64_t m_rows, int64_t k, int64_t block, const int8_t* signs,
+                         float* out) {
+    if (!x || !out || m_rows <= 0 || k <= 0 || block <= 0) return ORACLE_EINVAL;
+    if ((block & (block - 1)) != 0 || k % block != 0) return ORACLE_EINVAL;
+    const float scale = (float)(1.0 / sqrt((double)block));
+    for (int64_t m = 0; m < m_rows; ++m) {
+        const float* row = x + m * k;
+        float* o = out + m * k;
+        for (int64_t j = 0; j < k; ++j) o[j] = (signs && signs[j] < 0) ? -row[j] : row[j];
+        for (int64_t b0 = 0; b0 < k; b0 += block) {
+            float* v = o + b0;
+            for (int64_t h = 1; h < block; h *= 2) {
+                for (int64_t i = 0; i < block; i += 2 * h) {
+                    for (int64_t j = i; j < i + h; ++j) {
+                        float a = v[j], b = v[j + h];
+                        v[j] = a + b;
+                        v[j + h] = a - b;
+                    }
+                }
+            }
+            for (int64_t j = 0; j < block; ++j) v[j] = v[j] * scale;
         }
     }
     return ORACLE_OK;

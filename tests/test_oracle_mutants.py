@@ -39,6 +39,13 @@ MUTANTS = [
     ("bias subtracted", "if (bias) v = v + bias[n];", "if (bias) v = v - bias[n];"),
     ("per-row alpha indexed by token", "float a = alpha_rows ? alpha_rows[n] : alpha;",
      "float a = alpha_rows ? alpha_rows[m] : alpha;"),
+    ("reversed butterfly difference", "v[j + h] = a - b;", "v[j + h] = b - a;"),
+    ("descending butterfly strides", "for (int64_t h = 1; h < block; h *= 2) {",
+     "for (int64_t h = block / 2; h >= 1; h /= 2) {"),
+    ("rotation scaled by 1/B", "const float scale = (float)(1.0 / sqrt((double)block));",
+     "const float scale = (float)(1.0 / (double)block);"),
+    ("rotation signs ignored", "o[j] = (signs && signs[j] < 0) ? -row[j] : row[j];", "o[j] = row[j];"),
+    ("rotation block offset dropped", "float* v = o + b0;", "float* v = o;"),
 ]
 
 

@@ -331,3 +331,141 @@ def test_dequant_scale_precision_where_fp32_would_differ():
     for i, b in enumerate(betas):
         assert exact.fr(y[i, 0]) == exact.dequant_scale_exact(a, exact.fr(b))
         assert exact.fr(oracle.dequant_scale(alpha, b)) == exact.dequant_scale_exact(a, exact.fr(b))
+
+
+# ---------------------------------------------------------------- rotation before absmax
+# [P3 §6.2]: a randomized Hadamard rotation of x (and the same of W) before absmax.
+# Readings R10/R11: blocks of B along K, sign flip first, Sylvester butterflies with
+# stride 1, 2, ..., B/2 in fp32, one fp32 multiply by fp32(1/sqrt(B)) last.
+def _sylvester(b):
+    """Textbook closed form of the Sylvester Hadamard matrix: H[i, j] = (-1)^popcount(i & j)."""
+    i = np.arange(b)
+    bits = np.bitwise_and.outer(i, i)
+    pop = np.zeros_like(bits)
+    while bits.any():
+        pop += bits & 1
+        bits >>= 1
+    return np.where(pop % 2 == 0, 1.0, -1.0)
+
+
+def _rotate_dense_f64(x, block, signs):
+    """x . diag(d) . blockdiag(H_B / sqrt(B)) in fp64 (matrix form, no butterflies)."""
+    m, k = x.shape
+    d = np.ones(k) if signs is None else signs.astype(np.float64)
+    h = _sylvester(block) / math.sqrt(block)
+    xs = x.astype(np.float64) * d
+    return (xs.reshape(m, k // block, block) @ h).reshape(m, k)
+
+
+@pytest.mark.parametrize("block", [1, 2, 4, 8, 16, 32, 64, 256])
+def test_hadamard_matches_dense_matrix_within_fp32_bound(block):
+    k = 3 * block if block > 1 else 5
+    x = workloads.activations_with_outliers(7, 4, k)
+    d = workloads.rotation_signs(7, k)
+    got = oracle.hadamard_rows(x, block, d).astype(np.float64)
+    want = _rotate_dense_f64(x, block, d)
+    # log2(B) rounded additions on each path, a rounded scale and a rounded product
+    levels = int(round(math.log2(block)))
+    mag = np.abs(x.astype(np.float64)).reshape(4, k // block, block).sum(axis=2) / math.sqrt(block)
+    bound = np.repeat(mag, block, axis=1) * (levels + 2) * 2.0 ** -24 * 1.001
+    assert np.all(np.abs(got - want) <= bound + 1e-30)
+
+
+@pytest.mark.parametrize("block", [2, 8, 64, 512])
+def test_hadamard_rounding_matches_recursive_definition_bitwise(block):
+    """H_2n [a; b] = [H_n a + H_n b; H_n a - H_n b] evaluated recursively in fp32 (numpy
+    float32 arithmetic), then the fp32 scale: the same roundings as R11 stride order."""
+    def rec(v):
+        if v.shape[-1] == 1:
+            return v
+        n = v.shape[-1] // 2
+        a, b = rec(v[..., :n]), rec(v[..., n:])
+        return np.concatenate([a + b, a - b], axis=-1)
+
+    x = workloads.activations(8, 3, 2 * block)
+    v = x.reshape(3, 2, block)
+    want = (rec(v) * np.float32(1.0 / math.sqrt(block))).reshape(3, 2 * block).astype(np.float32)
+    got = oracle.hadamard_rows(x, block)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("block", [4, 16, 64, 256])
+def test_hadamard_is_an_exact_involution_on_small_integers(block):
+    """For B a power of 4 the scale is 2^-j, so small integers rotate without rounding and
+    H (H x) = x (H symmetric and orthonormal)."""
+    g = np.random.default_rng(11)
+    x = g.integers(-50, 51, size=(3, 2 * block)).astype(np.float32)
+    once = oracle.hadamard_rows(x, block)
+    assert np.array_equal(oracle.hadamard_rows(once, block), x)
+
+
+@pytest.mark.parametrize("block", [2, 16, 128])
+def test_hadamard_unit_vectors_give_scaled_rows(block):
+    h = _sylvester(block)
+    s = np.float32(1.0 / math.sqrt(block))
+    for i in (0, 1, block // 2, block - 1):
+        e = np.zeros((1, block), np.float32)
+        e[0, i] = 4.0
+        got = oracle.hadamard_rows(e, block)[0]
+        assert np.array_equal(got, (np.float32(4.0) * h[i].astype(np.float32)) * s)
+
+
+def test_hadamard_constant_block_concentrates_in_first_output():
+    x = np.full((1, 64), 3.0, np.float32)
+    got = oracle.hadamard_rows(x, 64)[0]
+    assert got[0] == np.float32(3.0 * 64 / 8) and not got[1:].any()
+
+
+def test_hadamard_signs_apply_before_the_transform_and_block_one_is_the_sign_flip():
+    x = workloads.activations(9, 2, 96)
+    d = workloads.rotation_signs(9, 96)
+    flipped = np.where(d < 0, -x, x).astype(np.float32)
+    assert np.array_equal(oracle.hadamard_rows(x, 32, d), oracle.hadamard_rows(flipped, 32))
+    assert np.array_equal(oracle.hadamard_rows(x, 1, d), flipped)
+    assert np.array_equal(oracle.hadamard_rows(x, 1), x)
+
+
+def test_hadamard_preserves_norms_and_products():
+    """R R^T = I: row norms and x . W^T survive the rotation up to fp32 rounding."""
+    k, block = 768, 256
+    x = workloads.activations_with_outliers(10, 4, k)
+    w = workloads.weights(10, 6, k)
+    d = workloads.rotation_signs(10, k)
+    xr = oracle.hadamard_rows(x, block, d).astype(np.float64)
+    wr = oracle.hadamard_rows(w, block, d).astype(np.float64)
+    x64, w64 = x.astype(np.float64), w.astype(np.float64)
+    assert np.allclose((xr ** 2).sum(1), (x64 ** 2).sum(1), rtol=1e-5, atol=0)
+    ref = x64 @ w64.T
+    scale = np.abs(x64) @ np.abs(w64).T
+    assert np.all(np.abs(xr @ wr.T - ref) <= 2e-5 * scale)
+
+
+def test_hadamard_rejects_bad_blocks():
+    x = np.zeros((1, 24), np.float32)
+    with pytest.raises(ValueError):
+        oracle.hadamard_rows(x, 3)
+    with pytest.raises(ValueError):
+        oracle.hadamard_rows(x, 16)
+
+
+def test_rotation_spreads_an_outlier_and_cuts_the_quantization_error():
+    """[P3 §6.2]: one large channel inflates beta and crushes the rest to 0; after the
+    rotation its energy is spread, beta falls, and the dequantized activations track the
+    float ones (and the float product) more closely."""
+    k, block = 1024, 256
+    x = workloads.activations(12, 8, k) * np.float32(0.05)
+    x[:, 17] = np.float32(40.0)
+    w = workloads.weights(12, 64, k)
+    d = workloads.rotation_signs(12, k)
+    xq, beta = oracle.quantize_act(x)
+    xq_r, beta_r = oracle.quantize_act_hadamard(x, block, d)
+    assert np.all(beta_r < beta / 4)
+    x64 = x.astype(np.float64)
+    xr64 = oracle.hadamard_rows(x, block, d).astype(np.float64)
+    wr64 = oracle.hadamard_rows(w, block, d).astype(np.float64)
+    deq = xq * (beta[:, None] / 127.0)
+    deq_r = xq_r * (beta_r[:, None] / 127.0)
+    rel = lambda a, b: np.linalg.norm(a - b) / np.linalg.norm(b)
+    assert rel(deq_r, xr64) < rel(deq, x64) / 4
+    ref = x64 @ w.astype(np.float64).T
+    assert rel(deq_r @ wr64.T, ref) < rel(deq @ w.astype(np.float64).T, ref) / 4

@@ -62,6 +62,13 @@ def activations_with_outliers(workload: int, m: int, k: int, index: int = 0) -> 
     return x
 
 
+def rotation_signs(workload: int, k: int, index: int = 0) -> np.ndarray:
+    """Random signs d [K] (int8, +1 or -1, each with probability 1/2): the random diagonal of
+    a randomized Hadamard rotation, drawn here and passed to both sides as an input."""
+    g = rng(workload, 3, index)
+    return np.where(g.random(k) < 0.5, -1, 1).astype(np.int8)
+
+
 # ---------------------------------------------------------------------------------------
 # Counter-based ternary codes for the 70B-class weight stream.
 #
