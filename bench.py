@@ -261,6 +261,76 @@ def quantize_bench(torch, bl, workloads, dev, reps=20):
     return out
 
 
+def hadamard_block(k: int) -> int:
+    """Largest power of two <= 4096 dividing K: the block of the rotation for that K."""
+    b = 1
+    while b < 4096 and k % (2 * b) == 0:
+        b *= 2
+    return b
+
+
+def hadamard_bench(torch, bl, workloads, dev, ms_plain_step, reps=20):
+    """Rotation before absmax [P3 §6.2].  Activations: rotate + per-token absmax int8 in one
+    pass reads x and the signs and writes x_q and beta, 5MK + 4M + K bytes.  Weights (offline):
+    rotate W [11008, 4096], 8NK + K bytes.  Decode: the 7B-class step with rotated projections,
+    each a rotation of x (hadamard_rows) then the fused GEMV on rotated, ternarized weights."""
+    out = {}
+    acts = []
+    for m, k in ((2048, 4096), (2048, 11008), (1, 4096)):
+        b = hadamard_block(k)
+        x = torch.from_numpy(workloads.activations_with_outliers(4, m, k)).to(dev)
+        d = torch.from_numpy(workloads.rotation_signs(4, k)).to(dev)
+        xq = torch.empty((m, k), dtype=torch.int8, device=dev)
+        beta = torch.empty(m, dtype=torch.float32, device=dev)
+        ms, _ = _graph_time(torch, lambda i: bl.bitlinear_quantize_act_hadamard(x, b, d, xq, beta),
+                            200 if m == 1 else reps)
+        ba = 5 * m * k + 4 * m + k
+        acts.append({"M": m, "K": k, "block": b, "alg_bytes": ba, "us": round(ms * 1e3, 2),
+                     "gbs": round(ba / (ms * 1e-3) / 1e9, 1),
+                     "pct_hbm": round(100 * ba / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)})
+    out["quantize_act_hadamard"] = acts
+    n, k = 11008, 4096
+    w = torch.from_numpy(workloads.weights(4, n, k)).to(dev)
+    d = torch.from_numpy(workloads.rotation_signs(4, k)).to(dev)
+    wr = torch.empty_like(w)
+    ms, _ = _graph_time(torch, lambda i: bl.bitlinear_hadamard_rows(w, 4096, d, wr), reps)
+    bw = 8 * n * k + k
+    out["hadamard_rows_weights"] = {"N": n, "K": k, "block": 4096, "alg_bytes": bw, "us": round(ms * 1e3, 2),
+                                    "gbs": round(bw / (ms * 1e-3) / 1e9, 1),
+                                    "pct_hbm": round(100 * bw / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+    del w, wr
+    per_step = sum(n * k // 4 for k, n in DECODE_SHAPES)
+    copies = max(2, POOL_BYTES // per_step)
+    shapes = []
+    for idx, (k, n) in enumerate(DECODE_SHAPES):
+        b = hadamard_block(k)
+        d = torch.from_numpy(workloads.rotation_signs(2, k, index=idx)).to(dev)
+        w = torch.from_numpy(workloads.weights(2, n, k, index=idx)).to(dev)
+        bl.bitlinear_hadamard_rows(w, b, d, out=w)
+        packed, alpha = bl.bitlinear_quantize_weights(w)
+        del w
+        pool = [packed] + [packed.clone() for _ in range(copies - 1)]
+        x = [torch.from_numpy(workloads.activations(2, 1, k, index=100 * idx + j)).to(dev) for j in range(8)]
+        shapes.append(dict(k=k, block=b, signs=d, pool=pool, alpha=alpha, x=x,
+                           xr=torch.empty((1, k), dtype=torch.float32, device=dev),
+                           y=torch.empty((1, n), dtype=torch.float32, device=dev)))
+    torch.cuda.synchronize()
+
+    def step(i):
+        for sh in shapes:
+            bl.bitlinear_hadamard_rows(sh["x"][i % 8], sh["block"], sh["signs"], out=sh["xr"])
+            bl.bitlinear_forward_fused(sh["xr"], sh["pool"][i % copies], sh["alpha"], y=sh["y"])
+
+    ms, _ = _graph_time(torch, step, 400)
+    out["decode_rotated"] = {"shapes_KN": DECODE_SHAPES, "blocks": [sh["block"] for sh in shapes],
+                             "us_per_step": round(ms * 1e3, 2), "weight_gbs": round(per_step / (ms * 1e-3) / 1e9, 1),
+                             "plain_us_per_step": round(ms_plain_step * 1e3, 2),
+                             "rotation_overhead_us": round((ms - ms_plain_step) * 1e3, 2)}
+    del shapes
+    torch.cuda.empty_cache()
+    return out
+
+
 def batched_bench(torch, bl, workloads, dev, reps=96):
     out = []
     for (k, n) in [(4096, 11008), (11008, 4096)]:
@@ -554,6 +624,8 @@ def main():
         extras.update(quantize_bench(torch, bl, workloads, dev))
         log(f"quantize_weights {extras['quantize_weights']}")
         log(f"quantize_act {extras['quantize_act']}")
+        extras["hadamard"] = hadamard_bench(torch, bl, workloads, dev, ms_step)
+        log(f"hadamard {extras['hadamard']}")
     if not args.no_extras and not args.no_chain:
         extras["chain70b"] = chain70b_bench(torch, bl, workloads, dev)
         log(f"chain70b {extras['chain70b']}")

@@ -40,6 +40,8 @@ SIGNATURES = {
     "bitlinear_forward_fused": (_INT, [_P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P, _P, _P]),
     "bitlinear_forward_fused_rows": (_INT, [_P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P, _P, _P]),
     "bitlinear_forward_fused_kernel": (ctypes.c_char_p, [_I64, _I64, _I64, _P, _P, _P]),
+    "bitlinear_hadamard_rows": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P]),
+    "bitlinear_quantize_act_hadamard": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
 }
 
 
@@ -143,6 +145,34 @@ def bitlinear_quantize_act(x, x_q=None, beta=None, stream=None):
     _check("bitlinear_quantize_act", lib.bitlinear_quantize_act(
         _dev(x, torch.float32, "x"), M, K, _dev(x_q, torch.int8, "x_q"),
         _dev(beta, torch.float32, "beta"), _stream(stream)))
+    return x_q, beta
+
+
+def bitlinear_hadamard_rows(x, block, signs=None, out=None, stream=None):
+    """x [M, K] fp32 -> rows rotated by diag(d) . blockdiag(H_block) / sqrt(block); out may be x."""
+    torch = _torch()
+    M, K = x.shape
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.float32, device=x.device)
+    _check("bitlinear_hadamard_rows", lib.bitlinear_hadamard_rows(
+        _dev(x, torch.float32, "x"), M, K, int(block),
+        _dev(signs, torch.int8, "signs") if signs is not None else None,
+        _dev(out, torch.float32, "out"), _stream(stream)))
+    return out
+
+
+def bitlinear_quantize_act_hadamard(x, block, signs=None, x_q=None, beta=None, stream=None):
+    """x [M, K] fp32 -> (x_q int8 [M, K], beta fp32 [M]) of the rotated rows."""
+    torch = _torch()
+    M, K = x.shape
+    if x_q is None:
+        x_q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if beta is None:
+        beta = torch.empty(M, dtype=torch.float32, device=x.device)
+    _check("bitlinear_quantize_act_hadamard", lib.bitlinear_quantize_act_hadamard(
+        _dev(x, torch.float32, "x"), M, K, int(block),
+        _dev(signs, torch.int8, "signs") if signs is not None else None,
+        _dev(x_q, torch.int8, "x_q"), _dev(beta, torch.float32, "beta"), _stream(stream)))
     return x_q, beta
 
 

@@ -190,6 +190,33 @@ int bitlinear_forward_fused_rows(const float* x, int64_t M, int64_t K, const uin
     return forward_fused(x, M, K, W_packed, alpha_rows, true, N, bias, y, x_q, beta, acc, stream);
 }
 
+static int check_hadamard(const float* x, int64_t M, int64_t K, int64_t block, const int8_t* signs) {
+    if (!x || M <= 0 || K <= 0 || block <= 0) return BITLINEAR_ERR_INVALID_ARG;
+    if ((block & (block - 1)) != 0 || block > HADAMARD_MAX_BLOCK || K % block != 0 || K % 4 != 0)
+        return BITLINEAR_ERR_SHAPE;
+    if (!mul_ok(M, K) || M > (int64_t)INT_MAX / ((K + 4095) / 4096)) return BITLINEAR_ERR_SHAPE;
+    if (!aligned(x, 16) || (signs && !aligned(signs, 4))) return BITLINEAR_ERR_ALIGNMENT;
+    return BITLINEAR_OK;
+}
+
+int bitlinear_hadamard_rows(const float* x, int64_t M, int64_t K, int64_t block, const int8_t* signs, float* out,
+                            hipStream_t stream) {
+    if (!out) return BITLINEAR_ERR_INVALID_ARG;
+    int st = check_hadamard(x, M, K, block, signs);
+    if (st) return st;
+    if (!aligned(out, 16)) return BITLINEAR_ERR_ALIGNMENT;
+    return hip_status(launch_hadamard_rows(x, M, K, (int)block, signs, out, stream));
+}
+
+int bitlinear_quantize_act_hadamard(const float* x, int64_t M, int64_t K, int64_t block, const int8_t* signs,
+                                    int8_t* x_q, float* beta, hipStream_t stream) {
+    if (!x_q || !beta) return BITLINEAR_ERR_INVALID_ARG;
+    int st = check_hadamard(x, M, K, block, signs);
+    if (st) return st;
+    if (!aligned(x_q, 4)) return BITLINEAR_ERR_ALIGNMENT;
+    return hip_status(launch_quantize_act_hadamard(x, M, K, (int)block, signs, x_q, beta, stream));
+}
+
 const char* bitlinear_forward_fused_kernel(int64_t M, int64_t K, int64_t N, const float* x, const uint8_t* W_packed,
                                            const int8_t* x_q) {
     (void)N;

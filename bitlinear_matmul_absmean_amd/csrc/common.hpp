@@ -87,6 +87,13 @@ hipError_t launch_alpha_rows(const float* W, int64_t N, int64_t K, float* alpha_
 hipError_t launch_ternary_pack(const float* W, int64_t N, int64_t K, const float* alpha, bool per_row,
                                uint8_t* packed, hipStream_t s);
 hipError_t launch_quantize_act(const float* x, int64_t M, int64_t K, int8_t* xq, float* beta, hipStream_t s);
+// Randomized Hadamard rotation along K (blocks of `block`, a power of two <= HADAMARD_MAX_BLOCK
+// dividing K; K % 4 == 0; x/out 16-byte aligned, signs and xq 4-byte aligned).
+constexpr int64_t HADAMARD_MAX_BLOCK = 4096;
+hipError_t launch_hadamard_rows(const float* x, int64_t M, int64_t K, int block, const int8_t* signs,
+                                float* out, hipStream_t s);
+hipError_t launch_quantize_act_hadamard(const float* x, int64_t M, int64_t K, int block, const int8_t* signs,
+                                        int8_t* xq, float* beta, hipStream_t s);
 
 struct ForwardArgs {
     const int8_t* xq;

@@ -4,10 +4,14 @@
 // [P3] chenxutan.com, "1.58-bit 大模型极限量化实战" §2.3 (absmean), §2.4 (absmax), §4.1 (code),
 //      §5.3 (2-bit packing 00/01/10 -> -1/0/+1).
 // [P2] nxmr.cn, "1.58 位大模型" §3.1, §4.2 (per-row absmean).
+// [P3] §6.2: the randomized Hadamard rotation of the activations (and, offline, of the
+//      weight rows) before the absmax.
 //
 // All of these are HBM-bound streaming kernels: float4 loads, one wave per row for the
 // fp64 |W| partial sums, a flat grid-stride pass for codes and packing, one workgroup
 // per token for the activations.
+#include <cmath>
+
 #include "common.hpp"
 
 namespace bitlinear {
@@ -176,6 +180,319 @@ __global__ __launch_bounds__(256) void k_quantize_act(const float* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------------------
+// Randomized Hadamard rotation [P3 §6.2] along K: sign flip by d[k] (negative int8 = flip),
+// the Sylvester transform of order B on each block of B consecutive elements, then one fp32
+// multiply by fp32(1/sqrt(B)).  The transform is evaluated as butterflies (a, b) -> (a + b,
+// a - b) on pairs (j, j + h) with h = 1, 2, 4, ..., B/2 in that order, so every result has a
+// fixed rounding sequence whatever the thread layout.
+//
+// A workgroup of 256 threads rotates a chunk of 4096 consecutive elements of a row (blocks
+// never straddle chunks: B divides both K and 4096).  The 12 index bits of a chunk element are
+// combined while they are register indices of the 16 values a thread holds, in three layouts:
+//   L0  v[4q + i] = element 4t + 1024q + i      (coalesced float4 loads, code stores)
+//       register strides 1, 2 -> h = 1, 2;  register strides 4, 8 -> h = 1024, 2048
+//   L1  v[j] = element (t & 3) + 4j + 64((t >> 2) & 15) + 1024(t >> 6)      h = 4 .. 32
+//   L2  v[j] = element (t & 63) + 64j + 1024(t >> 6)                        h = 64 .. 512
+// The order is L0 (h = 1, 2), L1, L2, back to L0 (h = 1024, 2048), through LDS, skipping the
+// layouts whose strides are all >= B.  A ragged last chunk holds zeros past its end; whole
+// blocks are zero there, so they never mix with real data.
+constexpr int HAD_CHUNK = 4096;
+constexpr int HAD_LDS = HAD_CHUNK + HAD_CHUNK / 16;   // 4 words of padding per 64 elements
+
+// LDS word of chunk element e; the padding makes every layout's access conflict-free.
+__device__ __forceinline__ int had_addr(int e) { return e + ((e >> 6) << 2); }
+
+// Butterflies between registers j and j + rs (rs = 1, 2, 4 or 8): lower + upper, lower - upper.
+__device__ __forceinline__ void had_stage(float (&v)[16], int rs) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        if (!(j & rs)) {
+            const float a = v[j], b = v[j + rs];
+            v[j] = a + b;
+            v[j + rs] = a - b;
+        }
+    }
+}
+
+// Block size known at compile time (FixedBlock<B>) or only at run time (int).  With a fixed
+// block every stage test folds away, and the register renaming of the butterflies needs no
+// moves at the joins of skipped stages.
+template <int B>
+struct FixedBlock {
+    __device__ constexpr operator int() const { return B; }
+};
+
+// Register strides 1, 2, 4, 8 standing for element strides base, 2 base, 4 base, 8 base.
+template <typename Blk>
+__device__ __forceinline__ void had_stages16(float (&v)[16], int base, Blk block) {
+    if (base < (int)block) had_stage(v, 1);
+    if (2 * base < (int)block) had_stage(v, 2);
+    if (4 * base < (int)block) had_stage(v, 4);
+    if (8 * base < (int)block) had_stage(v, 8);
+}
+
+// Workgroup barrier that orders LDS accesses only: global loads in flight (the next row's
+// prefetch) stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// SCALE = false leaves the final multiply by fp32(1/sqrt(B)) to the caller.
+template <bool SCALE = true, typename Blk>
+__device__ __forceinline__ void hadamard_chunk(float (&v)[16], Blk block_, float scale, float* buf) {
+    const int block = (int)block_;
+    const int t = threadIdx.x;
+    if (block > 1) had_stage(v, 1);
+    if (block > 2) had_stage(v, 2);
+    if (block > 4) {
+        lds_barrier();                                  // buf is free again
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<float4*>(buf + had_addr(4 * t + 1024 * q)) =
+                make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        lds_barrier();
+        // each element returns to the word it came from: one owner per word in each layout
+        const int e1 = (t & 3) + 64 * ((t >> 2) & 15) + 1024 * (t >> 6);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = buf[had_addr(e1 + 4 * j)];
+        had_stages16(v, 4, block_);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) buf[had_addr(e1 + 4 * j)] = v[j];
+        lds_barrier();
+        if (block > 64) {
+            const int e2 = (t & 63) + 1024 * (t >> 6);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) v[j] = buf[had_addr(e2 + 64 * j)];
+            had_stages16(v, 64, block_);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) buf[had_addr(e2 + 64 * j)] = v[j];
+            lds_barrier();
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 f = *reinterpret_cast<const float4*>(buf + had_addr(4 * t + 1024 * q));
+            v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+        }
+        if (block > 1024) had_stage(v, 4);
+        if (block > 2048) had_stage(v, 8);
+    }
+    if constexpr (SCALE) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = v[j] * scale;
+    }
+}
+
+// Load thread t's 16 elements of chunk [c0, c0 + len) of a row (len % 4 == 0) in layout L0,
+// with the sign flips applied (an exact sign-bit toggle); zeros past the end.
+__device__ __forceinline__ void load_chunk(const float* __restrict__ row, const int8_t* __restrict__ signs,
+                                           int64_t c0, int len, float (&v)[16]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = 4 * threadIdx.x + 1024 * q;
+        float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+        uint32_t sg = 0;
+        if (e < len) {
+            f = *reinterpret_cast<const float4*>(row + c0 + e);
+            if (signs) sg = *reinterpret_cast<const uint32_t*>(signs + c0 + e) & 0x80808080u;
+        }
+        v[4 * q + 0] = __uint_as_float(__float_as_uint(f.x) ^ (sg << 24));
+        v[4 * q + 1] = __uint_as_float(__float_as_uint(f.y) ^ ((sg << 16) & 0x80000000u));
+        v[4 * q + 2] = __uint_as_float(__float_as_uint(f.z) ^ ((sg << 8) & 0x80000000u));
+        v[4 * q + 3] = __uint_as_float(__float_as_uint(f.w) ^ (sg & 0x80000000u));
+    }
+}
+
+__device__ __forceinline__ int chunk_len(int64_t K, int64_t c0) {
+    return K - c0 < HAD_CHUNK ? (int)(K - c0) : HAD_CHUNK;
+}
+
+// One workgroup per (row, chunk): out = rotated x.  Every element is read into registers
+// before any is written, and a workgroup writes only its own chunk, so out may equal x.
+__global__ __launch_bounds__(256) void k_hadamard_rows(const float* x, int64_t K, int64_t chunks, int block,
+                                                       float scale, const int8_t* __restrict__ signs,
+                                                       float* out) {
+    __shared__ float buf[HAD_LDS];
+    const int64_t row = blockIdx.x / chunks;
+    const int64_t c0 = (blockIdx.x - row * chunks) * HAD_CHUNK;
+    const int len = chunk_len(K, c0);
+    float v[16];
+    load_chunk(x + row * K, signs, c0, len, v);
+    hadamard_chunk(v, block, scale, buf);
+    float* o = out + row * K + c0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = 4 * threadIdx.x + 1024 * q;
+        if (e < len) *reinterpret_cast<float4*>(o + e) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    }
+}
+
+// Four codes, packed little-endian, of values with |x| <= beta (true for every element of the
+// row beta was taken from).  The quotient t = fp32(127 x) / beta is formed as in act_code and
+// satisfies |t| < 127.5, so the clip of the definition never acts; adding 1.5 * 2^23 rounds t
+// half-to-even to an integer held in the low mantissa bits, whose low byte is the two's
+// complement code.  v_perm gathers the four bytes.  m127 = 127 s with s a power of two
+// (the unapplied rotation scale) gives the same codes: fp32(fp32(x s) 127) = fp32(x (127 s))
+// whenever x s is normal, and where it is subnormal both quotients round to code 0, since
+// beta >= 1e-8.
+__device__ __forceinline__ uint32_t act_codes4(float x0, float x1, float x2, float x3, float beta, float y,
+                                              float m127 = 127.0f) {
+    auto code = [&](float x) {
+        const float a = x * m127;
+        const float q = a * y;
+        const float r = __builtin_fmaf(-q, beta, a);
+        const float t = __builtin_fmaf(r, y, q);
+        return __float_as_uint(t + 12582912.0f);
+    };
+    const uint32_t lo = __builtin_amdgcn_perm(code(x1), code(x0), 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(code(x3), code(x2), 0x04000c0cu);
+    return lo | hi;
+}
+
+__device__ __forceinline__ void store_codes(int8_t* __restrict__ xrow, int64_t c0, int len, const float (&v)[16],
+                                            float b, float y) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = 4 * threadIdx.x + 1024 * q;
+        if (e < len)
+            *reinterpret_cast<uint32_t*>(xrow + c0 + e) = act_codes4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3], b, y);
+    }
+}
+
+// Rotation then per-token absmax int8 [P3 §6.2, §2.4]: one workgroup per token.  With
+// CH > 0 the row (at most CH chunks) stays in registers between the max and the codes; with
+// CH == 0 (long rows) each chunk is rotated twice, once for the max and once for the codes,
+// with identical results.
+template <int CH>
+__global__ __launch_bounds__(256) void k_quantize_act_hadamard(const float* __restrict__ x, int64_t K, int block,
+                                                               float scale, const int8_t* __restrict__ signs,
+                                                               int8_t* __restrict__ xq, float* __restrict__ beta) {
+    __shared__ float buf[HAD_LDS];
+    __shared__ float red[4];
+    const int64_t m = blockIdx.x;
+    const float* row = x + m * K;
+    int8_t* xrow = xq + m * K;
+    float mx = 0.0f;
+    if constexpr (CH > 0) {
+        float v[CH][16];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int64_t c0 = (int64_t)c * HAD_CHUNK;
+            if (c0 < K) {
+                load_chunk(row, signs, c0, chunk_len(K, c0), v[c]);
+                hadamard_chunk(v[c], block, scale, buf);
+#pragma unroll
+                for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(v[c][j]));
+            }
+        }
+        mx = block_max_256(mx, red);
+        const float b = mx + 1e-8f;
+        const float y = 1.0f / b;
+        if (threadIdx.x == 0) beta[m] = b;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int64_t c0 = (int64_t)c * HAD_CHUNK;
+            if (c0 < K) store_codes(xrow, c0, chunk_len(K, c0), v[c], b, y);
+        }
+    } else {
+        float v[16];
+        for (int64_t c0 = 0; c0 < K; c0 += HAD_CHUNK) {
+            load_chunk(row, signs, c0, chunk_len(K, c0), v);
+            hadamard_chunk(v, block, scale, buf);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(v[j]));
+        }
+        mx = block_max_256(mx, red);
+        const float b = mx + 1e-8f;
+        const float y = 1.0f / b;
+        if (threadIdx.x == 0) beta[m] = b;
+        for (int64_t c0 = 0; c0 < K; c0 += HAD_CHUNK) {
+            load_chunk(row, signs, c0, chunk_len(K, c0), v);
+            hadamard_chunk(v, block, scale, buf);
+            store_codes(xrow, c0, chunk_len(K, c0), v, b, y);
+        }
+    }
+}
+
+// Rows of K = 1024 NQ elements (NQ = 1..4), the prefill shapes: each workgroup walks rows
+// m = blockIdx.x, + gridDim.x, ... and issues the loads of its next row (clamped to the last
+// row) before it rotates and quantizes the current one, so HBM traffic overlaps the
+// arithmetic.  The signs are loaded once.  With K a multiple of 1024 every thread owns whole
+// float4 groups q < NQ, so loads and stores carry no guards and the compiler waits on the
+// prefetch alone, never on the previous row's stores.
+template <int NQ, bool FULL>
+__global__ __launch_bounds__(256) void k_quantize_act_hadamard_pipe(const float* __restrict__ x, int64_t M,
+                                                                    int block_rt, float scale,
+                                                                    const int8_t* __restrict__ signs,
+                                                                    int8_t* __restrict__ xq, float* __restrict__ beta) {
+    constexpr int K = 1024 * NQ;
+    // full-row block of 4^n elements: the scale 2^-n is exact and is applied to the max and
+    // folded into the factor 127 instead of to every element (identical results)
+    constexpr bool FOLD = FULL && (K == 1024 || K == 4096);
+    __shared__ float buf[HAD_LDS];
+    __shared__ float red[2][4];
+    const int t = threadIdx.x;
+    const bool wave0 = __builtin_amdgcn_readfirstlane(t >> 6) == 0;
+    uint32_t sg[4] = {0u, 0u, 0u, 0u};
+    if (signs) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) sg[q] = *reinterpret_cast<const uint32_t*>(signs + 4 * t + 1024 * q) & 0x80808080u;
+    }
+    float4 nx[NQ];
+    int64_t m = blockIdx.x;
+    {
+        const float* row = x + (m < M ? m : M - 1) * (int64_t)K;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) nx[q] = *reinterpret_cast<const float4*>(row + 4 * t + 1024 * q);
+    }
+    // The first row is peeled so that the loop is entered, like its back edge, with the
+    // prefetch followed by the previous row's stores: the wait at the loop head then leaves
+    // those stores in flight.
+    auto row_step = [&](int64_t m, int it) {
+        float v[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 f = q < NQ ? nx[q < NQ ? q : 0] : make_float4(0.f, 0.f, 0.f, 0.f);
+            v[4 * q + 0] = __uint_as_float(__float_as_uint(f.x) ^ (sg[q] << 24));
+            v[4 * q + 1] = __uint_as_float(__float_as_uint(f.y) ^ ((sg[q] << 16) & 0x80000000u));
+            v[4 * q + 2] = __uint_as_float(__float_as_uint(f.z) ^ ((sg[q] << 8) & 0x80000000u));
+            v[4 * q + 3] = __uint_as_float(__float_as_uint(f.w) ^ (sg[q] & 0x80000000u));
+        }
+        {
+            const int64_t mn = m + gridDim.x;
+            const float* row = x + (mn < M ? mn : M - 1) * (int64_t)K;
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) nx[q] = *reinterpret_cast<const float4*>(row + 4 * t + 1024 * q);
+        }
+        if constexpr (FULL) hadamard_chunk<!FOLD>(v, FixedBlock<K>{}, scale, buf);   // one block per row
+        else hadamard_chunk(v, block_rt, scale, buf);
+        float mx = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4 * NQ; ++j) mx = fmaxf(mx, fabsf(v[j]));
+        mx = wave_max_f32(mx);
+        float* rd = red[it & 1];                  // alternate buffers: no barrier needed before reuse
+        if ((t & 63) == 0) rd[t >> 6] = mx;
+        lds_barrier();
+        mx = fmaxf(fmaxf(rd[0], rd[1]), fmaxf(rd[2], rd[3]));
+        if constexpr (FOLD) mx = mx * scale;      // = the max of the scaled values (monotone rounding)
+        const float b = mx + 1e-8f;
+        const float y = 1.0f / b;
+        const float m127 = FOLD ? 127.0f * scale : 127.0f;
+        if (wave0) beta[m] = b;                   // every lane of wave 0 stores the same value
+        int8_t* xrow = xq + m * (int64_t)K;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+            *reinterpret_cast<uint32_t*>(xrow + 4 * t + 1024 * q) =
+                act_codes4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3], b, y, m127);
+    };
+    if (m >= M) return;
+    row_step(m, 0);
+    int it = 1;
+    for (m += gridDim.x; m < M; m += gridDim.x, ++it) row_step(m, it);
+}
+
+// ---------------------------------------------------------------------------------------
 hipError_t launch_row_abs_sums(const float* W, int64_t N, int64_t K, double* rowsum, hipStream_t s) {
     hipLaunchKernelGGL(k_row_abs_sums, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s, W, N, K, rowsum);
     return hipGetLastError();
@@ -211,6 +528,73 @@ hipError_t launch_quantize_act(const float* x, int64_t M, int64_t K, int8_t* xq,
         hipLaunchKernelGGL(k_quantize_act<true>, dim3((unsigned)M), dim3(256), 0, s, x, K, xq, beta);
     else
         hipLaunchKernelGGL(k_quantize_act<false>, dim3((unsigned)M), dim3(256), 0, s, x, K, xq, beta);
+    return hipGetLastError();
+}
+
+// Workgroups of the pipelined kernel: as many as the device holds at once (occupancy of the
+// kernel times the compute units), each walking rows with a stride of the grid.
+template <typename Kernel>
+static int64_t resident_wgs(Kernel k) {
+    int dev = 0, cus = 0, per = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k, 256, 0) != hipSuccess || cus <= 0 || per <= 0)
+        return 1024;
+    return (int64_t)cus * per;
+}
+
+static float hadamard_scale(int block) { return (float)(1.0 / std::sqrt((double)block)); }
+
+hipError_t launch_hadamard_rows(const float* x, int64_t M, int64_t K, int block, const int8_t* signs, float* out,
+                                hipStream_t s) {
+    const int64_t chunks = (K + HAD_CHUNK - 1) / HAD_CHUNK;
+    hipLaunchKernelGGL(k_hadamard_rows, dim3((unsigned)(M * chunks)), dim3(256), 0, s, x, K, chunks, block,
+                       hadamard_scale(block), signs, out);
+    return hipGetLastError();
+}
+
+// The full-row block (B == K) gets the compile-time stage pattern; K = 3072 has none.
+template <int NQ, bool FULL>
+static void launch_had_pipe_k(const float* x, int64_t M, int block, float sc, const int8_t* signs, int8_t* xq,
+                              float* beta, hipStream_t s) {
+    auto k = k_quantize_act_hadamard_pipe<NQ, FULL>;
+    const int64_t wgs = resident_wgs(k);
+    hipLaunchKernelGGL(k, dim3((unsigned)(M < wgs ? M : wgs)), dim3(256), 0, s, x, M, block, sc, signs, xq, beta);
+}
+
+template <int NQ>
+static void launch_had_pipe(const float* x, int64_t M, int block, float sc, const int8_t* signs, int8_t* xq,
+                            float* beta, hipStream_t s) {
+    constexpr bool pow2 = (NQ & (NQ - 1)) == 0;
+    if (pow2 && block == 1024 * NQ)
+        launch_had_pipe_k<NQ, pow2>(x, M, block, sc, signs, xq, beta, s);
+    else
+        launch_had_pipe_k<NQ, false>(x, M, block, sc, signs, xq, beta, s);
+}
+
+hipError_t launch_quantize_act_hadamard(const float* x, int64_t M, int64_t K, int block, const int8_t* signs,
+                                        int8_t* xq, float* beta, hipStream_t s) {
+    const int64_t chunks = (K + HAD_CHUNK - 1) / HAD_CHUNK;
+    const float sc = hadamard_scale(block);
+    const dim3 grid((unsigned)M), threads(256);
+    if (K == 4096)
+        launch_had_pipe<4>(x, M, block, sc, signs, xq, beta, s);
+    else if (K == 3072)
+        launch_had_pipe<3>(x, M, block, sc, signs, xq, beta, s);
+    else if (K == 2048)
+        launch_had_pipe<2>(x, M, block, sc, signs, xq, beta, s);
+    else if (K == 1024)
+        launch_had_pipe<1>(x, M, block, sc, signs, xq, beta, s);
+    else if (chunks == 1)
+        hipLaunchKernelGGL(k_quantize_act_hadamard<1>, grid, threads, 0, s, x, K, block, sc, signs, xq, beta);
+    else if (chunks == 2)
+        hipLaunchKernelGGL(k_quantize_act_hadamard<2>, grid, threads, 0, s, x, K, block, sc, signs, xq, beta);
+    else if (chunks <= 4)
+        hipLaunchKernelGGL(k_quantize_act_hadamard<4>, grid, threads, 0, s, x, K, block, sc, signs, xq, beta);
+    else if (chunks <= 8)
+        hipLaunchKernelGGL(k_quantize_act_hadamard<8>, grid, threads, 0, s, x, K, block, sc, signs, xq, beta);
+    else
+        hipLaunchKernelGGL(k_quantize_act_hadamard<0>, grid, threads, 0, s, x, K, block, sc, signs, xq, beta);
     return hipGetLastError();
 }
 

@@ -4,7 +4,8 @@
  * Page keys used in the citations below:
  *   [P2] nxmr.cn tutorial "1.58 位大模型" (per-row absmean, add/sub form of the matmul).
  *   [P3] chenxutan.com, "1.58-bit 大模型极限量化实战：从 BitNet 三值权重到单颗 CPU 跑起 100B 模型"
- *        (absmean / absmax formulas, BitLinear forward, 2-bit packing).
+ *        (absmean / absmax formulas, BitLinear forward, 2-bit packing, §6.2 the rotation
+ *        before absmax).
  *
  * The layer is split the way [P3 §3.2] describes BitLinear: weights are quantized once and
  * cached (bitlinear_quantize_weights); every call quantizes the activations
@@ -172,6 +173,43 @@ int bitlinear_forward_fused(const float* x, int64_t M, int64_t K, const uint8_t*
 int bitlinear_forward_fused_rows(const float* x, int64_t M, int64_t K, const uint8_t* W_packed,
                                  const float* alpha_rows, int64_t N, const float* bias, float* y,
                                  int8_t* x_q, float* beta, int32_t* acc, hipStream_t stream);
+
+/*
+ * Randomized Hadamard rotation along K [P3 §6.2], the preprocessing that spreads an outlier
+ * channel over all dimensions before the absmax.  For each row r of x and each block of B
+ * consecutive columns (B = `block`, a power of two, 1 <= B <= 4096, K % B == 0):
+ *     out[r, blk] = (d[blk] * x[r, blk]) . H_B / sqrt(B)
+ * with d[k] = -1 where signs[k] < 0, +1 elsewhere (signs NULL: all +1), and H_B the Sylvester
+ * Hadamard matrix (H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]]).  Evaluation, fixed so that
+ * results are reproducible bit for bit: the sign flip is exact; the transform runs as fp32
+ * butterflies (a, b) -> (a + b, a - b) on element pairs (j, j + h), h = 1, 2, 4, ..., B/2 in
+ * that order; every result is then multiplied once by fp32(1/sqrt(B)) (exact for B a power
+ * of 4).  The rotation is orthonormal (R R^T = I): rotating the rows of W with the same
+ * block and signs (once, before bitlinear_quantize_weights) and every x keeps x . W^T.
+ *
+ *   x      [M, K] fp32, 16-byte aligned.            (in)
+ *   signs  [K] int8, 4-byte aligned, or NULL.       (in; the caller draws them)
+ *   out    [M, K] fp32, 16-byte aligned; may be x (in place), else must not overlap it. (out)
+ * K % 4 == 0.  Errors: INVALID_ARG, SHAPE (block not a power of two in [1, 4096], K % block,
+ * K % 4, size overflow), ALIGNMENT, HIP.
+ */
+int bitlinear_hadamard_rows(const float* x, int64_t M, int64_t K, int64_t block, const int8_t* signs,
+                            float* out, hipStream_t stream);
+
+/*
+ * Rotation then activation quantization in one pass [P3 §6.2, §2.4]: x_q and beta are those
+ * bitlinear_quantize_act gives for the rows rotated by bitlinear_hadamard_rows (same block
+ * and signs), without writing the rotated rows.  Feed x_q and beta to bitlinear_forward with
+ * weights quantized from rotated rows.
+ *
+ *   x      [M, K] fp32, 16-byte aligned.            (in)
+ *   signs  [K] int8, 4-byte aligned, or NULL.       (in)
+ *   x_q    [M, K] int8, 4-byte aligned.             (out)
+ *   beta   [M] fp32.                                (out)
+ * Errors as bitlinear_hadamard_rows.
+ */
+int bitlinear_quantize_act_hadamard(const float* x, int64_t M, int64_t K, int64_t block,
+                                    const int8_t* signs, int8_t* x_q, float* beta, hipStream_t stream);
 
 /* Kernel(s) bitlinear_forward_fused launches for these arguments ("gemv_fused" or
  * "quantize_act+forward"); a static string. */

@@ -190,3 +190,23 @@ def test_binding_has_no_host_fallback():
     for f in os.listdir(os.path.join(ROOT, "bitlinear_matmul_absmean_amd", "csrc")):
         text = open(os.path.join(ROOT, "bitlinear_matmul_absmean_amd", "csrc", f)).read()
         assert "oracle" not in text.lower(), f
+
+
+def test_hadamard_validation(bl):
+    """Rotation calls reject bad blocks, shapes and alignments before any HIP call."""
+    h, q = bl.lib.bitlinear_hadamard_rows, bl.lib.bitlinear_quantize_act_hadamard
+    for block in (0, 3, 6, 8192):
+        assert h(A, 1, 8192, block, None, A, None) in (bl.BITLINEAR_ERR_SHAPE, bl.BITLINEAR_ERR_INVALID_ARG)
+        assert q(A, 1, 8192, block, None, A, A, None) in (bl.BITLINEAR_ERR_SHAPE, bl.BITLINEAR_ERR_INVALID_ARG)
+    assert h(A, 1, 96, 64, None, A, None) == bl.BITLINEAR_ERR_SHAPE          # K % block
+    assert h(A, 1, 6, 2, None, A, None) == bl.BITLINEAR_ERR_SHAPE            # K % 4
+    assert h(None, 1, 64, 64, None, A, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert h(A, 1, 64, 64, None, None, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert h(A, 0, 64, 64, None, A, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert h(A + 4, 1, 64, 64, None, A, None) == bl.BITLINEAR_ERR_ALIGNMENT   # x 16-byte
+    assert h(A, 1, 64, 64, None, A + 8, None) == bl.BITLINEAR_ERR_ALIGNMENT   # out 16-byte
+    assert h(A, 1, 64, 64, A + 2, A, None) == bl.BITLINEAR_ERR_ALIGNMENT      # signs 4-byte
+    assert q(A, 1, 64, 64, None, None, A, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert q(A, 1, 64, 64, None, A, None, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert q(A, 1, 64, 64, None, A + 2, A, None) == bl.BITLINEAR_ERR_ALIGNMENT  # x_q 4-byte
+    assert q(A, 1, 64, 64, A + 1, A, A, None) == bl.BITLINEAR_ERR_ALIGNMENT

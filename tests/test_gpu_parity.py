@@ -398,3 +398,111 @@ def test_forward_fused_rows_per_row_alpha(dev, m, k, n):
     y = bl.bitlinear_forward_fused_rows(_to(torch, x), _to(torch, packed_o), _to(torch, alpha_rows_o))
     torch.cuda.synchronize()
     assert np.array_equal(y.cpu().numpy(), y_o)
+
+
+# ------------------------------------------------------------------ rotation before absmax [P3 §6.2]
+# (M, K, block, with signs): every chunk path (1, 2, 4, 8 chunks of 4096 held in registers,
+# and the two-pass path past 8 chunks), ragged last chunks, blocks from 1 to 4096.
+HAD_CASES = [(3, 4096, 4096, True), (2, 8192, 2048, True), (2, 11008, 256, True), (1, 12, 4, True),
+             (2, 4100, 4, False), (5, 1024, 1024, True), (2, 12352, 64, True), (1, 36, 1, True),
+             (2, 28672, 4096, True), (1, 40960, 4096, True), (4, 2048, 2, False), (64, 4096, 4096, True),
+             (2, 20480, 1024, True), (3, 6144, 2048, False), (3, 3072, 1024, True), (2500, 1024, 256, True),
+             (1030, 2048, 8, False), (6, 2048, 2048, True)]
+
+
+def _had_inputs(m, k, with_signs, seed=5):
+    x = workloads.activations_with_outliers(seed, m, k)
+    d = workloads.rotation_signs(seed, k) if with_signs else None
+    return x, d
+
+
+@pytest.mark.parametrize("m,k,block,with_signs", HAD_CASES)
+def test_hadamard_rows_parity(dev, m, k, block, with_signs):
+    torch, bl = dev
+    _say(f"hadamard_rows M={m} K={k} B={block} signs={with_signs}")
+    x, d = _had_inputs(m, k, with_signs)
+    want = oracle.hadamard_rows(x, block, d)
+    got = bl.bitlinear_hadamard_rows(_to(torch, x), block, None if d is None else _to(torch, d))
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+def test_hadamard_rows_in_place(dev):
+    torch, bl = dev
+    x, d = _had_inputs(3, 12288, True, seed=6)
+    want = oracle.hadamard_rows(x, 4096, d)
+    xt = _to(torch, x)
+    out = bl.bitlinear_hadamard_rows(xt, 4096, _to(torch, d), out=xt)
+    torch.cuda.synchronize()
+    assert out.data_ptr() == xt.data_ptr()
+    assert np.array_equal(xt.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("m,k,block,with_signs", HAD_CASES)
+def test_quantize_act_hadamard_parity(dev, m, k, block, with_signs):
+    torch, bl = dev
+    _say(f"quantize_act_hadamard M={m} K={k} B={block} signs={with_signs}")
+    x, d = _had_inputs(m, k, with_signs)
+    xq_o, beta_o = oracle.quantize_act_hadamard(x, block, d)
+    xq, beta = bl.bitlinear_quantize_act_hadamard(_to(torch, x), block, None if d is None else _to(torch, d))
+    torch.cuda.synchronize()
+    assert np.array_equal(beta.cpu().numpy().view(np.uint32), beta_o.view(np.uint32))
+    assert np.array_equal(xq.cpu().numpy(), xq_o)
+
+
+@pytest.mark.parametrize("k,block", [(4096, 4096), (1024, 1024), (2048, 2048), (4096, 64)])
+def test_quantize_act_hadamard_tiny_and_zero_rows(dev, k, block):
+    """Rows whose rotated values are subnormal (all of them, or all but the largest), an
+    all-zero row and a single spike: codes and beta still match bit for bit."""
+    torch, bl = dev
+    _say(f"quantize_act_hadamard tiny rows K={k} B={block}")
+    g = np.random.default_rng(3)
+    x = np.zeros((5, k), np.float32)
+    x[0] = (g.standard_normal(k) * 1e-37).astype(np.float32)          # every rotated value subnormal
+    x[1] = (g.standard_normal(k) * 1e-36).astype(np.float32)
+    x[1, 7] = np.float32(1.0)                                           # one normal spike
+    x[3, k - 1] = np.float32(-3.5)                                      # x[2] stays all zero
+    x[4] = (g.standard_normal(k) * 1e-41).astype(np.float32)          # subnormal inputs
+    d = workloads.rotation_signs(7, k)
+    xq_o, beta_o = oracle.quantize_act_hadamard(x, block, d)
+    xq, beta = bl.bitlinear_quantize_act_hadamard(_to(torch, x), block, _to(torch, d))
+    torch.cuda.synchronize()
+    assert np.array_equal(beta.cpu().numpy().view(np.uint32), beta_o.view(np.uint32))
+    assert np.array_equal(xq.cpu().numpy(), xq_o)
+
+
+def test_quantize_act_hadamard_prefill_full_size(dev):
+    """Prefill activations [2048, 4096] with 0.1% outliers, block 4096: all rows compared."""
+    torch, bl = dev
+    _say("quantize_act_hadamard M=2048 K=4096 B=4096")
+    x = workloads.activations_with_outliers(4, 2048, 4096)
+    d = workloads.rotation_signs(4, 4096)
+    xq_o, beta_o = oracle.quantize_act_hadamard(x, 4096, d)
+    xq, beta = bl.bitlinear_quantize_act_hadamard(_to(torch, x), 4096, _to(torch, d))
+    torch.cuda.synchronize()
+    assert np.array_equal(beta.cpu().numpy().view(np.uint32), beta_o.view(np.uint32))
+    assert np.array_equal(xq.cpu().numpy(), xq_o)
+
+
+@pytest.mark.parametrize("m,k,n,block", [(1, 4096, 1024, 4096), (1, 11008, 300, 256), (24, 2048, 200, 2048),
+                                         (130, 1024, 96, 512)])
+def test_end_to_end_rotated_bitlinear(dev, m, k, n, block):
+    """Rotated weights (offline: hadamard_rows then quantize_weights) and rotated activations
+    (quantize_act_hadamard) into bitlinear_forward, against the oracle's rotated BitLinear."""
+    torch, bl = dev
+    _say(f"rotated bitlinear M={m} K={k} N={n} B={block}")
+    w = workloads.weights(6, n, k)
+    x = workloads.activations_with_outliers(6, m, k)
+    d = workloads.rotation_signs(6, k)
+    r = oracle.bitlinear_hadamard(x, w, block, d)
+    dt = _to(torch, d)
+    wr = bl.bitlinear_hadamard_rows(_to(torch, w), block, dt)
+    packed, alpha = bl.bitlinear_quantize_weights(wr)
+    xq, beta = bl.bitlinear_quantize_act_hadamard(_to(torch, x), block, dt)
+    y, acc = bl.bitlinear_forward(xq, beta, packed, alpha, acc=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(packed.cpu().numpy(), r["packed"])
+    assert np.float32(alpha.cpu().numpy()[0]) == r["alpha"]
+    assert np.array_equal(xq.cpu().numpy(), r["xq"])
+    assert np.array_equal(acc.cpu().numpy(), r["acc"])
+    assert _rel_ok(y.cpu().numpy(), r["y"])
