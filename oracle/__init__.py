@@ -7,6 +7,8 @@ package imports nothing from the GPU library.
 The arithmetic lives in ``oracle.c`` (plain scalar C, built with ``-ffp-contract=off``);
 this module only marshals NumPy arrays through ctypes.  Page keys used in citations:
 
+* [P1] 2kiu.com, article on 1.58-bit quantization and hardware co-optimization (§2.3 and
+  §4.2: one scale per block of 128 weights, shape [C_out, C_in/128]).
 * [P2] nxmr.cn tutorial "1.58 位大模型" (per-row absmean, add/sub derivation, memory estimate).
 * [P3] chenxutan.com, "1.58-bit 大模型极限量化实战：从 BitNet 三值权重到单颗 CPU 跑起 100B 模型"
   (absmean / absmax formulas, worked example, BitLinear forward, 2-bit packing, §6.2 the
@@ -58,6 +60,10 @@ def _load():
         "oracle_dequant_scale": (f32, [f32, f32]),
         "oracle_dequant": (ctypes.c_int, [p, p, f32, p, i64, i64, p, p, i64, i64]),
         "oracle_hadamard_rows": (ctypes.c_int, [p, i64, i64, i64, p, p]),
+        "oracle_absmean_blocks": (ctypes.c_int, [p, i64, i64, p]),
+        "oracle_ternarize_blocks": (ctypes.c_int, [p, i64, i64, p, p]),
+        "oracle_ternary_matmul_blocks": (ctypes.c_int, [p, i64, i64, p, i64, p]),
+        "oracle_dequant_blocks": (ctypes.c_int, [p, p, p, i64, i64, i64, p, p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -243,3 +249,76 @@ def bitlinear_hadamard(x: np.ndarray, w: np.ndarray, block: int, signs: np.ndarr
     """BitLinear forward with the rotation of [P3 §6.2] on both operands: W and x are rotated
     by the same R, then quantized and multiplied as in :func:`bitlinear`."""
     return bitlinear(hadamard_rows(x, block, signs), hadamard_rows(w, block, signs), bias=bias)
+
+
+# ------------------------------------------------------------------ block scales (R12)
+BLOCK = 128
+
+
+def absmean_blocks(w: np.ndarray) -> np.ndarray:
+    """[P1 §2.3, §4.2] alpha [N, K/128]: mean |W| over each block of 128 weights of a row."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    n, k = w.shape
+    out = np.empty((n, k // BLOCK), np.float32)
+    _check(_load().oracle_absmean_blocks(_ptr(w), n, k, _ptr(out)), "absmean_blocks")
+    return out
+
+
+def ternarize_blocks(w: np.ndarray, alpha_blocks: np.ndarray) -> np.ndarray:
+    """[P3 §2.3] codes with every weight divided by its block's alpha."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    a = np.ascontiguousarray(alpha_blocks, dtype=np.float32)
+    n, k = w.shape
+    assert a.shape == (n, k // BLOCK)
+    out = np.empty((n, k), np.int8)
+    _check(_load().oracle_ternarize_blocks(_ptr(w), n, k, _ptr(a), _ptr(out)), "ternarize_blocks")
+    return out
+
+
+def quantize_weights_blocks(w: np.ndarray):
+    """Block-scaled weight quantization: returns (codes int8 [N,K], packed uint8 [N,K/4],
+    alpha_blocks fp32 [N,K/128]); the packing is the 2-bit layout of :func:`pack`."""
+    a = absmean_blocks(w)
+    codes = ternarize_blocks(w, a)
+    return codes, pack(codes), a
+
+
+def ternary_matmul_blocks(xq: np.ndarray, codes: np.ndarray) -> np.ndarray:
+    """[P2 §3.3] per-block integer sums acc [M, N, K/128] (int32)."""
+    xq = np.ascontiguousarray(xq, dtype=np.int8)
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    m, k = xq.shape
+    n = codes.shape[0]
+    out = np.zeros((m, n, k // BLOCK), np.int32)
+    _check(_load().oracle_ternary_matmul_blocks(_ptr(xq), m, k, _ptr(codes), n, _ptr(out)), "ternary_matmul_blocks")
+    return out
+
+
+def dequant_blocks(acc: np.ndarray, beta: np.ndarray, alpha_blocks: np.ndarray,
+                   bias: np.ndarray | None = None) -> np.ndarray:
+    """[P1 §2.3; P3 §2.4] y = fp32(sum_b alpha[n,b] acc[m,n,b] * beta[m]/127) in fp64 (+ bias)."""
+    acc = np.ascontiguousarray(acc, dtype=np.int32)
+    beta = np.ascontiguousarray(beta, dtype=np.float32)
+    a = np.ascontiguousarray(alpha_blocks, dtype=np.float32)
+    m, n, kb = acc.shape
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    out = np.empty((m, n), np.float32)
+    _check(_load().oracle_dequant_blocks(_ptr(acc), _ptr(beta), _ptr(a), m, n, kb, _ptr(b), _ptr(out)),
+           "dequant_blocks")
+    return out
+
+
+def forward_blocks(xq: np.ndarray, beta: np.ndarray, packed: np.ndarray, k: int, alpha_blocks: np.ndarray,
+                   bias: np.ndarray | None = None):
+    """Block-scaled forward on packed codes: returns (acc_blocks [M,N,K/128], y [M,N])."""
+    acc = ternary_matmul_blocks(xq, unpack(packed, k))
+    return acc, dequant_blocks(acc, beta, alpha_blocks, bias)
+
+
+def bitlinear_blocks(x: np.ndarray, w: np.ndarray, bias: np.ndarray | None = None):
+    """Whole BitLinear forward with block scales; returns every intermediate."""
+    codes, packed, a = quantize_weights_blocks(w)
+    xq, beta = quantize_act(x)
+    acc = ternary_matmul_blocks(xq, codes)
+    y = dequant_blocks(acc, beta, a, bias)
+    return dict(codes=codes, packed=packed, alpha_blocks=a, xq=xq, beta=beta, acc_blocks=acc, y=y)

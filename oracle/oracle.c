@@ -33,6 +33,11 @@
  *       one after another (row-major along K).
  *   R7  s = fp32((double)alpha * (double)beta / 127.0), y = fp32((float)acc * s), then
  *       + bias as a separate fp32 rounding.
+ *   R12 block scales [P1 §2.3, §4.2]: one alpha per 128 consecutive weights of a row,
+ *       alpha[n, b] = mean |W[n, 128b .. 128b+127]| (R1 for a block), codes divided by their
+ *       block's alpha; the integer sums are kept per block, acc[m, n, b], and
+ *       y[m, n] = fp32(S * (beta[m] / 127)) with S = sum_b alpha[n, b] * acc[m, n, b]
+ *       accumulated in fp64 in ascending b and beta/127 an fp64 division; + bias in fp32.
  *   R10 the rotation before absmax [P3 §6.2] is a randomized Walsh-Hadamard transform
  *       applied to each row along K in blocks of B (a power of two dividing K): a sign
  *       flip by d[k] in {+1, -1} (the random part; an input, negative int8 = flip), then
@@ -242,6 +247,67 @@ int oracle_hadamard_rows(const float* x, int64_t m_rows, int64_t k, int64_t bloc
                 }
             }
             for (int64_t j = 0; j < block; ++j) v[j] = v[j] * scale;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------- block scales (R12) */
+#define ORACLE_BLOCK 128
+
+/* [P1 §2.3, §4.2] alpha[n, b] over each block of 128 weights of row n; alpha is [N, K/128]. */
+int oracle_absmean_blocks(const float* w, int64_t n_rows, int64_t k, float* alpha) {
+    if (!w || !alpha || n_rows <= 0 || k <= 0 || k % ORACLE_BLOCK != 0) return ORACLE_EINVAL;
+    const int64_t kb = k / ORACLE_BLOCK;
+    for (int64_t n = 0; n < n_rows; ++n)
+        for (int64_t b = 0; b < kb; ++b)
+            alpha[n * kb + b] = oracle_absmean(w + n * k + b * ORACLE_BLOCK, ORACLE_BLOCK);
+    return ORACLE_OK;
+}
+
+/* [P3 §2.3] codes with each weight divided by its own block's alpha. */
+int oracle_ternarize_blocks(const float* w, int64_t n_rows, int64_t k, const float* alpha, int8_t* codes) {
+    if (!w || !alpha || !codes || n_rows <= 0 || k <= 0 || k % ORACLE_BLOCK != 0) return ORACLE_EINVAL;
+    const int64_t kb = k / ORACLE_BLOCK;
+    for (int64_t n = 0; n < n_rows; ++n)
+        for (int64_t j = 0; j < k; ++j)
+            codes[n * k + j] = ternary_code(w[n * k + j], alpha[n * kb + j / ORACLE_BLOCK]);
+    return ORACLE_OK;
+}
+
+/* [P2 §3.3] the add/sub sums kept per block: acc[m, n, b] over k in block b (int32). */
+int oracle_ternary_matmul_blocks(const int8_t* xq, int64_t m_rows, int64_t k, const int8_t* codes,
+                                 int64_t n_rows, int32_t* acc) {
+    if (!xq || !codes || !acc || m_rows <= 0 || n_rows <= 0 || k <= 0 || k % ORACLE_BLOCK != 0)
+        return ORACLE_EINVAL;
+    const int64_t kb = k / ORACLE_BLOCK;
+    for (int64_t m = 0; m < m_rows; ++m)
+        for (int64_t n = 0; n < n_rows; ++n)
+            for (int64_t b = 0; b < kb; ++b) {
+                int32_t s = 0;
+                for (int64_t j = b * ORACLE_BLOCK; j < (b + 1) * ORACLE_BLOCK; ++j) {
+                    int8_t c = codes[n * k + j];
+                    if (c == 1) s += xq[m * k + j];
+                    else if (c == -1) s -= xq[m * k + j];
+                }
+                acc[(m * n_rows + n) * kb + b] = s;
+            }
+    return ORACLE_OK;
+}
+
+/* [P1 §2.3; P3 §2.4] y[m, n] = fp32(S * (beta[m] / 127)) (+ bias), S = sum_b alpha[n, b] *
+ * acc[m, n, b] in fp64, ascending b (R12). */
+int oracle_dequant_blocks(const int32_t* acc, const float* beta, const float* alpha, int64_t m_rows,
+                          int64_t n_rows, int64_t kb, const float* bias, float* y) {
+    if (!acc || !beta || !alpha || !y || m_rows <= 0 || n_rows <= 0 || kb <= 0) return ORACLE_EINVAL;
+    for (int64_t m = 0; m < m_rows; ++m) {
+        const double t = (double)beta[m] / 127.0;
+        for (int64_t n = 0; n < n_rows; ++n) {
+            double s = 0.0;
+            for (int64_t b = 0; b < kb; ++b) s += (double)alpha[n * kb + b] * (double)acc[(m * n_rows + n) * kb + b];
+            float v = (float)(s * t);
+            if (bias) v = v + bias[n];
+            y[m * n_rows + n] = v;
         }
     }
     return ORACLE_OK;

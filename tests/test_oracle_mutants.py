@@ -46,6 +46,14 @@ MUTANTS = [
      "const float scale = (float)(1.0 / (double)block);"),
     ("rotation signs ignored", "o[j] = (signs && signs[j] < 0) ? -row[j] : row[j];", "o[j] = row[j];"),
     ("rotation block offset dropped", "float* v = o + b0;", "float* v = o;"),
+    ("block alpha from the wrong row", "alpha[n * kb + b] = oracle_absmean(w + n * k + b * ORACLE_BLOCK, ORACLE_BLOCK);",
+     "alpha[n * kb + b] = oracle_absmean(w + b * ORACLE_BLOCK, ORACLE_BLOCK);"),
+    ("block code uses a neighbouring block", "alpha[n * kb + j / ORACLE_BLOCK]", "alpha[n * kb + (j + 64) / ORACLE_BLOCK % kb]"),
+    ("block sums over half a block", "for (int64_t j = b * ORACLE_BLOCK; j < (b + 1) * ORACLE_BLOCK; ++j) {",
+     "for (int64_t j = b * ORACLE_BLOCK; j < b * ORACLE_BLOCK + ORACLE_BLOCK / 2; ++j) {"),
+    ("block dequant in fp32", "const double t = (double)beta[m] / 127.0;", "const double t = (double)(beta[m] / 127.0f);"),
+    ("block dequant drops alpha", "s += (double)alpha[n * kb + b] * (double)acc[(m * n_rows + n) * kb + b];",
+     "s += (double)acc[(m * n_rows + n) * kb + b];"),
 ]
 
 

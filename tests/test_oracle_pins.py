@@ -469,3 +469,103 @@ def test_rotation_spreads_an_outlier_and_cuts_the_quantization_error():
     assert rel(deq_r, xr64) < rel(deq, x64) / 4
     ref = x64 @ w.astype(np.float64).T
     assert rel(deq_r @ wr64.T, ref) < rel(deq @ w.astype(np.float64).T, ref) / 4
+
+
+# ---------------------------------------------------------------- block scales (R12)
+# [P1 §2.3, §4.2]: one scale per 128 consecutive weights of a row, shape [C_out, C_in/128].
+def _block_weights(seed, n, k):
+    """W ~ N(0, 0.02) with a different magnitude per 128-block, so block scales matter."""
+    g = np.random.default_rng(seed)
+    w = g.standard_normal((n, k)).astype(np.float32) * np.float32(0.02)
+    gain = np.exp(g.uniform(np.log(0.05), np.log(5.0), size=(n, k // 128))).astype(np.float32)
+    return (w * np.repeat(gain, 128, axis=1)).astype(np.float32)
+
+
+def test_block_alpha_is_the_exact_mean_of_each_block():
+    w = _block_weights(21, 5, 384)
+    w[2, 128:256] = 0.0                                              # an all-zero block
+    a = oracle.absmean_blocks(w)
+    assert a.shape == (5, 3)
+    for n in range(5):
+        for b in range(3):
+            assert exact.fr(a[n, b]) == exact.absmean_exact(w[n, 128 * b:128 * b + 128])
+    assert a[2, 1] == 0
+
+
+def test_block_codes_use_their_own_block_scale():
+    w = _block_weights(22, 4, 256)
+    w[1, :128] = 0.0
+    a = oracle.absmean_blocks(w)
+    codes = oracle.ternarize_blocks(w, a)
+    for n in range(4):
+        for b in range(2):
+            blk = slice(128 * b, 128 * b + 128)
+            assert np.array_equal(codes[n, blk], exact.codes_exact(w[n, blk], exact.fr(a[n, b])))
+    assert not codes[1, :128].any()                                  # alpha = 0 -> codes 0 (R3)
+    # a block scale differs from the row scale where magnitudes vary: the codes differ too
+    row_codes = oracle.ternarize_rows(w, oracle.absmean_rows(w))
+    assert (row_codes != codes).any()
+
+
+def test_block_sums_brute_force_and_total():
+    g = np.random.default_rng(23)
+    xq = g.integers(-127, 128, size=(3, 384)).astype(np.int8)
+    codes = g.integers(-1, 2, size=(7, 384)).astype(np.int8)
+    acc = oracle.ternary_matmul_blocks(xq, codes)
+    want = np.einsum("mbk,nbk->mnb", xq.reshape(3, 3, 128).astype(np.int64),
+                     codes.reshape(7, 3, 128).astype(np.int64))
+    assert np.array_equal(acc, want)
+    assert np.array_equal(acc.sum(axis=2), oracle.ternary_matmul(xq, codes))
+
+
+def test_block_dequant_within_one_rounding_of_the_exact_value():
+    g = np.random.default_rng(24)
+    m, n, kb = 3, 9, 5
+    acc = g.integers(-127 * 128, 127 * 128 + 1, size=(m, n, kb)).astype(np.int32)
+    acc[0, 0] = 0
+    a = (g.uniform(0.001, 0.05, size=(n, kb))).astype(np.float32)
+    a[3, 2] = 0.0
+    beta = g.uniform(0.5, 30.0, size=m).astype(np.float32)
+    bias = g.standard_normal(n).astype(np.float32)
+    y = oracle.dequant_blocks(acc, beta, a)
+    yb = oracle.dequant_blocks(acc, beta, a, bias)
+    same = 0
+    for i in range(m):
+        t = exact.fr(beta[i]) / 127
+        for j in range(n):
+            s = sum((exact.fr(a[j, b]) * int(acc[i, j, b]) for b in range(kb)), Fraction(0))
+            want = exact.rne32(s * t)
+            got = exact.fr(y[i, j])
+            ulp = abs(float(want)) * 2.0 ** -23 if want != 0 else 2.0 ** -149
+            assert abs(float(got - want)) <= ulp
+            same += got == want
+            assert yb[i, j] == np.float32(y[i, j] + bias[j])
+    assert y[0, 0] == 0.0
+    assert same >= m * n - 1
+
+
+def test_block_forward_matches_dense_float64_product():
+    """y = (x_q . (alpha_b W_hat)^T) beta/127 with the block-scaled weights dequantized."""
+    w = _block_weights(25, 6, 512)
+    x = workloads.activations(25, 3, 512)
+    r = oracle.bitlinear_blocks(x, w)
+    wdq = r["codes"].astype(np.float64) * np.repeat(r["alpha_blocks"].astype(np.float64), 128, axis=1)
+    ref = (r["xq"].astype(np.float64) @ wdq.T) * (r["beta"].astype(np.float64)[:, None] / 127.0)
+    scale = (np.abs(r["xq"].astype(np.float64)) @ np.abs(wdq).T) * (r["beta"].astype(np.float64)[:, None] / 127.0)
+    assert np.all(np.abs(r["y"] - ref) <= np.abs(ref) * 2.0 ** -23 + scale * 1e-14)
+    acc2, y2 = oracle.forward_blocks(r["xq"], r["beta"], r["packed"], 512, r["alpha_blocks"])
+    assert np.array_equal(acc2, r["acc_blocks"]) and np.array_equal(y2, r["y"])
+
+
+def test_block_scales_track_blockwise_magnitudes_better_than_one_scale():
+    """[P1 §2.3]: a scale per 128 weights follows weights whose magnitude changes along K."""
+    w = _block_weights(26, 64, 1024)
+    x = workloads.activations(26, 4, 1024)
+    ref = x.astype(np.float64) @ w.astype(np.float64).T
+    rel = lambda y: np.linalg.norm(y - ref) / np.linalg.norm(ref)
+    assert rel(oracle.bitlinear_blocks(x, w)["y"]) < 0.75 * rel(oracle.bitlinear(x, w)["y"])   # 0.52 vs 0.79
+
+
+def test_block_functions_reject_k_not_a_multiple_of_128():
+    with pytest.raises(ValueError):
+        oracle.absmean_blocks(np.zeros((2, 192), np.float32))
