@@ -284,13 +284,13 @@ int oracle_ternary_matmul_blocks(const int8_t* xq, int64_t m_rows, int64_t k, co
     for (int64_t m = 0; m < m_rows; ++m)
         for (int64_t n = 0; n < n_rows; ++n)
             for (int64_t b = 0; b < kb; ++b) {
-                int32_t s = 0;
+                int32_t part = 0;
                 for (int64_t j = b * ORACLE_BLOCK; j < (b + 1) * ORACLE_BLOCK; ++j) {
-                    int8_t c = codes[n * k + j];
-                    if (c == 1) s += xq[m * k + j];
-                    else if (c == -1) s -= xq[m * k + j];
+                    const int8_t cj = codes[n * k + j];
+                    if (cj == 1) part += xq[m * k + j];
+                    else if (cj == -1) part -= xq[m * k + j];
                 }
-                acc[(m * n_rows + n) * kb + b] = s;
+                acc[(m * n_rows + n) * kb + b] = part;
             }
     return ORACLE_OK;
 }
@@ -305,9 +305,8 @@ int oracle_dequant_blocks(const int32_t* acc, const float* beta, const float* al
         for (int64_t n = 0; n < n_rows; ++n) {
             double s = 0.0;
             for (int64_t b = 0; b < kb; ++b) s += (double)alpha[n * kb + b] * (double)acc[(m * n_rows + n) * kb + b];
-            float v = (float)(s * t);
-            if (bias) v = v + bias[n];
-            y[m * n_rows + n] = v;
+            const float yv = (float)(s * t);
+            y[m * n_rows + n] = bias ? yv + bias[n] : yv;
         }
     }
     return ORACLE_OK;
