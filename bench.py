@@ -331,6 +331,48 @@ def hadamard_bench(torch, bl, workloads, dev, ms_plain_step, reps=20):
     return out
 
 
+def blocks_bench(torch, bl, workloads, dev, ms_plain_step):
+    """Block-scaled weights [P1 §2.3, §4.2] (one alpha per 128 weights): the 7B decode step
+    (three GEMVs, M = 1) with block-scaled weights and x_q given, its bytes (NK/4 codes +
+    NK/32 scales + K x_q + 4N y per shape), and batched M = 16 on (4096, 11008)."""
+    per_step = sum(n * k // 4 + n * k // 32 for k, n in DECODE_SHAPES)
+    copies = max(2, POOL_BYTES // per_step)
+    shapes = []
+    for idx, (k, n) in enumerate(DECODE_SHAPES):
+        w = torch.from_numpy(workloads.weights(2, n, k, index=idx)).to(dev)
+        packed, ab = bl.bitlinear_quantize_weights_blocks(w)
+        del w
+        pool = [(packed, ab)] + [(packed.clone(), ab.clone()) for _ in range(copies - 1)]
+        x = torch.from_numpy(workloads.activations(2, 1, k, index=100 * idx)).to(dev)
+        xq, beta = bl.bitlinear_quantize_act(x)
+        shapes.append(dict(pool=pool, xq=xq, beta=beta, y=torch.empty((1, n), dtype=torch.float32, device=dev)))
+    torch.cuda.synchronize()
+
+    def step(i):
+        for sh in shapes:
+            p, ab = sh["pool"][i % copies]
+            bl.bitlinear_forward_blocks(sh["xq"], sh["beta"], p, ab, y=sh["y"])
+
+    ms, _ = _graph_time(torch, step, 400)
+    out = {"decode_step": {"shapes_KN": DECODE_SHAPES, "bytes_per_step": per_step, "us_per_step": round(ms * 1e3, 2),
+                           "gbs": round(per_step / (ms * 1e-3) / 1e9, 1),
+                           "pct_hbm": round(100 * per_step / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                           "per_tensor_fused_us_per_step": round(ms_plain_step * 1e3, 2)}}
+    del shapes
+    k, n, m = 4096, 11008, 16
+    w = torch.from_numpy(workloads.weights(3, n, k)).to(dev)
+    packed, ab = bl.bitlinear_quantize_weights_blocks(w)
+    del w
+    x = torch.from_numpy(workloads.activations(3, m, k)).to(dev)
+    xq, beta = bl.bitlinear_quantize_act(x)
+    y = torch.empty((m, n), dtype=torch.float32, device=dev)
+    ms, _ = _graph_time(torch, lambda i: bl.bitlinear_forward_blocks(xq, beta, packed, ab, y=y), 50)
+    out["batched"] = {"M": m, "K": k, "N": n, "us": round(ms * 1e3, 2),
+                      "note": "GEMV over groups of four tokens: the codes are re-read per group"}
+    torch.cuda.empty_cache()
+    return out
+
+
 def batched_bench(torch, bl, workloads, dev, reps=96):
     out = []
     for (k, n) in [(4096, 11008), (11008, 4096)]:
@@ -626,6 +668,8 @@ def main():
         log(f"quantize_act {extras['quantize_act']}")
         extras["hadamard"] = hadamard_bench(torch, bl, workloads, dev, ms_step)
         log(f"hadamard {extras['hadamard']}")
+        extras["blocks"] = blocks_bench(torch, bl, workloads, dev, ms_step)
+        log(f"blocks {extras['blocks']}")
     if not args.no_extras and not args.no_chain:
         extras["chain70b"] = chain70b_bench(torch, bl, workloads, dev)
         log(f"chain70b {extras['chain70b']}")

@@ -40,6 +40,8 @@ SIGNATURES = {
     "bitlinear_forward_fused": (_INT, [_P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P, _P, _P]),
     "bitlinear_forward_fused_rows": (_INT, [_P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P, _P, _P]),
     "bitlinear_forward_fused_kernel": (ctypes.c_char_p, [_I64, _I64, _I64, _P, _P, _P]),
+    "bitlinear_quantize_weights_blocks": (_INT, [_P, _I64, _I64, _P, _P, _P]),
+    "bitlinear_forward_blocks": (_INT, [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _P]),
     "bitlinear_hadamard_rows": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "bitlinear_quantize_act_hadamard": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
 }
@@ -146,6 +148,37 @@ def bitlinear_quantize_act(x, x_q=None, beta=None, stream=None):
         _dev(x, torch.float32, "x"), M, K, _dev(x_q, torch.int8, "x_q"),
         _dev(beta, torch.float32, "beta"), _stream(stream)))
     return x_q, beta
+
+
+def bitlinear_quantize_weights_blocks(W, W_packed=None, alpha_blocks=None, stream=None):
+    """W [N, K] fp32 -> (W_packed uint8 [N, K/4], alpha_blocks fp32 [N, K/128])."""
+    torch = _torch()
+    N, K = W.shape
+    if W_packed is None:
+        W_packed = torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
+    if alpha_blocks is None:
+        alpha_blocks = torch.empty((N, K // 128), dtype=torch.float32, device=W.device)
+    _check("bitlinear_quantize_weights_blocks", lib.bitlinear_quantize_weights_blocks(
+        _dev(W, torch.float32, "W"), N, K, _dev(W_packed, torch.uint8, "W_packed"),
+        _dev(alpha_blocks, torch.float32, "alpha_blocks"), _stream(stream)))
+    return W_packed, alpha_blocks
+
+
+def bitlinear_forward_blocks(x_q, beta, W_packed, alpha_blocks, bias=None, y=None, stream=None):
+    """y [M, N] from x_q, beta and block-scaled packed weights."""
+    torch = _torch()
+    M, K = x_q.shape
+    N = W_packed.shape[0]
+    if W_packed.shape[1] * 4 != K:
+        raise ValueError("W_packed must be [N, K/4]")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x_q.device)
+    _check("bitlinear_forward_blocks", lib.bitlinear_forward_blocks(
+        _dev(x_q, torch.int8, "x_q"), _dev(beta, torch.float32, "beta"), M, K,
+        _dev(W_packed, torch.uint8, "W_packed"), _dev(alpha_blocks, torch.float32, "alpha_blocks"), N,
+        _dev(bias, torch.float32, "bias") if bias is not None else None, _dev(y, torch.float32, "y"),
+        _stream(stream)))
+    return y
 
 
 def bitlinear_hadamard_rows(x, block, signs=None, out=None, stream=None):

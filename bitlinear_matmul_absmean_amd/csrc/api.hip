@@ -190,6 +190,25 @@ int bitlinear_forward_fused_rows(const float* x, int64_t M, int64_t K, const uin
     return forward_fused(x, M, K, W_packed, alpha_rows, true, N, bias, y, x_q, beta, acc, stream);
 }
 
+int bitlinear_quantize_weights_blocks(const float* W, int64_t N, int64_t K, uint8_t* W_packed, float* alpha_blocks,
+                                      hipStream_t stream) {
+    if (!W || !W_packed || !alpha_blocks) return BITLINEAR_ERR_INVALID_ARG;
+    if (N <= 0 || K <= 0) return BITLINEAR_ERR_INVALID_ARG;
+    if (K % 128 != 0 || K > BITLINEAR_MAX_K || !mul_ok(N, K) || N * (K / 128) > (int64_t)INT_MAX * 4)
+        return BITLINEAR_ERR_SHAPE;
+    if (!aligned(W, 16) || !aligned(alpha_blocks, 4)) return BITLINEAR_ERR_ALIGNMENT;
+    return hip_status(launch_quantize_blocks(W, N, K, W_packed, alpha_blocks, stream));
+}
+
+int bitlinear_forward_blocks(const int8_t* x_q, const float* beta, int64_t M, int64_t K, const uint8_t* W_packed,
+                             const float* alpha_blocks, int64_t N, const float* bias, float* y, hipStream_t stream) {
+    int st = check_forward(x_q, beta, M, K, W_packed, alpha_blocks, N, y);
+    if (st) return st;
+    if (!blocks_supports(K) || (M + 3) / 4 > 65535) return BITLINEAR_ERR_SHAPE;
+    if (!aligned(x_q, 16) || !aligned(W_packed, 16) || !aligned(alpha_blocks, 4)) return BITLINEAR_ERR_ALIGNMENT;
+    return hip_status(launch_forward_blocks(x_q, beta, M, K, W_packed, alpha_blocks, N, bias, y, stream));
+}
+
 static int check_hadamard(const float* x, int64_t M, int64_t K, int64_t block, const int8_t* signs) {
     if (!x || M <= 0 || K <= 0 || block <= 0) return BITLINEAR_ERR_INVALID_ARG;
     if ((block & (block - 1)) != 0 || block > HADAMARD_MAX_BLOCK || K % block != 0 || K % 4 != 0)

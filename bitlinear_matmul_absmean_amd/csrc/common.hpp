@@ -87,6 +87,11 @@ hipError_t launch_alpha_rows(const float* W, int64_t N, int64_t K, float* alpha_
 hipError_t launch_ternary_pack(const float* W, int64_t N, int64_t K, const float* alpha, bool per_row,
                                uint8_t* packed, hipStream_t s);
 hipError_t launch_quantize_act(const float* x, int64_t M, int64_t K, int8_t* xq, float* beta, hipStream_t s);
+// Block scales: one alpha per 128 consecutive weights of a row, alpha [N, K / 128].
+hipError_t launch_quantize_blocks(const float* W, int64_t N, int64_t K, uint8_t* packed, float* alpha, hipStream_t s);
+bool blocks_supports(int64_t K);
+hipError_t launch_forward_blocks(const int8_t* xq, const float* beta, int64_t M, int64_t K, const uint8_t* wp,
+                                 const float* alpha, int64_t N, const float* bias, float* y, hipStream_t s);
 // Randomized Hadamard rotation along K (blocks of `block`, a power of two <= HADAMARD_MAX_BLOCK
 // dividing K; K % 4 == 0; x/out 16-byte aligned, signs and xq 4-byte aligned).
 constexpr int64_t HADAMARD_MAX_BLOCK = 4096;

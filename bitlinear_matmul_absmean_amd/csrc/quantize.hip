@@ -124,6 +124,33 @@ __global__ __launch_bounds__(256) void k_ternary_pack(const float* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------------------
+// Block scales [P1 §2.3, §4.2]: alpha[n, b] = mean |W| over the 128 weights of block b of row
+// n.  In row-major W the blocks are consecutive, so W is a flat array of N K / 128 blocks and
+// the codes of block i are packed bytes 32 i .. 32 i + 31.  A wave takes two blocks per step
+// (lanes 0-31 the first, 32-63 the second, one float4 per lane); the fp64 |w| sum runs over
+// the half-wave in a fixed butterfly, then each lane packs its four codes into one byte.  W
+// is read once.
+__global__ __launch_bounds__(256) void k_quantize_blocks(const float* __restrict__ W, int64_t nblocks,
+                                                         float* __restrict__ alpha, uint8_t* __restrict__ packed) {
+    const int lane = threadIdx.x & 63, half = lane >> 5, hl = lane & 31;
+    const int64_t waves = (int64_t)gridDim.x * 4;
+    for (int64_t p = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6; 2 * p < nblocks; p += waves) {
+        const int64_t blk = 2 * p + half;
+        const bool ok = blk < nblocks;
+        const float4 v = reinterpret_cast<const float4*>(W)[(ok ? blk : 2 * p) * 32 + hl];
+        double s = (double)fabsf(v.x) + (double)fabsf(v.y) + (double)fabsf(v.z) + (double)fabsf(v.w);
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) s += __shfl_xor(s, o, kWave);
+        const float a = (float)(s / 128.0);
+        if (ok) {
+            if (hl == 0) alpha[blk] = a;
+            packed[blk * 32 + hl] = (uint8_t)(ternary_code(v.x, a) | (ternary_code(v.y, a) << 2) |
+                                              (ternary_code(v.z, a) << 4) | (ternary_code(v.w, a) << 6));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
 // Per-token absmax int8 [P3 §2.4, §4.1].  One 256-thread workgroup per token.
 __device__ __forceinline__ float block_max_256(float v, float* red) {
     v = wave_max_f32(v);
@@ -519,6 +546,14 @@ hipError_t launch_ternary_pack(const float* W, int64_t N, int64_t K, const float
         hipLaunchKernelGGL(k_ternary_pack<true>, dim3((unsigned)blocks), dim3(256), 0, s, W, total, K, alpha, packed);
     else
         hipLaunchKernelGGL(k_ternary_pack<false>, dim3((unsigned)blocks), dim3(256), 0, s, W, total, K, alpha, packed);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_blocks(const float* W, int64_t N, int64_t K, uint8_t* packed, float* alpha, hipStream_t s) {
+    const int64_t nblocks = N * (K / 128);
+    int64_t wgs = ((nblocks + 1) / 2 + 3) / 4;
+    if (wgs > 8192) wgs = 8192;
+    hipLaunchKernelGGL(k_quantize_blocks, dim3((unsigned)wgs), dim3(256), 0, s, W, nblocks, alpha, packed);
     return hipGetLastError();
 }
 

@@ -2,6 +2,8 @@
  * bitlinear.h -- C ABI of the MI355X (gfx950) BitNet b1.58 BitLinear library (W1.58A8).
  *
  * Page keys used in the citations below:
+ *   [P1] 2kiu.com, article on 1.58-bit quantization and hardware co-optimization (block
+ *        scales, §2.3 and §4.2).
  *   [P2] nxmr.cn tutorial "1.58 位大模型" (per-row absmean, add/sub form of the matmul).
  *   [P3] chenxutan.com, "1.58-bit 大模型极限量化实战：从 BitNet 三值权重到单颗 CPU 跑起 100B 模型"
  *        (absmean / absmax formulas, BitLinear forward, 2-bit packing, §6.2 the rotation
@@ -173,6 +175,39 @@ int bitlinear_forward_fused(const float* x, int64_t M, int64_t K, const uint8_t*
 int bitlinear_forward_fused_rows(const float* x, int64_t M, int64_t K, const uint8_t* W_packed,
                                  const float* alpha_rows, int64_t N, const float* bias, float* y,
                                  int8_t* x_q, float* beta, int32_t* acc, hipStream_t stream);
+
+/*
+ * Block-scaled weights [P1 §2.3, §4.2]: one scale per block of 128 consecutive weights of a
+ * row, alpha_blocks of shape [N, K/128]:
+ *     alpha_blocks[n, b] = mean |W[n, 128b .. 128b+127]|   (fp64 sum, one fp32 rounding)
+ *     W_hat[n, k]        = clip(round(W[n, k] / alpha_blocks[n, k/128]), -1, 1)
+ * (fp32 division, round-half-to-even; an all-zero block has alpha 0 and codes 0), packed as
+ * above.  W is read once.
+ *   W [N, K] fp32, 16-byte aligned (in); W_packed [N, K/4] uint8 (out);
+ *   alpha_blocks [N, K/128] fp32, 4-byte aligned (out).
+ * Errors: INVALID_ARG, SHAPE (K % 128, sizes), ALIGNMENT, HIP.
+ */
+int bitlinear_quantize_weights_blocks(const float* W, int64_t N, int64_t K, uint8_t* W_packed,
+                                      float* alpha_blocks, hipStream_t stream);
+
+/*
+ * Forward with block-scaled weights [P1 §2.3; P2 §3.3; P3 §2.4]:
+ *     acc[m, n, b] = sum over k in block b of x_q[m, k] * W_hat[n, k]      (int32, exact)
+ *     y[m, n]      = fp32(S * (beta[m] / 127))  (+ bias[n], a separate fp32 addition)
+ *     S            = sum_b alpha_blocks[n, b] * acc[m, n, b]
+ * with S and beta/127 in fp64.  The products alpha*acc are exact in fp64; the additions run
+ * in an order fixed by the kernel, so y can differ from an fp64 sum taken in another order by
+ * one fp32 rounding in rare cases (results are reproducible run to run).
+ *   x_q [M, K] int8, beta [M] fp32 (from bitlinear_quantize_act); W_packed [N, K/4] uint8 and
+ *   alpha_blocks [N, K/128] fp32 (from bitlinear_quantize_weights_blocks); bias [N] or NULL;
+ *   y [M, N] fp32 (out).  x_q and W_packed 16-byte aligned, alpha_blocks 4-byte aligned.
+ * K % 128 == 0, K <= 32768 and M <= 262140 (groups of four tokens in the grid).  Any M runs;
+ * the kernel is a GEMV built for M <= 4, and larger M re-read the codes per four tokens.
+ * Errors: INVALID_ARG, SHAPE, ALIGNMENT, HIP.
+ */
+int bitlinear_forward_blocks(const int8_t* x_q, const float* beta, int64_t M, int64_t K,
+                             const uint8_t* W_packed, const float* alpha_blocks, int64_t N,
+                             const float* bias, float* y, hipStream_t stream);
 
 /*
  * Randomized Hadamard rotation along K [P3 §6.2], the preprocessing that spreads an outlier

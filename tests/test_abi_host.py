@@ -210,3 +210,17 @@ def test_hadamard_validation(bl):
     assert q(A, 1, 64, 64, None, A, None, None) == bl.BITLINEAR_ERR_INVALID_ARG
     assert q(A, 1, 64, 64, None, A + 2, A, None) == bl.BITLINEAR_ERR_ALIGNMENT  # x_q 4-byte
     assert q(A, 1, 64, 64, A + 1, A, A, None) == bl.BITLINEAR_ERR_ALIGNMENT
+
+
+def test_blocks_validation(bl):
+    q, f = bl.lib.bitlinear_quantize_weights_blocks, bl.lib.bitlinear_forward_blocks
+    assert q(None, 4, 128, A, A, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert q(A, 4, 192, A, A, None) == bl.BITLINEAR_ERR_SHAPE                 # K % 128
+    assert q(A + 4, 4, 128, A, A, None) == bl.BITLINEAR_ERR_ALIGNMENT
+    assert q(A, 4, 128, A, A + 2, None) == bl.BITLINEAR_ERR_ALIGNMENT
+    assert f(A, A, 1, 192, A, A, 8, None, A, None) == bl.BITLINEAR_ERR_SHAPE   # K % 128
+    assert f(A, A, 1, 65536, A, A, 8, None, A, None) == bl.BITLINEAR_ERR_SHAPE # K > 32768
+    assert f(A + 4, A, 1, 128, A, A, 8, None, A, None) == bl.BITLINEAR_ERR_ALIGNMENT
+    assert f(A, A, 1, 128, A + 8, A, 8, None, A, None) == bl.BITLINEAR_ERR_ALIGNMENT
+    assert f(A, A, 1, 128, A, None, 8, None, A, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert f(A, A, 0, 128, A, A, 8, None, A, None) == bl.BITLINEAR_ERR_INVALID_ARG

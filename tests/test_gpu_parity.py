@@ -506,3 +506,89 @@ def test_end_to_end_rotated_bitlinear(dev, m, k, n, block):
     assert np.array_equal(xq.cpu().numpy(), r["xq"])
     assert np.array_equal(acc.cpu().numpy(), r["acc"])
     assert _rel_ok(y.cpu().numpy(), r["y"])
+
+
+# ------------------------------------------------------------------ block scales [P1 §2.3, §4.2]
+def _block_w(seed, n, k, zero_block=False):
+    g = np.random.default_rng(seed)
+    w = g.standard_normal((n, k)).astype(np.float32) * np.float32(0.02)
+    gain = np.exp(g.uniform(np.log(0.05), np.log(5.0), size=(n, k // 128))).astype(np.float32)
+    w = (w * np.repeat(gain, 128, axis=1)).astype(np.float32)
+    if zero_block:
+        w[0, :128] = 0.0
+    return w
+
+
+@pytest.mark.parametrize("n,k", [(1024, 1024), (11008, 4096), (4096, 11008), (33, 128), (7, 384), (5, 256)])
+def test_quantize_weights_blocks_parity(dev, n, k):
+    torch, bl = dev
+    _say(f"quantize_weights_blocks N={n} K={k}")
+    w = _block_w(31, n, k, zero_block=True)
+    _, packed_o, a_o = oracle.quantize_weights_blocks(w)
+    packed, a = bl.bitlinear_quantize_weights_blocks(_to(torch, w))
+    torch.cuda.synchronize()
+    assert np.array_equal(a.cpu().numpy().view(np.uint32), a_o.view(np.uint32))
+    assert np.array_equal(packed.cpu().numpy(), packed_o)
+
+
+def _blocks_bound_ok(y, acc_b, alpha_b, beta, y_ref):
+    """|y - y_ref| <= one fp32 rounding of y_ref + 2^-40 sum_b |alpha acc| beta/127 (the fp64
+    additions in another order), and at least 99% of the outputs bit-identical."""
+    t = beta.astype(np.float64)[:, None] / 127.0
+    mag = np.einsum("mnb,nb->mn", np.abs(acc_b.astype(np.float64)), np.abs(alpha_b.astype(np.float64))) * t
+    ref = y_ref.astype(np.float64)
+    ulp = np.maximum(np.abs(ref) * 2.0 ** -23, 2.0 ** -149)
+    ok = np.abs(y.astype(np.float64) - ref) <= ulp + mag * 2.0 ** -40
+    same = np.mean(y.view(np.uint32) == y_ref.view(np.uint32))
+    return bool(ok.all()), same
+
+
+BLOCK_CASES = [(1, 4096, 4096), (1, 11008, 300), (2, 128, 77), (3, 4096, 1000), (4, 28672, 64), (1, 32768, 40),
+               (7, 1024, 333), (64, 2048, 130), (1, 256, 1), (9, 384, 65)]
+
+
+@pytest.mark.parametrize("m,k,n", BLOCK_CASES)
+def test_forward_blocks_parity(dev, m, k, n):
+    torch, bl = dev
+    _say(f"forward_blocks M={m} K={k} N={n}")
+    w = _block_w(32, n, k, zero_block=True)
+    x = workloads.activations_with_outliers(32, m, k)
+    codes, packed, a = oracle.quantize_weights_blocks(w)
+    xq, beta = oracle.quantize_act(x)
+    bias = workloads.activations(33, 1, n)[0] if m % 2 else None
+    acc_b, y_ref = oracle.forward_blocks(xq, beta, packed, k, a, bias=bias)
+    y = bl.bitlinear_forward_blocks(_to(torch, xq), _to(torch, beta), _to(torch, packed), _to(torch, a),
+                                    bias=None if bias is None else _to(torch, bias))
+    torch.cuda.synchronize()
+    yv = y.cpu().numpy()
+    if bias is None:
+        ok, same = _blocks_bound_ok(yv, acc_b, a, beta, y_ref)
+    else:
+        # one rounding of the pre-bias value (carried through the bias addition) plus the
+        # rounding of that addition itself
+        y_nb = oracle.dequant_blocks(acc_b, beta, a).astype(np.float64)
+        t = beta.astype(np.float64)[:, None] / 127.0
+        mag = np.einsum("mnb,nb->mn", np.abs(acc_b.astype(np.float64)), np.abs(a.astype(np.float64))) * t
+        ulp = lambda v: np.maximum(np.abs(v) * 2.0 ** -23, 2.0 ** -149)
+        ok = bool(np.all(np.abs(yv.astype(np.float64) - y_ref) <= ulp(y_nb) + ulp(y_ref) + mag * 2.0 ** -40))
+        same = np.mean(yv.view(np.uint32) == y_ref.view(np.uint32))
+    _say(f"  bit-identical fraction {same:.6f}")
+    assert ok
+    assert same >= 0.99
+
+
+def test_end_to_end_block_scaled_bitlinear(dev):
+    torch, bl = dev
+    _say("block-scaled bitlinear M=1 K=4096 N=4096")
+    w = _block_w(34, 4096, 4096)
+    x = workloads.activations(34, 1, 4096)
+    r = oracle.bitlinear_blocks(x, w)
+    packed, a = bl.bitlinear_quantize_weights_blocks(_to(torch, w))
+    xq, beta = bl.bitlinear_quantize_act(_to(torch, x))
+    y = bl.bitlinear_forward_blocks(xq, beta, packed, a)
+    torch.cuda.synchronize()
+    assert np.array_equal(packed.cpu().numpy(), r["packed"])
+    assert np.array_equal(a.cpu().numpy().view(np.uint32), r["alpha_blocks"].view(np.uint32))
+    assert np.array_equal(xq.cpu().numpy(), r["xq"])
+    ok, same = _blocks_bound_ok(y.cpu().numpy(), r["acc_blocks"], r["alpha_blocks"], r["beta"], r["y"])
+    assert ok and same >= 0.99
