@@ -11,8 +11,8 @@ this module only marshals NumPy arrays through ctypes.  Page keys used in citati
   §4.2: one scale per block of 128 weights, shape [C_out, C_in/128]).
 * [P2] nxmr.cn tutorial "1.58 位大模型" (per-row absmean, add/sub derivation, memory estimate).
 * [P3] chenxutan.com, "1.58-bit 大模型极限量化实战：从 BitNet 三值权重到单颗 CPU 跑起 100B 模型"
-  (absmean / absmax formulas, worked example, BitLinear forward, 2-bit packing, §6.2 the
-  rotation before absmax).
+  (absmean / absmax formulas, worked example, BitLinear forward, 2-bit packing, §6.1 the
+  BitMLP, §6.2 the rotation before absmax).
 """
 from __future__ import annotations
 
@@ -64,6 +64,7 @@ def _load():
         "oracle_ternarize_blocks": (ctypes.c_int, [p, i64, i64, p, p]),
         "oracle_ternary_matmul_blocks": (ctypes.c_int, [p, i64, i64, p, i64, p]),
         "oracle_dequant_blocks": (ctypes.c_int, [p, p, p, i64, i64, i64, p, p]),
+        "oracle_gelu": (ctypes.c_int, [p, i64, p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -322,3 +323,22 @@ def bitlinear_blocks(x: np.ndarray, w: np.ndarray, bias: np.ndarray | None = Non
     acc = ternary_matmul_blocks(xq, codes)
     y = dequant_blocks(acc, beta, a, bias)
     return dict(codes=codes, packed=packed, alpha_blocks=a, xq=xq, beta=beta, acc_blocks=acc, y=y)
+
+
+# ------------------------------------------------------------------ BitMLP (R13)
+def gelu(h: np.ndarray) -> np.ndarray:
+    """[P3 §6.1] torch.nn.GELU (erf form) in fp64, one fp32 rounding (reading R13)."""
+    h = np.ascontiguousarray(h, dtype=np.float32)
+    out = np.empty(h.shape, np.float32)
+    _check(_load().oracle_gelu(_ptr(h), h.size, _ptr(out)), "gelu")
+    return out
+
+
+def bitmlp(x: np.ndarray, w1: np.ndarray, w2: np.ndarray, b1: np.ndarray | None = None,
+           b2: np.ndarray | None = None):
+    """[P3 §6.1] BitMLP forward fc2(GELU(fc1(x))), both layers BitLinear (per-tensor alpha).
+    Returns a dict with fc1's and fc2's intermediates (``fc1``, ``fc2``), ``g`` and ``y``."""
+    r1 = bitlinear(x, w1, bias=b1)
+    g = gelu(r1["y"])
+    r2 = bitlinear(g, w2, bias=b2)
+    return dict(fc1=r1, g=g, fc2=r2, y=r2["y"])

@@ -38,6 +38,10 @@
  *       block's alpha; the integer sums are kept per block, acc[m, n, b], and
  *       y[m, n] = fp32(S * (beta[m] / 127)) with S = sum_b alpha[n, b] * acc[m, n, b]
  *       accumulated in fp64 in ascending b and beta/127 an fp64 division; + bias in fp32.
+ *   R13 the BitMLP of [P3 §6.1] is fc2(GELU(fc1(x))) with two BitLinears; GELU is the
+ *       erf form of torch.nn.GELU, 0.5 h (1 + erf(h / sqrt 2)), evaluated in fp64 as
+ *       (0.5 h) (1 + erf(h * RN64(1/sqrt 2))) and rounded to fp32 once; fc2 quantizes the
+ *       fp32 GELU output like any activation.
  *   R10 the rotation before absmax [P3 §6.2] is a randomized Walsh-Hadamard transform
  *       applied to each row along K in blocks of B (a power of two dividing K): a sign
  *       flip by d[k] in {+1, -1} (the random part; an input, negative int8 = flip), then
@@ -308,6 +312,17 @@ int oracle_dequant_blocks(const int32_t* acc, const float* beta, const float* al
             const float yv = (float)(s * t);
             y[m * n_rows + n] = bias ? yv + bias[n] : yv;
         }
+    }
+    return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------- BitMLP (R13) */
+/* [P3 §6.1] the GELU between the two BitLinears of the BitMLP, elementwise. */
+int oracle_gelu(const float* h, int64_t count, float* g) {
+    if (!h || !g || count <= 0) return ORACLE_EINVAL;
+    for (int64_t i = 0; i < count; ++i) {
+        const double v = (double)h[i];
+        g[i] = (float)(0.5 * v * (1.0 + erf(v * 0.70710678118654752440)));
     }
     return ORACLE_OK;
 }

@@ -54,6 +54,9 @@ MUTANTS = [
     ("block dequant in fp32", "const double t = (double)beta[m] / 127.0;", "const double t = (double)(beta[m] / 127.0f);"),
     ("block dequant drops alpha", "s += (double)alpha[n * kb + b] * (double)acc[(m * n_rows + n) * kb + b];",
      "s += (double)acc[(m * n_rows + n) * kb + b];"),
+    ("gelu with sqrt 2 for 1/sqrt 2", "erf(v * 0.70710678118654752440)", "erf(v * 1.41421356237309504880)"),
+    ("gelu without the half", "g[i] = (float)(0.5 * v * (1.0 + erf(", "g[i] = (float)(v * (1.0 + erf("),
+    ("gelu with 1 - erf", "(1.0 + erf(v", "(1.0 - erf(v"),
 ]
 
 

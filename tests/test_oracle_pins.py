@@ -569,3 +569,49 @@ def test_block_scales_track_blockwise_magnitudes_better_than_one_scale():
 def test_block_functions_reject_k_not_a_multiple_of_128():
     with pytest.raises(ValueError):
         oracle.absmean_blocks(np.zeros((2, 192), np.float32))
+
+
+# ---------------------------------------------------------------- BitMLP (R13)
+# Textbook values of the standard normal CDF: GELU(x) = x * Phi(x).
+PHI = {0.5: "0.691462461274013103637704610608", 1.0: "0.841344746068542948585232545632",
+       2.0: "0.977249868051820792799717362", 3.0: "0.998650101968369896532351092",
+       -1.0: "0.158655253931457051414767454368", -2.0: "0.022750131948179207200282637"}
+
+
+def test_gelu_matches_normal_cdf_table():
+    from decimal import Decimal
+    xs = np.array(sorted(PHI), np.float32)
+    g = oracle.gelu(xs)
+    for x, v in zip(xs, g):
+        want = exact.rne32(Fraction(Decimal(PHI[float(x)])) * exact.fr(x))
+        assert exact.fr(v) == want
+
+
+def test_gelu_odd_part_identity_and_limits():
+    """Phi(x) + Phi(-x) = 1, so GELU(x) - GELU(-x) = x; GELU(0) = 0; GELU(10) = 10."""
+    x = np.linspace(-6, 6, 2001).astype(np.float32)
+    gp, gm = oracle.gelu(x).astype(np.float64), oracle.gelu(-x).astype(np.float64)
+    ulp = np.maximum(np.abs(gp), np.abs(gm)) * 2.0 ** -23
+    assert np.all(np.abs(gp - gm - x) <= 2 * ulp + 2.0 ** -149)
+    assert oracle.gelu(np.array([0.0, 10.0], np.float32)).tolist() == [0.0, 10.0]
+    # the minimum of GELU is about -0.16997 near x = -0.7518
+    xs = np.linspace(-1.5, 0.0, 30001).astype(np.float32)
+    gs = oracle.gelu(xs)
+    assert abs(float(xs[np.argmin(gs)]) + 0.7518) < 2e-3 and abs(float(gs.min()) + 0.16997) < 1e-4
+
+
+def test_bitmlp_tracks_the_float_mlp():
+    """[P3 §6.1]: the BitMLP follows the float MLP it replaces (cosine > 0.75 for Gaussian
+    weights of std 0.02 and N(0, 1) inputs)."""
+    d, f = 512, 2048
+    w1 = workloads.weights(40, f, d)
+    w2 = workloads.weights(41, d, f)
+    x = workloads.activations(40, 8, d)
+    r = oracle.bitmlp(x, w1, w2)
+    h = x.astype(np.float64) @ w1.astype(np.float64).T
+    from math import erf, sqrt
+    ref = (0.5 * h * (1.0 + np.vectorize(erf)(h / sqrt(2.0)))) @ w2.astype(np.float64).T
+    cos = (r["y"].astype(np.float64) * ref).sum() / (np.linalg.norm(r["y"]) * np.linalg.norm(ref))
+    assert cos > 0.75
+    assert np.array_equal(r["g"], oracle.gelu(r["fc1"]["y"]))
+    assert np.array_equal(r["fc2"]["xq"], oracle.quantize_act(r["g"])[0])
