@@ -373,6 +373,49 @@ def blocks_bench(torch, bl, workloads, dev, ms_plain_step):
     return out
 
 
+def mlp_bench(torch, bl, workloads, dev, d=4096, f=11008):
+    """BitMLP [P3 §6.1], y = fc2(GELU(fc1(x))) at 7B-class sizes (d_model 4096, d_ff 11008),
+    one bitlinear_mlp_forward call: decode (M = 1, weights rotated through a pool, packed
+    bytes 2 d f / 4 per step) and prefill (M = 2048, int8 ops 2 * 2 M d f)."""
+    per_step = 2 * d * f // 4
+    copies = max(2, POOL_BYTES // per_step)
+    w1 = torch.from_numpy(workloads.weights(6, f, d)).to(dev)
+    w2 = torch.from_numpy(workloads.weights(6, d, f, index=1)).to(dev)
+    p1, a1 = bl.bitlinear_quantize_weights(w1)
+    p2, a2 = bl.bitlinear_quantize_weights(w2)
+    del w1, w2
+    pool = [(p1, p2)] + [(p1.clone(), p2.clone()) for _ in range(copies - 1)]
+    x = torch.from_numpy(workloads.activations(6, 1, d)).to(dev)
+    y = torch.empty((1, d), dtype=torch.float32, device=dev)
+    g = torch.empty((1, f), dtype=torch.float32, device=dev)
+
+    def step(i):
+        q1, q2 = pool[i % copies]
+        bl.bitlinear_mlp_forward(x, q1, a1, q2, a2, y=y, g=g)
+
+    ms, _ = _graph_time(torch, step, 400)
+    out = {"shape": {"d_model": d, "d_ff": f},
+           "decode": {"M": 1, "us": round(ms * 1e3, 2), "weight_bytes": per_step,
+                      "weight_gbs": round(per_step / (ms * 1e-3) / 1e9, 1),
+                      "pct_hbm": round(100 * per_step / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}}
+    del pool
+    m = 2048
+    xp = torch.from_numpy(workloads.activations(6, m, d)).to(dev)
+    yp = torch.empty((m, d), dtype=torch.float32, device=dev)
+    gp = torch.empty((m, f), dtype=torch.float32, device=dev)
+    xq1 = torch.empty((m, d), dtype=torch.int8, device=dev)
+    xq2 = torch.empty((m, f), dtype=torch.int8, device=dev)
+    b1 = torch.empty(m, dtype=torch.float32, device=dev)
+    b2 = torch.empty(m, dtype=torch.float32, device=dev)
+    ms, _ = _graph_time(torch, lambda i: bl.bitlinear_mlp_forward(xp, p1, a1, p2, a2, y=yp, g=gp, x_q1=xq1, beta1=b1,
+                                                                   x_q2=xq2, beta2=b2), 10)
+    ops = 2.0 * 2 * m * d * f
+    out["prefill"] = {"M": m, "us": round(ms * 1e3, 2), "tops": round(ops / (ms * 1e-3) / 1e12, 1),
+                      "pct_mfma_peak": round(100 * ops / (ms * 1e-3) / 1e12 / INT8_MFMA_PEAK_TOPS, 2)}
+    torch.cuda.empty_cache()
+    return out
+
+
 def batched_bench(torch, bl, workloads, dev, reps=96):
     out = []
     for (k, n) in [(4096, 11008), (11008, 4096)]:
@@ -670,6 +713,8 @@ def main():
         log(f"hadamard {extras['hadamard']}")
         extras["blocks"] = blocks_bench(torch, bl, workloads, dev, ms_step)
         log(f"blocks {extras['blocks']}")
+        extras["mlp"] = mlp_bench(torch, bl, workloads, dev)
+        log(f"mlp {extras['mlp']}")
     if not args.no_extras and not args.no_chain:
         extras["chain70b"] = chain70b_bench(torch, bl, workloads, dev)
         log(f"chain70b {extras['chain70b']}")

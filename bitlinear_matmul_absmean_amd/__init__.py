@@ -42,6 +42,7 @@ SIGNATURES = {
     "bitlinear_forward_fused_kernel": (ctypes.c_char_p, [_I64, _I64, _I64, _P, _P, _P]),
     "bitlinear_quantize_weights_blocks": (_INT, [_P, _I64, _I64, _P, _P, _P]),
     "bitlinear_forward_blocks": (_INT, [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _P]),
+    "bitlinear_mlp_forward": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "bitlinear_hadamard_rows": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "bitlinear_quantize_act_hadamard": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
 }
@@ -179,6 +180,39 @@ def bitlinear_forward_blocks(x_q, beta, W_packed, alpha_blocks, bias=None, y=Non
         _dev(bias, torch.float32, "bias") if bias is not None else None, _dev(y, torch.float32, "y"),
         _stream(stream)))
     return y
+
+
+def bitlinear_mlp_forward(x, W1_packed, alpha1, W2_packed, alpha2, bias1=None, bias2=None, y=None, g=None,
+                          x_q1=None, beta1=None, x_q2=None, beta2=None, stream=None):
+    """BitMLP y = fc2(GELU(fc1(x))); returns (y, g).  x_q1/beta1/x_q2/beta2 are allocated
+    when M > 4 (the two-call path needs them) and not given."""
+    torch = _torch()
+    M, d_model = x.shape
+    d_ff = W1_packed.shape[0]
+    if W1_packed.shape[1] * 4 != d_model or W2_packed.shape != (d_model, d_ff // 4):
+        raise ValueError("W1_packed must be [d_ff, d_model/4] and W2_packed [d_model, d_ff/4]")
+    if y is None:
+        y = torch.empty((M, d_model), dtype=torch.float32, device=x.device)
+    if g is None:
+        g = torch.empty((M, d_ff), dtype=torch.float32, device=x.device)
+    if M > 4:
+        if x_q1 is None:
+            x_q1 = torch.empty((M, d_model), dtype=torch.int8, device=x.device)
+        if beta1 is None:
+            beta1 = torch.empty(M, dtype=torch.float32, device=x.device)
+        if x_q2 is None:
+            x_q2 = torch.empty((M, d_ff), dtype=torch.int8, device=x.device)
+        if beta2 is None:
+            beta2 = torch.empty(M, dtype=torch.float32, device=x.device)
+    opt = lambda t, dt, n: _dev(t, dt, n) if t is not None else None
+    _check("bitlinear_mlp_forward", lib.bitlinear_mlp_forward(
+        _dev(x, torch.float32, "x"), M, d_model, d_ff, _dev(W1_packed, torch.uint8, "W1_packed"),
+        _dev(alpha1, torch.float32, "alpha1"), opt(bias1, torch.float32, "bias1"),
+        _dev(W2_packed, torch.uint8, "W2_packed"), _dev(alpha2, torch.float32, "alpha2"),
+        opt(bias2, torch.float32, "bias2"), _dev(y, torch.float32, "y"), _dev(g, torch.float32, "g"),
+        opt(x_q1, torch.int8, "x_q1"), opt(beta1, torch.float32, "beta1"), opt(x_q2, torch.int8, "x_q2"),
+        opt(beta2, torch.float32, "beta2"), _stream(stream)))
+    return y, g
 
 
 def bitlinear_hadamard_rows(x, block, signs=None, out=None, stream=None):

@@ -159,35 +159,57 @@ int bitlinear_forward_rows(const int8_t* x_q, const float* beta, int64_t M, int6
     return run_forward(a, stream);
 }
 
-static int forward_fused(const float* x, int64_t M, int64_t K, const uint8_t* W_packed, const float* alpha,
-                         bool per_row, int64_t N, const float* bias, float* y, int8_t* x_q, float* beta, int32_t* acc,
-                         hipStream_t stream) {
+// Validation of a fused call, without launching anything.
+static int check_fused(const float* x, int64_t M, int64_t K, const uint8_t* W_packed, const float* alpha, int64_t N,
+                       float* y, int8_t* x_q, float* beta) {
     if (!x) return BITLINEAR_ERR_INVALID_ARG;
     int st = check_forward(reinterpret_cast<const int8_t*>(x), reinterpret_cast<const float*>(x), M, K, W_packed,
                            alpha, N, y);
     if (st) return st;
-    if (fused_fast_ok(M, K, x, W_packed, x_q)) {
-        ForwardArgs a{nullptr, nullptr, M, K, N, W_packed, alpha, per_row, bias, y, acc};
-        return hip_status(launch_gemv_fused(a, x, x_q, beta, stream));
-    }
+    if (fused_fast_ok(M, K, x, W_packed, x_q)) return BITLINEAR_OK;
     // other shapes: the two-call path, which needs x_q and beta as its intermediate
     if (!x_q || !beta) return BITLINEAR_ERR_INVALID_ARG;
+    return BITLINEAR_OK;
+}
+
+static int forward_fused(const float* x, int64_t M, int64_t K, const uint8_t* W_packed, const float* alpha,
+                         bool per_row, int64_t N, const float* bias, float* y, int8_t* x_q, float* beta, int32_t* acc,
+                         int act, hipStream_t stream) {
+    int st = check_fused(x, M, K, W_packed, alpha, N, y, x_q, beta);
+    if (st) return st;
+    ForwardArgs a{nullptr, nullptr, M, K, N, W_packed, alpha, per_row, bias, y, acc, act};
+    if (fused_fast_ok(M, K, x, W_packed, x_q)) return hip_status(launch_gemv_fused(a, x, x_q, beta, stream));
     st = bitlinear_quantize_act(x, M, K, x_q, beta, stream);
     if (st) return st;
-    return per_row ? bitlinear_forward_rows(x_q, beta, M, K, W_packed, alpha, N, bias, y, acc, stream)
-                   : bitlinear_forward(x_q, beta, M, K, W_packed, alpha, N, bias, y, acc, stream);
+    a.xq = x_q;
+    a.beta = beta;
+    return run_forward(a, stream);
 }
 
 int bitlinear_forward_fused(const float* x, int64_t M, int64_t K, const uint8_t* W_packed, const float* alpha,
                             int64_t N, const float* bias, float* y, int8_t* x_q, float* beta, int32_t* acc,
                             hipStream_t stream) {
-    return forward_fused(x, M, K, W_packed, alpha, false, N, bias, y, x_q, beta, acc, stream);
+    return forward_fused(x, M, K, W_packed, alpha, false, N, bias, y, x_q, beta, acc, 0, stream);
 }
 
 int bitlinear_forward_fused_rows(const float* x, int64_t M, int64_t K, const uint8_t* W_packed,
                                  const float* alpha_rows, int64_t N, const float* bias, float* y, int8_t* x_q,
                                  float* beta, int32_t* acc, hipStream_t stream) {
-    return forward_fused(x, M, K, W_packed, alpha_rows, true, N, bias, y, x_q, beta, acc, stream);
+    return forward_fused(x, M, K, W_packed, alpha_rows, true, N, bias, y, x_q, beta, acc, 0, stream);
+}
+
+int bitlinear_mlp_forward(const float* x, int64_t M, int64_t d_model, int64_t d_ff, const uint8_t* W1_packed,
+                          const float* alpha1, const float* bias1, const uint8_t* W2_packed, const float* alpha2,
+                          const float* bias2, float* y, float* g, int8_t* x_q1, float* beta1, int8_t* x_q2,
+                          float* beta2, hipStream_t stream) {
+    // both layers are validated before either is enqueued
+    int st = check_fused(x, M, d_model, W1_packed, alpha1, d_ff, g, x_q1, beta1);
+    if (st) return st;
+    st = check_fused(g, M, d_ff, W2_packed, alpha2, d_model, y, x_q2, beta2);
+    if (st) return st;
+    st = forward_fused(x, M, d_model, W1_packed, alpha1, false, d_ff, bias1, g, x_q1, beta1, nullptr, 1, stream);
+    if (st) return st;
+    return forward_fused(g, M, d_ff, W2_packed, alpha2, false, d_model, bias2, y, x_q2, beta2, nullptr, 0, stream);
 }
 
 int bitlinear_quantize_weights_blocks(const float* W, int64_t N, int64_t K, uint8_t* W_packed, float* alpha_blocks,

@@ -110,7 +110,17 @@ struct ForwardArgs {
     const float* bias;
     float* y;
     int32_t* acc;
+    int act = 0;          // activation applied to y after the dequantization: 0 none, 1 GELU
 };
+
+// GELU (the erf form of torch.nn.GELU) between the two BitLinears of the BitMLP [P3 §6.1]:
+// 0.5 h (1 + erf(h / sqrt 2)) in fp64, rounded to fp32 once.
+__device__ __attribute__((noinline)) float gelu_f32(float h) {
+    const double v = (double)h;
+    return (float)(0.5 * v * (1.0 + erf(v * 0.70710678118654752440)));
+}
+
+__device__ __forceinline__ float activate(float v, int act) { return act == 1 ? gelu_f32(v) : v; }
 
 bool gemv_supports(int64_t M, int64_t K);
 struct GemvShape {

@@ -199,7 +199,7 @@ __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec(ForwardArgs a) {
 #pragma unroll
             for (int w = 0; w < BD_WAVES; ++w) xs_ += tsum_w[w][m];
             const int total = sum[i] - xs_;
-            a.y[(int64_t)m * N + n] = dequant(total, dequant_scale(al, a.beta[m]), a.bias, n);
+            a.y[(int64_t)m * N + n] = activate(dequant(total, dequant_scale(al, a.beta[m]), a.bias, n), a.act);
             if (a.acc) a.acc[(int64_t)m * N + n] = total;
         }
     }
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec16(ForwardArgs a) {
 #pragma unroll
             for (int w = 0; w < BD_WAVES; ++w) xs += tsum_w[w][m];
             const int total = sum[i] - xs;
-            a.y[(int64_t)m * N + n] = dequant(total, dequant_scale(al, a.beta[m]), a.bias, n);
+            a.y[(int64_t)m * N + n] = activate(dequant(total, dequant_scale(al, a.beta[m]), a.bias, n), a.act);
             if (a.acc) a.acc[(int64_t)m * N + n] = total;
         }
     }

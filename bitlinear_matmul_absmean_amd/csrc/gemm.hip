@@ -237,7 +237,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(ForwardArgs a, int tiles_m
                 if (n < N) {
                     const int total = acc[i][j][r] - xs;
                     const float s = a.alpha_per_row ? dequant_scale(a.alpha[n], a.beta[m]) : s0;
-                    a.y[m * N + n] = dequant(total, s, a.bias, n);
+                    a.y[m * N + n] = activate(dequant(total, s, a.bias, n), a.act);
                     if (a.acc) a.acc[m * N + n] = total;
                 }
             }
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(256) void k_forward_generic(ForwardArgs a) {
         s = wave_sum_i32(s);
         if (lane == 0) {
             const float al = a.alpha_per_row ? a.alpha[n] : a.alpha[0];
-            a.y[m * a.N + n] = dequant(s, dequant_scale(al, a.beta[m]), a.bias, n);
+            a.y[m * a.N + n] = activate(dequant(s, dequant_scale(al, a.beta[m]), a.bias, n), a.act);
             if (a.acc) a.acc[m * a.N + n] = s;
         }
     }

@@ -332,7 +332,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(GemvArgs g) {
             if (n < re && my_t < M) {
                 const int total = mine - my_xsum;
                 const float s = a.alpha_per_row ? dequant_scale(a.alpha[n], my_beta) : my_sc;
-                a.y[my_t * N + n] = dequant(total, s, a.bias, n);
+                a.y[my_t * N + n] = activate(dequant(total, s, a.bias, n), a.act);
                 if (a.acc) a.acc[my_t * N + n] = total;
             }
         }

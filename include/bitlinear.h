@@ -6,8 +6,8 @@
  *        scales, §2.3 and §4.2).
  *   [P2] nxmr.cn tutorial "1.58 位大模型" (per-row absmean, add/sub form of the matmul).
  *   [P3] chenxutan.com, "1.58-bit 大模型极限量化实战：从 BitNet 三值权重到单颗 CPU 跑起 100B 模型"
- *        (absmean / absmax formulas, BitLinear forward, 2-bit packing, §6.2 the rotation
- *        before absmax).
+ *        (absmean / absmax formulas, BitLinear forward, 2-bit packing, §6.1 the BitMLP,
+ *        §6.2 the rotation before absmax).
  *
  * The layer is split the way [P3 §3.2] describes BitLinear: weights are quantized once and
  * cached (bitlinear_quantize_weights); every call quantizes the activations
@@ -245,6 +245,30 @@ int bitlinear_hadamard_rows(const float* x, int64_t M, int64_t K, int64_t block,
  */
 int bitlinear_quantize_act_hadamard(const float* x, int64_t M, int64_t K, int64_t block,
                                     const int8_t* signs, int8_t* x_q, float* beta, hipStream_t stream);
+
+/*
+ * BitMLP forward [P3 §6.1]: y = fc2(GELU(fc1(x))) with both layers BitLinear (per-tensor
+ * alpha, weights from bitlinear_quantize_weights), fc1: d_model -> d_ff, fc2: d_ff -> d_model.
+ * GELU is the erf form, 0.5 h (1 + erf(h / sqrt 2)), evaluated in fp64 and rounded to fp32
+ * once, applied in fc1's dequantization epilogue; fc2 quantizes its fp32 input per token
+ * like any activation.  Each layer runs as bitlinear_forward_fused would (one fused launch
+ * for M <= 4, else quantize_act then forward), so results equal the two calls
+ *     g = GELU(bitlinear_forward_fused(x, W1...)),  y = bitlinear_forward_fused(g, W2...).
+ *
+ *   x        [M, d_model] fp32.                                   (in)
+ *   W1_packed [d_ff, d_model/4], alpha1 [1], bias1 [d_ff] or NULL. (in)
+ *   W2_packed [d_model, d_ff/4], alpha2 [1], bias2 [d_model] or NULL. (in)
+ *   y        [M, d_model] fp32.                                   (out)
+ *   g        [M, d_ff] fp32: GELU(fc1(x)), fc2's input.            (out, required)
+ *   x_q1, beta1 / x_q2, beta2: each layer's quantized input ([M, d] int8, [M] fp32), as
+ *   the x_q / beta of bitlinear_forward_fused (required when M > 4 or unaligned).
+ * Both layers are validated before anything is enqueued.  Errors as bitlinear_forward_fused.
+ */
+int bitlinear_mlp_forward(const float* x, int64_t M, int64_t d_model, int64_t d_ff,
+                          const uint8_t* W1_packed, const float* alpha1, const float* bias1,
+                          const uint8_t* W2_packed, const float* alpha2, const float* bias2,
+                          float* y, float* g, int8_t* x_q1, float* beta1, int8_t* x_q2,
+                          float* beta2, hipStream_t stream);
 
 /* Kernel(s) bitlinear_forward_fused launches for these arguments ("gemv_fused" or
  * "quantize_act+forward"); a static string. */

@@ -224,3 +224,15 @@ def test_blocks_validation(bl):
     assert f(A, A, 1, 128, A + 8, A, 8, None, A, None) == bl.BITLINEAR_ERR_ALIGNMENT
     assert f(A, A, 1, 128, A, None, 8, None, A, None) == bl.BITLINEAR_ERR_INVALID_ARG
     assert f(A, A, 0, 128, A, A, 8, None, A, None) == bl.BITLINEAR_ERR_INVALID_ARG
+
+
+def test_mlp_validation_checks_both_layers_first(bl):
+    """A bad second layer is reported before the first is enqueued (nothing runs)."""
+    f = bl.lib.bitlinear_mlp_forward
+    ok = (A, 1, 64, 128, A, A, None, A, A, None, A, A, None, None, None, None, None)
+    assert f(*ok[:11], None, *ok[12:]) == bl.BITLINEAR_ERR_INVALID_ARG        # g missing
+    assert f(A, 1, 64, 130, A, A, None, A, A, None, A, A, None, None, None, None, None) == bl.BITLINEAR_ERR_SHAPE
+    assert f(A, 1, 66, 128, A, A, None, A, A, None, A, A, None, None, None, None, None) == bl.BITLINEAR_ERR_SHAPE
+    # M > 4 needs each layer's x_q / beta: missing for the second layer only
+    assert f(A, 8, 64, 128, A, A, None, A, A, None, A, A, A, A, None, None, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert f(A, 8, 64, 128, A, None, None, A, A, None, A, A, A, A, A, A, None) == bl.BITLINEAR_ERR_INVALID_ARG

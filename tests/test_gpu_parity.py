@@ -592,3 +592,35 @@ def test_end_to_end_block_scaled_bitlinear(dev):
     assert np.array_equal(xq.cpu().numpy(), r["xq"])
     ok, same = _blocks_bound_ok(y.cpu().numpy(), r["acc_blocks"], r["alpha_blocks"], r["beta"], r["y"])
     assert ok and same >= 0.99
+
+
+# ------------------------------------------------------------------ BitMLP [P3 §6.1]
+# (M, d_model, d_ff, bias): fc1's GELU epilogue on every kernel path -- fused GEMV (M <= 4),
+# 16x16x64 and 32x32x32 batched decode, the MFMA GEMM, the generic kernel (d % 64 != 0).
+MLP_CASES = [(1, 1024, 4096, False), (1, 4096, 11008, True), (3, 512, 2048, True), (8, 512, 1024, False),
+             (48, 256, 1024, True), (200, 256, 512, False), (5, 100, 36, True)]
+
+
+@pytest.mark.parametrize("m,d,f,with_bias", MLP_CASES)
+def test_mlp_forward_parity(dev, m, d, f, with_bias):
+    torch, bl = dev
+    _say(f"mlp_forward M={m} d_model={d} d_ff={f} bias={with_bias}")
+    w1 = workloads.weights(50, f, d)
+    w2 = workloads.weights(51, d, f)
+    x = workloads.activations_with_outliers(50, m, d)
+    b1 = workloads.activations(52, 1, f)[0] * np.float32(0.1) if with_bias else None
+    b2 = workloads.activations(53, 1, d)[0] * np.float32(0.1) if with_bias else None
+    r = oracle.bitmlp(x, w1, w2, b1, b2)
+    p1, a1 = bl.bitlinear_quantize_weights(_to(torch, w1))
+    p2, a2 = bl.bitlinear_quantize_weights(_to(torch, w2))
+    xq2 = torch.empty((m, f), dtype=torch.int8, device="cuda")
+    beta2 = torch.empty(m, dtype=torch.float32, device="cuda")
+    y, g = bl.bitlinear_mlp_forward(_to(torch, x), p1, a1, p2, a2,
+                                    bias1=None if b1 is None else _to(torch, b1),
+                                    bias2=None if b2 is None else _to(torch, b2), x_q2=xq2, beta2=beta2)
+    torch.cuda.synchronize()
+    assert np.array_equal(g.cpu().numpy().view(np.uint32), r["g"].view(np.uint32))
+    assert np.array_equal(xq2.cpu().numpy(), r["fc2"]["xq"])
+    assert np.array_equal(beta2.cpu().numpy().view(np.uint32), r["fc2"]["beta"].view(np.uint32))
+    assert _rel_ok(y.cpu().numpy(), r["y"])
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), r["y"].view(np.uint32))
