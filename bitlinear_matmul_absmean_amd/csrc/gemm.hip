@@ -56,6 +56,9 @@ __device__ __forceinline__ i32x4 unpack16(uint32_t v) {
 
 constexpr int GEMM_BM = 128, GEMM_BN = 256, GEMM_BK = 64;
 
+// GELU: the BitMLP activation in the epilogue, fixed at compile time so that the plain
+// kernel carries no call.
+template <bool GELU>
 __global__ __launch_bounds__(256, 2) void k_gemm_mfma(ForwardArgs a, int tiles_m, int tiles_n) {
     constexpr int BM = GEMM_BM, BN = GEMM_BN, BK = GEMM_BK;
     constexpr int WN = BN / 4;                 // wave tile 128 x 64
@@ -237,7 +240,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(ForwardArgs a, int tiles_m
                 if (n < N) {
                     const int total = acc[i][j][r] - xs;
                     const float s = a.alpha_per_row ? dequant_scale(a.alpha[n], a.beta[m]) : s0;
-                    a.y[m * N + n] = activate(dequant(total, s, a.bias, n), a.act);
+                    const float v = dequant(total, s, a.bias, n);
+                    a.y[m * N + n] = GELU ? gelu_f32(v) : v;
                     if (a.acc) a.acc[m * N + n] = total;
                 }
             }
@@ -248,7 +252,10 @@ bool gemm_supports_k(int64_t K) { return K % GEMM_BK == 0; }
 
 hipError_t launch_gemm_mfma(const ForwardArgs& a, hipStream_t s) {
     const int tm = (int)((a.M + GEMM_BM - 1) / GEMM_BM), tn = (int)((a.N + GEMM_BN - 1) / GEMM_BN);
-    hipLaunchKernelGGL(k_gemm_mfma, dim3((unsigned)(tm * tn)), dim3(256), 0, s, a, tm, tn);
+    if (a.act == 1)
+        hipLaunchKernelGGL(k_gemm_mfma<true>, dim3((unsigned)(tm * tn)), dim3(256), 0, s, a, tm, tn);
+    else
+        hipLaunchKernelGGL(k_gemm_mfma<false>, dim3((unsigned)(tm * tn)), dim3(256), 0, s, a, tm, tn);
     return hipGetLastError();
 }
 
