@@ -9,7 +9,8 @@ this module only marshals NumPy arrays through ctypes.  Page keys used in citati
 
 * [P1] 2kiu.com, article on 1.58-bit quantization and hardware co-optimization (§2.3 and
   §4.2: one scale per block of 128 weights, shape [C_out, C_in/128]).
-* [P2] nxmr.cn tutorial "1.58 位大模型" (per-row absmean, add/sub derivation, memory estimate).
+* [P2] nxmr.cn tutorial "1.58 位大模型" (per-row absmean, add/sub derivation, memory estimate,
+  §1.1 and §6.1: more compact encodings than 2 bits).
 * [P3] chenxutan.com, "1.58-bit 大模型极限量化实战：从 BitNet 三值权重到单颗 CPU 跑起 100B 模型"
   (absmean / absmax formulas, worked example, BitLinear forward, 2-bit packing, §6.1 the
   BitMLP, §6.2 the rotation before absmax).
@@ -65,6 +66,9 @@ def _load():
         "oracle_ternary_matmul_blocks": (ctypes.c_int, [p, i64, i64, p, i64, p]),
         "oracle_dequant_blocks": (ctypes.c_int, [p, p, p, i64, i64, i64, p, p]),
         "oracle_gelu": (ctypes.c_int, [p, i64, p]),
+        "oracle_t5_row_bytes": (i64, [i64]),
+        "oracle_pack_t5": (ctypes.c_int, [p, i64, i64, p]),
+        "oracle_unpack_t5": (ctypes.c_int, [p, i64, i64, p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -342,3 +346,36 @@ def bitmlp(x: np.ndarray, w1: np.ndarray, w2: np.ndarray, b1: np.ndarray | None 
     g = gelu(r1["y"])
     r2 = bitlinear(g, w2, bias=b2)
     return dict(fc1=r1, g=g, fc2=r2, y=r2["y"])
+
+
+# ------------------------------------------------------------------ 5 trits per byte (R14)
+def t5_row_bytes(k: int) -> int:
+    """Bytes per row of the 5-trit packing: 16 * ceil(K / 80)."""
+    return int(_load().oracle_t5_row_bytes(int(k)))
+
+
+def pack_t5(codes: np.ndarray) -> np.ndarray:
+    """[P2 §1.1, §6.1] five codes per byte, sum_i (W_hat[5b+i] + 1) 3^i (reading R14)."""
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    n, k = codes.shape
+    out = np.empty((n, t5_row_bytes(k)), np.uint8)
+    _check(_load().oracle_pack_t5(_ptr(codes), n, k, _ptr(out)), "pack_t5")
+    return out
+
+
+def unpack_t5(packed: np.ndarray, k: int) -> np.ndarray:
+    """Inverse of :func:`pack_t5` (first K weights of each row)."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    n = packed.shape[0]
+    assert packed.shape[1] == t5_row_bytes(k)
+    out = np.empty((n, k), np.int8)
+    _check(_load().oracle_unpack_t5(_ptr(packed), n, k, _ptr(out)), "unpack_t5")
+    return out
+
+
+def forward_t5(xq: np.ndarray, beta: np.ndarray, packed_t5: np.ndarray, k: int, alpha,
+               bias: np.ndarray | None = None):
+    """Forward on 5-trit packed codes: unpack, then the integer matmul and dequant of
+    :func:`forward`.  Returns (acc, y)."""
+    acc = ternary_matmul(xq, unpack_t5(packed_t5, k))
+    return acc, dequant(acc, beta, alpha, bias=bias)

@@ -38,6 +38,10 @@
  *       block's alpha; the integer sums are kept per block, acc[m, n, b], and
  *       y[m, n] = fp32(S * (beta[m] / 127)) with S = sum_b alpha[n, b] * acc[m, n, b]
  *       accumulated in fp64 in ascending b and beta/127 an fp64 division; + bias in fp32.
+ *   R14 sub-2-bit packing [P2 §1.1, §6.1] (a "more compact" encoding, format not given):
+ *       five codes c = W_hat + 1 per byte as the base-3 number sum_i c_i 3^i, c_i the code of
+ *       weight 5b + i of the row; a row takes 16 ceil(K / 80) bytes, and trits past K hold
+ *       code 1 (weight 0), so a byte with no weight left is 121.
  *   R13 the BitMLP of [P3 §6.1] is fc2(GELU(fc1(x))) with two BitLinears; GELU is the
  *       erf form of torch.nn.GELU, 0.5 h (1 + erf(h / sqrt 2)), evaluated in fp64 as
  *       (0.5 h) (1 + erf(h * RN64(1/sqrt 2))) and rounded to fp32 once; fc2 quantizes the
@@ -323,6 +327,48 @@ int oracle_gelu(const float* h, int64_t count, float* g) {
     for (int64_t i = 0; i < count; ++i) {
         const double v = (double)h[i];
         g[i] = (float)(0.5 * v * (1.0 + erf(v * 0.70710678118654752440)));
+    }
+    return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------- 5 trits per byte (R14) */
+int64_t oracle_t5_row_bytes(int64_t k) { return 16 * ((k + 79) / 80); }
+
+/* [P2 §1.1, §6.1] pack codes [n_rows, k] (values -1, 0, 1) five to a byte, reading R14. */
+int oracle_pack_t5(const int8_t* codes, int64_t n_rows, int64_t k, uint8_t* packed) {
+    if (!codes || !packed || n_rows <= 0 || k <= 0) return ORACLE_EINVAL;
+    const int64_t rb = oracle_t5_row_bytes(k);
+    for (int64_t n = 0; n < n_rows; ++n) {
+        for (int64_t b = 0; b < rb; ++b) {
+            unsigned v = 0, p3 = 1;
+            for (int i = 0; i < 5; ++i, p3 *= 3) {
+                const int64_t j = 5 * b + i;
+                int c = 1;                                     /* past K: weight 0 */
+                if (j < k) {
+                    const int8_t w = codes[n * k + j];
+                    if (w < -1 || w > 1) return ORACLE_EBADCODE;
+                    c = w + 1;
+                }
+                v += (unsigned)c * p3;
+            }
+            packed[n * rb + b] = (uint8_t)v;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* Inverse of oracle_pack_t5 for the first k weights of each row; bytes above 242 are
+ * rejected. */
+int oracle_unpack_t5(const uint8_t* packed, int64_t n_rows, int64_t k, int8_t* codes) {
+    if (!codes || !packed || n_rows <= 0 || k <= 0) return ORACLE_EINVAL;
+    const int64_t rb = oracle_t5_row_bytes(k);
+    for (int64_t n = 0; n < n_rows; ++n) {
+        for (int64_t j = 0; j < k; ++j) {
+            unsigned v = packed[n * rb + j / 5];
+            if (v > 242) return ORACLE_EBADCODE;
+            for (int i = 0; i < (int)(j % 5); ++i) v /= 3;
+            codes[n * k + j] = (int8_t)((int)(v % 3) - 1);
+        }
     }
     return ORACLE_OK;
 }

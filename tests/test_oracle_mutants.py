@@ -57,6 +57,13 @@ MUTANTS = [
     ("gelu with sqrt 2 for 1/sqrt 2", "erf(v * 0.70710678118654752440)", "erf(v * 1.41421356237309504880)"),
     ("gelu without the half", "g[i] = (float)(0.5 * v * (1.0 + erf(", "g[i] = (float)(v * (1.0 + erf("),
     ("gelu with 1 - erf", "(1.0 + erf(v", "(1.0 - erf(v"),
+    ("t5 radix 4", "for (int i = 0; i < 5; ++i, p3 *= 3) {", "for (int i = 0; i < 5; ++i, p3 *= 4) {"),
+    ("t5 padding as weight -1", "int c = 1;                                     /* past K: weight 0 */",
+     "int c = 0;"),
+    ("t5 trit order reversed on unpack", "for (int i = 0; i < (int)(j % 5); ++i) v /= 3;",
+     "for (int i = 0; i < 4 - (int)(j % 5); ++i) v /= 3;"),
+    ("t5 rows of 16 ceil(K/64) bytes", "int64_t oracle_t5_row_bytes(int64_t k) { return 16 * ((k + 79) / 80); }",
+     "int64_t oracle_t5_row_bytes(int64_t k) { return 16 * ((k + 63) / 64); }"),
 ]
 
 

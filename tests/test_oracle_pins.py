@@ -615,3 +615,48 @@ def test_bitmlp_tracks_the_float_mlp():
     assert cos > 0.75
     assert np.array_equal(r["g"], oracle.gelu(r["fc1"]["y"]))
     assert np.array_equal(r["fc2"]["xq"], oracle.quantize_act(r["g"])[0])
+
+
+# ---------------------------------------------------------------- 5 trits per byte (R14)
+def test_t5_every_trit_tuple_has_its_own_byte():
+    """All 3^5 = 243 code tuples pack to the distinct bytes 0..242, in base-3 order."""
+    import itertools
+    tuples = np.array(list(itertools.product((-1, 0, 1), repeat=5)), np.int8)[:, ::-1]   # trit 0 fastest
+    packed = oracle.pack_t5(tuples.reshape(1, -1)[:, :5 * 243])
+    got = packed[0, :243]
+    want = np.array([sum((int(c) + 1) * 3 ** i for i, c in enumerate(t)) for t in tuples])
+    assert np.array_equal(got, want) and sorted(got.tolist()) == list(range(243))
+    assert np.array_equal(oracle.unpack_t5(packed, 5 * 243), tuples.reshape(1, -1))
+
+
+def test_t5_hand_value_padding_and_density():
+    # W_hat = +1, 0, -1, +1, 0 -> c = 2, 1, 0, 2, 1 -> 2 + 3 + 0 + 54 + 81 = 140
+    p = oracle.pack_t5(np.array([[1, 0, -1, 1, 0, -1]], np.int8))
+    assert p.shape == (1, 16)
+    assert p[0, 0] == 140
+    assert p[0, 1] == 0 + 3 + 9 + 27 + 81          # weight -1, then four padded weights 0
+    assert np.all(p[0, 2:] == 121)                 # bytes with no weight left
+    assert oracle.t5_row_bytes(4096) == 832 and oracle.t5_row_bytes(11008) == 2208   # vs 1024, 2752
+    assert oracle.t5_row_bytes(80) == 16 and oracle.t5_row_bytes(81) == 32
+
+
+@pytest.mark.parametrize("k", [1, 4, 5, 79, 80, 81, 203, 4096])
+def test_t5_round_trip(k):
+    g = np.random.default_rng(k)
+    codes = g.integers(-1, 2, size=(3, k)).astype(np.int8)
+    assert np.array_equal(oracle.unpack_t5(oracle.pack_t5(codes), k), codes)
+    bad = oracle.pack_t5(codes)
+    bad[1, 0] = 243
+    with pytest.raises(ValueError):
+        oracle.unpack_t5(bad, k)
+
+
+def test_t5_forward_equals_the_2bit_forward():
+    """The packing changes bytes, not the product: same acc and y as the 2-bit layout."""
+    w = workloads.weights(45, 37, 1000)
+    x = workloads.activations(45, 3, 1000)
+    codes, packed, alpha = oracle.quantize_weights(w)
+    xq, beta = oracle.quantize_act(x)
+    acc2, y2 = oracle.forward(xq, beta, packed, 1000, alpha)
+    acc5, y5 = oracle.forward_t5(xq, beta, oracle.pack_t5(codes), 1000, alpha)
+    assert np.array_equal(acc2, acc5) and np.array_equal(y2, y5)
