@@ -375,6 +375,40 @@ def blocks_bench(torch, bl, workloads, dev, ms_plain_step):
     return out
 
 
+def t5_bench(torch, bl, workloads, dev):
+    """Five codes per byte (1.6 bits per weight): the 7B decode step (three GEMVs, M = 1,
+    x_q given) on 5-trit weights beside the same step on the 2-bit packing, weights rotated
+    through pools of copies."""
+    out = {"shapes_KN": DECODE_SHAPES}
+    for tag in ("2bit", "t5"):
+        bytes_step = sum(n * (k // 4 if tag == "2bit" else bl.lib.bitlinear_t5_row_bytes(k)) for k, n in DECODE_SHAPES)
+        copies = max(2, POOL_BYTES // bytes_step)
+        shapes = []
+        for idx, (k, n) in enumerate(DECODE_SHAPES):
+            w = torch.from_numpy(workloads.weights(2, n, k, index=idx)).to(dev)
+            packed, alpha = bl.bitlinear_quantize_weights(w)
+            del w
+            p = packed if tag == "2bit" else bl.bitlinear_repack_t5(packed, k)
+            pool = [p] + [p.clone() for _ in range(copies - 1)]
+            x = torch.from_numpy(workloads.activations(2, 1, k, index=100 * idx)).to(dev)
+            xq, beta = bl.bitlinear_quantize_act(x)
+            shapes.append(dict(pool=pool, alpha=alpha, xq=xq, beta=beta,
+                               y=torch.empty((1, n), dtype=torch.float32, device=dev)))
+        torch.cuda.synchronize()
+        fwd = bl.bitlinear_forward if tag == "2bit" else bl.bitlinear_forward_t5
+
+        def step(i):
+            for sh in shapes:
+                fwd(sh["xq"], sh["beta"], sh["pool"][i % copies], sh["alpha"], y=sh["y"])
+
+        ms, _ = _graph_time(torch, step, 400)
+        out[tag] = {"bytes_per_step": bytes_step, "us_per_step": round(ms * 1e3, 2),
+                    "gbs": round(bytes_step / (ms * 1e-3) / 1e9, 1)}
+        del shapes
+        torch.cuda.empty_cache()
+    return out
+
+
 def mlp_bench(torch, bl, workloads, dev, d=4096, f=11008):
     """BitMLP [P3 §6.1], y = fc2(GELU(fc1(x))) at 7B-class sizes (d_model 4096, d_ff 11008),
     one bitlinear_mlp_forward call: decode (M = 1, weights rotated through a pool, packed
@@ -717,6 +751,8 @@ def main():
         log(f"blocks {extras['blocks']}")
         extras["mlp"] = mlp_bench(torch, bl, workloads, dev)
         log(f"mlp {extras['mlp']}")
+        extras["t5"] = t5_bench(torch, bl, workloads, dev)
+        log(f"t5 {extras['t5']}")
     if not args.no_extras and not args.no_chain:
         extras["chain70b"] = chain70b_bench(torch, bl, workloads, dev)
         log(f"chain70b {extras['chain70b']}")

@@ -40,6 +40,10 @@ SIGNATURES = {
     "bitlinear_forward_fused": (_INT, [_P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P, _P, _P]),
     "bitlinear_forward_fused_rows": (_INT, [_P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P, _P, _P]),
     "bitlinear_forward_fused_kernel": (ctypes.c_char_p, [_I64, _I64, _I64, _P, _P, _P]),
+    "bitlinear_t5_row_bytes": (_SZ, [_I64]),
+    "bitlinear_quantize_weights_t5": (_INT, [_P, _I64, _I64, _P, _P, _P, _SZ, _P]),
+    "bitlinear_forward_t5": (_INT, [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _P]),
+    "bitlinear_repack_t5": (_INT, [_P, _I64, _I64, _P, _P]),
     "bitlinear_quantize_weights_blocks": (_INT, [_P, _I64, _I64, _P, _P, _P]),
     "bitlinear_forward_blocks": (_INT, [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _P]),
     "bitlinear_mlp_forward": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
@@ -149,6 +153,53 @@ def bitlinear_quantize_act(x, x_q=None, beta=None, stream=None):
         _dev(x, torch.float32, "x"), M, K, _dev(x_q, torch.int8, "x_q"),
         _dev(beta, torch.float32, "beta"), _stream(stream)))
     return x_q, beta
+
+
+def bitlinear_quantize_weights_t5(W, W_t5=None, alpha=None, workspace=None, stream=None):
+    """W [N, K] fp32 -> (W_t5 uint8 [N, 16 ceil(K/80)], alpha fp32 [1]): five codes per byte."""
+    torch = _torch()
+    N, K = W.shape
+    rb = lib.bitlinear_t5_row_bytes(K)
+    if W_t5 is None:
+        W_t5 = torch.empty((N, rb), dtype=torch.uint8, device=W.device)
+    if alpha is None:
+        alpha = torch.empty(1, dtype=torch.float32, device=W.device)
+    need = lib.bitlinear_quantize_weights_workspace_size(N, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=W.device)
+    _check("bitlinear_quantize_weights_t5", lib.bitlinear_quantize_weights_t5(
+        _dev(W, torch.float32, "W"), N, K, _dev(W_t5, torch.uint8, "W_t5"), _dev(alpha, torch.float32, "alpha"),
+        _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
+    return W_t5, alpha
+
+
+def bitlinear_repack_t5(W_packed, K, W_t5=None, stream=None):
+    """2-bit packed [N, K/4] -> five codes per byte [N, 16 ceil(K/80)] (same codes)."""
+    torch = _torch()
+    N = W_packed.shape[0]
+    if W_packed.shape[1] * 4 != K:
+        raise ValueError("W_packed must be [N, K/4]")
+    if W_t5 is None:
+        W_t5 = torch.empty((N, lib.bitlinear_t5_row_bytes(K)), dtype=torch.uint8, device=W_packed.device)
+    _check("bitlinear_repack_t5", lib.bitlinear_repack_t5(
+        _dev(W_packed, torch.uint8, "W_packed"), N, K, _dev(W_t5, torch.uint8, "W_t5"), _stream(stream)))
+    return W_t5
+
+
+def bitlinear_forward_t5(x_q, beta, W_t5, alpha, bias=None, y=None, stream=None):
+    """y [M, N] from x_q, beta and 5-trit packed weights."""
+    torch = _torch()
+    M, K = x_q.shape
+    N = W_t5.shape[0]
+    if W_t5.shape[1] != lib.bitlinear_t5_row_bytes(K):
+        raise ValueError("W_t5 must be [N, bitlinear_t5_row_bytes(K)]")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x_q.device)
+    _check("bitlinear_forward_t5", lib.bitlinear_forward_t5(
+        _dev(x_q, torch.int8, "x_q"), _dev(beta, torch.float32, "beta"), M, K, _dev(W_t5, torch.uint8, "W_t5"),
+        _dev(alpha, torch.float32, "alpha"), N, _dev(bias, torch.float32, "bias") if bias is not None else None,
+        _dev(y, torch.float32, "y"), _stream(stream)))
+    return y
 
 
 def bitlinear_quantize_weights_blocks(W, W_packed=None, alpha_blocks=None, stream=None):

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libbitlinear.so")
 CEILING_LIB = os.path.join(PKG, "libbitlinear_ceiling.so")   # measurement kernels, not the path
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["api.hip", "quantize.hip", "gemv.hip", "decode.hip", "gemm.hip", "blocks.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemv.hip", "decode.hip", "gemm.hip", "blocks.hip", "t5.hip"]
 CEILING_SOURCES = ["ceiling.hip"]
 ARCH = os.environ.get("BITLINEAR_OFFLOAD_ARCH", "gfx950")
 

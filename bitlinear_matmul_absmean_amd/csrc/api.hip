@@ -212,6 +212,40 @@ int bitlinear_mlp_forward(const float* x, int64_t M, int64_t d_model, int64_t d_
     return forward_fused(g, M, d_ff, W2_packed, alpha2, false, d_model, bias2, y, x_q2, beta2, nullptr, 0, stream);
 }
 
+size_t bitlinear_t5_row_bytes(int64_t K) { return K > 0 ? (size_t)t5_row_bytes(K) : 0; }
+
+int bitlinear_quantize_weights_t5(const float* W, int64_t N, int64_t K, uint8_t* W_t5, float* alpha, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+    if (!W || !W_t5 || !alpha) return BITLINEAR_ERR_INVALID_ARG;
+    if (N <= 0 || K <= 0) return BITLINEAR_ERR_INVALID_ARG;
+    if (K % 4 != 0 || !t5_supports(K) || !mul_ok(N, K) || N > (int64_t)INT_MAX * 4) return BITLINEAR_ERR_SHAPE;
+    if (!aligned(W, 16)) return BITLINEAR_ERR_ALIGNMENT;
+    if (!workspace || workspace_bytes < bitlinear_quantize_weights_workspace_size(N, K)) return BITLINEAR_ERR_WORKSPACE;
+    if (!aligned(workspace, 8)) return BITLINEAR_ERR_ALIGNMENT;
+    double* rows = static_cast<double*>(workspace);
+    int st = hip_status(launch_row_abs_sums(W, N, K, rows, stream));
+    if (st) return st;
+    st = hip_status(launch_alpha_from_rows(rows, N, K, alpha, stream));
+    if (st) return st;
+    return hip_status(launch_pack_t5(W, N, K, alpha, W_t5, stream));
+}
+
+int bitlinear_repack_t5(const uint8_t* W_packed, int64_t N, int64_t K, uint8_t* W_t5, hipStream_t stream) {
+    if (!W_packed || !W_t5) return BITLINEAR_ERR_INVALID_ARG;
+    if (N <= 0 || K <= 0) return BITLINEAR_ERR_INVALID_ARG;
+    if (K % 4 != 0 || !t5_supports(K) || !mul_ok(N, K)) return BITLINEAR_ERR_SHAPE;
+    return hip_status(launch_repack_t5(W_packed, N, K, W_t5, stream));
+}
+
+int bitlinear_forward_t5(const int8_t* x_q, const float* beta, int64_t M, int64_t K, const uint8_t* W_t5,
+                         const float* alpha, int64_t N, const float* bias, float* y, hipStream_t stream) {
+    int st = check_forward(x_q, beta, M, K, W_t5, alpha, N, y);
+    if (st) return st;
+    if (!t5_supports(K) || M > 65535) return BITLINEAR_ERR_SHAPE;
+    if (!aligned(W_t5, 16)) return BITLINEAR_ERR_ALIGNMENT;
+    return hip_status(launch_forward_t5(x_q, beta, M, K, W_t5, alpha, N, bias, y, stream));
+}
+
 int bitlinear_quantize_weights_blocks(const float* W, int64_t N, int64_t K, uint8_t* W_packed, float* alpha_blocks,
                                       hipStream_t stream) {
     if (!W || !W_packed || !alpha_blocks) return BITLINEAR_ERR_INVALID_ARG;

@@ -87,6 +87,13 @@ hipError_t launch_alpha_rows(const float* W, int64_t N, int64_t K, float* alpha_
 hipError_t launch_ternary_pack(const float* W, int64_t N, int64_t K, const float* alpha, bool per_row,
                                uint8_t* packed, hipStream_t s);
 hipError_t launch_quantize_act(const float* x, int64_t M, int64_t K, int8_t* xq, float* beta, hipStream_t s);
+// Five ternary codes per byte (base 3), rows of 16 ceil(K / 80) bytes.
+int64_t t5_row_bytes(int64_t K);
+bool t5_supports(int64_t K);
+hipError_t launch_pack_t5(const float* W, int64_t N, int64_t K, const float* alpha, uint8_t* out, hipStream_t s);
+hipError_t launch_repack_t5(const uint8_t* w2, int64_t N, int64_t K, uint8_t* out, hipStream_t s);
+hipError_t launch_forward_t5(const int8_t* xq, const float* beta, int64_t M, int64_t K, const uint8_t* wp,
+                             const float* alpha, int64_t N, const float* bias, float* y, hipStream_t s);
 // Block scales: one alpha per 128 consecutive weights of a row, alpha [N, K / 128].
 hipError_t launch_quantize_blocks(const float* W, int64_t N, int64_t K, uint8_t* packed, float* alpha, hipStream_t s);
 bool blocks_supports(int64_t K);

@@ -4,7 +4,8 @@
  * Page keys used in the citations below:
  *   [P1] 2kiu.com, article on 1.58-bit quantization and hardware co-optimization (block
  *        scales, §2.3 and §4.2).
- *   [P2] nxmr.cn tutorial "1.58 位大模型" (per-row absmean, add/sub form of the matmul).
+ *   [P2] nxmr.cn tutorial "1.58 位大模型" (per-row absmean, add/sub form of the matmul, §1.1
+ *        and §6.1 more compact encodings).
  *   [P3] chenxutan.com, "1.58-bit 大模型极限量化实战：从 BitNet 三值权重到单颗 CPU 跑起 100B 模型"
  *        (absmean / absmax formulas, BitLinear forward, 2-bit packing, §6.1 the BitMLP,
  *        §6.2 the rotation before absmax).
@@ -175,6 +176,33 @@ int bitlinear_forward_fused(const float* x, int64_t M, int64_t K, const uint8_t*
 int bitlinear_forward_fused_rows(const float* x, int64_t M, int64_t K, const uint8_t* W_packed,
                                  const float* alpha_rows, int64_t N, const float* bias, float* y,
                                  int8_t* x_q, float* beta, int32_t* acc, hipStream_t stream);
+
+/*
+ * Ternary weights packed five to a byte [P2 §1.1, §6.1] (1.6 bits per weight; the pages name
+ * more compact encodings than 2 bits without a format).  Byte b of a row holds the codes
+ * c = W_hat + 1 of weights 5b .. 5b+4 as sum_i c_i 3^i (0..242); a row takes
+ * bitlinear_t5_row_bytes(K) = 16 ceil(K / 80) bytes; trits past K hold code 1 (weight 0).
+ * Quantization is that of bitlinear_quantize_weights (same alpha, same codes), packed this
+ * way: W_t5 is [N, bitlinear_t5_row_bytes(K)] uint8 (out); other arguments and errors as
+ * bitlinear_quantize_weights.  K % 4 == 0, K <= 65536.
+ */
+size_t bitlinear_t5_row_bytes(int64_t K);
+int bitlinear_quantize_weights_t5(const float* W, int64_t N, int64_t K, uint8_t* W_t5, float* alpha,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The 2-bit packing of bitlinear_quantize_weights ([N, K/4]) repacked five codes per byte
+ * into W_t5 ([N, bitlinear_t5_row_bytes(K)]): the same codes.  Errors: INVALID_ARG, SHAPE, HIP. */
+int bitlinear_repack_t5(const uint8_t* W_packed, int64_t N, int64_t K, uint8_t* W_t5, hipStream_t stream);
+
+/*
+ * bitlinear_forward on 5-trit packed weights (16-byte aligned W_t5): the same acc and y as
+ * bitlinear_forward on the 2-bit packing of the same codes.  The kernel is a decode GEMV
+ * (one token per grid row; more tokens re-read the weights).  No acc output.  Bytes above
+ * 242 are never written by the packers; if present they give unspecified outputs.
+ * Errors: INVALID_ARG, SHAPE (K > 65536, M > 65535, ...), ALIGNMENT, HIP.
+ */
+int bitlinear_forward_t5(const int8_t* x_q, const float* beta, int64_t M, int64_t K, const uint8_t* W_t5,
+                         const float* alpha, int64_t N, const float* bias, float* y, hipStream_t stream);
 
 /*
  * Block-scaled weights [P1 §2.3, §4.2]: one scale per block of 128 consecutive weights of a

@@ -236,3 +236,17 @@ def test_mlp_validation_checks_both_layers_first(bl):
     # M > 4 needs each layer's x_q / beta: missing for the second layer only
     assert f(A, 8, 64, 128, A, A, None, A, A, None, A, A, A, A, None, None, None) == bl.BITLINEAR_ERR_INVALID_ARG
     assert f(A, 8, 64, 128, A, None, None, A, A, None, A, A, A, A, A, A, None) == bl.BITLINEAR_ERR_INVALID_ARG
+
+
+def test_t5_validation(bl):
+    assert bl.lib.bitlinear_t5_row_bytes(4096) == 832 and bl.lib.bitlinear_t5_row_bytes(0) == 0
+    q, f, r = bl.lib.bitlinear_quantize_weights_t5, bl.lib.bitlinear_forward_t5, bl.lib.bitlinear_repack_t5
+    assert q(None, 4, 64, A, A, A, 1 << 20, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert q(A, 4, 66, A, A, A, 1 << 20, None) == bl.BITLINEAR_ERR_SHAPE
+    assert q(A, 4, 1 << 17, A, A, A, 1 << 20, None) == bl.BITLINEAR_ERR_SHAPE
+    assert q(A, 4, 64, A, A, A, 8, None) == bl.BITLINEAR_ERR_WORKSPACE
+    assert f(A, A, 1, 64, A + 4, A, 8, None, A, None) == bl.BITLINEAR_ERR_ALIGNMENT
+    assert f(A, A, 1, 1 << 17, A, A, 8, None, A, None) == bl.BITLINEAR_ERR_SHAPE
+    assert f(A, A, 70000, 64, A, A, 8, None, A, None) == bl.BITLINEAR_ERR_SHAPE
+    assert r(None, 4, 64, A, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert r(A, 4, 66, A, None) == bl.BITLINEAR_ERR_SHAPE

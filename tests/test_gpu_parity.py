@@ -624,3 +624,62 @@ def test_mlp_forward_parity(dev, m, d, f, with_bias):
     assert np.array_equal(beta2.cpu().numpy().view(np.uint32), r["fc2"]["beta"].view(np.uint32))
     assert _rel_ok(y.cpu().numpy(), r["y"])
     assert np.array_equal(y.cpu().numpy().view(np.uint32), r["y"].view(np.uint32))
+
+
+# ------------------------------------------------------------------ five codes per byte (R14)
+@pytest.mark.parametrize("n,k", [(1024, 1024), (11008, 4096), (4096, 11008), (7, 12), (3, 84), (33, 4100)])
+def test_quantize_weights_t5_parity(dev, n, k):
+    torch, bl = dev
+    _say(f"quantize_weights_t5 N={n} K={k}")
+    w = workloads.weights(60, n, k)
+    codes, packed2, alpha = oracle.quantize_weights(w)
+    want = oracle.pack_t5(codes)
+    wt = _to(torch, w)
+    t5, a = bl.bitlinear_quantize_weights_t5(wt)
+    p2, _ = bl.bitlinear_quantize_weights(wt)
+    t5r = bl.bitlinear_repack_t5(p2, k)
+    torch.cuda.synchronize()
+    assert np.float32(a.cpu().numpy()[0]) == alpha
+    assert np.array_equal(t5.cpu().numpy(), want)
+    assert np.array_equal(t5r.cpu().numpy(), want)
+
+
+T5_CASES = [(1, 4096, 4096), (1, 11008, 300), (1, 28672, 64), (2, 100, 33), (3, 4096, 1000), (1, 80, 7),
+            (1, 84, 5), (5, 1024, 70), (1, 65536, 8), (1, 4096, 11008)]
+
+
+@pytest.mark.parametrize("m,k,n", T5_CASES)
+def test_forward_t5_parity(dev, m, k, n):
+    torch, bl = dev
+    _say(f"forward_t5 M={m} K={k} N={n}")
+    w = workloads.weights(61, n, k)
+    x = workloads.activations_with_outliers(61, m, k)
+    codes, _, alpha = oracle.quantize_weights(w)
+    xq, beta = oracle.quantize_act(x)
+    bias = workloads.activations(62, 1, n)[0] if m % 2 else None
+    _, y_ref = oracle.forward_t5(xq, beta, oracle.pack_t5(codes), k, alpha, bias=bias)
+    y = bl.bitlinear_forward_t5(_to(torch, xq), _to(torch, beta), _to(torch, oracle.pack_t5(codes)),
+                                _to(torch, np.array([alpha], np.float32)),
+                                bias=None if bias is None else _to(torch, bias))
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
+
+
+def test_forward_t5_extremes(dev):
+    """All-zero weights (every byte 121), all +1 / all -1 rows with x_q = +-127 (|acc| = 127 K)."""
+    torch, bl = dev
+    k, n = 8192, 4
+    codes = np.zeros((n, k), np.int8)
+    codes[1] = 1
+    codes[2] = -1
+    codes[3, ::3] = 1
+    xq = np.full((1, k), 127, np.int8)
+    xq[0, 1::2] = -127
+    xq[0, :4096] = 127
+    beta = np.array([3.0], np.float32)
+    alpha = np.float32(0.02)
+    _, y_ref = oracle.forward_t5(xq, beta, oracle.pack_t5(codes), k, alpha)
+    y = bl.bitlinear_forward_t5(_to(torch, xq), _to(torch, beta), _to(torch, oracle.pack_t5(codes)),
+                                _to(torch, np.array([alpha], np.float32)))
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
