@@ -168,6 +168,16 @@ __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec(ForwardArgs a) {
         if (xu == 0) tsum_w[wave][8 * i + xt] = v;
     }
     __syncthreads();                               // every wave is done with its staging region
+    // per token, once per workgroup: the x_q sum over all of K and (per-tensor alpha) the scale
+    __shared__ int tsum_t[MT * 32];
+    __shared__ float scale_t[MT * 32];
+    if (tid < MT * 32) {
+        int v = 0;
+#pragma unroll
+        for (int w = 0; w < BD_WAVES; ++w) v += tsum_w[w][tid];
+        tsum_t[tid] = v;
+        scale_t[tid] = (!a.alpha_per_row && tid < M) ? dequant_scale(a.alpha[0], a.beta[tid]) : 0.0f;
+    }
     // partial tiles to LDS: tile (r, t) of wave w at red[((w * RB * MT + r * MT + t) * 4 + c) * 64 + lane]
 #pragma unroll
     for (int r = 0; r < RB; ++r)
@@ -181,7 +191,6 @@ __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec(ForwardArgs a) {
 
     // epilogue: element e = (tile, c, lane) -> accumulator regs 4c..4c+3 of that lane:
     // token 32 t + 8 c + 4 (lane / 32) + i, weight row n0 + 32 r + lane % 32
-    const float alpha0 = a.alpha_per_row ? 0.0f : a.alpha[0];
     for (int e = tid; e < RB * MT * 4 * 64; e += BD_WAVES * 64) {
         const int l = e & 63, c = (e >> 6) & 3, tile = e >> 8;
         const int r = tile / MT, t = tile % MT;
@@ -190,16 +199,14 @@ __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec(ForwardArgs a) {
         for (int w = 0; w < BD_WAVES; ++w) sum += red[((w * RB * MT + tile) * 4 + c) * 64 + l];
         const int64_t n = n0 + 32 * r + (l & 31);
         if (n >= N) continue;
-        const float al = a.alpha_per_row ? a.alpha[n] : alpha0;
+        const float al = a.alpha_per_row ? a.alpha[n] : 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int m = 32 * t + 8 * c + 4 * (l >> 5) + i;
             if (m >= M) continue;
-            int xs_ = 0;
-#pragma unroll
-            for (int w = 0; w < BD_WAVES; ++w) xs_ += tsum_w[w][m];
-            const int total = sum[i] - xs_;
-            a.y[(int64_t)m * N + n] = activate(dequant(total, dequant_scale(al, a.beta[m]), a.bias, n), a.act);
+            const int total = sum[i] - tsum_t[m];
+            const float sc = a.alpha_per_row ? dequant_scale(al, a.beta[m]) : scale_t[m];
+            a.y[(int64_t)m * N + n] = activate(dequant(total, sc, a.bias, n), a.act);
             if (a.acc) a.acc[(int64_t)m * N + n] = total;
         }
     }
@@ -319,7 +326,17 @@ __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec16(ForwardArgs a) {
 #pragma unroll
         for (int t = 0; t < MT; ++t) red[(wave * RB * MT + r * MT + t) * 64 + lane] = acc[r][t];
     __syncthreads();
-    const float alpha0 = a.alpha_per_row ? 0.0f : a.alpha[0];
+    // per token, once per workgroup: the x_q sum over all of K and (per-tensor alpha) the scale
+    __shared__ int tsum_t[MT * 16];
+    __shared__ float scale_t[MT * 16];
+    if (tid < MT * 16) {
+        int v = 0;
+#pragma unroll
+        for (int w = 0; w < BD_WAVES; ++w) v += tsum_w[w][tid];
+        tsum_t[tid] = v;
+        scale_t[tid] = (!a.alpha_per_row && tid < M) ? dequant_scale(a.alpha[0], a.beta[tid]) : 0.0f;
+    }
+    __syncthreads();
     for (int e = tid; e < RB * MT * 64; e += BD_WAVES * 64) {
         const int l = e & 63, tile = e >> 6;
         const int r = tile / MT, t = tile % MT;
@@ -328,16 +345,14 @@ __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec16(ForwardArgs a) {
         for (int w = 0; w < BD_WAVES; ++w) sum += red[(w * RB * MT + tile) * 64 + l];
         const int64_t n = n0 + 16 * r + (l & 15);
         if (n >= N) continue;
-        const float al = a.alpha_per_row ? a.alpha[n] : alpha0;
+        const float al = a.alpha_per_row ? a.alpha[n] : 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int m = 16 * t + 4 * (l >> 4) + i;
             if (m >= M) continue;
-            int xs = 0;
-#pragma unroll
-            for (int w = 0; w < BD_WAVES; ++w) xs += tsum_w[w][m];
-            const int total = sum[i] - xs;
-            a.y[(int64_t)m * N + n] = activate(dequant(total, dequant_scale(al, a.beta[m]), a.bias, n), a.act);
+            const int total = sum[i] - tsum_t[m];
+            const float sc = a.alpha_per_row ? dequant_scale(al, a.beta[m]) : scale_t[m];
+            a.y[(int64_t)m * N + n] = activate(dequant(total, sc, a.bias, n), a.act);
             if (a.acc) a.acc[(int64_t)m * N + n] = total;
         }
     }
