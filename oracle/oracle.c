@@ -33,19 +33,6 @@
  *       one after another (row-major along K).
  *   R7  s = fp32((double)alpha * (double)beta / 127.0), y = fp32((float)acc * s), then
  *       + bias as a separate fp32 rounding.
- *   R12 block scales [P1 §2.3, §4.2]: one alpha per 128 consecutive weights of a row,
- *       alpha[n, b] = mean |W[n, 128b .. 128b+127]| (R1 for a block), codes divided by their
- *       block's alpha; the integer sums are kept per block, acc[m, n, b], and
- *       y[m, n] = fp32(S * (beta[m] / 127)) with S = sum_b alpha[n, b] * acc[m, n, b]
- *       accumulated in fp64 in ascending b and beta/127 an fp64 division; + bias in fp32.
- *   R14 sub-2-bit packing [P2 §1.1, §6.1] (a "more compact" encoding, format not given):
- *       five codes c = W_hat + 1 per byte as the base-3 number sum_i c_i 3^i, c_i the code of
- *       weight 5b + i of the row; a row takes 16 ceil(K / 80) bytes, and trits past K hold
- *       code 1 (weight 0), so a byte with no weight left is 121.
- *   R13 the BitMLP of [P3 §6.1] is fc2(GELU(fc1(x))) with two BitLinears; GELU is the
- *       erf form of torch.nn.GELU, 0.5 h (1 + erf(h / sqrt 2)), evaluated in fp64 as
- *       (0.5 h) (1 + erf(h * RN64(1/sqrt 2))) and rounded to fp32 once; fc2 quantizes the
- *       fp32 GELU output like any activation.
  *   R10 the rotation before absmax [P3 §6.2] is a randomized Walsh-Hadamard transform
  *       applied to each row along K in blocks of B (a power of two dividing K): a sign
  *       flip by d[k] in {+1, -1} (the random part; an input, negative int8 = flip), then
@@ -54,6 +41,19 @@
  *   R11 the rotation is evaluated in fp32 as butterflies (a, b) -> (a + b, a - b) on
  *       pairs (j, j + h), with h = 1, 2, 4, ..., B/2 in that order, then one fp32
  *       multiply of every result by fp32(1/sqrt(B)) (exact when B is a power of 4).
+ *   R12 block scales [P1 §2.3, §4.2]: one alpha per 128 consecutive weights of a row,
+ *       alpha[n, b] = mean |W[n, 128b .. 128b+127]| (R1 for a block), codes divided by their
+ *       block's alpha; the integer sums are kept per block, acc[m, n, b], and
+ *       y[m, n] = fp32(S * (beta[m] / 127)) with S = sum_b alpha[n, b] * acc[m, n, b]
+ *       accumulated in fp64 in ascending b and beta/127 an fp64 division; + bias in fp32.
+ *   R13 the BitMLP of [P3 §6.1] is fc2(GELU(fc1(x))) with two BitLinears; GELU is the
+ *       erf form of torch.nn.GELU, 0.5 h (1 + erf(h / sqrt 2)), evaluated in fp64 as
+ *       (0.5 h) (1 + erf(h * RN64(1/sqrt 2))) and rounded to fp32 once; fc2 quantizes the
+ *       fp32 GELU output like any activation.
+ *   R14 sub-2-bit packing [P2 §1.1, §6.1] (a "more compact" encoding, format not given):
+ *       five codes c = W_hat + 1 per byte as the base-3 number sum_i c_i 3^i, c_i the code of
+ *       weight 5b + i of the row; a row takes 16 ceil(K / 80) bytes, and trits past K hold
+ *       code 1 (weight 0), so a byte with no weight left is 121.
  */
 #include <math.h>
 #include <stddef.h>
