@@ -275,7 +275,8 @@ def hadamard_bench(torch, bl, workloads, dev, ms_plain_step, reps=20):
     """Rotation before absmax [P3 §6.2].  Activations: rotate + per-token absmax int8 in one
     pass reads x and the signs and writes x_q and beta, 5MK + 4M + K bytes.  Weights (offline):
     rotate W [11008, 4096], 8NK + K bytes.  Decode: the 7B-class step with rotated projections,
-    each a rotation of x (hadamard_rows) then the fused GEMV on rotated, ternarized weights."""
+    one bitlinear_forward_fused_hadamard call each (rotation, quantization and GEMV in one
+    launch), beside the two-launch form (hadamard_rows, then the fused GEMV)."""
     out = {}
     acts = []
     for m, k in ((2048, 4096), (2048, 11008), (1, 4096)):
@@ -320,14 +321,22 @@ def hadamard_bench(torch, bl, workloads, dev, ms_plain_step, reps=20):
 
     def step(i):
         for sh in shapes:
+            bl.bitlinear_forward_fused_hadamard(sh["x"][i % 8], sh["block"], sh["signs"], sh["pool"][i % copies],
+                                                sh["alpha"], y=sh["y"])
+
+    def step_two_launch(i):
+        for sh in shapes:
             bl.bitlinear_hadamard_rows(sh["x"][i % 8], sh["block"], sh["signs"], out=sh["xr"])
             bl.bitlinear_forward_fused(sh["xr"], sh["pool"][i % copies], sh["alpha"], y=sh["y"])
 
     ms, _ = _graph_time(torch, step, 400)
+    ms2, _ = _graph_time(torch, step_two_launch, 400)
     out["decode_rotated"] = {"shapes_KN": DECODE_SHAPES, "blocks": [sh["block"] for sh in shapes],
+                             "call": "bitlinear_forward_fused_hadamard",
                              "us_per_step": round(ms * 1e3, 2), "weight_gbs": round(per_step / (ms * 1e-3) / 1e9, 1),
                              "plain_us_per_step": round(ms_plain_step * 1e3, 2),
-                             "rotation_overhead_us": round((ms - ms_plain_step) * 1e3, 2)}
+                             "rotation_overhead_us": round((ms - ms_plain_step) * 1e3, 2),
+                             "two_launch_us_per_step": round(ms2 * 1e3, 2)}
     del shapes
     torch.cuda.empty_cache()
     return out

@@ -49,6 +49,7 @@ SIGNATURES = {
     "bitlinear_mlp_forward": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "bitlinear_hadamard_rows": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "bitlinear_quantize_act_hadamard": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "bitlinear_forward_fused_hadamard": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P, _P, _P]),
 }
 
 
@@ -292,6 +293,25 @@ def bitlinear_quantize_act_hadamard(x, block, signs=None, x_q=None, beta=None, s
         _dev(signs, torch.int8, "signs") if signs is not None else None,
         _dev(x_q, torch.int8, "x_q"), _dev(beta, torch.float32, "beta"), _stream(stream)))
     return x_q, beta
+
+
+def bitlinear_forward_fused_hadamard(x, block, signs, W_packed, alpha, bias=None, y=None, x_q=None, beta=None,
+                                     stream=None):
+    """y [M, N] from fp32 x: rotation (block, signs), absmax int8 and the forward in one call."""
+    torch = _torch()
+    M, K = x.shape
+    N = W_packed.shape[0]
+    if W_packed.shape[1] * 4 != K:
+        raise ValueError("W_packed must be [N, K/4]")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    opt = lambda t, dt, n: _dev(t, dt, n) if t is not None else None
+    _check("bitlinear_forward_fused_hadamard", lib.bitlinear_forward_fused_hadamard(
+        _dev(x, torch.float32, "x"), M, K, int(block), opt(signs, torch.int8, "signs"),
+        _dev(W_packed, torch.uint8, "W_packed"), _dev(alpha, torch.float32, "alpha"), N,
+        opt(bias, torch.float32, "bias"), _dev(y, torch.float32, "y"), opt(x_q, torch.int8, "x_q"),
+        opt(beta, torch.float32, "beta"), _stream(stream)))
+    return y
 
 
 def _forward(fn, what, x_q, beta, W_packed, alpha, bias, y, acc, stream):

@@ -292,6 +292,23 @@ int bitlinear_quantize_act_hadamard(const float* x, int64_t M, int64_t K, int64_
     return hip_status(launch_quantize_act_hadamard(x, M, K, (int)block, signs, x_q, beta, stream));
 }
 
+int bitlinear_forward_fused_hadamard(const float* x, int64_t M, int64_t K, int64_t block, const int8_t* signs,
+                                     const uint8_t* W_packed, const float* alpha, int64_t N, const float* bias, float* y,
+                                     int8_t* x_q, float* beta, hipStream_t stream) {
+    int st = check_hadamard(x, M, K, block, signs);
+    if (st) return st;
+    st = check_forward(reinterpret_cast<const int8_t*>(x), x, M, K, W_packed, alpha, N, y);
+    if (st) return st;
+    if (gemv_hadamard_supports(M, K) && aligned(W_packed, 16) && (!x_q || aligned(x_q, 4)))
+        return hip_status(launch_gemv_hadamard(x, K, (int)block, signs, W_packed, alpha, N, bias, y, x_q, beta, stream));
+    // other shapes: rotation + quantization, then the forward, through x_q and beta
+    if (!x_q || !beta) return BITLINEAR_ERR_INVALID_ARG;
+    if (!aligned(x_q, 4)) return BITLINEAR_ERR_ALIGNMENT;
+    st = hip_status(launch_quantize_act_hadamard(x, M, K, (int)block, signs, x_q, beta, stream));
+    if (st) return st;
+    return bitlinear_forward(x_q, beta, M, K, W_packed, alpha, N, bias, y, nullptr, stream);
+}
+
 const char* bitlinear_forward_fused_kernel(int64_t M, int64_t K, int64_t N, const float* x, const uint8_t* W_packed,
                                            const int8_t* x_q) {
     (void)N;

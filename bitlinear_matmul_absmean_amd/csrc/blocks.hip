@@ -34,24 +34,6 @@ struct BlockArgs {
 
 constexpr int BW_WAVES = 8;
 
-// The add/sub sum of one 64-weight chunk: codes c = W_hat + 1 in 2-bit fields; field i of a
-// code dword, masked in place, holds c * 4^i per byte (field 3 is shifted down so it stays
-// below 128); each field meets its transposed activations in v_dot4_i32_i8, the four sums
-// are recombined exactly, and sum (c - 1) x = sum c x - sum x.
-__device__ __forceinline__ int chunk_sum(const u32x4& w, const u32x4* xs, int stride, int xsum) {
-    int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
-    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const u32x4 t = xs[d * stride];
-        a0 = dot4(wd[d] & 0x03030303u, t.x, a0);
-        a1 = dot4(wd[d] & 0x0C0C0C0Cu, t.y, a1);
-        a2 = dot4(wd[d] & 0x30303030u, t.z, a2);
-        a3 = dot4((wd[d] >> 6) & 0x03030303u, t.w, a3);
-    }
-    return a0 + (a1 >> 2) + (a2 >> 4) + a3 - xsum;
-}
-
 // MT tokens per workgroup (tokens past M are zero; more tokens run as a second grid
 // dimension over groups of MT), CPL chunks of 64 weights per lane and row (K <= 4096 CPL),
 // R rows per wave step with every load of the step issued first.

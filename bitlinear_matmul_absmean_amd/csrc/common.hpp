@@ -80,6 +80,24 @@ __device__ __forceinline__ u32x4 transpose4x4_bytes(u32x4 s) {
 // Sum of the four signed bytes of a dword.
 __device__ __forceinline__ int byte_sum(uint32_t v) { return dot4(v, 0x01010101u, 0); }
 
+// The add/sub sum of one 64-weight chunk: codes c = W_hat + 1 in 2-bit fields; field i of a
+// code dword, masked in place, holds c * 4^i per byte (field 3 is shifted down so it stays
+// below 128); each field meets its transposed activations in v_dot4_i32_i8, the four sums
+// are recombined exactly, and sum (c - 1) x = sum c x - sum x.
+__device__ __forceinline__ int chunk_sum(const u32x4& w, const u32x4* xs, int stride, int xsum) {
+    int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const u32x4 t = xs[d * stride];
+        a0 = dot4(wd[d] & 0x03030303u, t.x, a0);
+        a1 = dot4(wd[d] & 0x0C0C0C0Cu, t.y, a1);
+        a2 = dot4(wd[d] & 0x30303030u, t.z, a2);
+        a3 = dot4((wd[d] >> 6) & 0x03030303u, t.w, a3);
+    }
+    return a0 + (a1 >> 2) + (a2 >> 4) + a3 - xsum;
+}
+
 // ---- launch wrappers (one per kernel family), defined in the .hip files -------------------
 hipError_t launch_row_abs_sums(const float* W, int64_t N, int64_t K, double* rowsum, hipStream_t s);
 hipError_t launch_alpha_from_rows(const double* rowsum, int64_t N, int64_t K, float* alpha, hipStream_t s);
@@ -104,6 +122,10 @@ hipError_t launch_forward_blocks(const int8_t* xq, const float* beta, int64_t M,
 constexpr int64_t HADAMARD_MAX_BLOCK = 4096;
 hipError_t launch_hadamard_rows(const float* x, int64_t M, int64_t K, int block, const int8_t* signs,
                                 float* out, hipStream_t s);
+bool gemv_hadamard_supports(int64_t M, int64_t K);
+hipError_t launch_gemv_hadamard(const float* x, int64_t K, int block, const int8_t* signs, const uint8_t* wp,
+                                const float* alpha, int64_t N, const float* bias, float* y, int8_t* xq_out,
+                                float* beta_out, hipStream_t s);
 hipError_t launch_quantize_act_hadamard(const float* x, int64_t M, int64_t K, int block, const int8_t* signs,
                                         int8_t* xq, float* beta, hipStream_t s);
 

@@ -267,10 +267,12 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // SCALE = false leaves the final multiply by fp32(1/sqrt(B)) to the caller.
+// t: this thread's index in the 256-thread group that rotates the chunk (every thread of the
+// workgroup must call it the same number of times: it holds workgroup barriers).
 template <bool SCALE = true, typename Blk>
-__device__ __forceinline__ void hadamard_chunk(float (&v)[16], Blk block_, float scale, float* buf) {
+__device__ __forceinline__ void hadamard_chunk(float (&v)[16], Blk block_, float scale, float* buf,
+                                               int t = threadIdx.x) {
     const int block = (int)block_;
-    const int t = threadIdx.x;
     if (block > 1) had_stage(v, 1);
     if (block > 2) had_stage(v, 2);
     if (block > 4) {
@@ -517,6 +519,187 @@ __global__ __launch_bounds__(256) void k_quantize_act_hadamard_pipe(const float*
     row_step(m, 0);
     int it = 1;
     for (m += gridDim.x; m < M; m += gridDim.x, ++it) row_step(m, it);
+}
+
+// ---------------------------------------------------------------------------------------
+// Rotation, quantization and the decode GEMV in one launch (one token, K <= 16384) [P3 §6.2,
+// §2.4, §3.2].  A workgroup of HALVES x four waves loads x (branch-free, so the weight loads
+// issued right after stay in flight); its 256-thread halves rotate alternate 4096-element
+// chunks as quantize_act_hadamard does (two halves when K spans several chunks, so that they
+// rotate in parallel; one otherwise, with no idle waves), the workgroup takes the absmax, writes the codes to LDS,
+// transposes each 16-byte group 4x4 into the operand layout of the GEMV and streams its rows:
+// each wave holds R rows of CPL 64-weight chunks per lane in registers, loaded before the
+// rotation starts.  The results equal those of quantize_act_hadamard followed by
+// bitlinear_forward, bit for bit.
+struct RotGemvArgs {
+    const float* x;
+    int64_t K;
+    int block;
+    float scale;
+    const int8_t* signs;
+    const uint8_t* wp;
+    const float* alpha;
+    int64_t N;
+    const float* bias;
+    float* y;
+    int8_t* xq_out;
+    float* beta_out;
+    int64_t rows_per_wave;
+};
+
+// CS chunk slots per half (chunk HALVES s + half), CPL 64-weight chunks per lane and row, R
+// rows per wave.
+template <int HALVES, int CS, int CPL, int R>
+__global__ __launch_bounds__(256 * HALVES) void k_gemv_hadamard(RotGemvArgs a) {
+    constexpr int RG_WAVES = 4 * HALVES;
+    extern __shared__ u32x4 xs[];                 // [CPL][4][64] transposed groups of x_q
+    __shared__ float buf[HALVES][HAD_LDS];        // each half's rotation exchange; then the x_q byte row
+    __shared__ float red[RG_WAVES];
+    __shared__ int redi[RG_WAVES];
+    const int t = threadIdx.x, lane = t & 63, half = HALVES == 1 ? 0 : t >> 8, th = t & 255;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int64_t K = a.K, N = a.N;
+    const int K64 = (int)(K >> 6);
+
+    // x: chunk HALVES s + half, float4 group q of thread th = elements c0 + 4 th + 1024 q; clamped
+    // address, masked value
+    float4 xv[CS][4];
+    uint32_t keep[CS][4], sg[CS][4];
+#pragma unroll
+    for (int c = 0; c < CS; ++c)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t e = (int64_t)(HALVES * c + half) * HAD_CHUNK + 4 * th + 1024 * q;
+            const bool ok = e < K;
+            const int64_t ec = ok ? e : 0;
+            keep[c][q] = ok ? 0xFFFFFFFFu : 0u;
+            xv[c][q] = *reinterpret_cast<const float4*>(a.x + ec);
+            sg[c][q] = a.signs ? *reinterpret_cast<const uint32_t*>(a.signs + ec) & 0x80808080u : 0u;
+        }
+    // this wave's weight rows, every load issued now
+    const int64_t r0 = ((int64_t)blockIdx.x * RG_WAVES + wave) * a.rows_per_wave;
+    const int64_t r1 = r0 + a.rows_per_wave < N ? r0 + a.rows_per_wave : N;
+    const u32x4* wp = reinterpret_cast<const u32x4*>(a.wp);
+    u32x4 w[R][CPL];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        int64_t row = r0 + r < r1 ? r0 + r : r1 - 1;
+        row = row < 0 ? 0 : row;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int cc = lane + 64 * j < K64 ? lane + 64 * j : 0;
+            w[r][j] = wp[row * K64 + cc];
+        }
+    }
+
+    float v[CS][16];
+    float mx = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CS; ++c) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 f = xv[c][q];
+            v[c][4 * q + 0] = __uint_as_float((__float_as_uint(f.x) & keep[c][q]) ^ (sg[c][q] << 24));
+            v[c][4 * q + 1] = __uint_as_float((__float_as_uint(f.y) & keep[c][q]) ^ ((sg[c][q] << 16) & 0x80000000u));
+            v[c][4 * q + 2] = __uint_as_float((__float_as_uint(f.z) & keep[c][q]) ^ ((sg[c][q] << 8) & 0x80000000u));
+            v[c][4 * q + 3] = __uint_as_float((__float_as_uint(f.w) & keep[c][q]) ^ (sg[c][q] & 0x80000000u));
+        }
+        // both halves rotate in every slot (a chunk past K holds zeros), so barriers match
+        hadamard_chunk(v[c], a.block, a.scale, buf[half], th);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(v[c][j]));
+    }
+    mx = wave_max_f32(mx);
+    if (lane == 0) red[wave] = mx;
+    lds_barrier();                                // also: every rotation read of buf is done
+    mx = red[0];
+#pragma unroll
+    for (int i = 1; i < RG_WAVES; ++i) mx = fmaxf(mx, red[i]);
+    const float b = mx + 1e-8f;
+    const float yi = 1.0f / b;
+
+    // codes -> the x_q byte row in LDS (and to x_q_out from workgroup 0), sum of x_q
+    uint8_t* xb = reinterpret_cast<uint8_t*>(&buf[0][0]);
+    int sx = 0;
+#pragma unroll
+    for (int c = 0; c < CS; ++c)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t e = (int64_t)(HALVES * c + half) * HAD_CHUNK + 4 * th + 1024 * q;
+            if (e < K) {
+                const uint32_t code = act_codes4(v[c][4 * q], v[c][4 * q + 1], v[c][4 * q + 2], v[c][4 * q + 3], b, yi);
+                *reinterpret_cast<uint32_t*>(xb + e) = code;
+                sx += byte_sum(code);
+                if (a.xq_out && blockIdx.x == 0) *reinterpret_cast<uint32_t*>(a.xq_out + e) = code;
+            }
+        }
+    sx = wave_sum_i32(sx);
+    if (lane == 0) redi[wave] = sx;
+    if (a.beta_out && blockIdx.x == 0 && t == 0) a.beta_out[0] = b;
+    lds_barrier();
+    int xsum = 0;
+#pragma unroll
+    for (int i = 0; i < RG_WAVES; ++i) xsum += redi[i];
+    // operand layout: unit (j, d, l) = 16-byte group d of 64-weight chunk l + 64 j, transposed
+    for (int u = t; u < CPL * 256; u += 64 * RG_WAVES) {
+        const int j = u >> 8, d = (u >> 6) & 3, l = u & 63;
+        const int cidx = l + 64 * j;
+        u32x4 g = {0u, 0u, 0u, 0u};
+        if (cidx < K64) g = *reinterpret_cast<const u32x4*>(xb + 64 * cidx + 16 * d);
+        xs[u] = transpose4x4_bytes(g);
+    }
+    lds_barrier();
+
+    const float s = dequant_scale(a.alpha[0], b);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        int acc = 0;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+            if (lane + 64 * j < K64) acc += chunk_sum(w[r][j], xs + j * 256 + lane, 64, 0);
+        const int total = wave_sum_i32(acc) - xsum;
+        const int64_t row = r0 + r;
+        if (lane == 0 && row < r1) a.y[row] = dequant(total, s, a.bias, row);
+    }
+}
+
+bool gemv_hadamard_supports(int64_t M, int64_t K) { return M == 1 && K % 64 == 0 && K <= 4 * HAD_CHUNK; }
+
+template <int HALVES, int CS, int CPL, int R>
+static hipError_t launch_gemv_hadamard_r(RotGemvArgs a, hipStream_t s) {
+    a.rows_per_wave = R;
+    const int64_t wgs = (a.N + 4 * HALVES * R - 1) / (4 * HALVES * R);
+    return launch_with_lds(k_gemv_hadamard<HALVES, CS, CPL, R>, dim3((unsigned)wgs), dim3(256 * HALVES),
+                           (size_t)CPL * 256 * sizeof(u32x4), s, a);
+}
+
+// R rows per wave (at most 16 chunk loads of 16 bytes per lane), measured on the decode
+// shapes: every workgroup repeats the rotation, so rows trade against workgroups.  One half:
+// about 1000 workgroups of four waves, at least two rows per wave; two halves: N / 4096 rows
+// per wave, at least two.
+template <int HALVES, int CS, int CPL>
+static hipError_t launch_gemv_hadamard_cpl(const RotGemvArgs& a, hipStream_t s) {
+    constexpr int RMAX = 16 / CPL;
+    int64_t want = HALVES == 1 ? (a.N + 3999) / 4000 : (a.N + 4095) / 4096;
+    if (want < 2) want = 2;
+    if (want <= 2 || RMAX < 4) return launch_gemv_hadamard_r<HALVES, CS, CPL, (RMAX >= 2 ? 2 : 1)>(a, s);
+    if (want <= 4 || RMAX < 8) return launch_gemv_hadamard_r<HALVES, CS, CPL, (RMAX >= 4 ? 4 : 1)>(a, s);
+    if (want <= 8 || RMAX < 16) return launch_gemv_hadamard_r<HALVES, CS, CPL, (RMAX >= 8 ? 8 : 1)>(a, s);
+    return launch_gemv_hadamard_r<HALVES, CS, CPL, (RMAX >= 16 ? 16 : 1)>(a, s);
+}
+
+hipError_t launch_gemv_hadamard(const float* x, int64_t K, int block, const int8_t* signs, const uint8_t* wp,
+                                const float* alpha, int64_t N, const float* bias, float* y, int8_t* xq_out,
+                                float* beta_out, hipStream_t s) {
+    const RotGemvArgs a{x, K, block, (float)(1.0 / std::sqrt((double)block)), signs, wp, alpha, N, bias, y,
+                        xq_out, beta_out, 0};
+    switch ((K / 64 + 63) / 64) {                 // = the number of 4096-element chunks
+        case 1: return launch_gemv_hadamard_cpl<1, 1, 1>(a, s);
+        case 2: return launch_gemv_hadamard_cpl<2, 1, 2>(a, s);
+        case 3: return launch_gemv_hadamard_cpl<2, 2, 3>(a, s);
+        case 4: return launch_gemv_hadamard_cpl<2, 2, 4>(a, s);
+        default: return hipErrorInvalidValue;     // K > 16384 is refused by gemv_hadamard_supports
+    }
 }
 
 // ---------------------------------------------------------------------------------------

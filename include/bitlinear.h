@@ -298,6 +298,20 @@ int bitlinear_mlp_forward(const float* x, int64_t M, int64_t d_model, int64_t d_
                           float* y, float* g, int8_t* x_q1, float* beta1, int8_t* x_q2,
                           float* beta2, hipStream_t stream);
 
+/*
+ * Rotation, activation quantization and forward in one call [P3 §6.2, §2.4, §3.2]: y from
+ * fp32 x with results identical to bitlinear_quantize_act_hadamard (same block and signs)
+ * followed by bitlinear_forward on weights quantized from rotated rows.  One token with
+ * K % 64 == 0, K <= 16384 and 16-byte aligned W_packed runs as a single launch (every
+ * workgroup rotates and quantizes x, then streams its weight rows); other calls need x_q and
+ * beta and run the two steps.  x_q / beta (may be NULL on the single-launch path) receive the
+ * quantized rotated activations.  Errors as bitlinear_quantize_act_hadamard and
+ * bitlinear_forward.
+ */
+int bitlinear_forward_fused_hadamard(const float* x, int64_t M, int64_t K, int64_t block, const int8_t* signs,
+                                     const uint8_t* W_packed, const float* alpha, int64_t N, const float* bias,
+                                     float* y, int8_t* x_q, float* beta, hipStream_t stream);
+
 /* Kernel(s) bitlinear_forward_fused launches for these arguments ("gemv_fused" or
  * "quantize_act+forward"); a static string. */
 const char* bitlinear_forward_fused_kernel(int64_t M, int64_t K, int64_t N, const float* x,

@@ -250,3 +250,14 @@ def test_t5_validation(bl):
     assert f(A, A, 70000, 64, A, A, 8, None, A, None) == bl.BITLINEAR_ERR_SHAPE
     assert r(None, 4, 64, A, None) == bl.BITLINEAR_ERR_INVALID_ARG
     assert r(A, 4, 66, A, None) == bl.BITLINEAR_ERR_SHAPE
+
+
+def test_forward_fused_hadamard_validation(bl):
+    f = bl.lib.bitlinear_forward_fused_hadamard
+    assert f(A, 1, 4096, 3, None, A, A, 8, None, A, None, None, None) == bl.BITLINEAR_ERR_SHAPE        # block
+    assert f(A, 1, 4096, 8192, None, A, A, 8, None, A, None, None, None) == bl.BITLINEAR_ERR_SHAPE     # block > 4096
+    assert f(A, 1, 96, 64, None, A, A, 8, None, A, None, None, None) == bl.BITLINEAR_ERR_SHAPE         # K % block
+    assert f(A + 4, 1, 4096, 4096, None, A, A, 8, None, A, None, None, None) == bl.BITLINEAR_ERR_ALIGNMENT
+    assert f(A, 1, 4096, 4096, None, A, None, 8, None, A, None, None, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    # the two-step path (M > 1) needs x_q and beta
+    assert f(A, 2, 4096, 4096, None, A, A, 8, None, A, None, None, None) == bl.BITLINEAR_ERR_INVALID_ARG

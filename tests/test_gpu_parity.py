@@ -683,3 +683,46 @@ def test_forward_t5_extremes(dev):
                                 _to(torch, np.array([alpha], np.float32)))
     torch.cuda.synchronize()
     assert np.array_equal(y.cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
+
+
+# (M, K, N, block): one launch for a token with K <= 16384, the two-step path otherwise
+FUSED_HAD_CASES = [(1, 4096, 4096, 4096), (1, 4096, 11008, 4096), (1, 11008, 4096, 256), (1, 1024, 300, 1024),
+                   (1, 16384, 64, 4096), (1, 8192, 1000, 2048), (1, 256, 7, 16), (1, 12288, 33, 4096),
+                   (3, 2048, 100, 512), (1, 20480, 40, 4096)]
+
+
+@pytest.mark.parametrize("m,k,n,block", FUSED_HAD_CASES)
+def test_forward_fused_hadamard_parity(dev, m, k, n, block):
+    torch, bl = dev
+    _say(f"forward_fused_hadamard M={m} K={k} N={n} B={block}")
+    w = workloads.weights(70, n, k)
+    x = workloads.activations_with_outliers(70, m, k)
+    d = workloads.rotation_signs(70, k)
+    bias = workloads.activations(71, 1, n)[0] if n % 2 else None
+    r = oracle.bitlinear_hadamard(x, w, block, d, bias=bias)
+    dt = _to(torch, d)
+    packed, alpha = bl.bitlinear_quantize_weights(bl.bitlinear_hadamard_rows(_to(torch, w), block, dt))
+    xq = torch.empty((m, k), dtype=torch.int8, device="cuda")
+    beta = torch.empty(m, dtype=torch.float32, device="cuda")
+    y = bl.bitlinear_forward_fused_hadamard(_to(torch, x), block, dt, packed, alpha,
+                                            bias=None if bias is None else _to(torch, bias), x_q=xq, beta=beta)
+    torch.cuda.synchronize()
+    assert np.array_equal(packed.cpu().numpy(), r["packed"])
+    assert np.array_equal(xq.cpu().numpy(), r["xq"])
+    assert np.array_equal(beta.cpu().numpy().view(np.uint32), r["beta"].view(np.uint32))
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), r["y"].view(np.uint32))
+
+
+def test_forward_fused_hadamard_without_outputs(dev):
+    """The single-launch path needs no x_q / beta buffers."""
+    torch, bl = dev
+    k, n, block = 4096, 512, 4096
+    w = workloads.weights(72, n, k)
+    x = workloads.activations(72, 1, k)
+    d = workloads.rotation_signs(72, k)
+    r = oracle.bitlinear_hadamard(x, w, block, d)
+    dt = _to(torch, d)
+    packed, alpha = bl.bitlinear_quantize_weights(bl.bitlinear_hadamard_rows(_to(torch, w), block, dt))
+    y = bl.bitlinear_forward_fused_hadamard(_to(torch, x), block, dt, packed, alpha)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), r["y"].view(np.uint32))
