@@ -14,7 +14,7 @@ from Python) and timed with HIP events on the capture stream, bracketed by devic
 
 Extra objects on the same JSON line: `roofline` for the dominant kernel (the decode GEMV on the
 (4096, 11008) shape, timed in isolation the same way), `prefill` (M = 2048 int8-MFMA TOPS),
-`batched` (M = 8/16/64), `chain70b` (one decode step of the 70B-class stream) and
+`batched` (M = 2/4/8/16/64), `chain70b` (one decode step of the 70B-class stream) and
 `cpu_baseline` (the CPU oracle on a bounded sample of the same workload).
 """
 from __future__ import annotations
@@ -345,7 +345,7 @@ def hadamard_bench(torch, bl, workloads, dev, ms_plain_step, reps=20):
 def blocks_bench(torch, bl, workloads, dev, ms_plain_step):
     """Block-scaled weights [P1 §2.3, §4.2] (one alpha per 128 weights): the 7B decode step
     (three GEMVs, M = 1) with block-scaled weights and x_q given, its bytes (NK/4 codes +
-    NK/32 scales + K x_q + 4N y per shape), and batched M = 16 on (4096, 11008)."""
+    NK/32 scales + K x_q + 4N y per shape), and batched M = 4 and 16 on (4096, 11008)."""
     per_step = sum(n * k // 4 + n * k // 32 for k, n in DECODE_SHAPES)
     copies = max(2, POOL_BYTES // per_step)
     shapes = []
@@ -370,16 +370,21 @@ def blocks_bench(torch, bl, workloads, dev, ms_plain_step):
                            "pct_hbm": round(100 * per_step / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                            "per_tensor_fused_us_per_step": round(ms_plain_step * 1e3, 2)}}
     del shapes
-    k, n, m = 4096, 11008, 16
+    k, n = 4096, 11008
     w = torch.from_numpy(workloads.weights(3, n, k)).to(dev)
     packed, ab = bl.bitlinear_quantize_weights_blocks(w)
     del w
-    x = torch.from_numpy(workloads.activations(3, m, k)).to(dev)
-    xq, beta = bl.bitlinear_quantize_act(x)
-    y = torch.empty((m, n), dtype=torch.float32, device=dev)
-    ms, _ = _graph_time(torch, lambda i: bl.bitlinear_forward_blocks(xq, beta, packed, ab, y=y), 50)
-    out["batched"] = {"M": m, "K": k, "N": n, "us": round(ms * 1e3, 2),
-                      "note": "GEMV over groups of four tokens: the codes are re-read per group"}
+    copies = max(2, POOL_BYTES // (n * k // 4 + n * k // 32))
+    pool = [(packed, ab)] + [(packed.clone(), ab.clone()) for _ in range(copies - 1)]
+    out["batched"] = []
+    for m in (4, 16):
+        x = torch.from_numpy(workloads.activations(3, m, k)).to(dev)
+        xq, beta = bl.bitlinear_quantize_act(x)
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+        ms, _ = _graph_time(torch, lambda i: bl.bitlinear_forward_blocks(xq, beta, *pool[i % copies], y=y), 96)
+        out["batched"].append({"M": m, "K": k, "N": n, "us": round(ms * 1e3, 2),
+                               "kernel": "16x16x64 int8 MFMA tiles, int32 sums per block scaled in fp64"})
+    del pool
     torch.cuda.empty_cache()
     return out
 
@@ -469,7 +474,7 @@ def batched_bench(torch, bl, workloads, dev, reps=96):
         del w
         copies = max(2, (1 << 30) // (n * k // 4))
         pool = [packed] + [packed.clone() for _ in range(copies - 1)]
-        for m in (8, 16, 64):
+        for m in (2, 4, 8, 16, 64):
             x = torch.from_numpy(workloads.activations(3, m, k)).to(dev)
             xq, beta = bl.bitlinear_quantize_act(x)
             y = torch.empty((m, n), dtype=torch.float32, device=dev)

@@ -40,11 +40,16 @@ int check_forward(const int8_t* x_q, const float* beta, int64_t M, int64_t K, co
 
 enum class Path { Gemv, Decode, Gemm, DecodeSliced, Generic };
 
-// M <= 4: VALU GEMV; up to 64 tokens: weight-streaming MFMA decode kernel; more: MFMA GEMM
+// One token: the VALU GEMV.  Two to four tokens: the GEMV for matrices of 2^26 weights or
+// more, where it streams the codes faster, else the MFMA decode kernel (measured with weights
+// not in cache, M = 2: 6.8 vs 9.2 us at K=4096, N=11008; 8.4 vs 8.1 us at K=N=8192; 23.7 vs
+// 19.0 us at K=8192, N=28672).  Up to 64 tokens: the MFMA decode kernel; more: the MFMA GEMM
 // (K % 128 == 0), else the decode kernel over 64-token slices.
-Path choose_path(int64_t M, int64_t K, const int8_t* xq, const uint8_t* wp) {
+constexpr int64_t GEMV_BATCH_MIN_WEIGHTS = (int64_t)1 << 26;
+Path choose_path(int64_t M, int64_t K, int64_t N, const int8_t* xq, const uint8_t* wp) {
     if (!fast_forward_ok(K, xq, wp)) return Path::Generic;
-    if (gemv_supports(M, K)) return Path::Gemv;
+    if (gemv_supports(M, K) && (M == 1 || N * K >= GEMV_BATCH_MIN_WEIGHTS || !decode_mfma_supports(M, K)))
+        return Path::Gemv;
     if (decode_mfma_supports(M, K)) return Path::Decode;
     if (gemm_supports_k(K)) return Path::Gemm;
     return Path::DecodeSliced;
@@ -69,7 +74,7 @@ bool fused_fast_ok(int64_t M, int64_t K, const float* x, const uint8_t* wp, cons
 }
 
 int run_forward(const ForwardArgs& a, hipStream_t stream) {
-    switch (choose_path(a.M, a.K, a.xq, a.wp)) {
+    switch (choose_path(a.M, a.K, a.N, a.xq, a.wp)) {
         case Path::Gemv: return hip_status(launch_gemv_dot4(a, stream));
         case Path::Decode: return hip_status(launch_decode_mfma(a, stream));
         case Path::Gemm: return hip_status(launch_gemm_mfma(a, stream));
@@ -317,8 +322,7 @@ const char* bitlinear_forward_fused_kernel(int64_t M, int64_t K, int64_t N, cons
 
 const char* bitlinear_forward_kernel(int64_t M, int64_t K, int64_t N, const int8_t* x_q,
                                      const uint8_t* W_packed) {
-    (void)N;
-    switch (choose_path(M, K, x_q, W_packed)) {
+    switch (choose_path(M, K, N, x_q, W_packed)) {
         case Path::Gemv: return "gemv_dot4";
         case Path::Decode: return "decode_mfma_i8";
         case Path::Gemm: return "gemm_mfma_i8";

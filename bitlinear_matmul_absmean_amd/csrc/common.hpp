@@ -77,6 +77,28 @@ __device__ __forceinline__ u32x4 transpose4x4_bytes(u32x4 s) {
     return o;
 }
 
+// 4x4 byte transpose with v_perm_b32: out[i] byte j = in[j] byte i.
+__device__ __forceinline__ u32x4 transpose4x4_perm(u32x4 s) {
+    const uint32_t a01l = __builtin_amdgcn_perm(s.y, s.x, 0x05010400u);   // s0b0 s1b0 s0b1 s1b1
+    const uint32_t a01h = __builtin_amdgcn_perm(s.y, s.x, 0x07030602u);   // s0b2 s1b2 s0b3 s1b3
+    const uint32_t a23l = __builtin_amdgcn_perm(s.w, s.z, 0x05010400u);
+    const uint32_t a23h = __builtin_amdgcn_perm(s.w, s.z, 0x07030602u);
+    u32x4 o;
+    o.x = __builtin_amdgcn_perm(a23l, a01l, 0x05040100u);
+    o.y = __builtin_amdgcn_perm(a23l, a01l, 0x07060302u);
+    o.z = __builtin_amdgcn_perm(a23h, a01h, 0x05040100u);
+    o.w = __builtin_amdgcn_perm(a23h, a01h, 0x07060302u);
+    return o;
+}
+
+// Workgroup barrier that orders LDS accesses only: global loads in flight (a prefetch) stay
+// in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Sum of the four signed bytes of a dword.
 __device__ __forceinline__ int byte_sum(uint32_t v) { return dot4(v, 0x01010101u, 0); }
 

@@ -29,20 +29,6 @@
 
 namespace bitlinear {
 
-// 4x4 byte transpose with v_perm_b32: out[i] byte j = in[j] byte i.
-__device__ __forceinline__ u32x4 transpose4x4_perm(u32x4 s) {
-    const uint32_t a01l = __builtin_amdgcn_perm(s.y, s.x, 0x05010400u);   // s0b0 s1b0 s0b1 s1b1
-    const uint32_t a01h = __builtin_amdgcn_perm(s.y, s.x, 0x07030602u);   // s0b2 s1b2 s0b3 s1b3
-    const uint32_t a23l = __builtin_amdgcn_perm(s.w, s.z, 0x05010400u);
-    const uint32_t a23h = __builtin_amdgcn_perm(s.w, s.z, 0x07030602u);
-    u32x4 o;
-    o.x = __builtin_amdgcn_perm(a23l, a01l, 0x05040100u);
-    o.y = __builtin_amdgcn_perm(a23l, a01l, 0x07060302u);
-    o.z = __builtin_amdgcn_perm(a23h, a01h, 0x05040100u);
-    o.w = __builtin_amdgcn_perm(a23h, a01h, 0x07060302u);
-    return o;
-}
-
 constexpr int BD_WAVES = 8;
 
 // MT: 32-token blocks (tokens <= 32*MT); RB: 32-row blocks per workgroup.

@@ -258,14 +258,6 @@ __device__ __forceinline__ void had_stages16(float (&v)[16], int base, Blk block
     if (8 * base < (int)block) had_stage(v, 8);
 }
 
-// Workgroup barrier that orders LDS accesses only: global loads in flight (the next row's
-// prefetch) stay in flight across it.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // SCALE = false leaves the final multiply by fp32(1/sqrt(B)) to the caller.
 // t: this thread's index in the 256-thread group that rotates the chunk (every thread of the
 // workgroup must call it the same number of times: it holds workgroup barriers).

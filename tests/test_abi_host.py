@@ -165,7 +165,10 @@ def test_forward_fused_validation(bl):
 def test_kernel_selection(bl):
     sel = bl.lib.bitlinear_forward_kernel
     assert sel(1, 4096, 4096, A, A).decode() == "gemv_dot4"
-    assert sel(4, 4096, 4096, A, A).decode() == "gemv_dot4"
+    assert sel(2, 4096, 4096, A, A).decode() == "decode_mfma_i8"   # 2-4 tokens, < 2^26 weights
+    assert sel(4, 8192, 8191, A, A).decode() == "decode_mfma_i8"
+    assert sel(2, 8192, 8192, A, A).decode() == "gemv_dot4"        # 2-4 tokens, >= 2^26 weights
+    assert sel(4, 16384, 4096, A, A).decode() == "gemv_dot4"
     assert sel(5, 4096, 4096, A, A).decode() == "decode_mfma_i8"
     assert sel(64, 11008, 4096, A, A).decode() == "decode_mfma_i8"
     assert sel(65, 4096, 4096, A, A).decode() == "gemm_mfma_i8"
@@ -176,8 +179,8 @@ def test_kernel_selection(bl):
     assert sel(64, 4096, 4096, A, A + 8).decode() == "generic"   # unaligned W_packed
     assert sel(1, 32768, 64, A, A).decode() == "gemv_dot4"
     assert sel(1, 32832, 64, A, A).decode() == "decode_mfma_i8"   # K beyond the GEMV's registers
-    assert sel(4, 16384, 64, A, A).decode() == "gemv_dot4"
-    assert sel(4, 16448, 64, A, A).decode() == "decode_mfma_i8"
+    assert sel(4, 16384, 4096, A, A).decode() == "gemv_dot4"
+    assert sel(4, 16448, 4096, A, A).decode() == "decode_mfma_i8"
     fsel = bl.lib.bitlinear_forward_fused_kernel
     assert fsel(1, 4096, 4096, A, A, None).decode() == "gemv_fused"
     assert fsel(1, 4096, 4096, A, A, A + 4).decode() == "quantize_act+forward"  # x_q export unaligned

@@ -164,6 +164,8 @@ FWD_CASES = [
     # lane, N >= 4096) with 1, 3 and 4 rows per wave; 8-wave workgroups for longer rows; ragged N
     (1, 4096, 4096), (1, 4096, 11008), (1, 12288, 4097), (1, 4096, 16385), (1, 16384, 2048),
     (1, 28672, 2100), (1, 8192, 2048),
+    # two to four tokens on the GEMV (matrices of 2^26 weights or more)
+    (2, 16384, 4100), (4, 8192, 8200), (3, 4096, 16400),
     # batched decode launch shapes: 16x16x64 tiles with 1/2/4/8 row blocks per workgroup and one or
     # two token blocks, 32x32x32 tiles with 1/2; K % 256 = 64 and K % 128 = 64 tails; ragged N
     (8, 256, 9000), (12, 128, 17000), (16, 192, 5000), (9, 4160, 700), (24, 320, 4100),
@@ -544,7 +546,10 @@ def _blocks_bound_ok(y, acc_b, alpha_b, beta, y_ref):
 
 
 BLOCK_CASES = [(1, 4096, 4096), (1, 11008, 300), (2, 128, 77), (3, 4096, 1000), (4, 28672, 64), (1, 32768, 40),
-               (7, 1024, 333), (64, 2048, 130), (1, 256, 1), (9, 384, 65)]
+               (7, 1024, 333), (64, 2048, 130), (1, 256, 1), (9, 384, 65),
+               # more than four tokens: 16x16x64 tiles, one or two token tiles, 1/2/4 row blocks per
+               # workgroup, K % 256 == 128 (a lone last block), slices of 32 tokens
+               (5, 4096, 4500), (16, 640, 8300), (32, 1152, 5000), (33, 256, 100), (17, 128, 17)]
 
 
 @pytest.mark.parametrize("m,k,n", BLOCK_CASES)
