@@ -265,7 +265,7 @@ int bitlinear_forward_blocks(const int8_t* x_q, const float* beta, int64_t M, in
                              const float* alpha_blocks, int64_t N, const float* bias, float* y, hipStream_t stream) {
     int st = check_forward(x_q, beta, M, K, W_packed, alpha_blocks, N, y);
     if (st) return st;
-    if (!blocks_supports(K) || (M + 3) / 4 > 65535) return BITLINEAR_ERR_SHAPE;
+    if (!blocks_supports(K) || M > 262140) return BITLINEAR_ERR_SHAPE;
     if (!aligned(x_q, 16) || !aligned(W_packed, 16) || !aligned(alpha_blocks, 4)) return BITLINEAR_ERR_ALIGNMENT;
     return hip_status(launch_forward_blocks(x_q, beta, M, K, W_packed, alpha_blocks, N, bias, y, stream));
 }

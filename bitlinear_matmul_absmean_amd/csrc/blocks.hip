@@ -12,11 +12,11 @@
 // additions round, so S matches an fp64 sum in any order to about 1e-16 of sum |alpha acc|
 // and y almost always matches bit for bit after the one fp32 rounding.
 //
-// Decode-shaped GEMV: a workgroup stages up to four tokens of x_q in LDS (each 16-byte group
+// One or two tokens, a GEMV: a workgroup stages the tokens' x_q in LDS (each 16-byte group
 // transposed 4x4 so that a masked dword of codes meets its activations, plus the sum of x_q
 // over each 64-weight chunk), then every wave streams its own rows, one 16-byte chunk of
-// codes per lane and load.  More than four tokens run as a second grid dimension over groups
-// of four, each group reading the codes again (mostly from L2 and the Infinity Cache).
+// codes per lane and load.  Three or more tokens run on the matrix cores (below), in slices
+// of 32 tokens.
 #include "common.hpp"
 
 namespace bitlinear {
@@ -34,8 +34,8 @@ struct BlockArgs {
 
 constexpr int BW_WAVES = 8;
 
-// MT tokens per workgroup (tokens past M are zero; more tokens run as a second grid
-// dimension over groups of MT), CPL chunks of 64 weights per lane and row (K <= 4096 CPL),
+// MT tokens per workgroup (one or two; a second grid dimension over groups of MT tokens is
+// supported, tokens past M are zero), CPL chunks of 64 weights per lane and row (K <= 4096 CPL),
 // R rows per wave step with every load of the step issued first.
 template <int MT, int CPL, int R>
 __global__ __launch_bounds__(64 * BW_WAVES) void k_gemv_blocks(BlockArgs a) {

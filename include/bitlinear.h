@@ -130,8 +130,9 @@ int bitlinear_quantize_act(const float* x, int64_t M, int64_t K, int8_t* x_q, fl
  *   bias      [N] fp32 or NULL.                             (in)
  *   y         [M, N] fp32.                                  (out)
  *   acc       [M, N] int32 or NULL; when given, receives the exact integer sums.  (out)
- * The kernel is chosen by shape: M <= 4 and K <= 32768 run a VALU GEMV (dot4 on unpacked
- * codes), other M an int8 MFMA GEMM that unpacks the ternary tiles on chip.  Both fast paths
+ * The kernel is chosen by shape: one token (and two to four on matrices of 2^26 weights or
+ * more) runs a VALU GEMV (dot4 on unpacked codes); up to 64 tokens a weight-streaming int8
+ * MFMA kernel; more an int8 MFMA GEMM that unpacks the ternary tiles on chip.  The fast paths
  * need K % 64 == 0 and 16-byte aligned x_q and W_packed; other inputs run a generic kernel
  * with identical results.
  * Errors: INVALID_ARG, SHAPE (K % 4, K > BITLINEAR_MAX_K, size overflow), HIP.
@@ -229,8 +230,8 @@ int bitlinear_quantize_weights_blocks(const float* W, int64_t N, int64_t K, uint
  *   x_q [M, K] int8, beta [M] fp32 (from bitlinear_quantize_act); W_packed [N, K/4] uint8 and
  *   alpha_blocks [N, K/128] fp32 (from bitlinear_quantize_weights_blocks); bias [N] or NULL;
  *   y [M, N] fp32 (out).  x_q and W_packed 16-byte aligned, alpha_blocks 4-byte aligned.
- * K % 128 == 0, K <= 32768 and M <= 262140 (groups of four tokens in the grid).  Any M runs;
- * the kernel is a GEMV built for M <= 4, and larger M re-read the codes per four tokens.
+ * K % 128 == 0, K <= 32768 and M <= 262140.  One or two tokens run a GEMV; more run an int8
+ * MFMA kernel over slices of 32 tokens, each slice reading the codes once.
  * Errors: INVALID_ARG, SHAPE, ALIGNMENT, HIP.
  */
 int bitlinear_forward_blocks(const int8_t* x_q, const float* beta, int64_t M, int64_t K,
