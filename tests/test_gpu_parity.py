@@ -41,7 +41,10 @@ def _rel_ok(y, ref, tol=1e-5):
 
 
 # ------------------------------------------------------------------ activation quantization
-ACT_CASES = [(1, 1024), (1, 4096), (1, 11008), (3, 28672), (64, 4096), (17, 1000), (2, 6), (5, 4100)]
+ACT_CASES = [(1, 1024), (1, 4096), (1, 11008), (3, 28672), (64, 4096), (17, 1000), (2, 6), (5, 4100),
+             # one-pass kernel (K <= 32768, K % 4 == 0) with 1..8 float4 per thread, 1024 threads
+             # per token, or 256 from 256 tokens with K <= 8192; the two-pass loop beyond
+             (1, 32768), (1, 32772), (255, 12), (256, 8192), (300, 4100), (257, 8196), (40, 28676)]
 
 
 @pytest.mark.parametrize("m,k", ACT_CASES)
