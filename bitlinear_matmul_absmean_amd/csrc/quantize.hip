@@ -346,10 +346,10 @@ __device__ __forceinline__ void hadamard_chunk(float (&v)[16], Blk block_, float
 // Load thread t's 16 elements of chunk [c0, c0 + len) of a row (len % 4 == 0) in layout L0,
 // with the sign flips applied (an exact sign-bit toggle); zeros past the end.
 __device__ __forceinline__ void load_chunk(const float* __restrict__ row, const int8_t* __restrict__ signs,
-                                           int64_t c0, int len, float (&v)[16]) {
+                                           int64_t c0, int len, float (&v)[16], int t = threadIdx.x) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const int e = 4 * threadIdx.x + 1024 * q;
+        const int e = 4 * t + 1024 * q;
         float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
         uint32_t sg = 0;
         if (e < len) {
@@ -410,10 +410,10 @@ __device__ __forceinline__ uint32_t act_codes4(float x0, float x1, float x2, flo
 }
 
 __device__ __forceinline__ void store_codes(int8_t* __restrict__ xrow, int64_t c0, int len, const float (&v)[16],
-                                            float b, float y) {
+                                            float b, float y, int t = threadIdx.x) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const int e = 4 * threadIdx.x + 1024 * q;
+        const int e = 4 * t + 1024 * q;
         if (e < len)
             *reinterpret_cast<uint32_t*>(xrow + c0 + e) = act_codes4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3], b, y);
     }
@@ -471,6 +471,52 @@ __global__ __launch_bounds__(256) void k_quantize_act_hadamard(const float* __re
             hadamard_chunk(v, block, scale, buf);
             store_codes(xrow, c0, chunk_len(K, c0), v, b, y);
         }
+    }
+}
+
+// Long rows of few tokens: four groups of 256 threads rotate four chunks at once, each in
+// its own LDS buffer (dynamic, 4 x HAD_LDS floats); group g takes chunks g, g + 4, ... in
+// RND rounds.  A group without a chunk in a round rotates zeros, so every thread meets the
+// same barriers.  The rotated row stays in registers between the max and the codes.
+template <int RND>
+__global__ __launch_bounds__(1024) void k_quantize_act_hadamard_wide(const float* __restrict__ x, int64_t K,
+                                                                    int block, float scale,
+                                                                    const int8_t* __restrict__ signs,
+                                                                    int8_t* __restrict__ xq,
+                                                                    float* __restrict__ beta) {
+    extern __shared__ float hbuf[];
+    __shared__ float red[16];
+    const int64_t m = blockIdx.x;
+    const int g = threadIdx.x >> 8, t = threadIdx.x & 255;
+    const float* row = x + m * K;
+    int8_t* xrow = xq + m * K;
+    float* buf = hbuf + g * HAD_LDS;
+    float v[RND][16];
+#pragma unroll
+    for (int r = 0; r < RND; ++r) {
+        const int64_t c0 = (int64_t)(4 * r + g) * HAD_CHUNK;
+        load_chunk(row, signs, c0, c0 < K ? chunk_len(K, c0) : 0, v[r], t);
+    }
+    float mx = 0.0f;
+#pragma unroll
+    for (int r = 0; r < RND; ++r) {
+        hadamard_chunk(v[r], block, scale, buf, t);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(v[r][j]));   // zeros past K: no effect
+    }
+    mx = wave_max_f32(mx);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    float r16 = red[0];
+#pragma unroll
+    for (int w = 1; w < 16; ++w) r16 = fmaxf(r16, red[w]);
+    const float b = r16 + 1e-8f;
+    const float y = 1.0f / b;
+    if (threadIdx.x == 0) beta[m] = b;
+#pragma unroll
+    for (int r = 0; r < RND; ++r) {
+        const int64_t c0 = (int64_t)(4 * r + g) * HAD_CHUNK;
+        if (c0 < K) store_codes(xrow, c0, chunk_len(K, c0), v[r], b, y, t);
     }
 }
 
@@ -845,6 +891,11 @@ static void launch_had_pipe(const float* x, int64_t M, int block, float sc, cons
         launch_had_pipe_k<NQ, false>(x, M, block, sc, signs, xq, beta, s);
 }
 
+// Fewer tokens than this with 2..12 chunks per row take the four-group kernel (one token,
+// K = 28672: 8.9 vs 18.1 us); more keep one 256-thread workgroup per token, which fits more
+// workgroups per CU (2048 tokens, K = 11008: 26.8 vs 29.6 us).
+constexpr int64_t HAD_WIDE_ROWS = 256;
+
 hipError_t launch_quantize_act_hadamard(const float* x, int64_t M, int64_t K, int block, const int8_t* signs,
                                         int8_t* xq, float* beta, hipStream_t s) {
     const int64_t chunks = (K + HAD_CHUNK - 1) / HAD_CHUNK;
@@ -858,6 +909,13 @@ hipError_t launch_quantize_act_hadamard(const float* x, int64_t M, int64_t K, in
         launch_had_pipe<2>(x, M, block, sc, signs, xq, beta, s);
     else if (K == 1024)
         launch_had_pipe<1>(x, M, block, sc, signs, xq, beta, s);
+    else if (chunks > 1 && chunks <= 12 && M < HAD_WIDE_ROWS) {
+        const size_t lds = (size_t)4 * HAD_LDS * sizeof(float);
+        const dim3 wide(1024);
+        if (chunks <= 4) return launch_with_lds(k_quantize_act_hadamard_wide<1>, grid, wide, lds, s, x, K, block, sc, signs, xq, beta);
+        if (chunks <= 8) return launch_with_lds(k_quantize_act_hadamard_wide<2>, grid, wide, lds, s, x, K, block, sc, signs, xq, beta);
+        return launch_with_lds(k_quantize_act_hadamard_wide<3>, grid, wide, lds, s, x, K, block, sc, signs, xq, beta);
+    }
     else if (chunks == 1)
         hipLaunchKernelGGL(k_quantize_act_hadamard<1>, grid, threads, 0, s, x, K, block, sc, signs, xq, beta);
     else if (chunks == 2)
