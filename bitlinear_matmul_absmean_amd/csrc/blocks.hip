@@ -34,6 +34,29 @@ struct BlockArgs {
 
 constexpr int BW_WAVES = 8;
 
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double d) {
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(d), CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(d), CTRL, 0xF, 0xF, false);
+    return __hiloint2double(hi, lo);
+}
+
+// Wave sum in fp64 through DPP row operations (quad swaps, then the half-row and row mirrors:
+// every lane of a 16-lane row ends with the row sum) and the four row sums read from lanes
+// 0, 16, 32, 48, added as (a + b) + (c + d).  The order is fixed, so results are
+// reproducible; a lane shuffle per step would go through the LDS unit, about 100 cycles each.
+__device__ __forceinline__ double wave_sum_f64_dpp(double v) {
+    v += dpp_f64<0xB1>(v);     // quad_perm [1,0,3,2]
+    v += dpp_f64<0x4E>(v);     // quad_perm [2,3,0,1]
+    v += dpp_f64<0x141>(v);    // row_half_mirror
+    v += dpp_f64<0x140>(v);    // row_mirror
+    auto lane_f64 = [&](int l) {
+        return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
+                                __builtin_amdgcn_readlane(__double2loint(v), l));
+    };
+    return (lane_f64(0) + lane_f64(16)) + (lane_f64(32) + lane_f64(48));
+}
+
 // MT tokens per workgroup (one or two; a second grid dimension over groups of MT tokens is
 // supported, tokens past M are zero), CPL chunks of 64 weights per lane and row (K <= 4096 CPL),
 // R rows per wave step with every load of the step issued first.
@@ -104,7 +127,7 @@ __global__ __launch_bounds__(64 * BW_WAVES) void k_gemv_blocks(BlockArgs a) {
             const int64_t row = rb + r;
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-                const double sum = wave_sum_f64(f[m]);
+                const double sum = wave_sum_f64_dpp(f[m]);
                 if (lane == m && row < r1 && m0 + m < a.M) {
                     float v = (float)(sum * tm[m]);
                     if (a.bias) v = v + a.bias[row];
@@ -343,13 +366,17 @@ static hipError_t launch_blocks_r(const BlockArgs& a, int64_t groups, hipStream_
                            a);
 }
 
-// Rows are spread over about two workgroups per CU (512 x 8 waves); a wave's step holds up to
-// 8 chunk loads per lane, so R rows of CPL chunks with R * CPL <= 8 and R <= the wave's rows.
+// Rows are spread over 1024 workgroups of 8 waves (four per CU) for rows of up to two chunks
+// per lane (K <= 8192), over 512 for longer rows, which gain from two rows per wave in the
+// double-buffered walk (measured with weights not in cache, one token: 5.9 vs 7.1 us at
+// K = 4096, N = 11008; 16.2 vs 16.8 us at K = 28672, N = 8192).  A wave's step holds up to 8
+// chunk loads per lane, so R rows of CPL chunks with R * CPL <= 8 and R <= the wave's rows.
 template <int MT, int CPL>
 static hipError_t launch_blocks_mt(const BlockArgs& a0, int64_t groups, hipStream_t s) {
     BlockArgs a = a0;
     constexpr int RMAX = CPL >= 8 ? 1 : 8 / CPL;
-    a.rows_per_wave = (a.N + 512 * BW_WAVES - 1) / (512 * BW_WAVES);
+    constexpr int64_t WGS = CPL <= 2 ? 1024 : 512;
+    a.rows_per_wave = (a.N + WGS * BW_WAVES - 1) / (WGS * BW_WAVES);
     if (RMAX >= 8 && a.rows_per_wave >= 8) return launch_blocks_r<MT, CPL, (RMAX >= 8 ? 8 : 1)>(a, groups, s);
     if (RMAX >= 4 && a.rows_per_wave >= 4) return launch_blocks_r<MT, CPL, (RMAX >= 4 ? 4 : 1)>(a, groups, s);
     if (RMAX >= 2 && a.rows_per_wave >= 2) return launch_blocks_r<MT, CPL, (RMAX >= 2 ? 2 : 1)>(a, groups, s);
