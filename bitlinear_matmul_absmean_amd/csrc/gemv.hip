@@ -154,6 +154,21 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(GemvArgs g) {
     };
     u32x4 wa[R][CPL], wb[SINGLE ? 1 : R][SINGLE ? 1 : CPL];
     float beta_t[MT];
+    // Scalars and per-row values are loaded ahead of the weights they go with: a wave's loads
+    // complete in order, so a load issued after a weight prefetch makes its first use wait
+    // for the whole prefetch.  The per-tensor alpha is read before anything else; a step's
+    // per-row alpha and bias (for the lane that finishes row r0 + lane / MT) just before its
+    // weight rows.  The loads are unconditional (element 0 when unused), so that no use of
+    // them is moved up next to them.
+    const float alpha0 = a.alpha[0];
+    const float* bias_src = a.bias ? a.bias : a.alpha;
+    struct RowAux { float al, bi; };
+    auto load_aux = [&](int64_t r0) {
+        const int rr = lane / MT < R ? lane / MT : R - 1;
+        const int64_t row = r0 + rr < re ? r0 + rr : re - 1;
+        return RowAux{a.alpha[a.alpha_per_row ? row : 0], bias_src[a.bias ? row : 0]};
+    };
+    RowAux auxa, auxb;
     if constexpr (FUSED) {
         constexpr bool KEEP = UPT <= 4;       // keep x in registers between the two passes
         float4 xv[KEEP ? UPT : 1][4];
@@ -168,6 +183,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(GemvArgs g) {
                 for (int e = 0; e < 4; ++e) xv[k][e] = src[e];
             }
         }
+        auxa = load_aux(rb);
         load_rows(wa, rb);
         float mx[MT];
 #pragma unroll
@@ -248,6 +264,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(GemvArgs g) {
             const bool valid = unit_at(tid + NT * k, t, c, q);
             xr[k] = *reinterpret_cast<const u32x4*>(a.xq + (valid ? t * K + 64 * c + 16 * q : 0));
         }
+        auxa = load_aux(rb);
         load_rows(wa, rb);
 #pragma unroll
         for (int k = 0; k < UPT; ++k) {
@@ -271,17 +288,16 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(GemvArgs g) {
     __syncthreads();
     int xsum[MT];
     float sc[MT];
-    const float alpha0 = a.alpha_per_row ? 0.0f : a.alpha[0];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
         xsum[t] = 0;
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) xsum[t] += red_i[t][w];
-        sc[t] = dequant_scale(alpha0, beta_t[t]);
+        sc[t] = a.alpha_per_row ? 0.0f : dequant_scale(alpha0, beta_t[t]);
     }
 
     // ---- reduce R rows held in w, finish them ------------------------------------------
-    auto finish_rows = [&](const u32x4 (&w)[R][CPL], int64_t r0) {
+    auto finish_rows = [&](const u32x4 (&w)[R][CPL], const RowAux& aux, int64_t r0) {
         int s0[R][MT], s1[R][MT], s2[R][MT], s3[R][MT];
 #pragma unroll
         for (int r = 0; r < R; ++r)
@@ -331,8 +347,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(GemvArgs g) {
             const int64_t n = r0 + my_r;
             if (n < re && my_t < M) {
                 const int total = mine - my_xsum;
-                const float s = a.alpha_per_row ? dequant_scale(a.alpha[n], my_beta) : my_sc;
-                a.y[my_t * N + n] = activate(dequant(total, s, a.bias, n), a.act);
+                const float s = a.alpha_per_row ? dequant_scale(aux.al, my_beta) : my_sc;
+                float v = (float)total * s;
+                if (a.bias) v = v + aux.bi;
+                a.y[my_t * N + n] = activate(v, a.act);
                 if (a.acc) a.acc[my_t * N + n] = total;
             }
         }
@@ -341,14 +359,17 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(GemvArgs g) {
     // ---- walk the row range, two register buffers in turn -------------------------------
     if constexpr (SINGLE) {
         (void)wb;
-        if (rb < re) finish_rows(wa, rb);
+        (void)auxb;
+        if (rb < re) finish_rows(wa, auxa, rb);
     } else {
         for (int64_t r0 = rb; r0 < re; r0 += 2 * R) {
+            auxb = load_aux(r0 + R);
             load_rows(wb, r0 + R);
-            finish_rows(wa, r0);
+            finish_rows(wa, auxa, r0);
             if (r0 + R >= re) break;
+            auxa = load_aux(r0 + 2 * R);
             load_rows(wa, r0 + 2 * R);
-            finish_rows(wb, r0 + R);
+            finish_rows(wb, auxb, r0 + R);
         }
     }
 }
