@@ -95,12 +95,14 @@ __global__ __launch_bounds__(64 * BW_WAVES) void k_gemv_blocks(BlockArgs a) {
     const int64_t r0 = ((int64_t)blockIdx.x * BW_WAVES + wave) * a.rows_per_wave;
     const int64_t r1 = r0 + a.rows_per_wave < N ? r0 + a.rows_per_wave : N;
     const u32x4* wp = reinterpret_cast<const u32x4*>(a.wp);
+    const float* bias_src = a.bias ? a.bias : a.alpha;
     for (int64_t rb = r0; rb < r1; rb += R) {
         u32x4 w[R][CPL];
-        float al[R][CPL];
+        float al[R][CPL], bi[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int64_t row = rb + r < r1 ? rb + r : r1 - 1;      // clamped: loads stay branch-free
+            bi[r] = bias_src[a.bias ? row : 0];                       // with the step's loads
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
                 const int c = lane + 64 * j < K64 ? lane + 64 * j : 0;
@@ -130,7 +132,7 @@ __global__ __launch_bounds__(64 * BW_WAVES) void k_gemv_blocks(BlockArgs a) {
                 const double sum = wave_sum_f64_dpp(f[m]);
                 if (lane == m && row < r1 && m0 + m < a.M) {
                     float v = (float)(sum * tm[m]);
-                    if (a.bias) v = v + a.bias[row];
+                    if (a.bias) v = v + bi[r];
                     a.y[(m0 + m) * N + row] = v;
                 }
             }
@@ -157,6 +159,7 @@ __global__ __launch_bounds__(BB_WAVES * 64) void k_bdec16_blocks(BlockArgs a) {
     // LDS: the workgroup's alpha rows (stride KB + 1: the 16 rows a load reads fall in distinct
     // banks) during the K loop, then the waves' fp64 tiles [wave][RB * MT][4][64]
     extern __shared__ double redd[];
+    __shared__ double bsc[16 * MT];                // beta[m] / 127 of the slice's tokens
     float* as = reinterpret_cast<float*>(redd);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -165,6 +168,13 @@ __global__ __launch_bounds__(BB_WAVES * 64) void k_bdec16_blocks(BlockArgs a) {
     const int KB = (int)(K >> 7), KBp = KB + 1;
     const int64_t n0 = (int64_t)blockIdx.x * (16 * RB);
     const int rows = (int)(N - n0 < 16 * RB ? N - n0 : 16 * RB);
+    // the epilogue's per-token beta and this thread's bias (element e = tid of the epilogue,
+    // see below) are loaded before anything else: a wave's loads complete in order, so a load
+    // issued later would make its use wait for every load in flight
+    const float beta_ld = a.beta[tid < M ? tid : M - 1];
+    const float* bias_src = a.bias ? a.bias : a.alpha;
+    const int64_t nb_e = n0 + 16 * ((tid >> 6) / MT) + (tid & 15);
+    const float bias_e = bias_src[a.bias && tid < RB * MT * 64 ? (nb_e < N ? nb_e : N - 1) : 0];
     const int lr = lane & 15, lg = lane >> 4;
     const int SP = (int)((K + 255) / 256);
     const int s0 = (int)((int64_t)SP * wave / BB_WAVES), s1 = (int)((int64_t)SP * (wave + 1) / BB_WAVES);
@@ -293,6 +303,7 @@ __global__ __launch_bounds__(BB_WAVES * 64) void k_bdec16_blocks(BlockArgs a) {
     load(1, min(s0 + 1, last));
     __builtin_amdgcn_sched_barrier(0);
     if (one_batch) alpha_store(av0, 0);
+    if (tid < 16 * MT) bsc[tid] = (double)beta_ld / 127.0;
     lds_barrier();
     if (s0 < s1) {
         int s = s0;
@@ -316,21 +327,23 @@ __global__ __launch_bounds__(BB_WAVES * 64) void k_bdec16_blocks(BlockArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) redd[(((wave * RB * MT) + r * MT + t) * 4 + i) * 64 + lane] = f[r][t][i];
     __syncthreads();
-    for (int e = tid; e < RB * MT * 64; e += BB_WAVES * 64) {
-        const int l = e & 63, tile = e >> 6;
+    static_assert(RB * MT * 64 <= BB_WAVES * 64, "one epilogue element per thread");
+    if (tid < RB * MT * 64) {
+        const int l = tid & 63, tile = tid >> 6;
         const int r = tile / MT, t = tile % MT;
         const int64_t n = n0 + 16 * r + (l & 15);
-        if (n >= N) continue;
+        if (n < N) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = 16 * t + 4 * (l >> 4) + i;
-            if (m >= M) continue;
-            double sum = 0.0;
+            for (int i = 0; i < 4; ++i) {
+                const int m = 16 * t + 4 * (l >> 4) + i;
+                if (m >= M) continue;
+                double sum = 0.0;
 #pragma unroll
-            for (int w = 0; w < BB_WAVES; ++w) sum += redd[((w * RB * MT + tile) * 4 + i) * 64 + l];
-            float v = (float)(sum * ((double)a.beta[m] / 127.0));
-            if (a.bias) v = v + a.bias[n];
-            a.y[(int64_t)m * N + n] = v;
+                for (int w = 0; w < BB_WAVES; ++w) sum += redd[((w * RB * MT + tile) * 4 + i) * 64 + l];
+                float v = (float)(sum * bsc[m]);
+                if (a.bias) v = v + bias_e;
+                a.y[(int64_t)m * N + n] = v;
+            }
         }
     }
 }
