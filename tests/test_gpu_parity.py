@@ -211,6 +211,39 @@ def test_forward_bias_and_rows(dev, m, k, n):
     assert np.array_equal(yr.cpu().numpy(), yr_o)
 
 
+# Row ranges longer than one step of the decode GEMV (two register buffers in turn), with
+# per-row alpha and a bias, whose loads travel with each step's weight rows: (M, K, N, call).
+@pytest.mark.parametrize("m,k,n,call", [(1, 8192, 30000, "forward"), (1, 28672, 5000, "forward"),
+                                        (2, 8192, 8200, "forward"), (1, 8192, 30000, "fused")])
+def test_forward_rows_bias_multistep(dev, m, k, n, call):
+    torch, bl = dev
+    _say(f"{call} rows+bias M={m} K={k} N={n}")
+    xq, codes, packed, beta, alpha = _random_operands(m, k, n, seed=11)
+    rs = np.random.default_rng(12)
+    bias = rs.standard_normal(n).astype(np.float32)
+    ar = rs.uniform(0.01, 0.02, size=n).astype(np.float32)
+    if call == "fused":
+        x = workloads.activations(12, m, k)
+        xq, beta = oracle.quantize_act(x)
+        assert bl.bitlinear_forward_fused_kernel(m, k, n, _to(torch, x)) == "gemv_fused"
+    else:
+        assert bl.bitlinear_forward_kernel(m, k, n) == "gemv_dot4"
+    acc_o = oracle.ternary_matmul(xq, codes)
+    yr_o = oracle.dequant(acc_o, beta, alpha_rows=ar, bias=bias)
+    y_o = oracle.dequant(acc_o, beta, alpha, bias=bias)
+    pk, art, bt = _to(torch, packed), _to(torch, ar), _to(torch, bias)
+    if call == "fused":
+        yr = bl.bitlinear_forward_fused_rows(_to(torch, x), pk, art, bias=bt)
+        y = bl.bitlinear_forward_fused(_to(torch, x), pk, _to(torch, np.array([alpha], np.float32)), bias=bt)
+    else:
+        args = (_to(torch, xq), _to(torch, beta), pk)
+        yr = bl.bitlinear_forward_rows(*args, art, bias=bt)
+        y = bl.bitlinear_forward(*args, _to(torch, np.array([alpha], np.float32)), bias=bt)
+    torch.cuda.synchronize()
+    assert np.array_equal(yr.cpu().numpy(), yr_o)
+    assert np.array_equal(y.cpu().numpy(), y_o)
+
+
 def test_forward_extreme_values(dev):
     """|acc| = 127*K at the largest workload K, and every weight pattern."""
     torch, bl = dev
