@@ -754,6 +754,23 @@ def test_forward_fused_hadamard_parity(dev, m, k, n, block):
     assert np.array_equal(y.cpu().numpy().view(np.uint32), r["y"].view(np.uint32))
 
 
+# without a sign vector (a plain Sylvester rotation): one and two chunks, with and without bias
+@pytest.mark.parametrize("k,n,block", [(4096, 301, 4096), (8192, 300, 2048), (12288, 77, 4096)])
+def test_forward_fused_hadamard_without_signs(dev, k, n, block):
+    torch, bl = dev
+    _say(f"forward_fused_hadamard no signs K={k} N={n} B={block}")
+    w = workloads.weights(73, n, k)
+    x = workloads.activations_with_outliers(73, 1, k)
+    bias = workloads.activations(74, 1, n)[0] if n % 2 else None
+    r = oracle.bitlinear_hadamard(x, w, block, None, bias=bias)
+    packed, alpha = bl.bitlinear_quantize_weights(bl.bitlinear_hadamard_rows(_to(torch, w), block, None))
+    y = bl.bitlinear_forward_fused_hadamard(_to(torch, x), block, None, packed, alpha,
+                                            bias=None if bias is None else _to(torch, bias))
+    torch.cuda.synchronize()
+    assert np.array_equal(packed.cpu().numpy(), r["packed"])
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), r["y"].view(np.uint32))
+
+
 def test_forward_fused_hadamard_without_outputs(dev):
     """The single-launch path needs no x_q / beta buffers."""
     torch, bl = dev
