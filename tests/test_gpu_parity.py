@@ -585,7 +585,10 @@ BLOCK_CASES = [(1, 4096, 4096), (1, 11008, 300), (2, 128, 77), (3, 4096, 1000), 
                (7, 1024, 333), (64, 2048, 130), (1, 256, 1), (9, 384, 65),
                # more than four tokens: 16x16x64 tiles, one or two token tiles, 1/2/4 row blocks per
                # workgroup, K % 256 == 128 (a lone last block), slices of 32 tokens
-               (5, 4096, 4500), (16, 640, 8300), (32, 1152, 5000), (33, 256, 100), (17, 128, 17)]
+               (5, 4096, 4500), (16, 640, 8300), (32, 1152, 5000), (33, 256, 100), (17, 128, 17),
+               # the largest K (alpha rows of 257 floats per row in LDS), and four row blocks at a
+               # K whose alpha rows take 33 KB of LDS
+               (5, 32768, 70), (4, 16384, 8300)]
 
 
 @pytest.mark.parametrize("m,k,n", BLOCK_CASES)
