@@ -604,7 +604,8 @@ def kernel_only(kind: str, launches: int):
     """Run only one kernel, `launches` times, for counter collection under rocprofv3:
     gemv_fused = the roofline kernel (decode GEMV, K=4096, N=11008, weights rotating through
     64 copies so every launch reads HBM); copy = a plain 256 MiB device copy (calibrates
-    FETCH_SIZE / WRITE_SIZE); gemm = the prefill GEMM (M=2048, K=4096, N=11008)."""
+    FETCH_SIZE / WRITE_SIZE); gemm = the prefill GEMM (M=2048, K=4096, N=11008); batched =
+    the batched decode kernel at M=64, K=4096, N=11008 (weights rotating through 32 copies)."""
     import torch
     import bitlinear_matmul_absmean_amd as bl
     import workloads
@@ -632,6 +633,21 @@ def kernel_only(kind: str, launches: int):
             bl.bitlinear_forward_fused(x, pool[i % len(pool)], alpha, y=y)
         torch.cuda.synchronize()
         log(f"gemv_fused: {launches} launches of {bl.bitlinear_forward_fused_kernel(1, k, n, x, packed)}")
+        return
+    if kind == "batched":
+        m, k, n = 64, 4096, 11008
+        w = torch.from_numpy(workloads.weights(3, n, k)).to(dev)
+        packed, alpha = bl.bitlinear_quantize_weights(w)
+        del w
+        pool = [packed] + [packed.clone() for _ in range(31)]
+        x = torch.from_numpy(workloads.activations(3, m, k)).to(dev)
+        xq, beta = bl.bitlinear_quantize_act(x)
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        for i in range(launches):
+            bl.bitlinear_forward(xq, beta, pool[i % len(pool)], alpha, y=y)
+        torch.cuda.synchronize()
+        log(f"batched: {launches} launches of {bl.bitlinear_forward_kernel(m, k, n, xq, packed)}")
         return
     if kind == "gemm":
         m, k, n = 2048, 4096, 11008
@@ -709,7 +725,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extras", action="store_true", help="headline workload and roofline only")
     ap.add_argument("--no-chain", action="store_true", help="skip the 70B-class chain")
-    ap.add_argument("--kernel-only", choices=["gemv_fused", "copy", "gemm"],
+    ap.add_argument("--kernel-only", choices=["gemv_fused", "copy", "gemm", "batched"],
                     help="run only this kernel (for rocprofv3 counter runs)")
     ap.add_argument("--launches", type=int, default=50)
     ap.add_argument("--pmc-summary", nargs=4, metavar=("GEMV_FETCH", "GEMV_WRITE", "COPY_FETCH", "COPY_WRITE"),
