@@ -41,14 +41,16 @@ int check_forward(const int8_t* x_q, const float* beta, int64_t M, int64_t K, co
 enum class Path { Gemv, Decode, Gemm, DecodeSliced, Generic };
 
 // One token: the VALU GEMV.  Two to four tokens: the GEMV for matrices of 2^26 weights or
-// more, where it streams the codes faster, else the MFMA decode kernel (measured with weights
-// not in cache, M = 2: 6.8 vs 9.2 us at K=4096, N=11008; 8.4 vs 8.1 us at K=N=8192; 23.7 vs
-// 19.0 us at K=8192, N=28672).  Up to 64 tokens: the MFMA decode kernel; more: the MFMA GEMM
-// (K % 128 == 0), else the decode kernel over 64-token slices.
+// more, and for two tokens with K >= 8192, where it streams the codes faster; else the MFMA
+// decode kernel (measured with weights not in cache: M = 4, 7.2 vs 9.6 us at K = 4096,
+// N = 11008; M = 2, 4.2 vs 4.9 us at K = N = 4096, 5.9 vs 6.8 us at K = 11008, N = 4096;
+// 13.8 vs 23.7 us at K = 8192, N = 28672).  Up to 64 tokens: the MFMA decode kernel; more:
+// the MFMA GEMM (K % 128 == 0), else the decode kernel over 64-token slices.
 constexpr int64_t GEMV_BATCH_MIN_WEIGHTS = (int64_t)1 << 26;
 Path choose_path(int64_t M, int64_t K, int64_t N, const int8_t* xq, const uint8_t* wp) {
     if (!fast_forward_ok(K, xq, wp)) return Path::Generic;
-    if (gemv_supports(M, K) && (M == 1 || N * K >= GEMV_BATCH_MIN_WEIGHTS || !decode_mfma_supports(M, K)))
+    if (gemv_supports(M, K) && (M == 1 || (M == 2 && K >= 8192) || N * K >= GEMV_BATCH_MIN_WEIGHTS ||
+                                !decode_mfma_supports(M, K)))
         return Path::Gemv;
     if (decode_mfma_supports(M, K)) return Path::Decode;
     if (gemm_supports_k(K)) return Path::Gemm;

@@ -392,7 +392,14 @@ static int64_t rows_per_step(int64_t rpw) {      // the single-step row counts i
 
 GemvShape gemv_shape(int64_t M, int64_t K, int64_t N, bool fused) {
     GemvShape sh{4, 2048};
-    if (M != 1) return sh;
+    if (M != 1) {
+        // several tokens, fused: every workgroup reads all M rows of fp32 x (twice when they do
+        // not fit its registers), so 128 workgroups of 8 waves (measured with weights not in
+        // cache, four tokens: 19.1 vs 32.7 us at K = 11008, N = 4096; 29.6 vs 47.7 us at
+        // K = 16384, N = 8192)
+        if (fused && N >= 8 * 256) sh = GemvShape{8, 1024};
+        return sh;
+    }
     const int64_t cpl = (K / 64 + 63) / 64;
     GemvShape want;
     if (!fused)
@@ -470,6 +477,17 @@ static hipError_t launch_m1(const GemvArgs& g, hipStream_t s) {
     }
 }
 
+// Two tokens in their own instances: the four-token kernel would do twice the dot products.
+template <bool FUSED>
+static hipError_t launch_m2(const GemvArgs& g, hipStream_t s) {
+    switch ((g.C + 63) / 64) {
+        case 1: return launch_cpl<2, 1, FUSED>(g, s);
+        case 2: return launch_cpl<2, 2, FUSED>(g, s);
+        case 3: return launch_cpl<2, 3, FUSED>(g, s);
+        default: return launch_cpl<2, 4, FUSED>(g, s);
+    }
+}
+
 template <bool FUSED>
 static hipError_t launch_m4(const GemvArgs& g, hipStream_t s) {
     switch ((g.C + 63) / 64) {
@@ -489,12 +507,12 @@ bool gemv_supports(int64_t M, int64_t K) {
 
 hipError_t launch_gemv_dot4(const ForwardArgs& a, hipStream_t s) {
     GemvArgs g{a, nullptr, nullptr, nullptr, (int)(a.K / 64), 0};
-    return a.M == 1 ? launch_m1<false>(g, s) : launch_m4<false>(g, s);
+    return a.M == 1 ? launch_m1<false>(g, s) : a.M == 2 ? launch_m2<false>(g, s) : launch_m4<false>(g, s);
 }
 
 hipError_t launch_gemv_fused(const ForwardArgs& a, const float* x, int8_t* xq_out, float* beta_out, hipStream_t s) {
     GemvArgs g{a, x, xq_out, beta_out, (int)(a.K / 64), 0};
-    return a.M == 1 ? launch_m1<true>(g, s) : launch_m4<true>(g, s);
+    return a.M == 1 ? launch_m1<true>(g, s) : a.M == 2 ? launch_m2<true>(g, s) : launch_m4<true>(g, s);
 }
 
 }  // namespace bitlinear

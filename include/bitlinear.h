@@ -130,8 +130,8 @@ int bitlinear_quantize_act(const float* x, int64_t M, int64_t K, int8_t* x_q, fl
  *   bias      [N] fp32 or NULL.                             (in)
  *   y         [M, N] fp32.                                  (out)
  *   acc       [M, N] int32 or NULL; when given, receives the exact integer sums.  (out)
- * The kernel is chosen by shape: one token (and two to four on matrices of 2^26 weights or
- * more) runs a VALU GEMV (dot4 on unpacked codes); up to 64 tokens a weight-streaming int8
+ * The kernel is chosen by shape: one token (two to four on matrices of 2^26 weights or more,
+ * two with K >= 8192) runs a VALU GEMV (dot4 on unpacked codes); up to 64 tokens a weight-streaming int8
  * MFMA kernel; more an int8 MFMA GEMM that unpacks the ternary tiles on chip.  The fast paths
  * need K % 64 == 0 and 16-byte aligned x_q and W_packed; other inputs run a generic kernel
  * with identical results.

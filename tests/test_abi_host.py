@@ -166,6 +166,8 @@ def test_kernel_selection(bl):
     sel = bl.lib.bitlinear_forward_kernel
     assert sel(1, 4096, 4096, A, A).decode() == "gemv_dot4"
     assert sel(2, 4096, 4096, A, A).decode() == "decode_mfma_i8"   # 2-4 tokens, < 2^26 weights
+    assert sel(2, 8192, 1000, A, A).decode() == "gemv_dot4"         # two tokens with K >= 8192
+    assert sel(3, 8192, 1000, A, A).decode() == "decode_mfma_i8"
     assert sel(4, 8192, 8191, A, A).decode() == "decode_mfma_i8"
     assert sel(2, 8192, 8192, A, A).decode() == "gemv_dot4"        # 2-4 tokens, >= 2^26 weights
     assert sel(4, 16384, 4096, A, A).decode() == "gemv_dot4"
