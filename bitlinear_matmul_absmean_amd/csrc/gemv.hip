@@ -394,10 +394,11 @@ GemvShape gemv_shape(int64_t M, int64_t K, int64_t N, bool fused) {
     GemvShape sh{4, 2048};
     if (M != 1) {
         // several tokens, fused: every workgroup reads all M rows of fp32 x (twice when they do
-        // not fit its registers), so 128 workgroups of 8 waves (measured with weights not in
-        // cache, four tokens: 19.1 vs 32.7 us at K = 11008, N = 4096; 29.6 vs 47.7 us at
-        // K = 16384, N = 8192)
-        if (fused && N >= 8 * 256) sh = GemvShape{8, 1024};
+        // not fit its registers), so half the workgroups: 1024 waves, 256 workgroups of 4
+        // (several-token instances exist with 4 waves only; with 8 or 16 they spill).  Measured
+        // with weights not in cache, four tokens: 19.1 vs 32.7 us at K = 11008, N = 4096; 29.6
+        // vs 47.7 us at K = 16384, N = 8192; 512 waves is slower again (22.4 and 39.2 us).
+        if (fused && N >= 8 * 256) sh = GemvShape{4, 1024};
         return sh;
     }
     const int64_t cpl = (K / 64 + 63) / 64;
