@@ -478,14 +478,15 @@ static hipError_t launch_m1(const GemvArgs& g, hipStream_t s) {
     }
 }
 
-// Two tokens in their own instances: the four-token kernel would do twice the dot products.
-template <bool FUSED>
-static hipError_t launch_m2(const GemvArgs& g, hipStream_t s) {
+// Two and three tokens in their own instances: the four-token kernel would do up to twice
+// the dot products.
+template <int MT, bool FUSED>
+static hipError_t launch_mt(const GemvArgs& g, hipStream_t s) {
     switch ((g.C + 63) / 64) {
-        case 1: return launch_cpl<2, 1, FUSED>(g, s);
-        case 2: return launch_cpl<2, 2, FUSED>(g, s);
-        case 3: return launch_cpl<2, 3, FUSED>(g, s);
-        default: return launch_cpl<2, 4, FUSED>(g, s);
+        case 1: return launch_cpl<MT, 1, FUSED>(g, s);
+        case 2: return launch_cpl<MT, 2, FUSED>(g, s);
+        case 3: return launch_cpl<MT, 3, FUSED>(g, s);
+        default: return launch_cpl<MT, 4, FUSED>(g, s);
     }
 }
 
@@ -508,12 +509,14 @@ bool gemv_supports(int64_t M, int64_t K) {
 
 hipError_t launch_gemv_dot4(const ForwardArgs& a, hipStream_t s) {
     GemvArgs g{a, nullptr, nullptr, nullptr, (int)(a.K / 64), 0};
-    return a.M == 1 ? launch_m1<false>(g, s) : a.M == 2 ? launch_m2<false>(g, s) : launch_m4<false>(g, s);
+    return a.M == 1 ? launch_m1<false>(g, s) : a.M == 2 ? launch_mt<2, false>(g, s)
+         : a.M == 3 ? launch_mt<3, false>(g, s) : launch_m4<false>(g, s);
 }
 
 hipError_t launch_gemv_fused(const ForwardArgs& a, const float* x, int8_t* xq_out, float* beta_out, hipStream_t s) {
     GemvArgs g{a, x, xq_out, beta_out, (int)(a.K / 64), 0};
-    return a.M == 1 ? launch_m1<true>(g, s) : a.M == 2 ? launch_m2<true>(g, s) : launch_m4<true>(g, s);
+    return a.M == 1 ? launch_m1<true>(g, s) : a.M == 2 ? launch_mt<2, true>(g, s)
+         : a.M == 3 ? launch_mt<3, true>(g, s) : launch_m4<true>(g, s);
 }
 
 }  // namespace bitlinear

@@ -168,7 +168,7 @@ FWD_CASES = [
     (1, 4096, 4096), (1, 4096, 11008), (1, 12288, 4097), (1, 4096, 16385), (1, 16384, 2048),
     (1, 28672, 2100), (1, 8192, 2048),
     # two to four tokens on the GEMV (matrices of 2^26 weights or more; two tokens with K >= 8192)
-    (2, 16384, 4100), (4, 8192, 8200), (3, 4096, 16400), (2, 8192, 1000), (2, 11008, 4099),
+    (2, 16384, 4100), (4, 8192, 8200), (3, 4096, 16400), (2, 8192, 1000), (2, 11008, 4099), (3, 16384, 4200),
     # batched decode launch shapes: 16x16x64 tiles with 1/2/4/8 row blocks per workgroup and one or
     # two token blocks, 32x32x32 tiles with 1/2; K % 256 = 64 and K % 128 = 64 tails; ragged N
     (8, 256, 9000), (12, 128, 17000), (16, 192, 5000), (9, 4160, 700), (24, 320, 4100),
