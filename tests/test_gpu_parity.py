@@ -789,3 +789,85 @@ def test_forward_fused_hadamard_without_outputs(dev):
     y = bl.bitlinear_forward_fused_hadamard(_to(torch, x), block, dt, packed, alpha)
     torch.cuda.synchronize()
     assert np.array_equal(y.cpu().numpy().view(np.uint32), r["y"].view(np.uint32))
+
+
+# ------------------------------------------------------------------ seeded random shapes
+# Shapes drawn around every dispatch boundary (token counts 1-4 on the GEMV, 2-4 on the MFMA
+# decode kernel below 2^26 weights, 5-64 on the batched decode tiles, slices of 32 and 64,
+# the GEMM from 65 tokens; K multiples of 4, 64 and 128, ragged N), each call against the
+# oracle bit for bit (block scales: the bound above).
+_RS_TOKENS = [1, 1, 2, 3, 4, 5, 8, 16, 17, 31, 32, 33, 48, 64, 65, 70, 129]
+
+
+def _rs_shapes(seed, count, k_mult, k_max=2304, n_max=700):
+    g = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        m = int(g.choice(_RS_TOKENS))
+        k = int(g.integers(1, k_max // k_mult + 1)) * k_mult
+        n = int(g.integers(1, n_max + 1))
+        out.append((m, k, n))
+    return out
+
+
+@pytest.mark.parametrize("m,k,n", _rs_shapes(101, 12, 4) + _rs_shapes(102, 14, 64) + _rs_shapes(103, 8, 128, 4096))
+def test_random_shapes_forward(dev, m, k, n):
+    torch, bl = dev
+    _say(f"random forward M={m} K={k} N={n} kernel={bl.bitlinear_forward_kernel(m, k, n)}")
+    xq, codes, packed, beta, alpha = _random_operands(m, k, n, seed=m * 131 + k * 7 + n)
+    rs = np.random.default_rng(k + n)
+    bias = rs.standard_normal(n).astype(np.float32)
+    ar = rs.uniform(0.01, 0.02, size=n).astype(np.float32)
+    acc_o = oracle.ternary_matmul(xq, codes)
+    args = (_to(torch, xq), _to(torch, beta), _to(torch, packed))
+    y, acc = bl.bitlinear_forward(*args, _to(torch, np.array([alpha], np.float32)), acc=True)
+    yr = bl.bitlinear_forward_rows(*args, _to(torch, ar), bias=_to(torch, bias))
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), acc_o)
+    assert np.array_equal(y.cpu().numpy(), oracle.dequant(acc_o, beta, alpha))
+    assert np.array_equal(yr.cpu().numpy(), oracle.dequant(acc_o, beta, alpha_rows=ar, bias=bias))
+
+
+@pytest.mark.parametrize("m,k,n", _rs_shapes(104, 10, 4) + _rs_shapes(105, 10, 64))
+def test_random_shapes_fused(dev, m, k, n):
+    torch, bl = dev
+    x = workloads.activations_with_outliers(m + k, m, k)
+    _say(f"random fused M={m} K={k} N={n}")
+    _, codes, packed, _, alpha = _random_operands(m, k, n, seed=m * 17 + k + n)
+    xq_o, beta_o = oracle.quantize_act(x)
+    y_o = oracle.dequant(oracle.ternary_matmul(xq_o, codes), beta_o, alpha)
+    xq = torch.empty((m, k), dtype=torch.int8, device="cuda")
+    beta = torch.empty(m, dtype=torch.float32, device="cuda")
+    y = bl.bitlinear_forward_fused(_to(torch, x), _to(torch, packed), _to(torch, np.array([alpha], np.float32)),
+                                   x_q=xq, beta=beta)
+    torch.cuda.synchronize()
+    assert np.array_equal(xq.cpu().numpy(), xq_o)
+    assert np.array_equal(beta.cpu().numpy().view(np.uint32), beta_o.view(np.uint32))
+    assert np.array_equal(y.cpu().numpy(), y_o)
+
+
+@pytest.mark.parametrize("m,k,n", _rs_shapes(106, 12, 128, 4096))
+def test_random_shapes_blocks(dev, m, k, n):
+    torch, bl = dev
+    _say(f"random blocks M={m} K={k} N={n}")
+    w = _block_w(m + n, n, k)
+    x = workloads.activations_with_outliers(m + n, m, k)
+    _, packed, a = oracle.quantize_weights_blocks(w)
+    xq, beta = oracle.quantize_act(x)
+    acc_b, y_ref = oracle.forward_blocks(xq, beta, packed, k, a)
+    y = bl.bitlinear_forward_blocks(_to(torch, xq), _to(torch, beta), _to(torch, packed), _to(torch, a))
+    torch.cuda.synchronize()
+    ok, same = _blocks_bound_ok(y.cpu().numpy(), acc_b, a, beta, y_ref)
+    assert ok and same >= 0.99
+
+
+@pytest.mark.parametrize("m,k,n", _rs_shapes(107, 8, 4))
+def test_random_shapes_t5(dev, m, k, n):
+    torch, bl = dev
+    _say(f"random t5 M={m} K={k} N={n}")
+    xq, codes, _, beta, alpha = _random_operands(m, k, n, seed=m + k * 3 + n)
+    t5 = oracle.pack_t5(codes)
+    _, y_ref = oracle.forward_t5(xq, beta, t5, k, alpha)
+    y = bl.bitlinear_forward_t5(_to(torch, xq), _to(torch, beta), _to(torch, t5), _to(torch, np.array([alpha], np.float32)))
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
