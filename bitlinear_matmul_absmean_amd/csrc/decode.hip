@@ -1,4 +1,4 @@
-// decode.hip -- batched-decode ternary x int8 matmul (5 to 64 tokens) on the int8 matrix
+// decode.hip -- batched-decode ternary x int8 matmul (2 to 64 tokens) on the int8 matrix
 // cores (v_mfma_i32_32x32x32_i8 and v_mfma_i32_16x16x64_i8), gfx950.
 //
 // What is computed ([P3] chenxutan.com "1.58-bit 大模型极限量化实战" §2.4-§2.5, §3.2;
