@@ -237,7 +237,8 @@ def bitlinear_forward_blocks(x_q, beta, W_packed, alpha_blocks, bias=None, y=Non
 def bitlinear_mlp_forward(x, W1_packed, alpha1, W2_packed, alpha2, bias1=None, bias2=None, y=None, g=None,
                           x_q1=None, beta1=None, x_q2=None, beta2=None, stream=None):
     """BitMLP y = fc2(GELU(fc1(x))); returns (y, g).  x_q1/beta1/x_q2/beta2 are allocated
-    when M > 4 (the two-call path needs them) and not given."""
+    when M > 1 and not given (the two-call path needs them beyond four tokens and is the
+    faster one for most several-token shapes)."""
     torch = _torch()
     M, d_model = x.shape
     d_ff = W1_packed.shape[0]
@@ -247,7 +248,7 @@ def bitlinear_mlp_forward(x, W1_packed, alpha1, W2_packed, alpha2, bias1=None, b
         y = torch.empty((M, d_model), dtype=torch.float32, device=x.device)
     if g is None:
         g = torch.empty((M, d_ff), dtype=torch.float32, device=x.device)
-    if M > 4:
+    if M > 1:
         if x_q1 is None:
             x_q1 = torch.empty((M, d_model), dtype=torch.int8, device=x.device)
         if beta1 is None:

@@ -75,6 +75,19 @@ bool fused_fast_ok(int64_t M, int64_t K, const float* x, const uint8_t* wp, cons
     return gemv_supports(M, K) && aligned(x, 16) && aligned(wp, 16) && (!xq_out || aligned(xq_out, 16));
 }
 
+// Several tokens: every workgroup of the one-kernel path reads all M rows of fp32 x, so for
+// three or four tokens, and for two with K > 4096, quantize_act followed by the forward is the
+// faster route (measured with weights not in cache: M = 4, 9.9 vs 19.1 us at K = 11008,
+// N = 4096; M = 2, 12.4 vs 17.5 us at K = 16384, N = 8192; 8.9 vs 7.7 us at K = 4096,
+// N = 11008).  It needs x_q and beta, so it is taken when the caller gives them; without them
+// the call stays one launch.
+static bool two_launch_preferred(int64_t M, int64_t K) { return M >= 3 || (M == 2 && K > 4096); }
+
+static bool use_fused_kernel(int64_t M, int64_t K, const float* x, const uint8_t* wp, const int8_t* x_q,
+                             const float* beta) {
+    return fused_fast_ok(M, K, x, wp, x_q) && !(x_q && beta && two_launch_preferred(M, K));
+}
+
 int run_forward(const ForwardArgs& a, hipStream_t stream) {
     switch (choose_path(a.M, a.K, a.N, a.xq, a.wp)) {
         case Path::Gemv: return hip_status(launch_gemv_dot4(a, stream));
@@ -185,7 +198,7 @@ static int forward_fused(const float* x, int64_t M, int64_t K, const uint8_t* W_
     int st = check_fused(x, M, K, W_packed, alpha, N, y, x_q, beta);
     if (st) return st;
     ForwardArgs a{nullptr, nullptr, M, K, N, W_packed, alpha, per_row, bias, y, acc, act};
-    if (fused_fast_ok(M, K, x, W_packed, x_q)) return hip_status(launch_gemv_fused(a, x, x_q, beta, stream));
+    if (use_fused_kernel(M, K, x, W_packed, x_q, beta)) return hip_status(launch_gemv_fused(a, x, x_q, beta, stream));
     st = bitlinear_quantize_act(x, M, K, x_q, beta, stream);
     if (st) return st;
     a.xq = x_q;
@@ -319,7 +332,9 @@ int bitlinear_forward_fused_hadamard(const float* x, int64_t M, int64_t K, int64
 const char* bitlinear_forward_fused_kernel(int64_t M, int64_t K, int64_t N, const float* x, const uint8_t* W_packed,
                                            const int8_t* x_q) {
     (void)N;
-    return fused_fast_ok(M, K, x, W_packed, x_q) ? "gemv_fused" : "quantize_act+forward";
+    // x_q given stands for x_q and beta given
+    return use_fused_kernel(M, K, x, W_packed, x_q, reinterpret_cast<const float*>(x_q)) ? "gemv_fused"
+                                                                                       : "quantize_act+forward";
 }
 
 const char* bitlinear_forward_kernel(int64_t M, int64_t K, int64_t N, const int8_t* x_q,

@@ -153,7 +153,9 @@ int bitlinear_forward_rows(const int8_t* x_q, const float* beta, int64_t M, int6
  * Activation quantization and forward in one call [P3 §3.2 steps 2-4]: y from fp32 x,
  * with results identical to bitlinear_quantize_act followed by bitlinear_forward.
  * For M <= 4, K % 64 == 0, K <= 32768 and 16-byte aligned x, W_packed (and x_q if given)
- * it is one kernel that quantizes x on chip; otherwise it makes the two calls.
+ * it is one kernel that quantizes x on chip; otherwise it makes the two calls.  For three or
+ * four tokens, and for two with K > 4096, the two calls are faster, and they are made
+ * whenever x_q and beta are given.
  *
  *   x      [M, K] fp32.                                               (in)
  *   x_q    [M, K] int8 or NULL; receives the quantized activations.   (out)
@@ -314,7 +316,7 @@ int bitlinear_forward_fused_hadamard(const float* x, int64_t M, int64_t K, int64
                                      float* y, int8_t* x_q, float* beta, hipStream_t stream);
 
 /* Kernel(s) bitlinear_forward_fused launches for these arguments ("gemv_fused" or
- * "quantize_act+forward"); a static string. */
+ * "quantize_act+forward"; a non-NULL x_q stands for x_q and beta given); a static string. */
 const char* bitlinear_forward_fused_kernel(int64_t M, int64_t K, int64_t N, const float* x,
                                            const uint8_t* W_packed, const int8_t* x_q);
 

@@ -187,6 +187,10 @@ def test_kernel_selection(bl):
     assert fsel(1, 4096, 4096, A, A, None).decode() == "gemv_fused"
     assert fsel(1, 4096, 4096, A, A, A + 4).decode() == "quantize_act+forward"  # x_q export unaligned
     assert fsel(5, 4096, 4096, A, A, A).decode() == "quantize_act+forward"
+    assert fsel(3, 4096, 4096, A, A, None).decode() == "gemv_fused"            # no buffers: one launch
+    assert fsel(3, 4096, 4096, A, A, A).decode() == "quantize_act+forward"     # buffers: the faster route
+    assert fsel(2, 4096, 4096, A, A, A).decode() == "gemv_fused"
+    assert fsel(2, 4160, 4096, A, A, A).decode() == "quantize_act+forward"
     assert fsel(1, 32768, 4096, A, A, None).decode() == "gemv_fused"
     assert fsel(1, 32832, 4096, A, A, None).decode() == "quantize_act+forward"   # K beyond the GEMV
 
