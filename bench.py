@@ -13,7 +13,7 @@ from Python) and timed with HIP events on the capture stream, bracketed by devic
 `value` = packed weight bytes streamed per step * K / elapsed (GB/s).
 
 Extra objects on the same JSON line: `roofline` for the dominant kernel (the decode GEMV on the
-(4096, 11008) shape, timed in isolation the same way), `prefill` (M = 2048 int8-MFMA TOPS),
+(4096, 11008) shape, timed in isolation the same way), `prefill` and `prefill_n4096` (M = 2048, K = 4096, N = 11008 and 4096: int8-MFMA TOPS),
 `batched` (M = 2/4/8/16/64), `chain70b` (one decode step of the 70B-class stream) and
 `cpu_baseline` (the CPU oracle on a bounded sample of the same workload).
 """
@@ -770,6 +770,8 @@ def main():
     if not args.no_extras:
         extras["prefill"] = prefill_bench(torch, bl, workloads, dev)
         log(f"prefill {extras['prefill']}")
+        extras["prefill_n4096"] = prefill_bench(torch, bl, workloads, dev, n=4096)
+        log(f"prefill_n4096 {extras['prefill_n4096']}")
         extras["batched"] = batched_bench(torch, bl, workloads, dev)
         log(f"batched {extras['batched']}")
         extras.update(quantize_bench(torch, bl, workloads, dev))
@@ -792,9 +794,10 @@ def main():
     read_ceiling = list(ceil["hbm_read_gbs"].values())[0]
     roof["measured_ceiling"] = {"gbs": read_ceiling, "what": "streaming read of the same byte count, same timing",
                                 "frac": round(roof["achieved"] / read_ceiling, 4)}
-    if "prefill" in extras:
-        extras["prefill"]["pct_measured_mfma_random"] = round(
-            100 * extras["prefill"]["tops"] / ceil["mfma_i8_tops"]["random"], 2)
+    for key in ("prefill", "prefill_n4096"):
+        if key in extras:
+            extras[key]["pct_measured_mfma_random"] = round(
+                100 * extras[key]["tops"] / ceil["mfma_i8_tops"]["random"], 2)
     cpu = None if args.no_cpu else cpu_baseline(workloads)
 
     line = {

@@ -55,14 +55,17 @@ __device__ __forceinline__ i32x4 unpack16(uint32_t v) {
 #define MF(i, j, av, bv) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, acc[i][j], 0, 0, 0)
 
 constexpr int GEMM_BM = 128, GEMM_BN = 256, GEMM_BK = 64;
+constexpr int64_t GEMM_SMALL_GRID = 128;
 
 // GELU: the BitMLP activation in the epilogue, fixed at compile time so that the plain
-// kernel carries no call.
-template <bool GELU>
+// kernel carries no call.  FM: 32-token blocks per tile, 4 (128 x 256 tiles) or 2 (64 x 256,
+// for grids that 128-token tiles would leave short of the workgroup slots).
+template <bool GELU, int FM>
 __global__ __launch_bounds__(256, 2) void k_gemm_mfma(ForwardArgs a, int tiles_m, int tiles_n) {
-    constexpr int BM = GEMM_BM, BN = GEMM_BN, BK = GEMM_BK;
-    constexpr int WN = BN / 4;                 // wave tile 128 x 64
-    constexpr int FM = 4, FN = 2;
+    static_assert(FM == 4 || FM == 2, "128- or 64-token tiles");
+    constexpr int BM = 32 * FM, BN = GEMM_BN, BK = GEMM_BK;
+    constexpr int WN = BN / 4;                 // wave tile BM x 64
+    constexpr int FN = 2;
     constexpr int GK = BK / 16, APT = BM * GK / 256, ASTR = GK + 1;
     __shared__ u32x4 As[2][BM * ASTR];
     __shared__ u32x4 Bs[2][BN];
@@ -156,6 +159,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(ForwardArgs a, int tiles_m
         for (int j = 0; j < FN; ++j) b0[j] = unpack16(bw[0][j]);
         SB();
         const int ob = buf ^ 1;
+        uint32_t q[APT][4];
+        if constexpr (FM == 4) {
         // first half: B expansion of kk = 1 and the transposes of both A units
         MF(0, 0, av[0][0], b0[0]);
         b1[0].x = (int)(bw[1][0] & 0x03030303u); b1[0].y = (int)((bw[1][0] >> 2) & 0x03030303u); SB();
@@ -165,7 +170,6 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(ForwardArgs a, int tiles_m
         b1[1].x = (int)(bw[1][1] & 0x03030303u); b1[1].y = (int)((bw[1][1] >> 2) & 0x03030303u); SB();
         MF(1, 1, av[0][1], b0[1]);
         b1[1].z = (int)((bw[1][1] >> 4) & 0x03030303u); b1[1].w = (int)((bw[1][1] >> 6) & 0x03030303u); SB();
-        uint32_t q[2][4];
         MF(2, 0, av[0][2], b0[0]);
         q[0][0] = __builtin_amdgcn_perm(rc[0].y, rc[0].x, 0x05010400u); q[0][1] = __builtin_amdgcn_perm(rc[0].y, rc[0].x, 0x07030602u);
         q[0][2] = __builtin_amdgcn_perm(rc[0].w, rc[0].z, 0x05010400u); q[0][3] = __builtin_amdgcn_perm(rc[0].w, rc[0].z, 0x07030602u); SB();
@@ -174,28 +178,54 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(ForwardArgs a, int tiles_m
                                                      __builtin_amdgcn_perm(q[0][3], q[0][1], 0x05040100u), __builtin_amdgcn_perm(q[0][3], q[0][1], 0x07060302u)};
         SB();
         MF(3, 0, av[0][3], b0[0]);
-        q[1][0] = __builtin_amdgcn_perm(rc[1].y, rc[1].x, 0x05010400u); q[1][1] = __builtin_amdgcn_perm(rc[1].y, rc[1].x, 0x07030602u);
-        q[1][2] = __builtin_amdgcn_perm(rc[1].w, rc[1].z, 0x05010400u); q[1][3] = __builtin_amdgcn_perm(rc[1].w, rc[1].z, 0x07030602u); SB();
+        q[APT - 1][0] = __builtin_amdgcn_perm(rc[APT - 1].y, rc[APT - 1].x, 0x05010400u); q[APT - 1][1] = __builtin_amdgcn_perm(rc[APT - 1].y, rc[APT - 1].x, 0x07030602u);
+        q[APT - 1][2] = __builtin_amdgcn_perm(rc[APT - 1].w, rc[APT - 1].z, 0x05010400u); q[APT - 1][3] = __builtin_amdgcn_perm(rc[APT - 1].w, rc[APT - 1].z, 0x07030602u); SB();
         MF(3, 1, av[0][3], b0[1]);
-        As[ob][((tid + 256) / GK) * ASTR + tid % GK] = u32x4{__builtin_amdgcn_perm(q[1][2], q[1][0], 0x05040100u), __builtin_amdgcn_perm(q[1][2], q[1][0], 0x07060302u),
-                                                             __builtin_amdgcn_perm(q[1][3], q[1][1], 0x05040100u), __builtin_amdgcn_perm(q[1][3], q[1][1], 0x07060302u)};
+        As[ob][((tid + 256) / GK) * ASTR + tid % GK] = u32x4{__builtin_amdgcn_perm(q[APT - 1][2], q[APT - 1][0], 0x05040100u), __builtin_amdgcn_perm(q[APT - 1][2], q[APT - 1][0], 0x07060302u),
+                                                             __builtin_amdgcn_perm(q[APT - 1][3], q[APT - 1][1], 0x05040100u), __builtin_amdgcn_perm(q[APT - 1][3], q[APT - 1][1], 0x07060302u)};
         SB();
         // second half: sums and the B store
-        int v0 = rs[0], v1 = rs[1];
+        int v0 = rs[0], v1 = rs[APT - 1];
         MF(0, 0, av[1][0], b1[0]);
         v0 = __builtin_amdgcn_sdot4((int)rc[0].x, 0x01010101, v0, false); v0 = __builtin_amdgcn_sdot4((int)rc[0].y, 0x01010101, v0, false); SB();
         MF(0, 1, av[1][0], b1[1]);
         v0 = __builtin_amdgcn_sdot4((int)rc[0].z, 0x01010101, v0, false); v0 = __builtin_amdgcn_sdot4((int)rc[0].w, 0x01010101, v0, false); SB();
         MF(1, 0, av[1][1], b1[0]);
-        v1 = __builtin_amdgcn_sdot4((int)rc[1].x, 0x01010101, v1, false); v1 = __builtin_amdgcn_sdot4((int)rc[1].y, 0x01010101, v1, false); SB();
+        v1 = __builtin_amdgcn_sdot4((int)rc[APT - 1].x, 0x01010101, v1, false); v1 = __builtin_amdgcn_sdot4((int)rc[APT - 1].y, 0x01010101, v1, false); SB();
         MF(1, 1, av[1][1], b1[1]);
-        v1 = __builtin_amdgcn_sdot4((int)rc[1].z, 0x01010101, v1, false); v1 = __builtin_amdgcn_sdot4((int)rc[1].w, 0x01010101, v1, false); SB();
+        v1 = __builtin_amdgcn_sdot4((int)rc[APT - 1].z, 0x01010101, v1, false); v1 = __builtin_amdgcn_sdot4((int)rc[APT - 1].w, 0x01010101, v1, false); SB();
         MF(2, 0, av[1][2], b1[0]);
-        rs[0] = count ? v0 : rs[0]; rs[1] = count ? v1 : rs[1]; SB();
+        rs[0] = count ? v0 : rs[0]; rs[APT - 1] = count ? v1 : rs[APT - 1]; SB();
         MF(2, 1, av[1][2], b1[1]);
         stage_b(rbc, ob); SB();
         MF(3, 0, av[1][3], b1[0]); SB();
         MF(3, 1, av[1][3], b1[1]); SB();
+        } else {
+        // 64-token tiles, one A unit per thread: first half the B expansion of kk = 1, second
+        // half the transpose, the sum and the stores
+        MF(0, 0, av[0][0], b0[0]);
+        b1[0].x = (int)(bw[1][0] & 0x03030303u); b1[0].y = (int)((bw[1][0] >> 2) & 0x03030303u); SB();
+        MF(0, 1, av[0][0], b0[1]);
+        b1[0].z = (int)((bw[1][0] >> 4) & 0x03030303u); b1[0].w = (int)((bw[1][0] >> 6) & 0x03030303u); SB();
+        MF(1, 0, av[0][1], b0[0]);
+        b1[1].x = (int)(bw[1][1] & 0x03030303u); b1[1].y = (int)((bw[1][1] >> 2) & 0x03030303u); SB();
+        MF(1, 1, av[0][1], b0[1]);
+        b1[1].z = (int)((bw[1][1] >> 4) & 0x03030303u); b1[1].w = (int)((bw[1][1] >> 6) & 0x03030303u); SB();
+        int v0 = rs[0];
+        MF(0, 0, av[1][0], b1[0]);
+        q[0][0] = __builtin_amdgcn_perm(rc[0].y, rc[0].x, 0x05010400u); q[0][1] = __builtin_amdgcn_perm(rc[0].y, rc[0].x, 0x07030602u);
+        q[0][2] = __builtin_amdgcn_perm(rc[0].w, rc[0].z, 0x05010400u); q[0][3] = __builtin_amdgcn_perm(rc[0].w, rc[0].z, 0x07030602u); SB();
+        MF(0, 1, av[1][0], b1[1]);
+        As[ob][(tid / GK) * ASTR + tid % GK] = u32x4{__builtin_amdgcn_perm(q[0][2], q[0][0], 0x05040100u), __builtin_amdgcn_perm(q[0][2], q[0][0], 0x07060302u),
+                                                     __builtin_amdgcn_perm(q[0][3], q[0][1], 0x05040100u), __builtin_amdgcn_perm(q[0][3], q[0][1], 0x07060302u)};
+        SB();
+        MF(1, 0, av[1][1], b1[0]);
+        v0 = __builtin_amdgcn_sdot4((int)rc[0].x, 0x01010101, v0, false); v0 = __builtin_amdgcn_sdot4((int)rc[0].y, 0x01010101, v0, false);
+        v0 = __builtin_amdgcn_sdot4((int)rc[0].z, 0x01010101, v0, false); v0 = __builtin_amdgcn_sdot4((int)rc[0].w, 0x01010101, v0, false); SB();
+        MF(1, 1, av[1][1], b1[1]);
+        rs[0] = count ? v0 : rs[0];
+        stage_b(rbc, ob); SB();
+        }
     };
 
     // Two register stages: at the top of an iteration LDS buffer 0 holds step ks and ra1/rb1 hold
@@ -250,13 +280,25 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(ForwardArgs a, int tiles_m
 
 bool gemm_supports_k(int64_t K) { return K % GEMM_BK == 0; }
 
-hipError_t launch_gemm_mfma(const ForwardArgs& a, hipStream_t s) {
-    const int tm = (int)((a.M + GEMM_BM - 1) / GEMM_BM), tn = (int)((a.N + GEMM_BN - 1) / GEMM_BN);
+template <int FM>
+static hipError_t launch_gemm_fm(const ForwardArgs& a, hipStream_t s) {
+    const int bm = 32 * FM;
+    const int tm = (int)((a.M + bm - 1) / bm), tn = (int)((a.N + GEMM_BN - 1) / GEMM_BN);
     if (a.act == 1)
-        hipLaunchKernelGGL(k_gemm_mfma<true>, dim3((unsigned)(tm * tn)), dim3(256), 0, s, a, tm, tn);
+        hipLaunchKernelGGL((k_gemm_mfma<true, FM>), dim3((unsigned)(tm * tn)), dim3(256), 0, s, a, tm, tn);
     else
-        hipLaunchKernelGGL(k_gemm_mfma<false>, dim3((unsigned)(tm * tn)), dim3(256), 0, s, a, tm, tn);
+        hipLaunchKernelGGL((k_gemm_mfma<false, FM>), dim3((unsigned)(tm * tn)), dim3(256), 0, s, a, tm, tn);
     return hipGetLastError();
+}
+
+// 128 x 256 tiles, or 64 x 256 for grids of at most 128 such tiles (a quarter of the 512
+// workgroup slots).  Measured: M = 1024, K = N = 4096: 34.3 vs 45.6 us; M = 512: 31.0 vs
+// 44.7 us; M = 128, N = 11008: 30.0 vs 43.2 us.  With more tiles the 128-token tiles win even
+// at half the slots, since a 64-token tile reads the weights twice as often (M = 2048,
+// K = 11008, N = 4096: 100 vs 126 us; M = 512, N = 11008, 172 tiles: level).
+hipError_t launch_gemm_mfma(const ForwardArgs& a, hipStream_t s) {
+    const int64_t tiles128 = ((a.M + GEMM_BM - 1) / GEMM_BM) * ((a.N + GEMM_BN - 1) / GEMM_BN);
+    return tiles128 <= GEMM_SMALL_GRID ? launch_gemm_fm<2>(a, s) : launch_gemm_fm<4>(a, s);
 }
 
 // ---------------------------------------------------------------------------------------
