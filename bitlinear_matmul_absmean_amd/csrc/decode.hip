@@ -355,7 +355,8 @@ static hipError_t launch_bdec16(const ForwardArgs& a, hipStream_t s) {
 bool decode_mfma_supports(int64_t M, int64_t K) { return M >= 1 && M <= 64 && K % 64 == 0; }
 
 // Tile shape by token count: 16 x 16 x 64 tiles up to 32 tokens (better weight loads, fewer
-// token rows of x_q), 32 x 32 x 32 tiles up to 64.  Row blocks per workgroup: the fewest that
+// token rows of x_q) except 17 to 32 tokens on wide matrices of K <= 8192, 32 x 32 x 32 tiles
+// up to 64.  Row blocks per workgroup: the fewest that
 // keep the grid within about one workgroup per CU (256), so that x_q is read as few times as
 // possible, within the registers (no spills) and the LDS of the final reduction.
 hipError_t launch_decode_mfma(const ForwardArgs& a, hipStream_t s) {
@@ -366,11 +367,20 @@ hipError_t launch_decode_mfma(const ForwardArgs& a, hipStream_t s) {
         if (nb16 <= 1024) return launch_bdec16<1, 4>(a, s);
         return launch_bdec16<1, 8>(a, s);
     }
+    const int64_t nb = (a.N + 31) / 32;
+    // 17 to 32 tokens on wide matrices of moderate K: 32x32x32 tiles with one 32-token block
+    // (measured with weights not in cache, M = 24: 19.8 vs 28.0 us at K = 8192, N = 10240;
+    // 38.9 vs 54.5 us at K = 8192, N = 28672; level at K = 4096, N = 11008; the 16x16x64
+    // tiles stay ahead at K = 11008 and 28672)
+    if (a.M > 16 && a.M <= 32 && a.K <= 8192 && a.N >= 8192) {
+        if (nb <= 256) return launch_bdec<1, 1>(a, s);
+        if (nb <= 512) return launch_bdec<1, 2>(a, s);
+        return launch_bdec<1, 4>(a, s);
+    }
     if (a.M <= 32) {
         if (nb16 <= 256) return launch_bdec16<2, 1>(a, s);
         return launch_bdec16<2, 2>(a, s);
     }
-    const int64_t nb = (a.N + 31) / 32;
     if (nb <= 256) return launch_bdec<2, 1>(a, s);
     return launch_bdec<2, 2>(a, s);
 }

@@ -176,6 +176,9 @@ FWD_CASES = [
     # two token blocks, 32x32x32 tiles with 1/2; K % 256 = 64 and K % 128 = 64 tails; ragged N
     (8, 256, 9000), (12, 128, 17000), (16, 192, 5000), (9, 4160, 700), (24, 320, 4100),
     (32, 64, 8300), (20, 4352, 300), (48, 192, 8200), (64, 4160, 600), (41, 128, 33),
+    # 17-32 tokens on 32x32x32 tiles with one token block (K <= 8192, N >= 8192): 1, 2 and 4
+    # row blocks per workgroup, K % 128 = 64
+    (17, 192, 8192), (24, 1088, 9000), (32, 256, 20000),
 ]
 
 
