@@ -93,7 +93,9 @@ def _torch():
     return torch
 
 
-def _dev(t, dtype, name):
+def _dev(t, dtype, name, numel=None):
+    """Device pointer of t after checking device, dtype, layout and (numel) the minimum number of
+    elements the library reads or writes through it."""
     torch = _torch()
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
@@ -101,6 +103,8 @@ def _dev(t, dtype, name):
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} must hold at least {numel} elements, got {t.numel()}")
     return t.data_ptr()
 
 
@@ -122,8 +126,8 @@ def bitlinear_quantize_weights(W, W_packed=None, alpha=None, workspace=None, str
     if workspace is None:
         workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=W.device)
     _check("bitlinear_quantize_weights", lib.bitlinear_quantize_weights(
-        _dev(W, torch.float32, "W"), N, K, _dev(W_packed, torch.uint8, "W_packed"),
-        _dev(alpha, torch.float32, "alpha"), _dev(workspace, torch.uint8, "workspace"),
+        _dev(W, torch.float32, "W", N * K), N, K, _dev(W_packed, torch.uint8, "W_packed", N * (K // 4)),
+        _dev(alpha, torch.float32, "alpha", 1), _dev(workspace, torch.uint8, "workspace"),
         workspace.numel(), _stream(stream)))
     return W_packed, alpha
 
@@ -137,8 +141,8 @@ def bitlinear_quantize_weights_rows(W, W_packed=None, alpha_rows=None, stream=No
     if alpha_rows is None:
         alpha_rows = torch.empty(N, dtype=torch.float32, device=W.device)
     _check("bitlinear_quantize_weights_rows", lib.bitlinear_quantize_weights_rows(
-        _dev(W, torch.float32, "W"), N, K, _dev(W_packed, torch.uint8, "W_packed"),
-        _dev(alpha_rows, torch.float32, "alpha_rows"), _stream(stream)))
+        _dev(W, torch.float32, "W", N * K), N, K, _dev(W_packed, torch.uint8, "W_packed", N * (K // 4)),
+        _dev(alpha_rows, torch.float32, "alpha_rows", N), _stream(stream)))
     return W_packed, alpha_rows
 
 
@@ -151,8 +155,8 @@ def bitlinear_quantize_act(x, x_q=None, beta=None, stream=None):
     if beta is None:
         beta = torch.empty(M, dtype=torch.float32, device=x.device)
     _check("bitlinear_quantize_act", lib.bitlinear_quantize_act(
-        _dev(x, torch.float32, "x"), M, K, _dev(x_q, torch.int8, "x_q"),
-        _dev(beta, torch.float32, "beta"), _stream(stream)))
+        _dev(x, torch.float32, "x", M * K), M, K, _dev(x_q, torch.int8, "x_q", M * K),
+        _dev(beta, torch.float32, "beta", M), _stream(stream)))
     return x_q, beta
 
 
@@ -169,7 +173,8 @@ def bitlinear_quantize_weights_t5(W, W_t5=None, alpha=None, workspace=None, stre
     if workspace is None:
         workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=W.device)
     _check("bitlinear_quantize_weights_t5", lib.bitlinear_quantize_weights_t5(
-        _dev(W, torch.float32, "W"), N, K, _dev(W_t5, torch.uint8, "W_t5"), _dev(alpha, torch.float32, "alpha"),
+        _dev(W, torch.float32, "W", N * K), N, K, _dev(W_t5, torch.uint8, "W_t5", N * rb),
+        _dev(alpha, torch.float32, "alpha", 1),
         _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
     return W_t5, alpha
 
@@ -183,7 +188,8 @@ def bitlinear_repack_t5(W_packed, K, W_t5=None, stream=None):
     if W_t5 is None:
         W_t5 = torch.empty((N, lib.bitlinear_t5_row_bytes(K)), dtype=torch.uint8, device=W_packed.device)
     _check("bitlinear_repack_t5", lib.bitlinear_repack_t5(
-        _dev(W_packed, torch.uint8, "W_packed"), N, K, _dev(W_t5, torch.uint8, "W_t5"), _stream(stream)))
+        _dev(W_packed, torch.uint8, "W_packed"), N, K,
+        _dev(W_t5, torch.uint8, "W_t5", N * lib.bitlinear_t5_row_bytes(K)), _stream(stream)))
     return W_t5
 
 
@@ -197,9 +203,10 @@ def bitlinear_forward_t5(x_q, beta, W_t5, alpha, bias=None, y=None, stream=None)
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=x_q.device)
     _check("bitlinear_forward_t5", lib.bitlinear_forward_t5(
-        _dev(x_q, torch.int8, "x_q"), _dev(beta, torch.float32, "beta"), M, K, _dev(W_t5, torch.uint8, "W_t5"),
-        _dev(alpha, torch.float32, "alpha"), N, _dev(bias, torch.float32, "bias") if bias is not None else None,
-        _dev(y, torch.float32, "y"), _stream(stream)))
+        _dev(x_q, torch.int8, "x_q"), _dev(beta, torch.float32, "beta", M), M, K, _dev(W_t5, torch.uint8, "W_t5"),
+        _dev(alpha, torch.float32, "alpha", 1), N,
+        _dev(bias, torch.float32, "bias", N) if bias is not None else None,
+        _dev(y, torch.float32, "y", M * N), _stream(stream)))
     return y
 
 
@@ -212,8 +219,8 @@ def bitlinear_quantize_weights_blocks(W, W_packed=None, alpha_blocks=None, strea
     if alpha_blocks is None:
         alpha_blocks = torch.empty((N, K // 128), dtype=torch.float32, device=W.device)
     _check("bitlinear_quantize_weights_blocks", lib.bitlinear_quantize_weights_blocks(
-        _dev(W, torch.float32, "W"), N, K, _dev(W_packed, torch.uint8, "W_packed"),
-        _dev(alpha_blocks, torch.float32, "alpha_blocks"), _stream(stream)))
+        _dev(W, torch.float32, "W", N * K), N, K, _dev(W_packed, torch.uint8, "W_packed", N * (K // 4)),
+        _dev(alpha_blocks, torch.float32, "alpha_blocks", N * (K // 128)), _stream(stream)))
     return W_packed, alpha_blocks
 
 
@@ -227,9 +234,9 @@ def bitlinear_forward_blocks(x_q, beta, W_packed, alpha_blocks, bias=None, y=Non
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=x_q.device)
     _check("bitlinear_forward_blocks", lib.bitlinear_forward_blocks(
-        _dev(x_q, torch.int8, "x_q"), _dev(beta, torch.float32, "beta"), M, K,
-        _dev(W_packed, torch.uint8, "W_packed"), _dev(alpha_blocks, torch.float32, "alpha_blocks"), N,
-        _dev(bias, torch.float32, "bias") if bias is not None else None, _dev(y, torch.float32, "y"),
+        _dev(x_q, torch.int8, "x_q"), _dev(beta, torch.float32, "beta", M), M, K,
+        _dev(W_packed, torch.uint8, "W_packed"), _dev(alpha_blocks, torch.float32, "alpha_blocks", N * (K // 128)),
+        N, _dev(bias, torch.float32, "bias", N) if bias is not None else None, _dev(y, torch.float32, "y", M * N),
         _stream(stream)))
     return y
 
@@ -257,14 +264,15 @@ def bitlinear_mlp_forward(x, W1_packed, alpha1, W2_packed, alpha2, bias1=None, b
             x_q2 = torch.empty((M, d_ff), dtype=torch.int8, device=x.device)
         if beta2 is None:
             beta2 = torch.empty(M, dtype=torch.float32, device=x.device)
-    opt = lambda t, dt, n: _dev(t, dt, n) if t is not None else None
+    opt = lambda t, dt, n, k: _dev(t, dt, n, k) if t is not None else None
     _check("bitlinear_mlp_forward", lib.bitlinear_mlp_forward(
-        _dev(x, torch.float32, "x"), M, d_model, d_ff, _dev(W1_packed, torch.uint8, "W1_packed"),
-        _dev(alpha1, torch.float32, "alpha1"), opt(bias1, torch.float32, "bias1"),
-        _dev(W2_packed, torch.uint8, "W2_packed"), _dev(alpha2, torch.float32, "alpha2"),
-        opt(bias2, torch.float32, "bias2"), _dev(y, torch.float32, "y"), _dev(g, torch.float32, "g"),
-        opt(x_q1, torch.int8, "x_q1"), opt(beta1, torch.float32, "beta1"), opt(x_q2, torch.int8, "x_q2"),
-        opt(beta2, torch.float32, "beta2"), _stream(stream)))
+        _dev(x, torch.float32, "x", M * d_model), M, d_model, d_ff, _dev(W1_packed, torch.uint8, "W1_packed"),
+        _dev(alpha1, torch.float32, "alpha1", 1), opt(bias1, torch.float32, "bias1", d_ff),
+        _dev(W2_packed, torch.uint8, "W2_packed"), _dev(alpha2, torch.float32, "alpha2", 1),
+        opt(bias2, torch.float32, "bias2", d_model), _dev(y, torch.float32, "y", M * d_model),
+        _dev(g, torch.float32, "g", M * d_ff), opt(x_q1, torch.int8, "x_q1", M * d_model),
+        opt(beta1, torch.float32, "beta1", M), opt(x_q2, torch.int8, "x_q2", M * d_ff),
+        opt(beta2, torch.float32, "beta2", M), _stream(stream)))
     return y, g
 
 
@@ -275,9 +283,9 @@ def bitlinear_hadamard_rows(x, block, signs=None, out=None, stream=None):
     if out is None:
         out = torch.empty((M, K), dtype=torch.float32, device=x.device)
     _check("bitlinear_hadamard_rows", lib.bitlinear_hadamard_rows(
-        _dev(x, torch.float32, "x"), M, K, int(block),
-        _dev(signs, torch.int8, "signs") if signs is not None else None,
-        _dev(out, torch.float32, "out"), _stream(stream)))
+        _dev(x, torch.float32, "x", M * K), M, K, int(block),
+        _dev(signs, torch.int8, "signs", K) if signs is not None else None,
+        _dev(out, torch.float32, "out", M * K), _stream(stream)))
     return out
 
 
@@ -290,9 +298,9 @@ def bitlinear_quantize_act_hadamard(x, block, signs=None, x_q=None, beta=None, s
     if beta is None:
         beta = torch.empty(M, dtype=torch.float32, device=x.device)
     _check("bitlinear_quantize_act_hadamard", lib.bitlinear_quantize_act_hadamard(
-        _dev(x, torch.float32, "x"), M, K, int(block),
-        _dev(signs, torch.int8, "signs") if signs is not None else None,
-        _dev(x_q, torch.int8, "x_q"), _dev(beta, torch.float32, "beta"), _stream(stream)))
+        _dev(x, torch.float32, "x", M * K), M, K, int(block),
+        _dev(signs, torch.int8, "signs", K) if signs is not None else None,
+        _dev(x_q, torch.int8, "x_q", M * K), _dev(beta, torch.float32, "beta", M), _stream(stream)))
     return x_q, beta
 
 
@@ -306,16 +314,16 @@ def bitlinear_forward_fused_hadamard(x, block, signs, W_packed, alpha, bias=None
         raise ValueError("W_packed must be [N, K/4]")
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=x.device)
-    opt = lambda t, dt, n: _dev(t, dt, n) if t is not None else None
+    opt = lambda t, dt, n, k: _dev(t, dt, n, k) if t is not None else None
     _check("bitlinear_forward_fused_hadamard", lib.bitlinear_forward_fused_hadamard(
-        _dev(x, torch.float32, "x"), M, K, int(block), opt(signs, torch.int8, "signs"),
-        _dev(W_packed, torch.uint8, "W_packed"), _dev(alpha, torch.float32, "alpha"), N,
-        opt(bias, torch.float32, "bias"), _dev(y, torch.float32, "y"), opt(x_q, torch.int8, "x_q"),
-        opt(beta, torch.float32, "beta"), _stream(stream)))
+        _dev(x, torch.float32, "x", M * K), M, K, int(block), opt(signs, torch.int8, "signs", K),
+        _dev(W_packed, torch.uint8, "W_packed"), _dev(alpha, torch.float32, "alpha", 1), N,
+        opt(bias, torch.float32, "bias", N), _dev(y, torch.float32, "y", M * N), opt(x_q, torch.int8, "x_q", M * K),
+        opt(beta, torch.float32, "beta", M), _stream(stream)))
     return y
 
 
-def _forward(fn, what, x_q, beta, W_packed, alpha, bias, y, acc, stream):
+def _forward(fn, what, x_q, beta, W_packed, alpha, bias, y, acc, stream, alpha_n=1):
     torch = _torch()
     M, K = x_q.shape
     N = W_packed.shape[0]
@@ -325,12 +333,12 @@ def _forward(fn, what, x_q, beta, W_packed, alpha, bias, y, acc, stream):
         y = torch.empty((M, N), dtype=torch.float32, device=x_q.device)
     if acc is True:
         acc = torch.empty((M, N), dtype=torch.int32, device=x_q.device)
-    acc_ptr = _dev(acc, torch.int32, "acc") if acc is not None and acc is not False else None
-    bias_ptr = _dev(bias, torch.float32, "bias") if bias is not None else None
+    acc_ptr = _dev(acc, torch.int32, "acc", M * N) if acc is not None and acc is not False else None
+    bias_ptr = _dev(bias, torch.float32, "bias", N) if bias is not None else None
     _check(what, fn(
-        _dev(x_q, torch.int8, "x_q"), _dev(beta, torch.float32, "beta"), M, K,
-        _dev(W_packed, torch.uint8, "W_packed"), _dev(alpha, torch.float32, "alpha"), N,
-        bias_ptr, _dev(y, torch.float32, "y"), acc_ptr, _stream(stream)))
+        _dev(x_q, torch.int8, "x_q"), _dev(beta, torch.float32, "beta", M), M, K,
+        _dev(W_packed, torch.uint8, "W_packed"), _dev(alpha, torch.float32, "alpha", alpha_n), N,
+        bias_ptr, _dev(y, torch.float32, "y", M * N), acc_ptr, _stream(stream)))
     return (y, acc) if acc_ptr is not None else y
 
 
@@ -344,7 +352,7 @@ def bitlinear_forward(x_q, beta, W_packed, alpha, bias=None, y=None, acc=None, s
 def bitlinear_forward_rows(x_q, beta, W_packed, alpha_rows, bias=None, y=None, acc=None, stream=None):
     """bitlinear_forward with one alpha per output row."""
     return _forward(lib.bitlinear_forward_rows, "bitlinear_forward_rows", x_q, beta, W_packed,
-                    alpha_rows, bias, y, acc, stream)
+                    alpha_rows, bias, y, acc, stream, alpha_n=W_packed.shape[0])
 
 
 def _forward_fused(name, x, W_packed, alpha, bias, y, x_q, beta, acc, stream):
@@ -357,13 +365,13 @@ def _forward_fused(name, x, W_packed, alpha, bias, y, x_q, beta, acc, stream):
         y = torch.empty((M, N), dtype=torch.float32, device=x.device)
     if acc is True:
         acc = torch.empty((M, N), dtype=torch.int32, device=x.device)
-    acc_ptr = _dev(acc, torch.int32, "acc") if acc is not None and acc is not False else None
+    acc_ptr = _dev(acc, torch.int32, "acc", M * N) if acc is not None and acc is not False else None
     _check(name, getattr(lib, name)(
-        _dev(x, torch.float32, "x"), M, K, _dev(W_packed, torch.uint8, "W_packed"),
-        _dev(alpha, torch.float32, "alpha"), N,
-        _dev(bias, torch.float32, "bias") if bias is not None else None, _dev(y, torch.float32, "y"),
-        _dev(x_q, torch.int8, "x_q") if x_q is not None else None,
-        _dev(beta, torch.float32, "beta") if beta is not None else None, acc_ptr, _stream(stream)))
+        _dev(x, torch.float32, "x", M * K), M, K, _dev(W_packed, torch.uint8, "W_packed"),
+        _dev(alpha, torch.float32, "alpha", N if name.endswith("_rows") else 1), N,
+        _dev(bias, torch.float32, "bias", N) if bias is not None else None, _dev(y, torch.float32, "y", M * N),
+        _dev(x_q, torch.int8, "x_q", M * K) if x_q is not None else None,
+        _dev(beta, torch.float32, "beta", M) if beta is not None else None, acc_ptr, _stream(stream)))
     return (y, acc) if acc_ptr is not None else y
 
 

@@ -165,10 +165,78 @@ struct ForwardArgs {
 };
 
 // GELU (the erf form of torch.nn.GELU) between the two BitLinears of the BitMLP [P3 §6.1]:
-// 0.5 h (1 + erf(h / sqrt 2)) in fp64, rounded to fp32 once.
-__device__ __attribute__((noinline)) float gelu_f32(float h) {
+// 0.5 h (1 + erf(h / sqrt 2)) in fp64, rounded to fp32 once.  This is that formula with the
+// library erf; the fast path below falls back to it whenever it cannot decide the rounding
+// (inlined there, so that the GELU functions make no calls and save nothing to scratch).
+__device__ __forceinline__ float gelu_f32_erf(float h) {
     const double v = (double)h;
     return (float)(0.5 * v * (1.0 + erf(v * 0.70710678118654752440)));
+}
+
+// Fast GELU in fp64 without branches: GELU(v) = v Phi(v) with Phi(v) = erfc(y) / 2 for v < 0 and
+// 1 - erfc(y) / 2 otherwise, y = |v| / sqrt 2, erfc(y) = exp(-v^2 / 2) erfcx(y), and erfcx as a
+// degree-16 polynomial in u = S (2 / (2 + y)) + O (Chebyshev interpolation on y in [0, 5.7], the
+// variable t = 2 / (2 + y) of the classical erfc expansions; u is clamped at y = 5.7, where
+// erfc < 2e-15).  Measured against long-double erfcl over v >= -4: relative error below 2e-14.
+// The coefficients come from csrc/fit_gelu.py.
+namespace gelu_poly {
+constexpr double kS2 = 2.0 * 2.7017543859649122, kO = -1.7017543859649122;
+constexpr double kC[17] = {
+    0.3840490174908751, 0.4210641425092814, 0.16628657095956959, 0.031638468914700096,
+    -0.0016874574521908601, -0.0015499149004059385, 0.00013185815934692365, 8.957503665028618e-05,
+    -2.0876744374376674e-05, -3.47183505293702e-06, 2.4538737264270885e-06, -2.7035081443788403e-07,
+    -1.586981502844185e-07, 7.209803422744851e-08, -4.939635762515718e-09, -5.870114231300212e-09,
+    1.7485565120006436e-09};
+}  // namespace gelu_poly
+
+__device__ __forceinline__ double gelu_approx(double v) {
+    const double y = fabs(v) * 0.70710678118654752440;
+    const double d = 2.0 + y;
+    double r = __builtin_amdgcn_rcp(d);                 // 1 / d, two Newton steps to full precision
+    r = fma(r, fma(-d, r, 1.0), r);
+    r = fma(r, fma(-d, r, 1.0), r);
+    const double u = fmax(fma(r, gelu_poly::kS2, gelu_poly::kO), -1.0);
+    double e = gelu_poly::kC[16];
+#pragma unroll
+    for (int i = 15; i >= 0; --i) e = fma(e, u, gelu_poly::kC[i]);
+    const double q = exp(-0.5 * v * v) * e;            // erfc(y); -v^2 / 2 is exact for fp32 v
+    return v * (v < 0.0 ? 0.5 * q : fma(-0.5, q, 1.0));
+}
+
+// The fp32 rounding of the fp64 formula, decided from the approximation c when possible (Ziv's
+// rounding test): c is within 6e-14 |GELU(v)| of the exact value, and for v >= -4 the formula
+// evaluated in fp64 is within 1.4e-16 |v| + 1.1e-16 |GELU(v)| of it (for v < 0, 1 + erf is exact
+// and the error of erf itself, scaled by v / 2, dominates).  When c - tol and c + tol round to
+// the same fp32 value, so do the exact value and the formula.  Fails for v < -4 (where 1 + erf
+// cancels so far that the formula's rounding depends on erf's last bit), NaN and infinity.
+__device__ __forceinline__ bool gelu_decided(double v, double c, float& g) {
+    const double tol = fma(fabs(c), 6e-14, 2.5e-16 * fabs(v));
+    g = (float)c;
+    return v >= -4.0 && (float)(c - tol) == (float)(c + tol);
+}
+
+__device__ __attribute__((noinline)) float gelu_f32(float h) {
+    float g;
+    if (gelu_decided((double)h, gelu_approx((double)h), g)) return g;
+    return gelu_f32_erf(h);
+}
+
+// Four GELUs per call: the four evaluations are independent, so their dependency chains
+// interleave (the epilogue of the MFMA GEMM runs at two waves per SIMD and would otherwise
+// wait on each chain in turn).
+__device__ __attribute__((noinline)) float4 gelu4_f32(float4 h) {
+    const float hv[4] = {h.x, h.y, h.z, h.w};
+    double c[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = gelu_approx((double)hv[i]);
+    float g[4];
+    bool ok[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ok[i] = gelu_decided((double)hv[i], c[i], g[i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (!ok[i]) g[i] = gelu_f32_erf(hv[i]);
+    return make_float4(g[0], g[1], g[2], g[3]);
 }
 
 __device__ __forceinline__ float activate(float v, int act) { return act == 1 ? gelu_f32(v) : v; }

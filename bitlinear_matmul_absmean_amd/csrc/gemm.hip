@@ -255,27 +255,52 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(ForwardArgs a, int tiles_m
         if (u % GK == 0) rsum[u / GK] = v;
     }
     __syncthreads();
+    // Output (i, r, j): token row mr, weight row n; returns false past M or N.
+    auto out_at = [&](int i, int r, int j, int64_t& m, int64_t& n, int& mr) {
+        mr = i * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
+        m = m0 + mr;
+        n = n0 + wn * WN + j * 32 + lr;
+        return m < M && n < N;
+    };
+    auto value = [&](int i, int r, int j, int64_t m, int64_t n, int mr) {
+        const int total = acc[i][j][r] - rsum[mr];
+        const float s = a.alpha_per_row ? dequant_scale(a.alpha[n], a.beta[m]) : ssc[mr];
+        if (a.acc) a.acc[m * N + n] = total;
+        return dequant(total, s, a.bias, n);
+    };
+    if constexpr (GELU) {
+        // Two token rows x two weight rows per call of the four-wide GELU.
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int mr = i * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
-            const int64_t m = m0 + mr;
-            if (m >= M) continue;
-            const int xs = rsum[mr];
-            const float s0 = ssc[mr];
+            for (int r = 0; r < 16; r += 2) {
+                float hv[4];
+                int64_t mm[4], nn[4];
+                bool in[4];
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int64_t n = n0 + wn * WN + j * 32 + lr;
-                if (n < N) {
-                    const int total = acc[i][j][r] - xs;
-                    const float s = a.alpha_per_row ? dequant_scale(a.alpha[n], a.beta[m]) : s0;
-                    const float v = dequant(total, s, a.bias, n);
-                    a.y[m * N + n] = GELU ? gelu_f32(v) : v;
-                    if (a.acc) a.acc[m * N + n] = total;
+                for (int q = 0; q < 4; ++q) {
+                    int mr;
+                    in[q] = out_at(i, r + q / 2, q % 2, mm[q], nn[q], mr);
+                    hv[q] = in[q] ? value(i, r + q / 2, q % 2, mm[q], nn[q], mr) : 0.0f;
                 }
+                const float4 g = gelu4_f32(make_float4(hv[0], hv[1], hv[2], hv[3]));
+                const float gv[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (in[q]) a.y[mm[q] * N + nn[q]] = gv[q];
             }
-        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    int64_t m, n;
+                    int mr;
+                    if (out_at(i, r, j, m, n, mr)) a.y[m * N + n] = value(i, r, j, m, n, mr);
+                }
+    }
 }
 
 bool gemm_supports_k(int64_t K) { return K % GEMM_BK == 0; }

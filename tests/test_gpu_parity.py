@@ -652,9 +652,11 @@ def test_end_to_end_block_scaled_bitlinear(dev):
 
 # ------------------------------------------------------------------ BitMLP [P3 §6.1]
 # (M, d_model, d_ff, bias): fc1's GELU epilogue on every kernel path -- fused GEMV (M <= 4),
-# 16x16x64 and 32x32x32 batched decode, the MFMA GEMM, the generic kernel (d % 64 != 0).
+# 16x16x64 and 32x32x32 batched decode, the MFMA GEMM (its four-wide GELU; ragged d_ff), the
+# generic kernel (d % 64 != 0); fc2's quantizer with 256-thread rows (M >= 256).
 MLP_CASES = [(1, 1024, 4096, False), (1, 4096, 11008, True), (3, 512, 2048, True), (8, 512, 1024, False),
-             (48, 256, 1024, True), (200, 256, 512, False), (5, 100, 36, True)]
+             (48, 256, 1024, True), (200, 256, 512, False), (5, 100, 36, True),
+             (300, 256, 1024, True), (130, 128, 1000, True)]
 
 
 @pytest.mark.parametrize("m,d,f,with_bias", MLP_CASES)
@@ -680,6 +682,94 @@ def test_mlp_forward_parity(dev, m, d, f, with_bias):
     assert np.array_equal(beta2.cpu().numpy().view(np.uint32), r["fc2"]["beta"].view(np.uint32))
     assert _rel_ok(y.cpu().numpy(), r["y"])
     assert np.array_equal(y.cpu().numpy().view(np.uint32), r["y"].view(np.uint32))
+
+
+def _gelu_probe_values():
+    """fp32 inputs for the GELU: every value in [-4.0625, -3.9375] (the edge of the range the
+    kernels evaluate without the library erf), random bit patterns over [-6, 12], normal samples,
+    values near 0, denormals, signed zeros, infinities and the largest finite values."""
+    lo, hi = np.float32(3.9375).view(np.uint32), np.float32(4.0625).view(np.uint32)
+    edge = -np.arange(lo, hi + 1, dtype=np.uint32).view(np.float32)
+    rng = np.random.default_rng(80)
+    pos = rng.integers(0, np.float32(12.0).view(np.uint32), 500_000, dtype=np.uint32).view(np.float32)
+    neg = -rng.integers(0, np.float32(6.0).view(np.uint32), 500_000, dtype=np.uint32).view(np.float32)
+    nrm = rng.normal(0.0, 1.0, 200_000).astype(np.float32)
+    fmax = np.finfo(np.float32).max
+    special = np.array([0.0, -0.0, 1e-45, -1e-45, 3e-45, -3e-45, 1.1754942e-38, -1.1754942e-38, 1e-30, -1e-30,
+                        np.inf, -np.inf, fmax, -fmax, 8.0625, 5.5, -5.5, 1.0, -1.0], np.float32)
+    v = np.concatenate([edge, pos, neg, nrm, special])
+    pad = (-v.size) % 256
+    return np.concatenate([v, np.zeros(pad, np.float32)])
+
+
+# (M, d_ff per call, calls): the one-token fused kernel; the MFMA GEMM's epilogue (four GELUs
+# per call), with all values in one call and in calls of 32768.
+GELU_VALUE_CASES = [(1, None, 1), (65, None, 1), (130, 32768, 49)]
+
+
+@pytest.mark.parametrize("m,chunk,calls", GELU_VALUE_CASES)
+def test_mlp_gelu_values(dev, m, chunk, calls):
+    """GELU against the oracle on up to 1.6M chosen inputs, bit for bit.  With x = 0 every
+    token's fc1 output is exactly bias1 (acc = 0, so y = 0 * scale + bias), which makes g =
+    GELU(bias1) row by row."""
+    torch, bl = dev
+    h_all = _gelu_probe_values()
+    d = 64
+    _say(f"mlp gelu values M={m} d_ff per call={chunk or h_all.size} calls={calls}")
+    # pin the premise on a slice with the oracle's fc1: x = 0 gives y == bias (+0 for -0)
+    codes = np.zeros((512, d), np.int8)
+    xq0, beta0 = oracle.quantize_act(np.zeros((1, d), np.float32))
+    _, y0 = oracle.forward(xq0, beta0, oracle.pack(codes), d, np.float32(1.0), bias=h_all[-512:])
+    assert np.array_equal(y0[0].view(np.uint32), (h_all[-512:] + np.float32(0.0)).view(np.uint32))
+    f = chunk or h_all.size
+    x = torch.zeros((m, d), dtype=torch.float32, device="cuda")
+    p1 = torch.full((f, d // 4), 0x55, dtype=torch.uint8, device="cuda")   # every code W = 0
+    p2 = torch.full((d, f // 4), 0x55, dtype=torch.uint8, device="cuda")
+    one = torch.ones(1, dtype=torch.float32, device="cuda")
+    xq2 = torch.empty((m, f), dtype=torch.int8, device="cuda")      # fc2's quantized input
+    beta2 = torch.empty(m, dtype=torch.float32, device="cuda")
+    g = torch.empty((m, f), dtype=torch.float32, device="cuda")
+    for c in range(calls):
+        h = h_all[c * f:(c + 1) * f]
+        h = np.concatenate([h, np.zeros(f - h.size, np.float32)])      # the last call's tail: zeros
+        bl.bitlinear_mlp_forward(x, p1, one, p2, one, bias1=_to(torch, h), g=g, x_q2=xq2, beta2=beta2)
+        torch.cuda.synchronize()
+        want = oracle.gelu(h + np.float32(0.0))
+        got = g.cpu().numpy()
+        nan = np.isnan(want)
+        for r in range(m):
+            assert np.array_equal(np.isnan(got[r]), nan)
+            bad = np.flatnonzero(got[r][~nan].view(np.uint32) != want[~nan].view(np.uint32))
+            assert bad.size == 0, (c, r, h[~nan][bad[:5]], got[r][~nan][bad[:5]], want[~nan][bad[:5]])
+        if c == 0 and np.isfinite(want).all():
+            xq_ref, beta_ref = oracle.quantize_act(want[None, :])
+            assert np.array_equal(xq2.cpu().numpy()[0], xq_ref[0])
+            assert np.array_equal(beta2.cpu().numpy()[:1].view(np.uint32), beta_ref.view(np.uint32))
+
+
+def test_binding_rejects_short_buffers(dev):
+    """The binding checks every buffer the library reads or writes by size before any launch."""
+    torch, bl = dev
+    m, k, n = 4, 256, 64
+    xq = torch.zeros((m, k), dtype=torch.int8, device="cuda")
+    beta = torch.ones(m, dtype=torch.float32, device="cuda")
+    wp = torch.full((n, k // 4), 0x55, dtype=torch.uint8, device="cuda")
+    one = torch.ones(1, dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError, match="bias"):
+        bl.bitlinear_forward(xq, beta, wp, one, bias=torch.zeros(n - 1, device="cuda"))
+    with pytest.raises(ValueError, match="y"):
+        bl.bitlinear_forward(xq, beta, wp, one, y=torch.zeros((m, n - 1), device="cuda"))
+    with pytest.raises(ValueError, match="beta"):
+        bl.bitlinear_forward(xq, beta[:m - 1], wp, one)
+    with pytest.raises(ValueError, match="alpha"):
+        bl.bitlinear_forward_rows(xq, beta, wp, torch.ones(n - 1, device="cuda"))
+    x = torch.zeros((m, k), dtype=torch.float32, device="cuda")
+    w2 = torch.full((k, n // 4), 0x55, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError, match="bias1"):
+        bl.bitlinear_mlp_forward(x, wp, one, w2, one, bias1=torch.zeros(n // 2, device="cuda"))
+    with pytest.raises(ValueError, match="x_q2"):
+        bl.bitlinear_mlp_forward(x, wp, one, w2, one, x_q2=torch.zeros((m, 1), dtype=torch.int8, device="cuda"))
+    torch.cuda.synchronize()
 
 
 # ------------------------------------------------------------------ five codes per byte (R14)
