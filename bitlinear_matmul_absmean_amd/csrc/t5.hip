@@ -74,7 +74,29 @@ __global__ __launch_bounds__(64 * T5_WAVES) void k_gemv_t5(T5Args a) {
     const int64_t m = blockIdx.y;
     const int8_t* xrow = a.xq + m * K;
 
+    const int64_t r0 = ((int64_t)blockIdx.x * T5_WAVES + wave) * a.rows_per_wave;
+    const int64_t r1 = r0 + a.rows_per_wave < N ? r0 + a.rows_per_wave : N;
+    const u32x4* wp = reinterpret_cast<const u32x4*>(a.wp);
+    // Rows past the wave's range (or past N, for a wave with none) are clamped to the last row, so
+    // the loads stay branch-free and in bounds; their sums are never stored.
+    auto load_rows = [&](u32x4 (&w)[R][CPL], int64_t rbase) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t row = rbase + r < r1 ? rbase + r : (r1 > 0 ? r1 - 1 : 0);
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                const int c = lane + 64 * j < nch ? lane + 64 * j : 0;
+                w[r][j] = wp[row * nch + c];
+            }
+        }
+    };
+    // The first rows are requested before the tables are built, so that their latency covers
+    // the table and the activation staging.
+    u32x4 w[R][CPL];
+    load_rows(w, r0);
+
     // bytes 243..255 are never written; their entries only keep every lookup in bounds
+    // (consecutive threads write consecutive entries: no bank conflicts)
     for (int e = tid; e < 256 * T5_COPIES; e += 64 * T5_WAVES) {
         const int v = e / T5_COPIES;
         const uint32_t c0 = v % 3, c1 = (v / 3) % 3, c2 = (v / 9) % 3, c3 = (v / 27) % 3, c4 = v / 81;
@@ -104,20 +126,11 @@ __global__ __launch_bounds__(64 * T5_WAVES) void k_gemv_t5(T5Args a) {
     const float s = dequant_scale(a.alpha[0], a.beta[m]);
 
     const uint2* myl = lut + (lane & (T5_COPIES - 1));
-    const int64_t r0 = ((int64_t)blockIdx.x * T5_WAVES + wave) * a.rows_per_wave;
-    const int64_t r1 = r0 + a.rows_per_wave < N ? r0 + a.rows_per_wave : N;
-    const u32x4* wp = reinterpret_cast<const u32x4*>(a.wp);
     for (int64_t rbase = r0; rbase < r1; rbase += R) {
-        u32x4 w[R][CPL];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int64_t row = rbase + r < r1 ? rbase + r : r1 - 1;    // clamped: loads stay branch-free
-#pragma unroll
-            for (int j = 0; j < CPL; ++j) {
-                const int c = lane + 64 * j < nch ? lane + 64 * j : 0;
-                w[r][j] = wp[row * nch + c];
-            }
-        }
+        // the next rows' loads go out before this step's sums; unconditional (clamped rows), so
+        // the wait for this step's rows leaves them in flight
+        u32x4 wn[R][CPL];
+        load_rows(wn, rbase + R);
         int acc[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = 0;
@@ -147,6 +160,10 @@ __global__ __launch_bounds__(64 * T5_WAVES) void k_gemv_t5(T5Args a) {
             const int64_t row = rbase + r;
             if (lane == 0 && row < r1) a.y[m * N + row] = dequant(total, s, a.bias, row);
         }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) w[r][j] = wn[r][j];
     }
 }
 
