@@ -66,6 +66,36 @@ def _graph_time(torch, fn, reps: int, warm_fn=None, warm_replays: int = 1):
     return e0.elapsed_time(e1) / reps, g
 
 
+def _eager_time(torch, fn, reps: int):
+    """Launch `fn(i)` for i < reps eagerly (no graph) back to back on the current stream, after
+    three untimed calls; return ms per rep, event to event on that stream."""
+    for i in range(min(reps, 3)):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def _single_call_us(torch, fn, trials: int = 50):
+    """Median over `trials` of one eager call on an idle GPU, events on either side of it."""
+    times = []
+    for i in range(trials):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    times.sort()
+    return times[len(times) // 2]
+
+
 def decode_setup(torch, bl, workloads, dev):
     """Quantize the three decode weights once, then fill rotation pools of packed copies."""
     per_step = sum(n * k // 4 for k, n in DECODE_SHAPES)
@@ -148,10 +178,13 @@ def roofline_gemv(torch, bl, sh, copies, reps=480):
     bl.bitlinear_quantize_act(sh["x"][0], sh["xq"], sh["beta"])
     ms_f, _ = _graph_time(torch, lambda i: bl.bitlinear_forward(sh["xq"], sh["beta"], sh["pool"][i % copies],
                                                                 sh["alpha"], y=sh["y"]), reps)
+    # one call from an idle GPU (weights from the pool, not in cache): launch to completion
+    single = _single_call_us(torch, lambda i: bl.bitlinear_forward_fused(sh["x"][i % 8], sh["pool"][(7 * i) % copies],
+                                                                         sh["alpha"], y=sh["y"]))
     return dict(kernel=bl.bitlinear_forward_fused_kernel(1, k, n, sh["x"][0], sh["pool"][0]),
                 shape=dict(M=1, K=k, N=n), bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
                 unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=committed_traffic(),
-                us_per_launch=round(ms * 1e3, 3), bytes_per_launch=alg,
+                us_per_launch=round(ms * 1e3, 3), bytes_per_launch=alg, single_call_us=round(single, 2),
                 forward_only=dict(kernel="gemv_dot4", us_per_launch=round(ms_f * 1e3, 3),
                                   gbs=round((n * k // 4 + k + 4 * n) / (ms_f * 1e-3) / 1e9, 1)))
 
@@ -538,10 +571,11 @@ def chain70b_bench(torch, bl, workloads, dev, layers=80, reps=3):
     ms, _ = _graph_time(torch, step, reps)
     ms2, _ = _graph_time(torch, step_two_call, reps)
     ms3, _ = _graph_time(torch, step_grouped, reps)
+    ms_e = _eager_time(torch, step, 1)
     gbs = total / (ms * 1e-3) / 1e9
     res = dict(layers=layers, weight_bytes=total, ms_per_step=round(ms, 3), weight_gbs=round(gbs, 1),
                pct_hbm=round(100 * gbs / HBM_PEAK_GBS, 2), tokens_per_s=round(1e3 / ms, 1),
-               two_call_ms_per_step=round(ms2, 3),
+               two_call_ms_per_step=round(ms2, 3), eager_ms_per_step=round(ms_e, 3),
                grouped=dict(calls_per_layer=4, ms_per_step=round(ms3, 3),
                             weight_gbs=round(total / (ms3 * 1e-3) / 1e9, 1),
                             pct_hbm=round(100 * total / (ms3 * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
@@ -761,6 +795,8 @@ def main():
     log(f"decode step {ms_step * 1e3:.2f} us -> {value:.1f} GB/s")
     ms_two, _ = _graph_time(torch, lambda i: decode_step_two_call(bl, shapes, copies, i), args.steps)
     log(f"decode step, two-call ABI {ms_two * 1e3:.2f} us")
+    ms_eager = _eager_time(torch, lambda i: decode_step(bl, shapes, copies, i), args.steps)
+    log(f"decode step, eager launches {ms_eager * 1e3:.2f} us")
 
     roof = roofline_gemv(torch, bl, shapes[1], copies)
     log(f"roofline {roof}")
@@ -812,6 +848,9 @@ def main():
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_two_call": {"us_per_step": round(ms_two * 1e3, 2),
                             "weight_gbs": round(per_step / (ms_two * 1e-3) / 1e9, 1)},
+        "decode_eager": {"us_per_step": round(ms_eager * 1e3, 2),
+                         "weight_gbs": round(per_step / (ms_eager * 1e-3) / 1e9, 1),
+                         "what": "the same steps launched without a graph (host launch rate included)"},
         "roofline": roof,
         "ceilings": ceil,
         "cpu_baseline": cpu,
