@@ -109,9 +109,16 @@ def _dev(t, dtype, name, numel=None):
 
 
 def _stream(stream):
+    """Raw HIP stream handle: `stream`, else torch's current stream on the current device (the
+    capture stream inside torch.cuda.graph).  The raw accessor skips building a Stream object,
+    a few microseconds of host time per call."""
+    if stream is not None:
+        return stream.cuda_stream
     torch = _torch()
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(torch.cuda.current_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def bitlinear_quantize_weights(W, W_packed=None, alpha=None, workspace=None, stream=None):
