@@ -668,6 +668,14 @@ def kernel_only(kind: str, launches: int):
         torch.cuda.synchronize()
         log(f"gemv_fused: {launches} launches of {bl.bitlinear_forward_fused_kernel(1, k, n, x, packed)}")
         return
+    if kind == "gemv_fused_graph":
+        # the roofline measurement itself: the same pool and graph as roofline_gemv
+        shapes, _, copies = decode_setup(torch, bl, workloads, dev)
+        roof = roofline_gemv(torch, bl, shapes[1], copies, reps=launches)
+        log(f"gemv_fused_graph: {launches} launches in one graph, {roof['us_per_launch']} us per launch "
+            f"(events, launch to launch), {roof['achieved']} GB/s")
+        print(json.dumps(roof), flush=True)
+        return
     if kind == "batched":
         m, k, n = 64, 4096, 11008
         w = torch.from_numpy(workloads.weights(3, n, k)).to(dev)
@@ -698,6 +706,43 @@ def kernel_only(kind: str, launches: int):
         log(f"gemm: {launches} launches")
         return
     raise SystemExit(f"unknown --kernel-only {kind}")
+
+
+def trace_summary(trace_dir: str, plain_json: str, traced_json: str, commands: str):
+    """Markdown summary of `--kernel-only gemv_fused_graph` run without and with
+    `rocprofv3 --kernel-trace`: the roofline kernel's launches in the trace are, in order, the
+    three eager warm-up calls of the graph timer, the untimed replay, the timed replay (L
+    launches each) and the 50 single calls; the timed replay's launch-to-launch time from the
+    trace is set against the events of the same traced run."""
+    import csv
+    import glob
+    import statistics
+    plain = json.loads(open(plain_json).read().strip().splitlines()[-1])
+    traced = json.loads(open(traced_json).read().strip().splitlines()[-1])
+    rows = []
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    name = next(r["Kernel_Name"] for r in rows if r["Kernel_Name"].startswith("void bitlinear::k_gemv<")
+                and ", true, " in r["Kernel_Name"])
+    ts = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows if r["Kernel_Name"] == name)
+    L = (len(ts) - 3 - 50) // 2
+    timed = ts[3 + L:3 + 2 * L]
+    dur = [e - b for b, e in timed]
+    span = (timed[-1][1] - timed[0][0]) / L / 1e3
+    out = ["# Roofline kernel: event timing against the kernel trace (fused decode GEMV, M=1, K=4096, N=11008)", "",
+           "Commands (repository root, one MI355X):", "", "```"] + [c.strip() for c in commands.split(";")] + [
+           "```", "",
+           f"Kernel: `{name}`; {L} launches in one graph, weights rotating through the decode pool.", "",
+           "| run | per launch, events (bench.py) | per launch, trace (first start to last end / launches) "
+           "| kernel duration in the trace (mean / median / min) |", "|---|---|---|---|",
+           f"| without the tracer | {plain['us_per_launch']} us ({plain['achieved']} GB/s) | - | - |",
+           f"| with `--kernel-trace` | {traced['us_per_launch']} us | {span:.2f} us "
+           f"| {statistics.mean(dur) / 1e3:.2f} / {statistics.median(dur) / 1e3:.2f} / {min(dur) / 1e3:.2f} us |", "",
+           "In the traced run the events and the trace agree on the time per launch; the kernel's own",
+           "duration is shorter by the dispatch gap between launches.  The tracer itself lengthens every",
+           "launch (compare the two event figures), so bench.py's roofline figure comes from the run",
+           "without it.", ""]
+    print("\n".join(out))
 
 
 def _pmc_means(d: str):
@@ -759,15 +804,20 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extras", action="store_true", help="headline workload and roofline only")
     ap.add_argument("--no-chain", action="store_true", help="skip the 70B-class chain")
-    ap.add_argument("--kernel-only", choices=["gemv_fused", "copy", "gemm", "batched"],
+    ap.add_argument("--kernel-only", choices=["gemv_fused", "gemv_fused_graph", "copy", "gemm", "batched"],
                     help="run only this kernel (for rocprofv3 counter runs)")
     ap.add_argument("--launches", type=int, default=50)
+    ap.add_argument("--trace-summary", nargs=3, metavar=("TRACE_DIR", "PLAIN_JSON", "TRACED_JSON"),
+                    help="summarise the roofline kernel's trace against its event timing")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("GEMV_FETCH", "GEMV_WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="write the traffic summary from four rocprofv3 --pmc output directories")
     ap.add_argument("--pmc-commands", default="", help="';'-separated commands recorded in the summary")
     args = ap.parse_args()
     if args.pmc_summary:
         print(pmc_summary(*args.pmc_summary, [c.strip() for c in args.pmc_commands.split(";") if c.strip()]))
+        return
+    if args.trace_summary:
+        trace_summary(*args.trace_summary, args.pmc_commands)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path. "
