@@ -162,9 +162,9 @@ FWD_CASES = [
     (65, 1024, 130), (128, 256, 256), (130, 4096, 200), (300, 128, 257),
     (64, 4160, 33), (7, 28672, 20), (40, 2048, 300), (16, 16448, 65), (2, 32832, 17), (63, 320, 1000),
     (200, 4160, 130), (129, 192, 300), (1000, 128, 70), (96, 11008, 514),
-    # the GEMM's 128-token tiles (more than 128 of them), ragged in M and N; 64-token tiles
-    # below (the smaller prefill cases above)
-    (1100, 128, 24577), (1030, 256, 2100),
+    # the GEMM's 128-token tiles (more than 128 of them: two rounds, 129 ragged, exactly 256),
+    # ragged in M and N; 64-token tiles below (the smaller prefill cases above)
+    (1100, 128, 24577), (1030, 256, 2100), (300, 192, 11000), (2048, 640, 4096),
     (1, 100, 33), (6, 4100, 65), (70, 12, 9),      # K % 64 != 0: generic kernel
     # one token, the launch shapes of the decode GEMV: 16-wave workgroups (rows of <= 3 chunks per
     # lane, N >= 4096) with 1, 3 and 4 rows per wave; 8-wave workgroups for longer rows; ragged N
@@ -656,7 +656,7 @@ def test_end_to_end_block_scaled_bitlinear(dev):
 # generic kernel (d % 64 != 0); fc2's quantizer with 256-thread rows (M >= 256).
 MLP_CASES = [(1, 1024, 4096, False), (1, 4096, 11008, True), (3, 512, 2048, True), (8, 512, 1024, False),
              (48, 256, 1024, True), (200, 256, 512, False), (5, 100, 36, True),
-             (300, 256, 1024, True), (130, 128, 1000, True)]
+             (300, 256, 1024, True), (130, 128, 1000, True), (260, 128, 16000, True)]
 
 
 @pytest.mark.parametrize("m,d,f,with_bias", MLP_CASES)
