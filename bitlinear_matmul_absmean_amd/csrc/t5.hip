@@ -149,7 +149,7 @@ __global__ __launch_bounds__(64 * T5_WAVES) void k_gemv_t5(T5Args a) {
                         const uint32_t b = (wd[q >> 2] >> (8 * (q & 3))) & 0xFFu;
                         const uint2 e = myl[b * T5_COPIES];
                         acc[r] = dot4(e.x, xv[q].x, acc[r]);
-                        acc[r] += (int)e.y * (int)xv[q].y;
+                        acc[r] = dot4(e.y, xv[q].y, acc[r]);    // c4 (byte 0) times x(5p+4): one full-rate op
                     }
                 }
             }
