@@ -207,6 +207,9 @@ static hipError_t launch_t5_cpl(const T5Args& a0, hipStream_t s) {
     a.rows_per_wave = (a.N + 512 * T5_WAVES - 1) / (512 * T5_WAVES);
     constexpr int RMAX = CPL >= 8 ? 1 : 8 / CPL;
     if (RMAX >= 4 && a.rows_per_wave >= 4) return launch_t5_r<CPL, (RMAX >= 4 ? 4 : 1)>(a, s);
+    // three rows per wave in one step rather than two steps of two (the second half wasted on a
+    // clamped row, the activations read twice)
+    if (RMAX >= 3 && a.rows_per_wave == 3) return launch_t5_r<CPL, (RMAX >= 3 ? 3 : 1)>(a, s);
     if (RMAX >= 2 && a.rows_per_wave >= 2) return launch_t5_r<CPL, (RMAX >= 2 ? 2 : 1)>(a, s);
     return launch_t5_r<CPL, 1>(a, s);
 }

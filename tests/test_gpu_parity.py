@@ -791,7 +791,7 @@ def test_quantize_weights_t5_parity(dev, n, k):
 
 
 T5_CASES = [(1, 4096, 4096), (1, 11008, 300), (1, 28672, 64), (2, 100, 33), (3, 4096, 1000), (1, 80, 7),
-            (1, 84, 5), (5, 1024, 70), (1, 65536, 8), (1, 4096, 11008)]
+            (1, 84, 5), (5, 1024, 70), (1, 65536, 8), (1, 4096, 11008), (2, 2000, 9000), (1, 6000, 12000)]
 
 
 @pytest.mark.parametrize("m,k,n", T5_CASES)
