@@ -198,8 +198,12 @@ def test_kernel_selection(bl):
 def test_binding_has_no_host_fallback():
     src = open(os.path.join(ROOT, "bitlinear_matmul_absmean_amd", "__init__.py")).read()
     assert "import oracle" not in src and "from oracle" not in src
-    for f in os.listdir(os.path.join(ROOT, "bitlinear_matmul_absmean_amd", "csrc")):
-        text = open(os.path.join(ROOT, "bitlinear_matmul_absmean_amd", "csrc", f)).read()
+    csrc = os.path.join(ROOT, "bitlinear_matmul_absmean_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        path = os.path.join(csrc, f)
+        if not os.path.isfile(path):
+            continue
+        text = open(path).read()
         assert "oracle" not in text.lower(), f
 
 

@@ -9,6 +9,7 @@ No GPU; the oracle is not involved.
 import importlib.util
 import os
 import re
+import sys
 
 import numpy as np
 
@@ -17,9 +18,15 @@ CSRC = os.path.join(ROOT, "bitlinear_matmul_absmean_amd", "csrc")
 
 
 def _fit_module():
+    # loaded without writing bytecode next to the kernel sources
     spec = importlib.util.spec_from_file_location("fit_gelu", os.path.join(CSRC, "fit_gelu.py"))
     mod = importlib.util.module_from_spec(spec)
-    spec.loader.exec_module(mod)
+    keep = sys.dont_write_bytecode
+    sys.dont_write_bytecode = True
+    try:
+        spec.loader.exec_module(mod)
+    finally:
+        sys.dont_write_bytecode = keep
     return mod
 
 
