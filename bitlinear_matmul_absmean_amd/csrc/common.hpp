@@ -243,7 +243,7 @@ __device__ __forceinline__ float activate(float v, int act) { return act == 1 ? 
 
 bool gemv_supports(int64_t M, int64_t K);
 struct GemvShape {
-    int waves_per_wg;         // 4 or 16
+    int waves_per_wg;         // 4 or 8
     int64_t waves_target;     // waves the grid aims at
 };
 GemvShape gemv_shape(int64_t M, int64_t K, int64_t N, bool fused);

@@ -383,13 +383,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(GemvArgs g) {
 //    workgroups win (4 waves, 8192 waves in all, 1-2 rows each: loads of many waves overlap
 //    the short compute of each); longer rows want about 2048 waves;
 //  * fused (x fp32 given): every workgroup reads all of x to find its absmax, so fewer, larger
-//    workgroups win: 8 waves and 2048 in all, or 16 waves and 4096 in all for rows of two or
-//    three chunks per lane (their registers fit the 128 that 16-wave workgroups allow).
+//    workgroups win: 8 waves and 2048 in all.  16 waves and 4096 in all for rows of two to
+//    four chunks per lane was 1-10% slower (weights not in cache: K = 8192, N = 4096, 5.80 vs
+//    5.21 us; K = 11008, N = 4096, 7.35 vs 6.68 us; K = 16384, N = 4096, 8.65 vs 7.93 us).
 // Shapes with too few rows for that many waves per CU fall back to 4-wave workgroups.
-static int64_t rows_per_step(int64_t rpw) {      // the single-step row counts instantiated
-    return rpw <= 4 ? rpw : rpw <= 6 ? 6 : rpw <= 8 ? 8 : 9;
-}
-
 GemvShape gemv_shape(int64_t M, int64_t K, int64_t N, bool fused) {
     GemvShape sh{4, 2048};
     if (M != 1) {
@@ -405,8 +402,6 @@ GemvShape gemv_shape(int64_t M, int64_t K, int64_t N, bool fused) {
     GemvShape want;
     if (!fused)
         want = cpl == 1 ? GemvShape{4, N >= 8192 ? 8192 : 2048} : GemvShape{cpl <= 3 ? 4 : 8, 2048};
-    else if (cpl >= 2 && rows_per_step((N + 4095) / 4096) * cpl <= 8)
-        want = GemvShape{16, 4096};    // one short step per wave within the 128 VGPRs of 16 waves
     else
         want = GemvShape{8, 2048};
     if (N >= (int64_t)want.waves_per_wg * 256) sh = want;
@@ -414,9 +409,8 @@ GemvShape gemv_shape(int64_t M, int64_t K, int64_t N, bool fused) {
 }
 
 // single step: R from {1, 2, 3, 4, 6, 8}, the smallest not below the rows per wave, within
-// single_loads(WAVES, CPL) loads of 16 bytes per lane: 8 in 16-wave workgroups (their 128
-// VGPRs; more rows there measured slower than two-buffer steps), 20 with 4 or 8 waves (256)
-constexpr int single_loads(int waves, int /*cpl*/) { return waves == 16 ? 8 : 20; }
+// 20 loads of 16 bytes per lane (4- and 8-wave workgroups have 256 VGPRs per wave)
+constexpr int single_loads(int /*waves*/, int /*cpl*/) { return 20; }
 constexpr int next_rows(int r) { return r == 1 ? 2 : r == 2 ? 3 : r == 3 ? 4 : r == 4 ? 6 : 8; }
 
 template <int MT, int CPL, bool FUSED, int WAVES, int R>
@@ -457,8 +451,6 @@ static hipError_t launch_shape(const GemvArgs& g0, int64_t waves_target, hipStre
 template <int MT, int CPL, bool FUSED>
 static hipError_t launch_cpl(const GemvArgs& g, hipStream_t s) {
     const GemvShape sh = gemv_shape(g.f.M, g.f.K, g.f.N, FUSED);
-    if constexpr (MT == 1)
-        if (sh.waves_per_wg == 16) return launch_shape<MT, CPL, FUSED, 16>(g, sh.waves_target, s);
     if constexpr (MT == 1)
         if (sh.waves_per_wg == 8) return launch_shape<MT, CPL, FUSED, 8>(g, sh.waves_target, s);
     return launch_shape<MT, CPL, FUSED, 4>(g, sh.waves_target, s);

@@ -166,8 +166,8 @@ FWD_CASES = [
     # ragged in M and N; 64-token tiles below (the smaller prefill cases above)
     (1100, 128, 24577), (1030, 256, 2100), (300, 192, 11000), (2048, 640, 4096),
     (1, 100, 33), (6, 4100, 65), (70, 12, 9),      # K % 64 != 0: generic kernel
-    # one token, the launch shapes of the decode GEMV: 16-wave workgroups (rows of <= 3 chunks per
-    # lane, N >= 4096) with 1, 3 and 4 rows per wave; 8-wave workgroups for longer rows; ragged N
+    # one token, the launch shapes of the decode GEMV: 4-wave workgroups for rows of up to three
+    # chunks per lane, 8-wave ones for longer rows, one to several rows per wave; ragged N
     (1, 4096, 4096), (1, 4096, 11008), (1, 12288, 4097), (1, 4096, 16385), (1, 16384, 2048),
     (1, 28672, 2100), (1, 8192, 2048),
     # two to four tokens on the GEMV (matrices of 2^26 weights or more; two tokens with K >= 8192)
