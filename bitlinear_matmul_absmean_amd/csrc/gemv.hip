@@ -381,7 +381,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(GemvArgs g) {
 // Measured on MI355X over the decode shapes (one token):
 //  * forward (x_q given): with rows of one 64-weight chunk per lane (K <= 4096) many small
 //    workgroups win (4 waves, 8192 waves in all, 1-2 rows each: loads of many waves overlap
-//    the short compute of each); longer rows want about 2048 waves;
+//    the short compute of each); longer rows want about 2048 waves, in workgroups of 8 except
+//    for three chunks per lane, where 4 win (weights not in cache: K = 8192, N = 4096, 3.84 vs
+//    4.42 us with 8 and 4 waves; N = 8192, 5.30 vs 6.38 us; K = 11008, N = 4096, 5.32 vs
+//    4.40 us; N = 8192, 8.01 vs 6.71 us);
 //  * fused (x fp32 given): every workgroup reads all of x to find its absmax, so fewer, larger
 //    workgroups win: 8 waves and 2048 in all.  16 waves and 4096 in all for rows of two to
 //    four chunks per lane was 1-10% slower (weights not in cache: K = 8192, N = 4096, 5.80 vs
@@ -401,7 +404,7 @@ GemvShape gemv_shape(int64_t M, int64_t K, int64_t N, bool fused) {
     const int64_t cpl = (K / 64 + 63) / 64;
     GemvShape want;
     if (!fused)
-        want = cpl == 1 ? GemvShape{4, N >= 8192 ? 8192 : 2048} : GemvShape{cpl <= 3 ? 4 : 8, 2048};
+        want = cpl == 1 ? GemvShape{4, N >= 8192 ? 8192 : 2048} : GemvShape{cpl == 3 ? 4 : 8, 2048};
     else
         want = GemvShape{8, 2048};
     if (N >= (int64_t)want.waves_per_wg * 256) sh = want;
