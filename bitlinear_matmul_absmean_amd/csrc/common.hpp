@@ -164,13 +164,16 @@ struct ForwardArgs {
     int act = 0;          // activation applied to y after the dequantization: 0 none, 1 GELU
 };
 
-// GELU (the erf form of torch.nn.GELU) between the two BitLinears of the BitMLP [P3 §6.1]:
-// 0.5 h (1 + erf(h / sqrt 2)) in fp64, rounded to fp32 once.  This is that formula with the
-// library erf; the fast path below falls back to it whenever it cannot decide the rounding
-// (inlined there, so that the GELU functions make no calls and save nothing to scratch).
+// GELU (the exact, erf-based GELU of torch.nn.GELU) between the two BitLinears of the BitMLP
+// [P3 §6.1]: h Phi(h) with Phi(h) = erfc(-h / sqrt 2) / 2, the complementary form, in which no
+// term cancels for negative h (1 + erf(h / sqrt 2) loses every digit below h = -8.3), evaluated
+// in fp64 as (0.5 h) erfc(-h * RN64(1/sqrt 2)) and rounded to fp32 once.  This is that formula
+// with the library erfc; the fast path below falls back to it whenever it cannot decide the
+// rounding (inlined there, so that the GELU functions make no calls and save nothing to
+// scratch).
 __device__ __forceinline__ float gelu_f32_erf(float h) {
     const double v = (double)h;
-    return (float)(0.5 * v * (1.0 + erf(v * 0.70710678118654752440)));
+    return (float)(0.5 * v * erfc(-v * 0.70710678118654752440));
 }
 
 // Fast GELU in fp64 without branches: GELU(v) = v Phi(v) with Phi(v) = erfc(y) / 2 for v < 0 and
@@ -204,11 +207,12 @@ __device__ __forceinline__ double gelu_approx(double v) {
 }
 
 // The fp32 rounding of the fp64 formula, decided from the approximation c when possible (Ziv's
-// rounding test): c is within 6e-14 |GELU(v)| of the exact value, and for v >= -4 the formula
-// evaluated in fp64 is within 1.4e-16 |v| + 1.1e-16 |GELU(v)| of it (for v < 0, 1 + erf is exact
-// and the error of erf itself, scaled by v / 2, dominates).  When c - tol and c + tol round to
-// the same fp32 value, so do the exact value and the formula.  Fails for v < -4 (where 1 + erf
-// cancels so far that the formula's rounding depends on erf's last bit), NaN and infinity.
+// rounding test): c is within 2e-14 |GELU(v)| of the exact value (measured against long-double
+// erfcl), and for v >= -4 the formula evaluated in fp64 is within 3e-15 |GELU(v)| of it (the
+// argument's rounding, scaled by at most 2 z^2 + 1 = 17 through erfc, erfc's own few ulps and
+// the product's rounding), so tol covers both.  When c - tol and c + tol round to the same
+// fp32 value, so do the exact value and the formula.  Not attempted for v < -4, where the
+// polynomial's range and error bound end, nor for NaN and infinity: those take the formula.
 __device__ __forceinline__ bool gelu_decided(double v, double c, float& g) {
     const double tol = fma(fabs(c), 6e-14, 2.5e-16 * fabs(v));
     g = (float)c;

@@ -47,9 +47,11 @@
  *       y[m, n] = fp32(S * (beta[m] / 127)) with S = sum_b alpha[n, b] * acc[m, n, b]
  *       accumulated in fp64 in ascending b and beta/127 an fp64 division; + bias in fp32.
  *   R13 the BitMLP of [P3 §6.1] is fc2(GELU(fc1(x))) with two BitLinears; GELU is the
- *       erf form of torch.nn.GELU, 0.5 h (1 + erf(h / sqrt 2)), evaluated in fp64 as
- *       (0.5 h) (1 + erf(h * RN64(1/sqrt 2))) and rounded to fp32 once; fc2 quantizes the
- *       fp32 GELU output like any activation.
+ *       exact (erf) GELU of torch.nn.GELU, h Phi(h) = 0.5 h (1 + erf(h / sqrt 2)), written
+ *       with the complementary error function, Phi(h) = erfc(-h / sqrt 2) / 2, so that no
+ *       term cancels for negative h (1 + erf(h / sqrt 2) loses every digit below h = -8.3);
+ *       evaluated in fp64 as (0.5 h) erfc(-h * RN64(1/sqrt 2)) and rounded to fp32 once;
+ *       fc2 quantizes the fp32 GELU output like any activation.
  *   R14 sub-2-bit packing [P2 §1.1, §6.1] (a "more compact" encoding, format not given):
  *       five codes c = W_hat + 1 per byte as the base-3 number sum_i c_i 3^i, c_i the code of
  *       weight 5b + i of the row; a row takes 16 ceil(K / 80) bytes, and trits past K hold
@@ -321,12 +323,13 @@ int oracle_dequant_blocks(const int32_t* acc, const float* beta, const float* al
 }
 
 /* ---------------------------------------------------------------- BitMLP (R13) */
-/* [P3 §6.1] the GELU between the two BitLinears of the BitMLP, elementwise. */
+/* [P3 §6.1] the GELU between the two BitLinears of the BitMLP, elementwise:
+ * GELU(h) = h Phi(h), Phi(h) = erfc(-h / sqrt 2) / 2 (R13). */
 int oracle_gelu(const float* h, int64_t count, float* g) {
     if (!h || !g || count <= 0) return ORACLE_EINVAL;
     for (int64_t i = 0; i < count; ++i) {
         const double v = (double)h[i];
-        g[i] = (float)(0.5 * v * (1.0 + erf(v * 0.70710678118654752440)));
+        g[i] = (float)(0.5 * v * erfc(-v * 0.70710678118654752440));
     }
     return ORACLE_OK;
 }

@@ -54,9 +54,12 @@ MUTANTS = [
     ("block dequant in fp32", "const double t = (double)beta[m] / 127.0;", "const double t = (double)(beta[m] / 127.0f);"),
     ("block dequant drops alpha", "s += (double)alpha[n * kb + b] * (double)acc[(m * n_rows + n) * kb + b];",
      "s += (double)acc[(m * n_rows + n) * kb + b];"),
-    ("gelu with sqrt 2 for 1/sqrt 2", "erf(v * 0.70710678118654752440)", "erf(v * 1.41421356237309504880)"),
-    ("gelu without the half", "g[i] = (float)(0.5 * v * (1.0 + erf(", "g[i] = (float)(v * (1.0 + erf("),
-    ("gelu with 1 - erf", "(1.0 + erf(v", "(1.0 - erf(v"),
+    ("gelu with sqrt 2 for 1/sqrt 2", "erfc(-v * 0.70710678118654752440)", "erfc(-v * 1.41421356237309504880)"),
+    ("gelu without the half", "g[i] = (float)(0.5 * v * erfc(", "g[i] = (float)(v * erfc("),
+    ("gelu with erfc(+h / sqrt 2)", "erfc(-v * 0.7071", "erfc(v * 0.7071"),
+    ("gelu as 1 + erf (cancels for h < -5)", "erfc(-v * 0.70710678118654752440)", "(1.0 + erf(v * 0.70710678118654752440))"),
+    ("gelu flushed to 0 below -6", "g[i] = (float)(0.5 * v * erfc(-v * 0.70710678118654752440));",
+     "g[i] = v < -6.0 ? 0.0f : (float)(0.5 * v * erfc(-v * 0.70710678118654752440));"),
     ("t5 radix 4", "for (int i = 0; i < 5; ++i, p3 *= 3) {", "for (int i = 0; i < 5; ++i, p3 *= 4) {"),
     ("t5 padding as weight -1", "int c = 1;                                     /* past K: weight 0 */",
      "int c = 0;"),

@@ -572,10 +572,50 @@ def test_block_functions_reject_k_not_a_multiple_of_128():
 
 
 # ---------------------------------------------------------------- BitMLP (R13)
-# Textbook values of the standard normal CDF: GELU(x) = x * Phi(x).
+# Values of the standard normal CDF (textbook tables give their leading digits): GELU(x) =
+# x * Phi(x).  The tail entries reach the range where 1 + erf(x / sqrt 2) has cancelled away
+# (x <= -8.3 in fp64) and where GELU is an fp32 subnormal (x = -14).
+# `test_phi_table_from_the_series` recomputes every entry from the series of erf.
 PHI = {0.5: "0.691462461274013103637704610608", 1.0: "0.841344746068542948585232545632",
-       2.0: "0.977249868051820792799717362", 3.0: "0.998650101968369896532351092",
-       -1.0: "0.158655253931457051414767454368", -2.0: "0.022750131948179207200282637"}
+       2.0: "0.977249868051820792799717362834", 3.0: "0.998650101968369905473348185232",
+       -1.0: "0.158655253931457051414767454368", -2.0: "0.022750131948179207200282637166",
+       -4.0: "3.16712418331199212537707567222e-5", -6.0: "9.86587645037698140700864132398e-10",
+       -8.0: "6.22096057427178412351599517259e-16", -10.0: "7.61985302416052606597334325160e-24",
+       -12.0: "1.77648211207767899769617100185e-33", -14.0: "7.79353681919280025435968183890e-45"}
+
+
+def _phi_series(x, digits=160):
+    """Phi(x) = (1 + erf(x / sqrt 2)) / 2 in decimal arithmetic with `digits` digits, erf from its
+    Maclaurin series 2/sqrt(pi) sum_n (-1)^n z^(2n+1) / (n! (2n+1)) and pi from the
+    Gauss-Legendre iteration.  The working precision covers the cancellation of the series
+    (terms up to e^(z^2), 43 digits at z = 14 / sqrt 2) and of 1 + erf."""
+    from decimal import Decimal, localcontext
+    with localcontext() as ctx:
+        ctx.prec = digits
+        a, b, t, p = Decimal(1), 1 / Decimal(2).sqrt(), Decimal(1) / 4, Decimal(1)
+        for _ in range(12):
+            an = (a + b) / 2
+            b, t, p, a = (a * b).sqrt(), t - p * (a - an) ** 2, 2 * p, an
+        pi = (a + b) ** 2 / (4 * t)
+        z = Decimal(x) / Decimal(2).sqrt()
+        s, term, n, tiny = Decimal(0), z, 0, Decimal(10) ** (-digits + 10)
+        while True:
+            add = term / (2 * n + 1)
+            s += add
+            if n > 8 and abs(add) < tiny:
+                break
+            n += 1
+            term = -term * z * z / n
+        return (1 + 2 * s / pi.sqrt()) / 2
+
+
+def test_phi_table_from_the_series():
+    from decimal import Decimal
+    for x, v in PHI.items():
+        got = _phi_series(x)
+        assert abs(got - Decimal(v)) <= Decimal(v) * Decimal("1e-28"), (x, got, v)
+    # the leading digits printed in standard normal tables
+    assert str(PHI[-6.0]).startswith("9.8658764") and str(PHI[-8.0]).startswith("6.2209605")
 
 
 def test_gelu_matches_normal_cdf_table():
@@ -585,6 +625,28 @@ def test_gelu_matches_normal_cdf_table():
     for x, v in zip(xs, g):
         want = exact.rne32(Fraction(Decimal(PHI[float(x)])) * exact.fr(x))
         assert exact.fr(v) == want
+
+
+def test_gelu_tail_is_not_flushed():
+    """Below about -5.5 the terms of 1 + erf(x / sqrt 2) cancel in fp64, yet GELU(x) = x Phi(x)
+    is a nonzero fp32 number down to x = -14.5.  On 20001 points of [-14, -4] the oracle is
+    negative, falls as x falls (GELU decreases left of its minimum at -0.75), and lies within
+    two fp32 ulps (or 2^-148 absolute) of x Phi(x) from the asymptotic normal tail
+    Phi(x) ~ phi(x)/|x| (1 - 1/x^2 + 3/x^4 - 15/x^6), whose relative error is below the first
+    omitted term 105/x^8 (1.6e-3 at x = -4, 6e-6 at x = -8)."""
+    import math
+    xs = np.linspace(-14.0, -4.0, 20001).astype(np.float32)
+    g = oracle.gelu(xs).astype(np.float64)
+    assert np.all(g < 0.0)
+    x64 = xs.astype(np.float64)
+    pdf = np.exp(-0.5 * x64 * x64) / math.sqrt(2.0 * math.pi)
+    inv2 = 1.0 / (x64 * x64)
+    tail = pdf / np.abs(x64) * (1.0 - inv2 + 3.0 * inv2 ** 2 - 15.0 * inv2 ** 3)
+    approx = x64 * tail
+    bound = 105.0 * inv2 ** 4 * np.abs(approx) + 2 * np.abs(approx) * 2.0 ** -23 + 2.0 ** -148
+    assert np.all(np.abs(g - approx) <= bound)
+    # monotone: GELU increases on (-inf, -0.75], so it decreases as x goes down
+    assert np.all(np.diff(g) <= 0.0)
 
 
 def test_gelu_odd_part_identity_and_limits():
