@@ -41,9 +41,10 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def _graph_time(torch, fn, reps: int, warm_fn=None, warm_replays: int = 1):
+def _graph_time(torch, fn, reps: int, warm_fn=None, warm_replays: int = 1, trials: int = 1):
     """Capture `fn(i)` for i < reps into one graph, replay it `warm_replays` times untimed, then
-    time one replay; return ms per rep."""
+    time `trials` replays (events on the replaying stream around each); return ms per rep of
+    the median replay, and the graph."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -58,12 +59,16 @@ def _graph_time(torch, fn, reps: int, warm_fn=None, warm_replays: int = 1):
     for _ in range(warm_replays):      # untimed replays (first-launch costs, clock ramp)
         g.replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps, g
+    times = []
+    for _ in range(trials):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / reps)
+    times.sort()
+    return times[len(times) // 2], g
 
 
 def _eager_time(torch, fn, reps: int):
@@ -165,26 +170,64 @@ def committed_traffic():
         return None
 
 
-def roofline_gemv(torch, bl, sh, copies, reps=480):
+TRACE_PROFILE = os.path.join(ROOT, "profiles", "gemv_fused_decode7b_kernel_trace.md")
+
+
+def _profile_fields(path):
+    """`- key: value` lines of a committed profile summary."""
+    vals = {}
+    try:
+        with open(path) as fh:
+            for line in fh:
+                if line.startswith("- ") and ": " in line:
+                    k, v = line[2:].split(": ", 1)
+                    vals[k.strip()] = v.strip().strip("`")
+    except OSError:
+        pass
+    return vals
+
+
+def committed_kernel_trace(alg_bytes):
+    """The roofline kernel's mean duration in the committed rocprofv3 kernel trace (the kernel
+    alone, without the dispatch gap, but lengthened by the tracer), with the fraction of the HBM
+    peak it gives; None when the summary is missing or the kernel sources changed since."""
+    v = _profile_fields(TRACE_PROFILE)
+    if v.get("source_sha256") != kernel_source_sha():
+        return None
+    try:
+        mean = float(v["kernel_duration_mean_us"])
+    except (KeyError, ValueError):
+        return None
+    gbs = alg_bytes / (mean * 1e-6) / 1e9
+    return {"profile": os.path.relpath(TRACE_PROFILE, ROOT), "kernel": v.get("kernel"),
+            "kernel_duration_mean_us": mean, "kernel_duration_median_us": float(v.get("kernel_duration_median_us", "nan")),
+            "achieved": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def roofline_gemv(torch, bl, sh, copies, reps=480, trials=21):
     """Dominant kernel: the fused decode GEMV on (K, N) = (4096, 11008), back to back in a
-    graph on one stream, weights rotating through the pool."""
+    graph on one stream, weights rotating through the pool; per launch = median over `trials`
+    replays of the graph of `reps` launches, launch to launch (events on the replaying stream)."""
     k, n = sh["k"], sh["n"]
     ms, _ = _graph_time(torch, lambda i: bl.bitlinear_forward_fused(sh["x"][i % 8], sh["pool"][i % copies],
-                                                                    sh["alpha"], y=sh["y"]), reps)
+                                                                    sh["alpha"], y=sh["y"]), reps, trials=trials)
     # algorithmic bytes of one launch: packed weights + x (fp32) + alpha + y (fp32)
     alg = n * k // 4 + 4 * k + 4 + 4 * n
     achieved = alg / (ms * 1e-3) / 1e9
     # the unfused forward kernel alone (x_q in), for reference
     bl.bitlinear_quantize_act(sh["x"][0], sh["xq"], sh["beta"])
     ms_f, _ = _graph_time(torch, lambda i: bl.bitlinear_forward(sh["xq"], sh["beta"], sh["pool"][i % copies],
-                                                                sh["alpha"], y=sh["y"]), reps)
+                                                                sh["alpha"], y=sh["y"]), reps, trials=trials)
     # one call from an idle GPU (weights from the pool, not in cache): launch to completion
     single = _single_call_us(torch, lambda i: bl.bitlinear_forward_fused(sh["x"][i % 8], sh["pool"][(7 * i) % copies],
                                                                          sh["alpha"], y=sh["y"]))
     return dict(kernel=bl.bitlinear_forward_fused_kernel(1, k, n, sh["x"][0], sh["pool"][0]),
                 shape=dict(M=1, K=k, N=n), bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
                 unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=committed_traffic(),
-                us_per_launch=round(ms * 1e3, 3), bytes_per_launch=alg, single_call_us=round(single, 2),
+                us_per_launch=round(ms * 1e3, 3), timing=f"launch to launch in a graph of {reps} launches, "
+                f"median of {trials} replays (HIP events on the replaying stream); includes the dispatch gap",
+                kernel_trace=committed_kernel_trace(alg), graph_launches=reps, graph_trials=trials,
+                bytes_per_launch=alg, single_call_us=round(single, 2),
                 forward_only=dict(kernel="gemv_dot4", us_per_launch=round(ms_f * 1e3, 3),
                                   gbs=round((n * k // 4 + k + 4 * n) / (ms_f * 1e-3) / 1e9, 1)))
 
@@ -523,8 +566,8 @@ def batched_bench(torch, bl, workloads, dev, reps=96):
 
 def chain70b_bench(torch, bl, workloads, dev, layers=80, reps=3):
     """One decode step of the 70B-class stream: 80 layers x 7 projections, one fused call
-    each (the two-call ABI reported beside it), weights generated on the device (17.1 GB
-    resident), one stream, in order.  The grouped variant makes 4 calls per layer: q, k and v
+    each on x = stream_activation(layer, projection) (the two-call ABI reported beside it),
+    weights generated on the device (17.1 GB resident), one stream, in order.  The grouped variant makes 4 calls per layer: q, k and v
     (which read the same x) as one bitlinear_forward_fused_rows call over their stacked rows,
     gate and up likewise, o and down alone -- the same bytes and, bit for bit, the same outputs.
     Each layer's q/k/v and gate/up rows are allocated adjacent, so the grouped calls take views."""
@@ -550,24 +593,27 @@ def chain70b_bench(torch, bl, workloads, dev, layers=80, reps=3):
             groups.append((k, rows, buf, torch.from_numpy(ar).to(dev)))
         for p, (name, k, n) in enumerate(P):
             projs.append((k, n, bufs[p], torch.tensor([alphas[p]], device=dev)))
-    xs = {k: torch.from_numpy(workloads.activations(5, 1, k)).to(dev) for k in (8192, 28672)}
+    # x per (layer, projection); a grouped call takes the x of its first projection
+    xs = [torch.from_numpy(workloads.stream_activation(layer, p, P[p][1])).to(dev)
+          for layer in range(layers) for p in range(len(P))]
+    gx = [xs[layer * len(P) + first] for layer in range(layers) for first in (0, 3, 4, 6)]
     xq = {k: torch.empty((1, k), dtype=torch.int8, device=dev) for k in (8192, 28672)}
     beta = torch.empty(1, dtype=torch.float32, device=dev)
     ys = {n: torch.empty((1, n), dtype=torch.float32, device=dev) for n in (1024, 8192, 10240, 28672, 57344)}
     torch.cuda.synchronize()
 
     def step(i):
-        for (k, n, wp, alpha) in projs:
-            bl.bitlinear_forward_fused(xs[k], wp, alpha, y=ys[n])
+        for x, (k, n, wp, alpha) in zip(xs, projs):
+            bl.bitlinear_forward_fused(x, wp, alpha, y=ys[n])
 
     def step_two_call(i):
-        for (k, n, wp, alpha) in projs:
-            bl.bitlinear_quantize_act(xs[k], xq[k], beta)
+        for x, (k, n, wp, alpha) in zip(xs, projs):
+            bl.bitlinear_quantize_act(x, xq[k], beta)
             bl.bitlinear_forward(xq[k], beta, wp, alpha, y=ys[n])
 
     def step_grouped(i):
-        for (k, n, wp, alpha_rows) in groups:
-            bl.bitlinear_forward_fused_rows(xs[k], wp, alpha_rows, y=ys[n])
+        for x, (k, n, wp, alpha_rows) in zip(gx, groups):
+            bl.bitlinear_forward_fused_rows(x, wp, alpha_rows, y=ys[n])
     ms, _ = _graph_time(torch, step, reps)
     ms2, _ = _graph_time(torch, step_two_call, reps)
     ms3, _ = _graph_time(torch, step_grouped, reps)
@@ -585,53 +631,129 @@ def chain70b_bench(torch, bl, workloads, dev, layers=80, reps=3):
     return res
 
 
-def cpu_baseline(workloads, budget_s=12.0):
-    """The CPU oracle (as it stands) on a bounded sample of the decode workload: whole steps
-    (quantize_act + unpack + integer matmul + dequant for the three shapes), output rows
-    split over threads.  Returns weight GB/s like the GPU value."""
+def host_cpu():
+    """nproc (CPUs this process may run on), physical cores among them, and the model name."""
+    try:
+        cpus = sorted(os.sched_getaffinity(0))
+    except AttributeError:
+        cpus = list(range(os.cpu_count() or 1))
+    cores = set()
+    for c in cpus:
+        try:
+            with open(f"/sys/devices/system/cpu/cpu{c}/topology/core_id") as f:
+                core = f.read().strip()
+            with open(f"/sys/devices/system/cpu/cpu{c}/topology/physical_package_id") as f:
+                pkg = f.read().strip()
+            cores.add((pkg, core))
+        except OSError:
+            cores.add(("?", str(c)))
+    model = "unknown"
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return len(cpus), len(cores), model
+
+
+def cpu_baseline(workloads, budget_s=3.0, max_threads=16):
+    """The CPU oracle (as it stands, never tuned) on bounded samples of the workloads, on this
+    host's cores, with 1 thread and with P threads = the physical cores this process may use
+    (at most 16, the host share of one GPU), output rows split over the threads:
+      * decode: whole 7B decode steps (quantize_act, unpack, integer matmul, dequant for the three
+        shapes), weight GB/s -- the headline's metric; `value` is the P-thread figure;
+      * batched: M = 64, K = 4096, N = 11008 on a slice of the output rows, scaled to the whole
+        matrix (weight GB/s);
+      * prefill: M = 2048, K = 4096, N = 11008 on a slice of the output rows, scaled (int8 GOPS);
+      * chain70b: one layer of the 70B-class stream (7 projections, the codes generated before
+        the timer), scaled by 80 layers (weight GB/s, tokens/s)."""
     import oracle
     from concurrent.futures import ThreadPoolExecutor
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count() or 1
-    cores = max(1, min(16, cores))
+    nproc, phys, model = host_cpu()
+    P = max(1, min(max_threads, phys))
+
+    def timed(fn, threads, budget):
+        pool = ThreadPoolExecutor(threads)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            fn(pool, threads)
+            reps += 1
+            if time.perf_counter() - t0 > budget:
+                break
+        dt = time.perf_counter() - t0
+        pool.shutdown()
+        return reps, dt
+
+    def forward_rows(pool, threads, xq, beta, packed, k, alpha, n0, n1):
+        bounds = np.linspace(n0, n1, threads + 1).astype(int)
+
+        def part(t):
+            a, b = bounds[t], bounds[t + 1]
+            if b > a:
+                oracle.forward(xq, beta, packed[a:b], k, alpha)
+        list(pool.map(part, range(threads)))
+
+    log(f"cpu_baseline: {nproc} CPUs, {phys} physical cores ({model}); P = {P} threads")
+    out = {"nproc": nproc, "physical_cores": phys, "model_name": model, "threads_p": P, "settings": []}
+    # decode steps
     data = []
     for idx, (k, n) in enumerate(DECODE_SHAPES):
         w = workloads.weights(2, n, k, index=idx)
         codes, packed, alpha = oracle.quantize_weights(w)
         data.append((k, n, packed, alpha, workloads.activations(2, 1, k, index=100 * idx)))
     per_step = sum(n * k // 4 for k, n in DECODE_SHAPES)
-    pool = ThreadPoolExecutor(cores)
 
-    def one_step():
+    def decode(pool, threads):
         for (k, n, packed, alpha, x) in data:
             xq, beta = oracle.quantize_act(x)
-            acc = np.zeros((1, n), np.int32)
-            y = np.zeros((1, n), np.float32)
-            bounds = np.linspace(0, n, cores + 1).astype(int)
+            forward_rows(pool, threads, xq, beta, packed, k, alpha, 0, n)
+    for th in (1, P):
+        reps, dt = timed(decode, th, budget_s)
+        out["settings"].append(dict(workload="decode", threads=th, value=round(per_step * reps / dt / 1e9, 4),
+                                    unit="GB/s", sample=f"{reps} whole decode steps in {dt:.1f} s"))
+    # batched decode and prefill: a slice of the output rows, scaled to the whole matrix
+    k, n = 4096, 11008
+    w = workloads.weights(3, n, k)
+    codes, packed, alpha = oracle.quantize_weights(w)
+    for name, m, rows in (("batched", 64, 512), ("prefill", 2048, 32)):
+        x = workloads.activations_with_outliers(4, m, k) if m >= 512 else workloads.activations(3, m, k)
+        xq, beta = oracle.quantize_act(x)
+        for th in (1, P):
+            reps, dt = timed(lambda pool, t: forward_rows(pool, t, xq, beta, packed, k, alpha, 0, rows), th, budget_s)
+            per = dt / reps * n / rows                         # seconds per whole call, scaled
+            if name == "batched":
+                v, unit = n * k / 4 / per / 1e9, "GB/s"
+            else:
+                v, unit = 2.0 * m * n * k / per / 1e9, "GOPS"
+            out["settings"].append(dict(workload=f"{name} M={m} K={k} N={n}", threads=th, value=round(v, 4), unit=unit,
+                                        sample=f"{reps} calls on {rows} of {n} output rows in {dt:.1f} s, scaled by {n / rows:.1f}"))
+    # one layer of the 70B-class chain, scaled by its 80 layers
+    layer = []
+    for p, (_, k, n) in enumerate(workloads.W5_PROJ):
+        layer.append((k, workloads.stream_packed_rows(0, p, k, np.arange(n), threads=P),
+                      workloads.stream_alpha(0, p), workloads.stream_activation(0, p, k)))
+    layer_bytes = sum(pk.nbytes for _, pk, _, _ in layer)
 
-            def part(t):
-                n0, n1 = bounds[t], bounds[t + 1]
-                if n1 <= n0:
-                    return
-                codes = oracle.unpack(packed[n0:n1], k)
-                acc[:, n0:n1] = oracle.ternary_matmul(xq, codes)
-                oracle.dequant(acc, beta, alpha, n0=n0, n1=n1, out=y)
-            list(pool.map(part, range(cores)))
-
-    steps = 0
-    t0 = time.perf_counter()
-    while True:
-        one_step()
-        steps += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
-    pool.shutdown()
-    return dict(value=round(per_step * steps / dt / 1e9, 3), unit="GB/s", cores=cores, kind="oracle",
-                sample=f"{steps} whole decode steps (M=1; K,N = 4096x4096, 4096x11008, 11008x4096), "
-                       f"{dt:.1f} s wall, output rows split over {cores} threads")
+    def chain_layer(pool, threads):
+        for (k, pk, alpha, x) in layer:
+            xq, beta = oracle.quantize_act(x)
+            forward_rows(pool, threads, xq, beta, pk, k, alpha, 0, pk.shape[0])
+    reps, dt = timed(chain_layer, P, 0.0)
+    per_token = dt / reps * workloads.W5_LAYERS
+    out["settings"].append(dict(workload="chain70b (80 layers x 7 projections, M=1)", threads=P,
+                                value=round(layer_bytes * workloads.W5_LAYERS / per_token / 1e9, 4), unit="GB/s",
+                                tokens_per_s=round(1.0 / per_token, 5),
+                                sample=f"{reps} pass of layer 0 ({layer_bytes} B of codes) in {dt:.1f} s, scaled by 80"))
+    dec = [st for st in out["settings"] if st["workload"] == "decode" and st["threads"] == P][0]
+    out.update(value=dec["value"], unit="GB/s", cores=P, kind="oracle",
+               sample=f"whole 7B decode steps (M=1; K,N = 4096x4096, 4096x11008, 11008x4096), {dec['sample']}, "
+                      f"output rows split over {P} threads (the physical cores available, at most {max_threads}); "
+                      f"the 1-thread figure and the batched, prefill and 70B-chain samples are in settings")
+    return out
 
 
 def kernel_only(kind: str, launches: int):
@@ -725,14 +847,19 @@ def trace_summary(trace_dir: str, plain_json: str, traced_json: str, commands: s
     name = next(r["Kernel_Name"] for r in rows if r["Kernel_Name"].startswith("void bitlinear::k_gemv<")
                 and ", true, " in r["Kernel_Name"])
     ts = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows if r["Kernel_Name"] == name)
-    L = (len(ts) - 3 - 50) // 2
-    timed = ts[3 + L:3 + 2 * L]
+    # in order: 3 eager warm-up calls, 1 untimed replay and `trials` timed replays of L launches,
+    # then the 50 single calls
+    L = int(traced["graph_launches"])
+    trials = int(traced["graph_trials"])
+    assert len(ts) == 3 + L * (1 + trials) + 50, (len(ts), L, trials)
+    timed = ts[3 + L:3 + L * (1 + trials)]
+    span = (timed[-1][1] - timed[0][0]) / len(timed) / 1e3
     dur = [e - b for b, e in timed]
-    span = (timed[-1][1] - timed[0][0]) / L / 1e3
     out = ["# Roofline kernel: event timing against the kernel trace (fused decode GEMV, M=1, K=4096, N=11008)", "",
            "Commands (repository root, one MI355X):", "", "```"] + [c.strip() for c in commands.split(";")] + [
            "```", "",
-           f"Kernel: `{name}`; {L} launches in one graph, weights rotating through the decode pool.", "",
+           f"Kernel: `{name}`; {L} launches in one graph, replayed {trials} times, weights rotating "
+           "through the decode pool.", "",
            "| run | per launch, events (bench.py) | per launch, trace (first start to last end / launches) "
            "| kernel duration in the trace (mean / median / min) |", "|---|---|---|---|",
            f"| without the tracer | {plain['us_per_launch']} us ({plain['achieved']} GB/s) | - | - |",
@@ -740,8 +867,19 @@ def trace_summary(trace_dir: str, plain_json: str, traced_json: str, commands: s
            f"| {statistics.mean(dur) / 1e3:.2f} / {statistics.median(dur) / 1e3:.2f} / {min(dur) / 1e3:.2f} us |", "",
            "In the traced run the events and the trace agree on the time per launch; the kernel's own",
            "duration is shorter by the dispatch gap between launches.  The tracer itself lengthens every",
-           "launch (compare the two event figures), so bench.py's roofline figure comes from the run",
-           "without it.", ""]
+           "launch (compare the two event figures), so bench.py's live roofline figure comes from the run",
+           "without it; bench.py also reports the fraction of the HBM peak that the trace's mean kernel",
+           "duration gives (`roofline.kernel_trace`), read from the fields below while the kernel's",
+           "sources still hash to `source_sha256`.", "",
+           f"- kernel: `{name}`",
+           f"- source_sha256: `{kernel_source_sha()}`",
+           f"- launches_timed: {L}",
+           f"- kernel_duration_mean_us: {statistics.mean(dur) / 1e3:.3f}",
+           f"- kernel_duration_median_us: {statistics.median(dur) / 1e3:.3f}",
+           f"- kernel_duration_min_us: {min(dur) / 1e3:.3f}",
+           f"- traced_launch_to_launch_us: {span:.3f}",
+           f"- untraced_events_us_per_launch: {plain['us_per_launch']}",
+           f"- traced_events_us_per_launch: {traced['us_per_launch']}", ""]
     print("\n".join(out))
 
 

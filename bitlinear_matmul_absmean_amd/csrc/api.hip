@@ -1,5 +1,6 @@
 // api.hip -- the C ABI declared in include/bitlinear.h: host-side validation, then kernel
-// selection by shape and launch on the caller's stream.  No allocation, no sync, no state.
+// selection by shape and launch on the caller's stream.  No allocation, no sync; the only
+// state is the per-thread code of the last HIP error, for bitlinear_last_hip_error.
 #include "bitlinear.h"
 
 #include <limits.h>
@@ -38,14 +39,15 @@ int check_forward(const int8_t* x_q, const float* beta, int64_t M, int64_t K, co
     return BITLINEAR_OK;
 }
 
-enum class Path { Gemv, Decode, Gemm, DecodeSliced, Generic };
+enum class Path { Gemv, Decode, Gemm, Generic };
 
 // One token: the VALU GEMV.  Two to four tokens: the GEMV for matrices of 2^26 weights or
 // more, and for two tokens with K >= 8192, where it streams the codes faster; else the MFMA
 // decode kernel (measured with weights not in cache: M = 4, 7.2 vs 9.6 us at K = 4096,
 // N = 11008; M = 2, 4.2 vs 4.9 us at K = N = 4096, 5.9 vs 6.8 us at K = 11008, N = 4096;
 // 13.8 vs 23.7 us at K = 8192, N = 28672).  Up to 64 tokens: the MFMA decode kernel; more:
-// the MFMA GEMM (K % 128 == 0), else the decode kernel over 64-token slices.
+// the MFMA GEMM.  Every fast path needs K % 64 == 0 and 16-byte aligned rows; other calls take
+// the generic kernel.
 constexpr int64_t GEMV_BATCH_MIN_WEIGHTS = (int64_t)1 << 26;
 Path choose_path(int64_t M, int64_t K, int64_t N, const int8_t* xq, const uint8_t* wp) {
     if (!fast_forward_ok(K, xq, wp)) return Path::Generic;
@@ -53,22 +55,7 @@ Path choose_path(int64_t M, int64_t K, int64_t N, const int8_t* xq, const uint8_
                                 !decode_mfma_supports(M, K)))
         return Path::Gemv;
     if (decode_mfma_supports(M, K)) return Path::Decode;
-    if (gemm_supports_k(K)) return Path::Gemm;
-    return Path::DecodeSliced;
-}
-
-hipError_t launch_decode_sliced(const ForwardArgs& a, hipStream_t stream) {
-    for (int64_t m0 = 0; m0 < a.M; m0 += 64) {
-        ForwardArgs s = a;
-        s.M = a.M - m0 < 64 ? a.M - m0 : 64;
-        s.xq = a.xq + m0 * a.K;
-        s.beta = a.beta + m0;
-        s.y = a.y + m0 * a.N;
-        s.acc = a.acc ? a.acc + m0 * a.N : nullptr;
-        hipError_t e = launch_decode_mfma(s, stream);
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    return Path::Gemm;
 }
 
 bool fused_fast_ok(int64_t M, int64_t K, const float* x, const uint8_t* wp, const int8_t* xq_out) {
@@ -93,7 +80,6 @@ int run_forward(const ForwardArgs& a, hipStream_t stream) {
         case Path::Gemv: return hip_status(launch_gemv_dot4(a, stream));
         case Path::Decode: return hip_status(launch_decode_mfma(a, stream));
         case Path::Gemm: return hip_status(launch_gemm_mfma(a, stream));
-        case Path::DecodeSliced: return hip_status(launch_decode_sliced(a, stream));
         default: return hip_status(launch_forward_generic(a, stream));
     }
 }
@@ -343,7 +329,6 @@ const char* bitlinear_forward_kernel(int64_t M, int64_t K, int64_t N, const int8
         case Path::Gemv: return "gemv_dot4";
         case Path::Decode: return "decode_mfma_i8";
         case Path::Gemm: return "gemm_mfma_i8";
-        case Path::DecodeSliced: return "decode_mfma_i8_sliced";
         default: return "generic";
     }
 }

@@ -17,8 +17,9 @@
  *
  * Conventions shared by every entry point
  *   - Memory: every array argument is DEVICE memory on the current HIP device, allocated and
- *     owned by the caller.  The library never allocates, frees or retains caller memory and
- *     keeps no state between calls; calls are reentrant.
+ *     owned by the caller.  The library never allocates, frees or retains caller memory.  Its
+ *     only state between calls is the per-thread code of the last HIP error (see
+ *     bitlinear_last_hip_error); calls are reentrant.
  *   - Execution: every call validates its arguments on the host, enqueues its kernels on
  *     `stream` (0 = the null stream) and returns without synchronising.  Results are
  *     visible to later work on the same stream.
@@ -322,7 +323,7 @@ const char* bitlinear_forward_fused_kernel(int64_t M, int64_t K, int64_t N, cons
 
 /*
  * Name of the kernel bitlinear_forward launches for these arguments ("gemv_dot4",
- * "gemm_mfma_i8", "generic"); a static string, for profiling and reports.
+ * "decode_mfma_i8", "gemm_mfma_i8" or "generic"); a static string, for profiling and reports.
  */
 const char* bitlinear_forward_kernel(int64_t M, int64_t K, int64_t N, const int8_t* x_q,
                                      const uint8_t* W_packed);

@@ -104,18 +104,41 @@ def splitmix64(state: int, index: np.ndarray) -> np.ndarray:
         return z ^ (z >> np.uint64(31))
 
 
-def stream_packed_rows(layer: int, proj: int, k: int, rows: np.ndarray) -> np.ndarray:
-    """Packed weight bytes [len(rows), K/4] of rows ``rows`` of one 70B-class projection."""
-    row_bytes = k // 4
-    rows = np.asarray(rows, dtype=np.int64)
-    idx = (rows[:, None] * row_bytes + np.arange(row_bytes, dtype=np.int64)[None, :]).reshape(-1)
-    z = splitmix64(stream_state(layer, proj), idx)
+def _packed_bytes(state: int, idx: np.ndarray) -> np.ndarray:
+    """Packed bytes at stream indices ``idx``: field j of output idx gives the code at bits 2j,
+    (u < T0) -> 01, (u >= T0 + T1) -> 10, else 00."""
+    z = splitmix64(state, idx)
     out = np.zeros(idx.shape, np.uint8)
     for j in range(4):
-        u = (z >> np.uint64(16 * j)) & np.uint64(0xFFFF)
-        code = np.where(u < CODE_T0, 1, np.where(u < CODE_T0 + CODE_T1, 0, 2)).astype(np.uint8)
+        u = (z >> np.uint64(16 * j)).astype(np.uint16)          # the low 16 bits of the shifted word
+        code = (u < CODE_T0).view(np.uint8) + ((u >= CODE_T0 + CODE_T1).view(np.uint8) << np.uint8(1))
         out |= code << np.uint8(2 * j)
-    return out.reshape(len(rows), row_bytes)
+    return out
+
+
+def stream_packed_rows(layer: int, proj: int, k: int, rows: np.ndarray, threads: int = 1) -> np.ndarray:
+    """Packed weight bytes [len(rows), K/4] of rows ``rows`` of one 70B-class projection
+    (optionally split over ``threads`` host threads; the bytes do not depend on the split)."""
+    row_bytes = k // 4
+    rows = np.asarray(rows, dtype=np.int64)
+    state = stream_state(layer, proj)
+    out = np.empty((len(rows), row_bytes), np.uint8)
+    span = np.arange(row_bytes, dtype=np.int64)
+
+    def part(r0: int, r1: int):
+        idx = (rows[r0:r1, None] * row_bytes + span[None, :]).reshape(-1)
+        out[r0:r1] = _packed_bytes(state, idx).reshape(r1 - r0, row_bytes)
+
+    step = max(1, (1 << 20) // row_bytes)                          # about 1 MiB of bytes per piece
+    pieces = [(r0, min(r0 + step, len(rows))) for r0 in range(0, len(rows), step)]
+    if threads <= 1 or len(pieces) == 1:
+        for r0, r1 in pieces:
+            part(r0, r1)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(lambda p: part(*p), pieces))
+    return out
 
 
 def stream_alpha(layer: int, proj: int) -> np.float32:
