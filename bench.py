@@ -715,22 +715,26 @@ def cpu_baseline(workloads, budget_s=3.0, max_threads=16):
         reps, dt = timed(decode, th, budget_s)
         out["settings"].append(dict(workload="decode", threads=th, value=round(per_step * reps / dt / 1e9, 4),
                                     unit="GB/s", sample=f"{reps} whole decode steps in {dt:.1f} s"))
-    # batched decode and prefill: a slice of the output rows, scaled to the whole matrix
+    # batched decode and prefill: a slice of the tokens over every output row, scaled to the whole
+    # call (a slice of the rows instead would repeat a few rows' code sequence for every token,
+    # which the host's branch predictor learns, and overstate the oracle's speed)
     k, n = 4096, 11008
     w = workloads.weights(3, n, k)
     codes, packed, alpha = oracle.quantize_weights(w)
-    for name, m, rows in (("batched", 64, 512), ("prefill", 2048, 32)):
+    for name, m, toks in (("batched", 64, 4), ("prefill", 2048, 4)):
         x = workloads.activations_with_outliers(4, m, k) if m >= 512 else workloads.activations(3, m, k)
         xq, beta = oracle.quantize_act(x)
+        xs, bs = np.ascontiguousarray(xq[:toks]), np.ascontiguousarray(beta[:toks])
         for th in (1, P):
-            reps, dt = timed(lambda pool, t: forward_rows(pool, t, xq, beta, packed, k, alpha, 0, rows), th, budget_s)
-            per = dt / reps * n / rows                         # seconds per whole call, scaled
+            reps, dt = timed(lambda pool, t: forward_rows(pool, t, xs, bs, packed, k, alpha, 0, n), th, budget_s)
+            per = dt / reps * m / toks                         # seconds per whole call, scaled
             if name == "batched":
                 v, unit = n * k / 4 / per / 1e9, "GB/s"
             else:
                 v, unit = 2.0 * m * n * k / per / 1e9, "GOPS"
             out["settings"].append(dict(workload=f"{name} M={m} K={k} N={n}", threads=th, value=round(v, 4), unit=unit,
-                                        sample=f"{reps} calls on {rows} of {n} output rows in {dt:.1f} s, scaled by {n / rows:.1f}"))
+                                        sample=f"{reps} calls on {toks} of {m} tokens (all {n} output rows) in "
+                                               f"{dt:.1f} s, scaled by {m / toks:.0f}"))
     # one layer of the 70B-class chain, scaled by its 80 layers
     layer = []
     for p, (_, k, n) in enumerate(workloads.W5_PROJ):
