@@ -22,6 +22,7 @@ BITLINEAR_ERR_SHAPE = -2
 BITLINEAR_ERR_ALIGNMENT = -3
 BITLINEAR_ERR_WORKSPACE = -4
 BITLINEAR_ERR_HIP = -5
+BITLINEAR_ERR_SCRATCH = -6
 BITLINEAR_MAX_K = 16909320
 
 # Every symbol the header declares, with (restype, argtypes).
@@ -32,6 +33,8 @@ SIGNATURES = {
     "bitlinear_last_hip_error": (_INT, []),
     "bitlinear_quantize_weights_workspace_size": (_SZ, [_I64, _I64]),
     "bitlinear_quantize_weights": (_INT, [_P, _I64, _I64, _P, _P, _P, _SZ, _P]),
+    "bitlinear_quantize_weights_noalloc": (_INT, [_P, _I64, _I64, _P, _P, _P]),
+    "bitlinear_quantize_weights_noalloc_max_rows": (_SZ, []),
     "bitlinear_quantize_weights_rows": (_INT, [_P, _I64, _I64, _P, _P, _P]),
     "bitlinear_quantize_act": (_INT, [_P, _I64, _I64, _P, _P, _P]),
     "bitlinear_forward": (_INT, [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P]),
@@ -136,6 +139,18 @@ def bitlinear_quantize_weights(W, W_packed=None, alpha=None, workspace=None, str
         _dev(W, torch.float32, "W", N * K), N, K, _dev(W_packed, torch.uint8, "W_packed", N * (K // 4)),
         _dev(alpha, torch.float32, "alpha", 1), _dev(workspace, torch.uint8, "workspace"),
         workspace.numel(), _stream(stream)))
+    return W_packed, alpha
+
+
+def bitlinear_quantize_weights_noalloc(W, W_packed, alpha, stream=None):
+    """bitlinear_quantize_weights into caller buffers W_packed uint8 [N, K/4] and alpha fp32 [1],
+    without a workspace: the library uses its fixed per-device scratch and allocates nothing
+    (neither does this wrapper).  Calls that overlap on one device race."""
+    torch = _torch()
+    N, K = W.shape
+    _check("bitlinear_quantize_weights_noalloc", lib.bitlinear_quantize_weights_noalloc(
+        _dev(W, torch.float32, "W", N * K), N, K, _dev(W_packed, torch.uint8, "W_packed", N * (K // 4)),
+        _dev(alpha, torch.float32, "alpha", 1), _stream(stream)))
     return W_packed, alpha
 
 

@@ -98,6 +98,7 @@ const char* bitlinear_status_string(int status) {
         case BITLINEAR_ERR_ALIGNMENT: return "pointer alignment";
         case BITLINEAR_ERR_WORKSPACE: return "workspace missing or too small";
         case BITLINEAR_ERR_HIP: return "HIP runtime error";
+        case BITLINEAR_ERR_SCRATCH: return "shape exceeds the fixed scratch of the allocation-free call";
         default: return "unknown status";
     }
 }
@@ -121,6 +122,27 @@ int bitlinear_quantize_weights(const float* W, int64_t N, int64_t K, uint8_t* W_
     if (!aligned(workspace, 8)) return BITLINEAR_ERR_ALIGNMENT;
     double* rows = static_cast<double*>(workspace);
     int st = hip_status(launch_row_abs_sums(W, N, K, rows, stream));
+    if (st) return st;
+    st = hip_status(launch_alpha_from_rows(rows, N, K, alpha, stream));
+    if (st) return st;
+    return hip_status(launch_ternary_pack(W, N, K, alpha, false, W_packed, stream));
+}
+
+size_t bitlinear_quantize_weights_noalloc_max_rows(void) { return (size_t)kQuantizeScratchRows; }
+
+int bitlinear_quantize_weights_noalloc(const float* W, int64_t N, int64_t K, uint8_t* W_packed, float* alpha,
+                                       hipStream_t stream) {
+    if (!W || !W_packed || !alpha) return BITLINEAR_ERR_INVALID_ARG;
+    if (N <= 0 || K <= 0) return BITLINEAR_ERR_INVALID_ARG;
+    if (K % 4 != 0 || K > BITLINEAR_MAX_K || !mul_ok(N, K) || N > (int64_t)INT_MAX * 4)
+        return BITLINEAR_ERR_SHAPE;
+    if (N > kQuantizeScratchRows) return BITLINEAR_ERR_SCRATCH;
+    if (!aligned(W, 16) || !aligned(W_packed, 4)) return BITLINEAR_ERR_ALIGNMENT;
+    double* rows = nullptr;
+    int st = hip_status(quantize_weights_scratch(&rows));
+    if (st) return st;
+    // the row sums are written, never accumulated, so the scratch needs no clearing
+    st = hip_status(launch_row_abs_sums(W, N, K, rows, stream));
     if (st) return st;
     st = hip_status(launch_alpha_from_rows(rows, N, K, alpha, stream));
     if (st) return st;

@@ -121,6 +121,10 @@ __device__ __forceinline__ int chunk_sum(const u32x4& w, const u32x4* xs, int st
 }
 
 // ---- launch wrappers (one per kernel family), defined in the .hip files -------------------
+// Rows of the fixed scratch of the allocation-free weight quantization, and the device address
+// of the current device's copy of it (looked up once per device).
+constexpr int64_t kQuantizeScratchRows = 262144;
+hipError_t quantize_weights_scratch(double** out);
 hipError_t launch_row_abs_sums(const float* W, int64_t N, int64_t K, double* rowsum, hipStream_t s);
 hipError_t launch_alpha_from_rows(const double* rowsum, int64_t N, int64_t K, float* alpha, hipStream_t s);
 hipError_t launch_alpha_rows(const float* W, int64_t N, int64_t K, float* alpha_rows, hipStream_t s);

@@ -11,10 +11,39 @@
 // fp64 |W| partial sums, a flat grid-stride pass for codes and packing, one workgroup
 // per token for the activations.
 #include <cmath>
+#include <mutex>
 
 #include "common.hpp"
 
 namespace bitlinear {
+
+// ---------------------------------------------------------------------------------------
+// Fixed scratch of the allocation-free weight quantization: the fp64 |W| row sums of up to
+// kQuantizeScratchRows rows (2 MiB).  Each device holds its own copy until the process ends.
+// Host code never passes `scratch` itself to a kernel (in host code the name stands for a
+// host-side shadow, not a device address): quantize_weights_scratch() looks up the device
+// address once per device, with that device current, and every launch takes that pointer.
+static __device__ __align__(256) double scratch[kQuantizeScratchRows];
+
+hipError_t quantize_weights_scratch(double** out) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static double* addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = static_cast<double*>(p);
+    }
+    *out = addr[dev];
+    return hipSuccess;
+}
 
 // ---------------------------------------------------------------------------------------
 // |W| row sums in fp64.  One wave per row; lane l adds float4 chunks l, l+64, ... in

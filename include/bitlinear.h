@@ -56,7 +56,8 @@ typedef enum bitlinear_status {
     BITLINEAR_ERR_SHAPE = -2,       /* K % 4 != 0, K > BITLINEAR_MAX_K, size overflow */
     BITLINEAR_ERR_ALIGNMENT = -3,   /* a pointer lacks the alignment the call documents */
     BITLINEAR_ERR_WORKSPACE = -4,   /* workspace null or smaller than required */
-    BITLINEAR_ERR_HIP = -5          /* the HIP runtime reported an error at launch */
+    BITLINEAR_ERR_HIP = -5,         /* the HIP runtime reported an error at launch */
+    BITLINEAR_ERR_SCRATCH = -6      /* beyond the fixed scratch of an allocation-free call */
 } bitlinear_status;
 
 /* Returns BITLINEAR_ABI_VERSION of the built library. */
@@ -92,6 +93,25 @@ size_t bitlinear_quantize_weights_workspace_size(int64_t N, int64_t K);
 int bitlinear_quantize_weights(const float* W, int64_t N, int64_t K, uint8_t* W_packed,
                                float* alpha, void* workspace, size_t workspace_bytes,
                                hipStream_t stream);
+
+/*
+ * bitlinear_quantize_weights without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops, harnesses that forbid
+ * hipMalloc).  The fp64 row sums go to a fixed scratch array inside the library, one copy per
+ * device, held until the process ends, of bitlinear_quantize_weights_noalloc_max_rows() rows
+ * (262144, 2 MiB).  The call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine); the first call on a device looks up the address of that device's scratch.
+ * Results are identical to bitlinear_quantize_weights.  All calls on one device share its
+ * scratch, so calls that overlap on one device (different streams, or different host
+ * threads) race and give undefined results; calls ordered on one stream do not.
+ *   Arguments as bitlinear_quantize_weights, without the workspace.
+ * Errors: as bitlinear_quantize_weights, and SCRATCH when N exceeds the scratch rows.
+ */
+int bitlinear_quantize_weights_noalloc(const float* W, int64_t N, int64_t K, uint8_t* W_packed,
+                                       float* alpha, hipStream_t stream);
+
+/* Rows (N) the fixed scratch of bitlinear_quantize_weights_noalloc holds. */
+size_t bitlinear_quantize_weights_noalloc_max_rows(void);
 
 /*
  * Per-output-row variant [P2 §3.1, §4.2]: alpha_rows[n] = mean_k |W[n, k]| (fp64 sum of

@@ -60,7 +60,7 @@ def test_ceiling_library_exports_its_header(bl):
 
 def test_abi_version_and_status_strings(bl):
     assert bl.abi_version() == 1
-    for st in (0, -1, -2, -3, -4, -5):
+    for st in (0, -1, -2, -3, -4, -5, -6):
         s = bl.lib.bitlinear_status_string(st).decode()
         assert s and s != "unknown status"
     assert bl.lib.bitlinear_status_string(-99).decode() == "unknown status"
@@ -74,6 +74,23 @@ def test_workspace_size(bl):
 
 
 A = 4096  # a fake, 4096-aligned "device address"; never dereferenced (calls are invalid)
+
+
+def test_quantize_weights_noalloc_validation(bl):
+    """The allocation-free call validates like bitlinear_quantize_weights and rejects N beyond
+    its fixed scratch before any HIP call."""
+    f = bl.lib.bitlinear_quantize_weights_noalloc
+    rows = bl.lib.bitlinear_quantize_weights_noalloc_max_rows()
+    assert rows == 262144
+    assert f(None, 4, 16, A, A, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert f(A, 4, 16, None, A, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert f(A, 4, 16, A, None, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert f(A, 0, 16, A, A, None) == bl.BITLINEAR_ERR_INVALID_ARG
+    assert f(A, 4, 18, A, A, None) == bl.BITLINEAR_ERR_SHAPE
+    assert f(A, rows + 1, 16, A, A, None) == bl.BITLINEAR_ERR_SCRATCH
+    assert f(A + 4, 4, 16, A, A, None) == bl.BITLINEAR_ERR_ALIGNMENT
+    assert f(A, 4, 16, A + 1, A, None) == bl.BITLINEAR_ERR_ALIGNMENT
+    assert bl.lib.bitlinear_last_hip_error() == 0
 
 
 def test_quantize_weights_validation(bl):
