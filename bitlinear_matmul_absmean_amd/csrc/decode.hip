@@ -352,6 +352,154 @@ static hipError_t launch_bdec16(const ForwardArgs& a, hipStream_t s) {
 }
 
 
+
+// 33 to 64 tokens with K % 128 == 0: the scheme of k_bdec without its K-tail selects (every
+// sub-step is whole), with plain (cached) weight loads.  A wave's 128-weight sub-steps read
+// 32 bytes of each of its rows' 128-byte lines in turn; streamed past the caches, every
+// sub-step fetched its line again, cached they hit in L2.  Both changes were measured with
+// weights not in cache, M = 64: 12.8 against 18.5 us at K = 4096, N = 11008 (two row blocks per
+// workgroup), 18.3 against 22.2 us at K = 11008, N = 4096 (one row block).  The kernel stays
+// bound by its VALU work (the 4x4 transposes and byte sums of x_q, the weight expansion: about
+// ten instructions per MFMA).
+template <int RB>
+__global__ __launch_bounds__(BD_WAVES * 64) void k_bdec64(ForwardArgs a) {
+    constexpr int MT = 2;
+    extern __shared__ i32x4 red[];
+    __shared__ int tsum_w[BD_WAVES][MT * 32];
+    __shared__ int tsum_t[MT * 32];
+    __shared__ float scale_t[MT * 32];
+    constexpr int XU = 9;
+    constexpr int XR = MT * 32 * XU;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int M = (int)a.M;
+    const int64_t K = a.K, N = a.N, rowb = K >> 2;
+    const int64_t n0 = (int64_t)blockIdx.x * (32 * RB);
+    const int lr = lane & 31, lg = lane >> 5;
+    i32x4* xs = red + wave * XR;
+    const int SP = (int)(K >> 7);
+    const int s0 = (int)((int64_t)SP * wave / BD_WAVES), s1 = (int)((int64_t)SP * (wave + 1) / BD_WAVES);
+    // x_q: instruction i covers tokens 8i + lane/8, 16 bytes at k0 + 16 (lane % 8); weights:
+    // lane (lr, lg) reads 16 bytes (64 codes at k0 + 64 lg) of row n0 + 32r + lr.  Rows past M
+    // or N are clamped (never written).
+    const int xu = lane & 7, xt = lane >> 3;
+    const int8_t* xrow[MT * 4];
+#pragma unroll
+    for (int i = 0; i < MT * 4; ++i) xrow[i] = a.xq + (int64_t)min(8 * i + xt, M - 1) * K + 16 * xu;
+    const uint8_t* wrow[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) wrow[r] = a.wp + min(n0 + 32 * r + lr, N - 1) * rowb + 16 * lg;
+    u32x4 xa[2][MT * 4], wb[2][RB];
+    auto load = [&](int st, int s) {
+#pragma unroll
+        for (int i = 0; i < MT * 4; ++i) xa[st][i] = *reinterpret_cast<const u32x4*>(xrow[i] + (int64_t)s * 128);
+#pragma unroll
+        for (int r = 0; r < RB; ++r) wb[st][r] = *reinterpret_cast<const u32x4*>(wrow[r] + (int64_t)s * 32);
+    };
+    i32x16 acc[RB][MT];
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[r][t] = i32x16{};
+    int ts[MT * 4];
+#pragma unroll
+    for (int i = 0; i < MT * 4; ++i) ts[i] = 0;
+    auto compute = [&](int st) {
+#pragma unroll
+        for (int i = 0; i < MT * 4; ++i) {
+            const u32x4 v = xa[st][i];
+            xs[(8 * i + xt) * XU + xu] = (i32x4)transpose4x4_perm(v);
+            int z = ts[i];
+            z = __builtin_amdgcn_sdot4((int)v.x, 0x01010101, z, false);
+            z = __builtin_amdgcn_sdot4((int)v.y, 0x01010101, z, false);
+            z = __builtin_amdgcn_sdot4((int)v.z, 0x01010101, z, false);
+            ts[i] = __builtin_amdgcn_sdot4((int)v.w, 0x01010101, z, false);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            i32x4 av[MT];
+#pragma unroll
+            for (int t = 0; t < MT; ++t) av[t] = xs[(32 * t + lr) * XU + 4 * lg + q];
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const uint32_t w = q == 0 ? wb[st][r].x : q == 1 ? wb[st][r].y : q == 2 ? wb[st][r].z : wb[st][r].w;
+                const i32x4 bv = {(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u),
+                                  (int)((w >> 4) & 0x03030303u), (int)((w >> 6) & 0x03030303u)};
+#pragma unroll
+                for (int t = 0; t < MT; ++t) acc[r][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[t], bv, acc[r][t], 0, 0, 0);
+            }
+        }
+    };
+    if (s0 < s1) {
+        const int last = s1 - 1;
+        load(0, s0);
+        for (int s = s0; s < s1; s += 2) {
+            __builtin_amdgcn_sched_barrier(0);
+            load(1, min(s + 1, last));
+            __builtin_amdgcn_sched_barrier(0);
+            compute(0);
+            if (s + 1 < s1) {
+                __builtin_amdgcn_sched_barrier(0);
+                load(0, min(s + 2, last));
+                __builtin_amdgcn_sched_barrier(0);
+                compute(1);
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < MT * 4; ++i) {
+        int v = ts[i];
+        v += __shfl_xor(v, 1, 64);
+        v += __shfl_xor(v, 2, 64);
+        v += __shfl_xor(v, 4, 64);
+        if (xu == 0) tsum_w[wave][8 * i + xt] = v;
+    }
+    __syncthreads();                               // every wave is done with its staging region
+    if (tid < MT * 32) {
+        int v = 0;
+#pragma unroll
+        for (int w = 0; w < BD_WAVES; ++w) v += tsum_w[w][tid];
+        tsum_t[tid] = v;
+        scale_t[tid] = (!a.alpha_per_row && tid < M) ? dequant_scale(a.alpha[0], a.beta[tid]) : 0.0f;
+    }
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                red[((wave * RB * MT + r * MT + t) * 4 + c) * 64 + lane] =
+                    i32x4{acc[r][t][4 * c], acc[r][t][4 * c + 1], acc[r][t][4 * c + 2], acc[r][t][4 * c + 3]};
+    __syncthreads();
+    for (int e = tid; e < RB * MT * 4 * 64; e += BD_WAVES * 64) {
+        const int l = e & 63, c = (e >> 6) & 3, tile = e >> 8;
+        const int r = tile / MT, t = tile % MT;
+        i32x4 sum = {0, 0, 0, 0};
+#pragma unroll
+        for (int w = 0; w < BD_WAVES; ++w) sum += red[((w * RB * MT + tile) * 4 + c) * 64 + l];
+        const int64_t n = n0 + 32 * r + (l & 31);
+        if (n >= N) continue;
+        const float al = a.alpha_per_row ? a.alpha[n] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = 32 * t + 8 * c + 4 * (l >> 5) + i;
+            if (m >= M) continue;
+            const int total = sum[i] - tsum_t[m];
+            const float sc = a.alpha_per_row ? dequant_scale(al, a.beta[m]) : scale_t[m];
+            a.y[(int64_t)m * N + n] = activate(dequant(total, sc, a.bias, n), a.act);
+            if (a.acc) a.acc[(int64_t)m * N + n] = total;
+        }
+    }
+}
+
+template <int RB>
+static hipError_t launch_bdec64(const ForwardArgs& a, hipStream_t s) {
+    const int64_t blocks = (a.N + 32 * RB - 1) / (32 * RB);
+    const size_t stage = (size_t)BD_WAVES * 2 * 32 * 9 * sizeof(i32x4);
+    const size_t tiles = (size_t)BD_WAVES * RB * 2 * 4 * 64 * sizeof(i32x4);
+    return launch_with_lds(k_bdec64<RB>, dim3((unsigned)blocks), dim3(BD_WAVES * 64), stage > tiles ? stage : tiles, s, a);
+}
+
 bool decode_mfma_supports(int64_t M, int64_t K) { return M >= 1 && M <= 64 && K % 64 == 0; }
 
 // Tile shape by token count: 16 x 16 x 64 tiles up to 32 tokens (better weight loads, fewer
@@ -381,6 +529,10 @@ hipError_t launch_decode_mfma(const ForwardArgs& a, hipStream_t s) {
         if (nb16 <= 256) return launch_bdec16<2, 1>(a, s);
         return launch_bdec16<2, 2>(a, s);
     }
+    // 33 to 64 tokens, whole 128-weight sub-steps: two row blocks per workgroup from 8192 rows
+    // (172 workgroups at N = 11008), one below (128 at N = 4096; two measured 29.7 against
+    // 18.3 us at K = 11008, N = 4096)
+    if (a.K % 128 == 0) return a.N >= 8192 ? launch_bdec64<2>(a, s) : launch_bdec64<1>(a, s);
     if (nb <= 256) return launch_bdec<2, 1>(a, s);
     return launch_bdec<2, 2>(a, s);
 }

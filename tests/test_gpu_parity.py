@@ -181,6 +181,11 @@ FWD_CASES = [
     # 17-32 tokens on 32x32x32 tiles with one token block (K <= 8192, N >= 8192): 1, 2 and 4
     # row blocks per workgroup, K % 128 = 64
     (17, 192, 8192), (24, 1088, 9000), (32, 256, 20000),
+    # 33-64 tokens with whole 128-weight sub-steps (K % 128 == 0): one row block per workgroup
+    # below N = 8192, two from it; sub-step counts not divisible by the eight waves (K = 128:
+    # seven waves idle; K = 1152: 9 sub-steps), odd per-wave counts, ragged N and M
+    (33, 128, 8193), (64, 1152, 8200), (40, 4096, 300), (64, 11008, 4100), (57, 384, 8191),
+    (64, 640, 12345), (35, 2176, 33),
 ]
 
 
@@ -663,7 +668,9 @@ def test_end_to_end_block_scaled_bitlinear(dev):
 # generic kernel (d % 64 != 0); fc2's quantizer with 256-thread rows (M >= 256).
 MLP_CASES = [(1, 1024, 4096, False), (1, 4096, 11008, True), (3, 512, 2048, True), (8, 512, 1024, False),
              (48, 256, 1024, True), (200, 256, 512, False), (5, 100, 36, True),
-             (300, 256, 1024, True), (130, 128, 1000, True), (260, 128, 16000, True)]
+             (300, 256, 1024, True), (130, 128, 1000, True), (260, 128, 16000, True),
+             # 33-64 tokens with K % 128 == 0, two row blocks per workgroup (N >= 8192) in fc1
+             (64, 256, 8320, True)]
 
 
 @pytest.mark.parametrize("m,d,f,with_bias", MLP_CASES)
