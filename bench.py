@@ -421,7 +421,8 @@ def hadamard_bench(torch, bl, workloads, dev, ms_plain_step, reps=20):
 def blocks_bench(torch, bl, workloads, dev, ms_plain_step):
     """Block-scaled weights [P1 §2.3, §4.2] (one alpha per 128 weights): the 7B decode step
     (three GEMVs, M = 1) with block-scaled weights and x_q given, its bytes (NK/4 codes +
-    NK/32 scales + K x_q + 4N y per shape), and batched M = 4 and 16 on (4096, 11008)."""
+    NK/32 scales + K x_q + 4N y per shape), batched M = 4, 16 and 64 on (4096, 11008), and
+    prefill M = 2048 on the same shape."""
     per_step = sum(n * k // 4 + n * k // 32 for k, n in DECODE_SHAPES)
     copies = max(2, POOL_BYTES // per_step)
     shapes = []
@@ -453,14 +454,25 @@ def blocks_bench(torch, bl, workloads, dev, ms_plain_step):
     copies = max(2, POOL_BYTES // (n * k // 4 + n * k // 32))
     pool = [(packed, ab)] + [(packed.clone(), ab.clone()) for _ in range(copies - 1)]
     out["batched"] = []
-    for m in (4, 16):
+    for m in (4, 16, 64):
         x = torch.from_numpy(workloads.activations(3, m, k)).to(dev)
         xq, beta = bl.bitlinear_quantize_act(x)
         y = torch.empty((m, n), dtype=torch.float32, device=dev)
         ms, _ = _graph_time(torch, lambda i: bl.bitlinear_forward_blocks(xq, beta, *pool[i % copies], y=y), 96)
         out["batched"].append({"M": m, "K": k, "N": n, "us": round(ms * 1e3, 2),
-                               "kernel": "16x16x64 int8 MFMA tiles, int32 sums per block scaled in fp64"})
+                               "kernel": "16x16x64 int8 MFMA tiles, int32 sums per block scaled in fp64" if m <= 32 else
+                                         "block-scaled GEMM, 128 x 128 tiles, fp64 sum per output"})
     del pool
+    # prefill with block scales: M = 2048 (int8 ops 2MNK) beside the per-tensor GEMM of the same shape
+    m = 2048
+    x = torch.from_numpy(workloads.activations_with_outliers(4, m, k)).to(dev)
+    xq, beta = bl.bitlinear_quantize_act(x)
+    y = torch.empty((m, n), dtype=torch.float32, device=dev)
+    ms, _ = _graph_time(torch, lambda i: bl.bitlinear_forward_blocks(xq, beta, packed, ab, y=y), 10, warm_replays=3)
+    ops = 2.0 * m * n * k
+    out["prefill"] = {"M": m, "K": k, "N": n, "us": round(ms * 1e3, 2), "tops": round(ops / (ms * 1e-3) / 1e12, 1),
+                      "pct_mfma_peak": round(100 * ops / (ms * 1e-3) / 1e12 / INT8_MFMA_PEAK_TOPS, 2),
+                      "kernel": "block-scaled GEMM, 128 x 128 tiles, fp64 sum per output"}
     torch.cuda.empty_cache()
     return out
 

@@ -645,6 +645,52 @@ def test_forward_blocks_parity(dev, m, k, n):
     assert same >= 0.99
 
 
+# More than 32 tokens: the block-scaled GEMM adds alpha * acc per block in fp64 in ascending
+# block order, the oracle's order, so y is compared bit for bit.  Cases: one and several 128 x 128
+# tiles, ragged M and N, K of one block and odd block counts, with and without bias.
+BLOCK_GEMM_CASES = [(33, 128, 100), (64, 256, 129), (128, 4096, 256), (129, 1152, 300), (300, 2048, 1000),
+                    (1000, 384, 257), (65, 4224, 4100)]
+
+
+@pytest.mark.parametrize("m,k,n", BLOCK_GEMM_CASES)
+def test_forward_blocks_gemm_bit_exact(dev, m, k, n):
+    torch, bl = dev
+    _say(f"forward_blocks GEMM M={m} K={k} N={n}")
+    w = _block_w(35, n, k, zero_block=True)
+    x = workloads.activations_with_outliers(35, m, k)
+    _, packed, a = oracle.quantize_weights_blocks(w)
+    xq, beta = oracle.quantize_act(x)
+    bias = workloads.activations(36, 1, n)[0] if (m + n) % 2 else None
+    _, y_ref = oracle.forward_blocks(xq, beta, packed, k, a, bias=bias)
+    y = bl.bitlinear_forward_blocks(_to(torch, xq), _to(torch, beta), _to(torch, packed), _to(torch, a),
+                                    bias=None if bias is None else _to(torch, bias))
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
+
+
+def test_forward_blocks_prefill_full_size_sampled(dev):
+    """M = 2048, K = 4096, N = 11008 with block scales (the prefill workload): every token on 64
+    sampled weight rows (first, last and random), bit for bit."""
+    torch, bl = dev
+    m, k, n = 2048, 4096, 11008
+    _say(f"forward_blocks prefill M={m} K={k} N={n}")
+    w = _block_w(37, n, k)
+    x = workloads.activations_with_outliers(37, m, k)
+    packed_t, a_t = bl.bitlinear_quantize_weights_blocks(_to(torch, w))
+    xq_t, beta_t = bl.bitlinear_quantize_act(_to(torch, x))
+    y = bl.bitlinear_forward_blocks(xq_t, beta_t, packed_t, a_t)
+    torch.cuda.synchronize()
+    _, packed, a = oracle.quantize_weights_blocks(w)
+    xq, beta = oracle.quantize_act(x)
+    assert np.array_equal(packed_t.cpu().numpy(), packed)
+    assert np.array_equal(a_t.cpu().numpy().view(np.uint32), a.view(np.uint32))
+    assert np.array_equal(xq_t.cpu().numpy(), xq)
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(n - 8, n),
+                                     np.random.default_rng(7).choice(n, 48, replace=False)]))
+    _, y_ref = oracle.forward_blocks(xq, beta, np.ascontiguousarray(packed[rows]), k, np.ascontiguousarray(a[rows]))
+    assert np.array_equal(y.cpu().numpy()[:, rows].view(np.uint32), y_ref.view(np.uint32))
+
+
 def test_end_to_end_block_scaled_bitlinear(dev):
     torch, bl = dev
     _say("block-scaled bitlinear M=1 K=4096 N=4096")
