@@ -353,6 +353,134 @@ static hipError_t launch_bdec16(const ForwardArgs& a, hipStream_t s) {
 
 
 
+// k_bdec16 for whole 256-weight sub-steps (K % 256 == 0, no K-tail selects) with an ST-stage
+// register pipeline, for grids of one 16-row block per workgroup (N <= 4096 rows).  Measured
+// with weights not in cache at K = 11008, N = 4096: 8 tokens 7.82 against 8.35 us, 16 tokens
+// 9.56 against 10.76 us (ST = 4), 24 tokens 12.99 against 14.39 us (ST = 3); six stages, which
+// hold every load of a wave at once, were slower (10.0 us at 16 tokens).
+template <int MT, int RB, int ST>
+__global__ __launch_bounds__(BD_WAVES * 64) void k_bdec16w(ForwardArgs a) {
+    extern __shared__ i32x4 red[];
+    __shared__ int tsum_w[BD_WAVES][16 * MT];
+    __shared__ int tsum_t[MT * 16];
+    __shared__ float scale_t[MT * 16];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int M = (int)a.M;
+    const int64_t K = a.K, N = a.N, rowb = K >> 2;
+    const int64_t n0 = (int64_t)blockIdx.x * (16 * RB);
+    const int lr = lane & 15, lg = lane >> 4;
+    const int SP = (int)(K >> 8);
+    const int s0 = (int)((int64_t)SP * wave / BD_WAVES), s1 = (int)((int64_t)SP * (wave + 1) / BD_WAVES);
+    const int8_t* xrow[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) xrow[t] = a.xq + (int64_t)min(16 * t + lr, M - 1) * K + 64 * lg;
+    const uint8_t* wrow[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) wrow[r] = a.wp + min(n0 + 16 * r + lr, N - 1) * rowb + 16 * lg;
+    u32x4 xa[ST][MT][4], wb[ST][RB];
+    auto load = [&](int st, int s) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) xa[st][t][q] = *reinterpret_cast<const u32x4*>(xrow[t] + (int64_t)s * 256 + 16 * q);
+#pragma unroll
+        for (int r = 0; r < RB; ++r) wb[st][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[r] + (int64_t)s * 64));
+    };
+    i32x4 acc[RB][MT];
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[r][t] = i32x4{0, 0, 0, 0};
+    int ts[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) ts[t] = 0;
+    auto compute = [&](int st) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            i32x4 av[MT];
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const u32x4 v = xa[st][t][q];
+                av[t] = (i32x4)transpose4x4_perm(v);
+                int z = ts[t];
+                z = __builtin_amdgcn_sdot4((int)v.x, 0x01010101, z, false);
+                z = __builtin_amdgcn_sdot4((int)v.y, 0x01010101, z, false);
+                z = __builtin_amdgcn_sdot4((int)v.z, 0x01010101, z, false);
+                ts[t] = __builtin_amdgcn_sdot4((int)v.w, 0x01010101, z, false);
+            }
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const uint32_t w = q == 0 ? wb[st][r].x : q == 1 ? wb[st][r].y : q == 2 ? wb[st][r].z : wb[st][r].w;
+                const i32x4 bv = {(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u),
+                                  (int)((w >> 4) & 0x03030303u), (int)((w >> 6) & 0x03030303u)};
+#pragma unroll
+                for (int t = 0; t < MT; ++t) acc[r][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[t], bv, acc[r][t], 0, 0, 0);
+            }
+        }
+    };
+    if (s0 < s1) {
+        const int last = s1 - 1;
+#pragma unroll
+        for (int j = 0; j < ST - 1; ++j) load(j, min(s0 + j, last));
+        for (int s = s0; s < s1; s += ST) {
+#pragma unroll
+            for (int j = 0; j < ST; ++j) {
+                if (s + j < s1) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (s + j + ST - 1 < s1) load((j + ST - 1) % ST, s + j + ST - 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    compute(j);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        int v = ts[t] + __shfl_xor(ts[t], 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        if (lg == 0) tsum_w[wave][16 * t + lr] = v;
+    }
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) red[(wave * RB * MT + r * MT + t) * 64 + lane] = acc[r][t];
+    __syncthreads();
+    if (tid < MT * 16) {
+        int v = 0;
+#pragma unroll
+        for (int w = 0; w < BD_WAVES; ++w) v += tsum_w[w][tid];
+        tsum_t[tid] = v;
+        scale_t[tid] = (!a.alpha_per_row && tid < M) ? dequant_scale(a.alpha[0], a.beta[tid]) : 0.0f;
+    }
+    __syncthreads();
+    for (int e = tid; e < RB * MT * 64; e += BD_WAVES * 64) {
+        const int l = e & 63, tile = e >> 6;
+        const int r = tile / MT, t = tile % MT;
+        i32x4 sum = {0, 0, 0, 0};
+#pragma unroll
+        for (int w = 0; w < BD_WAVES; ++w) sum += red[(w * RB * MT + tile) * 64 + l];
+        const int64_t n = n0 + 16 * r + (l & 15);
+        if (n >= N) continue;
+        const float al = a.alpha_per_row ? a.alpha[n] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = 16 * t + 4 * (l >> 4) + i;
+            if (m >= M) continue;
+            const int total = sum[i] - tsum_t[m];
+            const float sc = a.alpha_per_row ? dequant_scale(al, a.beta[m]) : scale_t[m];
+            a.y[(int64_t)m * N + n] = activate(dequant(total, sc, a.bias, n), a.act);
+            if (a.acc) a.acc[(int64_t)m * N + n] = total;
+        }
+    }
+}
+template <int MT, int RB, int ST>
+static hipError_t launch_bdec16w(const ForwardArgs& a, hipStream_t s) {
+    const int64_t blocks = (a.N + 16 * RB - 1) / (16 * RB);
+    const size_t lds = (size_t)BD_WAVES * RB * MT * 64 * sizeof(i32x4);
+    return launch_with_lds(k_bdec16w<MT, RB, ST>, dim3((unsigned)blocks), dim3(BD_WAVES * 64), lds, s, a);
+}
+
 // 33 to 64 tokens with K % 128 == 0: the scheme of k_bdec without its K-tail selects (every
 // sub-step is whole), with plain (cached) weight loads.  A wave's 128-weight sub-steps read
 // 32 bytes of each of its rows' 128-byte lines in turn; streamed past the caches, every
@@ -509,8 +637,9 @@ bool decode_mfma_supports(int64_t M, int64_t K) { return M >= 1 && M <= 64 && K 
 // possible, within the registers (no spills) and the LDS of the final reduction.
 hipError_t launch_decode_mfma(const ForwardArgs& a, hipStream_t s) {
     const int64_t nb16 = (a.N + 15) / 16;
+    const bool whole = a.K % 256 == 0;
     if (a.M <= 16) {
-        if (nb16 <= 256) return launch_bdec16<1, 1>(a, s);
+        if (nb16 <= 256) return whole ? launch_bdec16w<1, 1, 4>(a, s) : launch_bdec16<1, 1>(a, s);
         if (nb16 <= 512) return launch_bdec16<1, 2>(a, s);
         if (nb16 <= 1024) return launch_bdec16<1, 4>(a, s);
         return launch_bdec16<1, 8>(a, s);
@@ -526,7 +655,7 @@ hipError_t launch_decode_mfma(const ForwardArgs& a, hipStream_t s) {
         return launch_bdec<1, 4>(a, s);
     }
     if (a.M <= 32) {
-        if (nb16 <= 256) return launch_bdec16<2, 1>(a, s);
+        if (nb16 <= 256) return whole ? launch_bdec16w<2, 1, 3>(a, s) : launch_bdec16<2, 1>(a, s);
         return launch_bdec16<2, 2>(a, s);
     }
     // 33 to 64 tokens, whole 128-weight sub-steps: two row blocks per workgroup from 8192 rows

@@ -37,6 +37,9 @@ def test_graph_replays_match_eager(dev):
     w_had = workloads.weights(95, 300, 2048)             # rotated projection, one token
     w_blk = workloads.weights(96, 500, 1024)             # block scales, 4 tokens
     w_t5 = workloads.weights(97, 300, 1000)              # five codes per byte, one token
+    w_b64 = workloads.weights(100, 9000, 1024)           # batched decode, 64 tokens, whole sub-steps
+    w_b16 = workloads.weights(101, 700, 2048)            # batched decode, 12 tokens, one row block per workgroup
+    w_bg = workloads.weights(102, 300, 640)              # block-scaled GEMM, 96 tokens
     p_dec, a_dec = bl.bitlinear_quantize_weights(t(w_dec))
     p_gemm, a_gemm = bl.bitlinear_quantize_weights(t(w_gemm))
     p_bat, a_bat = bl.bitlinear_quantize_weights(t(w_bat))
@@ -46,6 +49,9 @@ def test_graph_replays_match_eager(dev):
     p_had, a_had = bl.bitlinear_quantize_weights(bl.bitlinear_hadamard_rows(t(w_had), 2048, signs))
     p_blk, a_blk = bl.bitlinear_quantize_weights_blocks(t(w_blk))
     p_t5, a_t5 = bl.bitlinear_quantize_weights_t5(t(w_t5))
+    p_b64, a_b64 = bl.bitlinear_quantize_weights(t(w_b64))
+    p_b16, a_b16 = bl.bitlinear_quantize_weights(t(w_b16))
+    p_bg, a_bg = bl.bitlinear_quantize_weights_blocks(t(w_bg))
     # activations and static outputs
     x_dec = t(workloads.activations_with_outliers(90, 1, 4096))
     x_gemm = t(workloads.activations_with_outliers(91, 200, 512))
@@ -54,13 +60,24 @@ def test_graph_replays_match_eager(dev):
     x_had = t(workloads.activations_with_outliers(95, 1, 2048))
     x_blk = t(workloads.activations_with_outliers(96, 4, 1024))
     x_t5 = t(workloads.activations_with_outliers(97, 1, 1000))
+    x_b64 = t(workloads.activations_with_outliers(100, 64, 1024))
+    x_b16 = t(workloads.activations_with_outliers(101, 12, 2048))
+    x_bg = t(workloads.activations_with_outliers(102, 96, 640))
     bias = t(workloads.activations(98, 1, 9000)[0])
     out = {
         "dec": torch.empty((1, 1000), **f32), "gemm": torch.empty((200, 700), **f32),
         "bat": torch.empty((24, 9000), **f32), "mlp_y": torch.empty((130, 256), **f32),
         "mlp_g": torch.empty((130, 1000), **f32), "had": torch.empty((1, 300), **f32),
         "blk": torch.empty((4, 500), **f32), "t5": torch.empty((1, 300), **f32),
+        "b64": torch.empty((64, 9000), **f32), "b16": torch.empty((12, 700), **f32),
+        "bg": torch.empty((96, 300), **f32),
     }
+    xq_b64 = torch.empty((64, 1024), dtype=torch.int8, device="cuda")
+    b_b64 = torch.empty(64, **f32)
+    xq_b16 = torch.empty((12, 2048), dtype=torch.int8, device="cuda")
+    b_b16 = torch.empty(12, **f32)
+    xq_bg = torch.empty((96, 640), dtype=torch.int8, device="cuda")
+    b_bg = torch.empty(96, **f32)
     xq_gemm = torch.empty((200, 512), dtype=torch.int8, device="cuda")
     b_gemm = torch.empty(200, **f32)
     xq_bat = torch.empty((24, 1024), dtype=torch.int8, device="cuda")
@@ -87,6 +104,12 @@ def test_graph_replays_match_eager(dev):
         bl.bitlinear_forward_blocks(xq_blk, b_blk, p_blk, a_blk, y=out["blk"])
         bl.bitlinear_quantize_act(x_t5, x_q=xq_t5, beta=b_t5)
         bl.bitlinear_forward_t5(xq_t5, b_t5, p_t5, a_t5, y=out["t5"])
+        bl.bitlinear_quantize_act(x_b64, x_q=xq_b64, beta=b_b64)
+        bl.bitlinear_forward(xq_b64, b_b64, p_b64, a_b64, bias=bias, y=out["b64"])
+        bl.bitlinear_quantize_act(x_b16, x_q=xq_b16, beta=b_b16)
+        bl.bitlinear_forward(xq_b16, b_b16, p_b16, a_b16, y=out["b16"])
+        bl.bitlinear_quantize_act(x_bg, x_q=xq_bg, beta=b_bg)
+        bl.bitlinear_forward_blocks(xq_bg, b_bg, p_bg, a_bg, bias=bias[:300], y=out["bg"])
 
     _say("graph: eager reference")
     calls()

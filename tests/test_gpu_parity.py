@@ -181,6 +181,11 @@ FWD_CASES = [
     # 17-32 tokens on 32x32x32 tiles with one token block (K <= 8192, N >= 8192): 1, 2 and 4
     # row blocks per workgroup, K % 128 = 64
     (17, 192, 8192), (24, 1088, 9000), (32, 256, 20000),
+    # up to 32 tokens, one 16-row block per workgroup (N <= 4096), whole 256-weight sub-steps
+    # (K % 256 == 0): four- and three-stage pipelines, sub-step counts below, at and above the
+    # pipeline depth per wave, ragged N and M
+    (5, 256, 33), (16, 4096, 4096), (9, 11008, 1000), (12, 8192, 257), (16, 768, 4095),
+    (17, 11008, 700), (32, 2048, 4096), (25, 256, 64),
     # 33-64 tokens with whole 128-weight sub-steps (K % 128 == 0): one row block per workgroup
     # below N = 8192, two from it; sub-step counts not divisible by the eight waves (K = 128:
     # seven waves idle; K = 1152: 9 sub-steps), odd per-wave counts, ragged N and M
