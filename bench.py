@@ -889,7 +889,7 @@ def trace_summary(trace_dir: str, plain_json: str, traced_json: str, commands: s
            "sources still hash to `source_sha256`.", "",
            f"- kernel: `{name}`",
            f"- source_sha256: `{kernel_source_sha()}`",
-           f"- launches_timed: {L}",
+           f"- launches_timed: {len(timed)} ({trials} replays of {L})",
            f"- kernel_duration_mean_us: {statistics.mean(dur) / 1e3:.3f}",
            f"- kernel_duration_median_us: {statistics.median(dur) / 1e3:.3f}",
            f"- kernel_duration_min_us: {min(dur) / 1e3:.3f}",

@@ -15,8 +15,8 @@
 // One or two tokens, a GEMV: a workgroup stages the tokens' x_q in LDS (each 16-byte group
 // transposed 4x4 so that a masked dword of codes meets its activations, plus the sum of x_q
 // over each 64-weight chunk), then every wave streams its own rows, one 16-byte chunk of
-// codes per lane and load.  Three to 32 tokens run on the matrix cores (below); more on the
-// block-scaled GEMM at the end of the file.
+// codes per lane and load.  Three to 127 tokens run on the matrix cores (below) in slices of
+// 32; 128 and more on the block-scaled GEMM at the end of the file.
 #include "common.hpp"
 
 namespace bitlinear {
@@ -370,7 +370,7 @@ static hipError_t launch_bdec16_blocks_m(const BlockArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------------------
-// More than 32 tokens (prefill): a GEMM on 128 x 128 tiles, four waves of 64 x 64 (2 x 2 tiles
+// 128 tokens and more (prefill): a GEMM on 128 x 128 tiles, four waves of 64 x 64 (2 x 2 tiles
 // of v_mfma_i32_32x32x32_i8), K steps of 64 through double-buffered LDS with one barrier per
 // step.  x_q is transposed 4x4 on its way into LDS (as in the per-tensor GEMM); the weight
 // codes go to the B operand as signed bytes W_hat = c - 1 through a v_perm table, so a
@@ -579,7 +579,10 @@ hipError_t launch_forward_blocks(const int8_t* xq, const float* beta, int64_t M,
     const BlockArgs a{xq, beta, M, K, N, wp, alpha, bias, y, 0};
     if (M == 1) return launch_blocks_cpl<1>(a, 1, s);
     if (M == 2) return launch_blocks_cpl<2>(a, 1, s);
-    if (M > 32) return launch_gemm_blocks<2>(a, s);
+    // from 128 tokens the GEMM (one 128-token tile row and more); below, 32-token slices of the
+    // decode kernel (measured at M = 64, K = 4096, N = 11008, weights not in cache: two slices
+    // 25.8 us against 46.0 us for the GEMM's 86 workgroups)
+    if (M >= 128) return launch_gemm_blocks<2>(a, s);
     for (int64_t m0 = 0; m0 < M; m0 += 32) {
         BlockArgs sl = a;
         sl.M = M - m0 < 32 ? M - m0 : 32;

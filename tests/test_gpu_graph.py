@@ -39,7 +39,7 @@ def test_graph_replays_match_eager(dev):
     w_t5 = workloads.weights(97, 300, 1000)              # five codes per byte, one token
     w_b64 = workloads.weights(100, 9000, 1024)           # batched decode, 64 tokens, whole sub-steps
     w_b16 = workloads.weights(101, 700, 2048)            # batched decode, 12 tokens, one row block per workgroup
-    w_bg = workloads.weights(102, 300, 640)              # block-scaled GEMM, 96 tokens
+    w_bg = workloads.weights(102, 300, 640)              # block-scaled GEMM, 160 tokens
     p_dec, a_dec = bl.bitlinear_quantize_weights(t(w_dec))
     p_gemm, a_gemm = bl.bitlinear_quantize_weights(t(w_gemm))
     p_bat, a_bat = bl.bitlinear_quantize_weights(t(w_bat))
@@ -62,7 +62,7 @@ def test_graph_replays_match_eager(dev):
     x_t5 = t(workloads.activations_with_outliers(97, 1, 1000))
     x_b64 = t(workloads.activations_with_outliers(100, 64, 1024))
     x_b16 = t(workloads.activations_with_outliers(101, 12, 2048))
-    x_bg = t(workloads.activations_with_outliers(102, 96, 640))
+    x_bg = t(workloads.activations_with_outliers(102, 160, 640))
     bias = t(workloads.activations(98, 1, 9000)[0])
     out = {
         "dec": torch.empty((1, 1000), **f32), "gemm": torch.empty((200, 700), **f32),
@@ -70,14 +70,14 @@ def test_graph_replays_match_eager(dev):
         "mlp_g": torch.empty((130, 1000), **f32), "had": torch.empty((1, 300), **f32),
         "blk": torch.empty((4, 500), **f32), "t5": torch.empty((1, 300), **f32),
         "b64": torch.empty((64, 9000), **f32), "b16": torch.empty((12, 700), **f32),
-        "bg": torch.empty((96, 300), **f32),
+        "bg": torch.empty((160, 300), **f32),
     }
     xq_b64 = torch.empty((64, 1024), dtype=torch.int8, device="cuda")
     b_b64 = torch.empty(64, **f32)
     xq_b16 = torch.empty((12, 2048), dtype=torch.int8, device="cuda")
     b_b16 = torch.empty(12, **f32)
-    xq_bg = torch.empty((96, 640), dtype=torch.int8, device="cuda")
-    b_bg = torch.empty(96, **f32)
+    xq_bg = torch.empty((160, 640), dtype=torch.int8, device="cuda")
+    b_bg = torch.empty(160, **f32)
     xq_gemm = torch.empty((200, 512), dtype=torch.int8, device="cuda")
     b_gemm = torch.empty(200, **f32)
     xq_bat = torch.empty((24, 1024), dtype=torch.int8, device="cuda")

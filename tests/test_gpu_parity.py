@@ -617,7 +617,9 @@ BLOCK_CASES = [(1, 4096, 4096), (1, 11008, 300), (2, 128, 77), (3, 4096, 1000), 
                (5, 4096, 4500), (16, 640, 8300), (32, 1152, 5000), (33, 256, 100), (17, 128, 17),
                # the largest K (alpha rows of 257 floats per row in LDS), and four row blocks at a
                # K whose alpha rows take 33 KB of LDS
-               (5, 32768, 70), (4, 16384, 8300)]
+               (5, 32768, 70), (4, 16384, 8300),
+               # 33-127 tokens: three and four slices of 32, the last ragged
+               (65, 4224, 4100), (127, 256, 129)]
 
 
 @pytest.mark.parametrize("m,k,n", BLOCK_CASES)
@@ -650,11 +652,11 @@ def test_forward_blocks_parity(dev, m, k, n):
     assert same >= 0.99
 
 
-# More than 32 tokens: the block-scaled GEMM adds alpha * acc per block in fp64 in ascending
+# 128 tokens and more: the block-scaled GEMM adds alpha * acc per block in fp64 in ascending
 # block order, the oracle's order, so y is compared bit for bit.  Cases: one and several 128 x 128
 # tiles, ragged M and N, K of one block and odd block counts, with and without bias.
-BLOCK_GEMM_CASES = [(33, 128, 100), (64, 256, 129), (128, 4096, 256), (129, 1152, 300), (300, 2048, 1000),
-                    (1000, 384, 257), (65, 4224, 4100)]
+BLOCK_GEMM_CASES = [(128, 128, 100), (200, 256, 129), (128, 4096, 256), (129, 1152, 300), (300, 2048, 1000),
+                    (1000, 384, 257), (160, 4224, 4100)]
 
 
 @pytest.mark.parametrize("m,k,n", BLOCK_GEMM_CASES)
