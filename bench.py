@@ -460,8 +460,8 @@ def blocks_bench(torch, bl, workloads, dev, ms_plain_step):
         y = torch.empty((m, n), dtype=torch.float32, device=dev)
         ms, _ = _graph_time(torch, lambda i: bl.bitlinear_forward_blocks(xq, beta, *pool[i % copies], y=y), 96)
         out["batched"].append({"M": m, "K": k, "N": n, "us": round(ms * 1e3, 2),
-                               "kernel": "16x16x64 int8 MFMA tiles, int32 sums per block scaled in fp64" if m <= 32 else
-                                         "block-scaled GEMM, 128 x 128 tiles, fp64 sum per output"})
+                               "kernel": "16x16x64 int8 MFMA tiles, int32 sums per block scaled in fp64" +
+                                         ("" if m <= 32 else f", {(m + 31) // 32} slices of 32 tokens")})
     del pool
     # prefill with block scales: M = 2048 (int8 ops 2MNK) beside the per-tensor GEMM of the same shape
     m = 2048
