@@ -170,17 +170,33 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(GemvArgs g) {
     };
     RowAux auxa, auxb;
     if constexpr (FUSED) {
-        constexpr bool KEEP = UPT <= 4;       // keep x in registers between the two passes
-        float4 xv[KEEP ? UPT : 1][4];
-        bool ok[UPT];
+        // x is read in float4s, consecutive threads on consecutive float4s of the workgroup's
+        // tokens (slot f = tid + NT * i is float4 f - 16 C t of token t), so every wave load
+        // covers 1 KiB of x in whole cache lines whatever the alignment of x.  (Read per
+        // 16-byte unit, the lanes of a wave load were 256 bytes apart; with x not at a multiple
+        // of 1 KiB that cost 0.4 us per launch on the 7B shapes.)  The four lanes of a quad hold
+        // the four dwords of one 16-weight group; two DPP exchanges inside the quad transpose it
+        // into the LDS image.
+        constexpr int SLOTS = MT * CPL * 1024;           // float4 slots, an upper bound of M * K / 4
+        constexpr int FPT = (SLOTS + NT - 1) / NT;
+        constexpr bool KEEP = FPT <= 16;                 // keep x in registers between the two passes
+        const int k4 = (int)(K >> 2);                    // float4s per token (K % 64 == 0, K <= 32768)
+        const int jj = tid & 3;                          // dword of the slot's 16-weight group
+        auto slot_at = [&](int i, int& t, int& fl) {
+            const int f = tid + NT * i;
+            t = 0;
+#pragma unroll
+            for (int tt = 1; tt < MT; ++tt) t += f >= tt * k4 ? 1 : 0;
+            fl = f - t * k4;
+            return t < M && fl < k4;
+        };
+        float4 xv[KEEP ? FPT : 1];
         if constexpr (KEEP) {
 #pragma unroll
-            for (int k = 0; k < UPT; ++k) {
-                int t, c, q;
-                ok[k] = unit_at(tid + NT * k, t, c, q);
-                const float4* src = reinterpret_cast<const float4*>(g.x + (ok[k] ? t * K + 64 * c + 16 * q : 0));
-#pragma unroll
-                for (int e = 0; e < 4; ++e) xv[k][e] = src[e];
+            for (int i = 0; i < FPT; ++i) {
+                int t, fl;
+                const bool valid = slot_at(i, t, fl);
+                xv[i] = reinterpret_cast<const float4*>(g.x)[valid ? t * k4 + fl : 0];
             }
         }
         auxa = load_aux(rb);
@@ -189,21 +205,13 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(GemvArgs g) {
 #pragma unroll
         for (int t = 0; t < MT; ++t) mx[t] = 0.0f;
 #pragma unroll
-        for (int k = 0; k < UPT; ++k) {
-            int t, c, q;
-            const bool valid = unit_at(tid + NT * k, t, c, q);
-            float4 v[4];
-            if constexpr (KEEP) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = xv[k][e];
-            } else {
-                const float4* src = reinterpret_cast<const float4*>(g.x + (valid ? t * K + 64 * c + 16 * q : 0));
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = src[e];
-            }
-            float m = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) m = fmaxf(m, fmaxf(fmaxf(fabsf(v[e].x), fabsf(v[e].y)), fmaxf(fabsf(v[e].z), fabsf(v[e].w))));
+        for (int i = 0; i < FPT; ++i) {
+            int t, fl;
+            const bool valid = slot_at(i, t, fl);
+            float4 v;
+            if constexpr (KEEP) v = xv[i];
+            else v = reinterpret_cast<const float4*>(g.x)[valid ? t * k4 + fl : 0];
+            const float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
 #pragma unroll
             for (int tt = 0; tt < MT; ++tt)
                 if (valid && tt == t) mx[tt] = fmaxf(mx[tt], m);
@@ -224,32 +232,39 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(GemvArgs g) {
             rcp[t] = 1.0f / beta_t[t];
         }
         const bool exporter = blockIdx.x == 0;
+        uint32_t* xs32 = reinterpret_cast<uint32_t*>(xs);
 #pragma unroll
-        for (int k = 0; k < UPT; ++k) {
-            const int u = tid + NT * k;
-            int t, c, q;
-            u32x4 o = {0u, 0u, 0u, 0u};
-            if (unit_at(u, t, c, q)) {
-                float bt = beta_t[0], rt = rcp[0];
+        for (int i = 0; i < FPT; ++i) {
+            int t, fl;
+            const bool valid = slot_at(i, t, fl);
+            float4 v;
+            if constexpr (KEEP) v = xv[i];
+            else v = reinterpret_cast<const float4*>(g.x)[valid ? t * k4 + fl : 0];
+            float bt = beta_t[0], rt = rcp[0];
 #pragma unroll
-                for (int tt = 1; tt < MT; ++tt)
-                    if (tt == t) { bt = beta_t[tt]; rt = rcp[tt]; }
-                float4 v[4];
-                if constexpr (KEEP) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = xv[k][e];
-                } else {
-                    const float4* src = reinterpret_cast<const float4*>(g.x + t * K + 64 * c + 16 * q);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = src[e];
-                }
-                const u32x4 sb = act_bytes16(v, bt, rt);
-                if (exporter && g.xq_out)
-                    *reinterpret_cast<u32x4*>(g.xq_out + t * K + 64 * c + 16 * q) = sb;
-                o = transpose4x4_bytes(sb);
-                add_part(t, byte_sum(sb.x) + byte_sum(sb.y) + byte_sum(sb.z) + byte_sum(sb.w));
+            for (int tt = 1; tt < MT; ++tt)
+                if (tt == t) { bt = beta_t[tt]; rt = rcp[tt]; }
+            // x_q of weights k = 4 fl .. 4 fl + 3 (byte i = weight 4 fl + i)
+            const uint32_t d = act_byte(v.x, bt, rt) | (act_byte(v.y, bt, rt) << 8) | (act_byte(v.z, bt, rt) << 16) |
+                               (act_byte(v.w, bt, rt) << 24);
+            // quad transpose: lane jj ends with byte j = weight 4 j + jj of the group
+            const uint32_t p1 = (uint32_t)dpp_i<0xB1>((int)d);              // from lane jj ^ 1
+            const uint32_t t1 = __builtin_amdgcn_perm(p1, d, (jj & 1) ? 0x03070105u : 0x06020400u);
+            const uint32_t p2 = (uint32_t)dpp_i<0x4E>((int)t1);             // from lane jj ^ 2
+            const uint32_t t2 = __builtin_amdgcn_perm(p2, t1, (jj & 2) ? 0x03020706u : 0x05040100u);
+            if (valid) {
+                const int G = fl >> 2;                       // 16-weight group within the token
+                const int c = G >> 2, q = G & 3;
+                xs32[((((t * CPL + (c >> 6)) * 4 + q) << 6) + (c & 63)) * 4 + jj] = t2;
+                add_part(t, byte_sum(d));
+                if (exporter && g.xq_out) reinterpret_cast<uint32_t*>(g.xq_out + t * K)[fl] = d;
             }
-            if (u < UNITS) xs[u] = o;
+        }
+        // units of chunks past the row end (and of tokens past M) hold zeros
+        for (int u = tid; u < UNITS; u += NT) {
+            const int i = u >> 8;
+            const int t = i / CPL, c = (u & 63) + 64 * (i % CPL);
+            if (c >= C || t >= M) xs[u] = u32x4{0u, 0u, 0u, 0u};
         }
         if (exporter && g.beta_out && tid < M) {
 #pragma unroll

@@ -392,6 +392,28 @@ def test_forward_fused_parity(dev, m, k, n):
     assert np.array_equal(y2.cpu().numpy(), y_o)
 
 
+@pytest.mark.parametrize("m,k,n,off", [(1, 4096, 11008, 16), (1, 4096, 4096, 512), (1, 11008, 4096, 128),
+                                       (2, 4096, 3000, 48), (4, 8192, 700, 1008), (1, 32768, 300, 272)])
+def test_forward_fused_unaligned_x(dev, m, k, n, off):
+    """x at an offset of `off` bytes from a large allocation (16-byte aligned, as the ABI asks,
+    but not at a multiple of the 1 KiB the fused kernel's loads cover)."""
+    torch, bl = dev
+    _say(f"forward_fused unaligned x M={m} K={k} N={n} offset={off}")
+    w = workloads.weights(6, n, k, index=5)
+    x = workloads.activations_with_outliers(6, m, k, index=5)
+    r = oracle.bitlinear(x, w)
+    buf = torch.zeros(m * k + 256, dtype=torch.float32, device="cuda")
+    start = ((off - buf.data_ptr() % 1024) % 1024) // 4           # x at an address = off mod 1 KiB
+    xt = buf[start: start + m * k].view(m, k)
+    xt.copy_(_to(torch, x))
+    assert xt.data_ptr() % 1024 == off
+    pk, al = _to(torch, r["packed"]), _to(torch, np.array([r["alpha"]], np.float32))
+    y, acc = bl.bitlinear_forward_fused(xt, pk, al, acc=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), r["acc"])
+    assert np.array_equal(y.cpu().numpy(), r["y"])
+
+
 @pytest.mark.parametrize("m,k,n", [(5, 4096, 130), (64, 1024, 64), (2, 100, 33), (3, 28672, 40)])
 def test_forward_fused_two_call_path(dev, m, k, n):
     torch, bl = dev
