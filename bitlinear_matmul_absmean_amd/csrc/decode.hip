@@ -354,10 +354,15 @@ static hipError_t launch_bdec16(const ForwardArgs& a, hipStream_t s) {
 
 
 // k_bdec16 for whole 256-weight sub-steps (K % 256 == 0, no K-tail selects) with an ST-stage
-// register pipeline, for grids of one 16-row block per workgroup (N <= 4096 rows).  Measured
-// with weights not in cache at K = 11008, N = 4096: 8 tokens 7.82 against 8.35 us, 16 tokens
-// 9.56 against 10.76 us (ST = 4), 24 tokens 12.99 against 14.39 us (ST = 3); six stages, which
-// hold every load of a wave at once, were slower (10.0 us at 16 tokens).
+// register pipeline whose loads past the wave's range are skipped.  With two stages and as
+// many 16-row blocks per workgroup as keep the grid within 256 workgroups (three at N = 11008:
+// 230 workgroups, where four left 84 CUs idle), measured with weights not in cache against the
+// earlier choices (k_bdec16 with 1, 2, 4 or 8 row blocks, k_bdec for 17 to 32 tokens on wide
+// matrices): K = 4096, N = 11008: 4 / 8 / 16 / 24 / 32 tokens 6.37 / 6.69 / 7.17 / 8.64 / 9.34 us
+// against 7.17 / 7.54 / 8.07 / 13.66 / 14.36 us; K = 8192, N = 10240: 8.8 / 9.6 / 11.4 / 14.4 /
+// 15.5 against 13.4 / 14.4 / 16.6 / 19.9 / 20.9 us; K = 8192, N = 28672, 24 tokens 24.9 against
+// 39.0 us; K = 11008, N = 4096 and K = 28672, N = 8192 level or up to 9% faster.  Three and four
+// stages were slower on every one of these shapes except a few within 2%.
 template <int MT, int RB, int ST>
 __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec16w(ForwardArgs a) {
     extern __shared__ i32x4 red[];
@@ -631,31 +636,46 @@ static hipError_t launch_bdec64(const ForwardArgs& a, hipStream_t s) {
 bool decode_mfma_supports(int64_t M, int64_t K) { return M >= 1 && M <= 64 && K % 64 == 0; }
 
 // Tile shape by token count: 16 x 16 x 64 tiles up to 32 tokens (better weight loads, fewer
-// token rows of x_q) except 17 to 32 tokens on wide matrices of K <= 8192, 32 x 32 x 32 tiles
-// up to 64.  Row blocks per workgroup: the fewest that
+// token rows of x_q; with K % 256 != 0, 17 to 32 tokens on wide matrices of K <= 8192 take
+// 32 x 32 x 32 tiles), 32 x 32 x 32 tiles up to 64.  Row blocks per workgroup: the fewest that
 // keep the grid within about one workgroup per CU (256), so that x_q is read as few times as
 // possible, within the registers (no spills) and the LDS of the final reduction.
+template <int MT>
+static hipError_t launch_bdec16w_fill(const ForwardArgs& a, hipStream_t s) {
+    const int64_t nb16 = (a.N + 15) / 16;
+    switch ((nb16 + 255) / 256) {
+        case 1: return launch_bdec16w<MT, 1, 2>(a, s);
+        case 2: return launch_bdec16w<MT, 2, 2>(a, s);
+        case 3: return launch_bdec16w<MT, 3, 2>(a, s);
+        case 4: return launch_bdec16w<MT, 4, 2>(a, s);
+        case 5: return launch_bdec16w<MT, 5, 2>(a, s);
+        case 6: return launch_bdec16w<MT, 6, 2>(a, s);
+        case 7: return launch_bdec16w<MT, 7, 2>(a, s);
+        default: return launch_bdec16w<MT, 8, 2>(a, s);   // more than 256 workgroups from N > 32768
+    }
+}
+
 hipError_t launch_decode_mfma(const ForwardArgs& a, hipStream_t s) {
     const int64_t nb16 = (a.N + 15) / 16;
-    const bool whole = a.K % 256 == 0;
+    // up to 32 tokens with whole 256-weight sub-steps: 16 x 16 x 64 tiles, the grid filled
+    if (a.M <= 32 && a.K % 256 == 0) return a.M <= 16 ? launch_bdec16w_fill<1>(a, s) : launch_bdec16w_fill<2>(a, s);
     if (a.M <= 16) {
-        if (nb16 <= 256) return whole ? launch_bdec16w<1, 1, 4>(a, s) : launch_bdec16<1, 1>(a, s);
+        if (nb16 <= 256) return launch_bdec16<1, 1>(a, s);
         if (nb16 <= 512) return launch_bdec16<1, 2>(a, s);
         if (nb16 <= 1024) return launch_bdec16<1, 4>(a, s);
         return launch_bdec16<1, 8>(a, s);
     }
     const int64_t nb = (a.N + 31) / 32;
-    // 17 to 32 tokens on wide matrices of moderate K: 32x32x32 tiles with one 32-token block
-    // (measured with weights not in cache, M = 24: 19.8 vs 28.0 us at K = 8192, N = 10240;
-    // 38.9 vs 54.5 us at K = 8192, N = 28672; level at K = 4096, N = 11008; the 16x16x64
-    // tiles stay ahead at K = 11008 and 28672)
+    // K % 256 != 0: 17 to 32 tokens on wide matrices of moderate K on 32x32x32 tiles with one
+    // 32-token block (measured with weights not in cache, M = 24: 19.8 vs 28.0 us at K = 8192,
+    // N = 10240 for k_bdec16 with its earlier row blocks; 38.9 vs 54.5 us at K = 8192, N = 28672)
     if (a.M > 16 && a.M <= 32 && a.K <= 8192 && a.N >= 8192) {
         if (nb <= 256) return launch_bdec<1, 1>(a, s);
         if (nb <= 512) return launch_bdec<1, 2>(a, s);
         return launch_bdec<1, 4>(a, s);
     }
     if (a.M <= 32) {
-        if (nb16 <= 256) return whole ? launch_bdec16w<2, 1, 3>(a, s) : launch_bdec16<2, 1>(a, s);
+        if (nb16 <= 256) return launch_bdec16<2, 1>(a, s);
         return launch_bdec16<2, 2>(a, s);
     }
     // 33 to 64 tokens, whole 128-weight sub-steps: two row blocks per workgroup from 8192 rows

@@ -174,18 +174,25 @@ FWD_CASES = [
     (1, 28672, 2100), (1, 8192, 2048),
     # two to four tokens on the GEMV (matrices of 2^26 weights or more; two tokens with K >= 8192)
     (2, 16384, 4100), (4, 8192, 8200), (3, 4096, 16400), (2, 8192, 1000), (2, 11008, 4099), (3, 16384, 4200),
-    # batched decode launch shapes: 16x16x64 tiles with 1/2/4/8 row blocks per workgroup and one or
-    # two token blocks, 32x32x32 tiles with 1/2; K % 256 = 64 and K % 128 = 64 tails; ragged N
-    (8, 256, 9000), (12, 128, 17000), (16, 192, 5000), (9, 4160, 700), (24, 320, 4100),
+    # batched decode with K % 256 != 0: 16x16x64 tiles with 1/2/4/8 row blocks per workgroup and
+    # one or two token blocks, 32x32x32 tiles with 1/2; K % 256 = 64 and K % 128 = 64 tails;
+    # ragged N
+    (12, 128, 17000), (16, 192, 5000), (9, 4160, 700), (24, 320, 4100),
     (32, 64, 8300), (20, 4352, 300), (48, 192, 8200), (64, 4160, 600), (41, 128, 33),
-    # 17-32 tokens on 32x32x32 tiles with one token block (K <= 8192, N >= 8192): 1, 2 and 4
-    # row blocks per workgroup, K % 128 = 64
-    (17, 192, 8192), (24, 1088, 9000), (32, 256, 20000),
-    # up to 32 tokens, one 16-row block per workgroup (N <= 4096), whole 256-weight sub-steps
-    # (K % 256 == 0): four- and three-stage pipelines, sub-step counts below, at and above the
-    # pipeline depth per wave, ragged N and M
+    # 17-32 tokens on 32x32x32 tiles with one token block (K % 256 != 0, K <= 8192, N >= 8192):
+    # 1, 2 and 4 row blocks per workgroup, K % 128 = 64
+    (17, 192, 8192), (24, 1088, 9000), (32, 1344, 20000),
+    # up to 32 tokens with whole 256-weight sub-steps (K % 256 == 0), two-stage pipeline: one
+    # 16-row block per workgroup (N <= 4096), sub-step counts per wave below, at and above two,
+    # ragged N and M
     (5, 256, 33), (16, 4096, 4096), (9, 11008, 1000), (12, 8192, 257), (16, 768, 4095),
     (17, 11008, 700), (32, 2048, 4096), (25, 256, 64),
+    # ... and 2 to 8 row blocks per workgroup (the fewest that keep the grid within 256
+    # workgroups; 8 beyond N = 32768, with more workgroups), one and two token blocks
+    (8, 256, 9000), (8, 256, 8000), (3, 512, 12001), (12, 256, 16300), (7, 512, 20000),
+    (16, 256, 24500), (10, 768, 28672), (5, 256, 40000),
+    (24, 512, 8100), (32, 256, 11008), (20, 256, 16001), (28, 256, 17000), (31, 512, 21000),
+    (18, 256, 25000), (32, 256, 33000), (24, 4096, 11008), (16, 8192, 10240),
     # 33-64 tokens with whole 128-weight sub-steps (K % 128 == 0): one row block per workgroup
     # below N = 8192, two from it; sub-step counts not divisible by the eight waves (K = 128:
     # seven waves idle; K = 1152: 9 sub-steps), odd per-wave counts, ragged N and M
