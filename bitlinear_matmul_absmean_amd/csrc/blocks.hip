@@ -357,16 +357,27 @@ static hipError_t launch_bdec16_blocks(const BlockArgs& a, hipStream_t s) {
                            tiles > alphas ? tiles : alphas, s, a);
 }
 
-// 5 to 32 tokens: row blocks per workgroup so that the grid stays near one workgroup per CU.
+// 3 to 32 tokens: the fewest row blocks per workgroup that keep the grid within 256
+// workgroups (three at N = 11008: 230 workgroups, where four left 84 CUs idle), at most 6 for
+// one token block and 3 for two (beyond, the fp64 accumulators spill); larger N gets more
+// workgroups.
 static hipError_t launch_bdec16_blocks_m(const BlockArgs& a, hipStream_t s) {
-    const int64_t nb16 = (a.N + 15) / 16;
+    const int64_t rb = ((a.N + 15) / 16 + 255) / 256;
     if (a.M <= 16) {
-        if (nb16 <= 256) return launch_bdec16_blocks<1, 1>(a, s);
-        if (nb16 <= 512) return launch_bdec16_blocks<1, 2>(a, s);
-        return launch_bdec16_blocks<1, 4>(a, s);
+        switch (rb) {
+            case 1: return launch_bdec16_blocks<1, 1>(a, s);
+            case 2: return launch_bdec16_blocks<1, 2>(a, s);
+            case 3: return launch_bdec16_blocks<1, 3>(a, s);
+            case 4: return launch_bdec16_blocks<1, 4>(a, s);
+            case 5: return launch_bdec16_blocks<1, 5>(a, s);
+            default: return launch_bdec16_blocks<1, 6>(a, s);
+        }
     }
-    if (nb16 <= 256) return launch_bdec16_blocks<2, 1>(a, s);
-    return launch_bdec16_blocks<2, 2>(a, s);
+    switch (rb) {
+        case 1: return launch_bdec16_blocks<2, 1>(a, s);
+        case 2: return launch_bdec16_blocks<2, 2>(a, s);
+        default: return launch_bdec16_blocks<2, 3>(a, s);
+    }
 }
 
 // ---------------------------------------------------------------------------------------

@@ -491,9 +491,9 @@ static hipError_t launch_bdec16w(const ForwardArgs& a, hipStream_t s) {
 // 32 bytes of each of its rows' 128-byte lines in turn; streamed past the caches, every
 // sub-step fetched its line again, cached they hit in L2.  Both changes were measured with
 // weights not in cache, M = 64: 12.8 against 18.5 us at K = 4096, N = 11008 (two row blocks per
-// workgroup), 18.3 against 22.2 us at K = 11008, N = 4096 (one row block).  The kernel stays
-// bound by its VALU work (the 4x4 transposes and byte sums of x_q, the weight expansion: about
-// ten instructions per MFMA).
+// workgroup), 18.3 against 22.2 us at K = 11008, N = 4096 (one row block).  The token sums of
+// x_q come from MFMAs against an all-ones operand (12.9 -> 12.6 us at K = 4096, N = 11008).
+// The kernel stays bound by its VALU work (the 4x4 transposes of x_q, the weight expansion).
 template <int RB>
 __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec64(ForwardArgs a) {
     constexpr int MT = 2;
@@ -534,25 +534,26 @@ __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec64(ForwardArgs a) {
     for (int r = 0; r < RB; ++r)
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[r][t] = i32x16{};
-    int ts[MT * 4];
+    // token sums of x_q from the matrix cores: A times an all-ones B gives, in every column,
+    // each token row's sum over the sub-step's k (the matrix cores are mostly idle here; the
+    // four v_dot4 per 16 bytes of x_q they replace are not)
+    const i32x4 ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+    i32x16 tsm[MT];
 #pragma unroll
-    for (int i = 0; i < MT * 4; ++i) ts[i] = 0;
+    for (int t = 0; t < MT; ++t) tsm[t] = i32x16{};
     auto compute = [&](int st) {
 #pragma unroll
         for (int i = 0; i < MT * 4; ++i) {
             const u32x4 v = xa[st][i];
             xs[(8 * i + xt) * XU + xu] = (i32x4)transpose4x4_perm(v);
-            int z = ts[i];
-            z = __builtin_amdgcn_sdot4((int)v.x, 0x01010101, z, false);
-            z = __builtin_amdgcn_sdot4((int)v.y, 0x01010101, z, false);
-            z = __builtin_amdgcn_sdot4((int)v.z, 0x01010101, z, false);
-            ts[i] = __builtin_amdgcn_sdot4((int)v.w, 0x01010101, z, false);
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             i32x4 av[MT];
 #pragma unroll
             for (int t = 0; t < MT; ++t) av[t] = xs[(32 * t + lr) * XU + 4 * lg + q];
+#pragma unroll
+            for (int t = 0; t < MT; ++t) tsm[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[t], ones, tsm[t], 0, 0, 0);
 #pragma unroll
             for (int r = 0; r < RB; ++r) {
                 const uint32_t w = q == 0 ? wb[st][r].x : q == 1 ? wb[st][r].y : q == 2 ? wb[st][r].z : wb[st][r].w;
@@ -579,13 +580,12 @@ __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec64(ForwardArgs a) {
             }
         }
     }
+    // column 0 (lanes 0 and 32) holds accumulator r of token 8 (r / 4) + 4 (lane / 32) + r % 4
+    if (lr == 0) {
 #pragma unroll
-    for (int i = 0; i < MT * 4; ++i) {
-        int v = ts[i];
-        v += __shfl_xor(v, 1, 64);
-        v += __shfl_xor(v, 2, 64);
-        v += __shfl_xor(v, 4, 64);
-        if (xu == 0) tsum_w[wave][8 * i + xt] = v;
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) tsum_w[wave][32 * t + 8 * (r / 4) + 4 * lg + r % 4] = tsm[t][r];
     }
     __syncthreads();                               // every wave is done with its staging region
     if (tid < MT * 32) {
@@ -678,10 +678,12 @@ hipError_t launch_decode_mfma(const ForwardArgs& a, hipStream_t s) {
         if (nb16 <= 256) return launch_bdec16<2, 1>(a, s);
         return launch_bdec16<2, 2>(a, s);
     }
-    // 33 to 64 tokens, whole 128-weight sub-steps: two row blocks per workgroup from 8192 rows
-    // (172 workgroups at N = 11008), one below (128 at N = 4096; two measured 29.7 against
-    // 18.3 us at K = 11008, N = 4096)
-    if (a.K % 128 == 0) return a.N >= 8192 ? launch_bdec64<2>(a, s) : launch_bdec64<1>(a, s);
+    // 33 to 64 tokens, whole 128-weight sub-steps: one 32-row block per workgroup up to 256
+    // workgroups (N <= 8192), two beyond (172 workgroups at N = 11008).  Measured with weights
+    // not in cache, M = 64: K = 8192, N = 8192, one block 15.8 against 18.6 us for two; K = 28672,
+    // N = 8192, 42.3 against 49.8 us; K = 11008, N = 4096, 18.3 against 23.9 us; K = 4096,
+    // N = 11008, two blocks 12.6 against 17.0 us for one.
+    if (a.K % 128 == 0) return nb <= 256 ? launch_bdec64<1>(a, s) : launch_bdec64<2>(a, s);
     if (nb <= 256) return launch_bdec<2, 1>(a, s);
     return launch_bdec<2, 2>(a, s);
 }

@@ -194,10 +194,10 @@ FWD_CASES = [
     (24, 512, 8100), (32, 256, 11008), (20, 256, 16001), (28, 256, 17000), (31, 512, 21000),
     (18, 256, 25000), (32, 256, 33000), (24, 4096, 11008), (16, 8192, 10240),
     # 33-64 tokens with whole 128-weight sub-steps (K % 128 == 0): one row block per workgroup
-    # below N = 8192, two from it; sub-step counts not divisible by the eight waves (K = 128:
+    # up to N = 8192, two beyond; sub-step counts not divisible by the eight waves (K = 128:
     # seven waves idle; K = 1152: 9 sub-steps), odd per-wave counts, ragged N and M
     (33, 128, 8193), (64, 1152, 8200), (40, 4096, 300), (64, 11008, 4100), (57, 384, 8191),
-    (64, 640, 12345), (35, 2176, 33),
+    (64, 640, 12345), (35, 2176, 33), (64, 1024, 8192), (48, 256, 30000),
 ]
 
 
@@ -644,9 +644,14 @@ BLOCK_CASES = [(1, 4096, 4096), (1, 11008, 300), (2, 128, 77), (3, 4096, 1000), 
                # more than four tokens: 16x16x64 tiles, one or two token tiles, 1/2/4 row blocks per
                # workgroup, K % 256 == 128 (a lone last block), slices of 32 tokens
                (5, 4096, 4500), (16, 640, 8300), (32, 1152, 5000), (33, 256, 100), (17, 128, 17),
-               # the largest K (alpha rows of 257 floats per row in LDS), and four row blocks at a
-               # K whose alpha rows take 33 KB of LDS
+               # the largest K (alpha rows of 257 floats per row in LDS), and three row blocks at a
+               # K whose alpha rows take 25 KB of LDS
                (5, 32768, 70), (4, 16384, 8300),
+               # the fewest row blocks that keep the grid within 256 workgroups: 3 to 6 with one
+               # token tile (6 also beyond 256 workgroups, with 6 x 16 alpha rows at K = 16384),
+               # 2 and 3 with two (3 also beyond 256 workgroups)
+               (6, 4096, 12000), (8, 1024, 16000), (5, 2048, 20000), (3, 16384, 23000), (7, 512, 30000),
+               (24, 128, 6000), (20, 1024, 9000), (32, 640, 15000),
                # 33-127 tokens: three and four slices of 32, the last ragged
                (65, 4224, 4100), (127, 256, 129)]
 
