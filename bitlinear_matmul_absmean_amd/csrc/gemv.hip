@@ -72,24 +72,25 @@ __device__ __forceinline__ float wave_max_dpp(float f) {
     return fmaxf(fmaxf(a, b), fmaxf(c, d));
 }
 
-// int8 code of one activation [P3 §2.4]: clip(rne(fp32(127 x) / beta), -127, 127), with
-// the correctly rounded quotient from the reciprocal y = RN(1/beta) (see the file header).
-__device__ __forceinline__ uint32_t act_byte(float x, float beta, float y) {
+// int8 codes of four activations [P3 §2.4], clip(rne(fp32(127 x) / beta), -127, 127), byte i
+// from component i.  The quotient is the correctly rounded one, from the reciprocal
+// y = RN(1/beta) (see the file header).  beta >= max |x|, so |t| <= 127 (up to one rounding of
+// fp32(127 x) above 127 beta, still far below 127.5): the clip never acts, and adding 1.5 * 2^23
+// rounds t to an integer half-to-even, the sum lying in [2^23, 2^24) where floats are one
+// apart.  The mantissa then holds 2^22 + rne(t), whose low byte is the two's-complement code
+// (2^22 is a multiple of 256); v_perm gathers the four low bytes.
+__device__ __forceinline__ uint32_t act_code_bits(float x, float beta, float y) {
     const float a = x * 127.0f;
     const float q = a * y;
     const float r = __builtin_fmaf(-q, beta, a);
     const float t = __builtin_fmaf(r, y, q);
-    const float c = __builtin_amdgcn_fmed3f(rintf(t), -127.0f, 127.0f);
-    return (uint32_t)((int)c) & 0xFFu;
+    return __float_as_uint(t + 12582912.0f);
 }
 
-__device__ __forceinline__ u32x4 act_bytes16(const float4 (&v)[4], float beta, float y) {
-    uint32_t d[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        d[i] = act_byte(v[i].x, beta, y) | (act_byte(v[i].y, beta, y) << 8) | (act_byte(v[i].z, beta, y) << 16) |
-               (act_byte(v[i].w, beta, y) << 24);
-    return u32x4{d[0], d[1], d[2], d[3]};
+__device__ __forceinline__ uint32_t act_dword(float4 v, float beta, float y) {
+    const uint32_t p01 = __builtin_amdgcn_perm(act_code_bits(v.y, beta, y), act_code_bits(v.x, beta, y), 0x0c0c0400u);
+    const uint32_t p23 = __builtin_amdgcn_perm(act_code_bits(v.w, beta, y), act_code_bits(v.z, beta, y), 0x0c0c0400u);
+    return __builtin_amdgcn_perm(p23, p01, 0x05040100u);
 }
 
 // MT tokens (the kernel masks tokens >= M), CPL chunks of 64 weights per lane and row,
@@ -245,8 +246,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(GemvArgs g) {
             for (int tt = 1; tt < MT; ++tt)
                 if (tt == t) { bt = beta_t[tt]; rt = rcp[tt]; }
             // x_q of weights k = 4 fl .. 4 fl + 3 (byte i = weight 4 fl + i)
-            const uint32_t d = act_byte(v.x, bt, rt) | (act_byte(v.y, bt, rt) << 8) | (act_byte(v.z, bt, rt) << 16) |
-                               (act_byte(v.w, bt, rt) << 24);
+            const uint32_t d = act_dword(v, bt, rt);
             // quad transpose: lane jj ends with byte j = weight 4 j + jj of the group
             const uint32_t p1 = (uint32_t)dpp_i<0xB1>((int)d);              // from lane jj ^ 1
             const uint32_t t1 = __builtin_amdgcn_perm(p1, d, (jj & 1) ? 0x03070105u : 0x06020400u);
