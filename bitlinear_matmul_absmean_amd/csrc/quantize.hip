@@ -202,6 +202,29 @@ __device__ __forceinline__ uint32_t act_code(float x, float beta, float y) {
     return (uint32_t)((int)c) & 0xFFu;
 }
 
+// Four codes, packed little-endian, of values with |x| <= beta (true for every element of the
+// row beta was taken from).  The quotient t = fp32(127 x) / beta is formed as in act_code and
+// satisfies |t| < 127.5, so the clip of the definition never acts; adding 1.5 * 2^23 rounds t
+// half-to-even to an integer held in the low mantissa bits, whose low byte is the two's
+// complement code.  v_perm gathers the four bytes.  m127 = 127 s with s a power of two
+// (the unapplied rotation scale) gives the same codes: fp32(fp32(x s) 127) = fp32(x (127 s))
+// whenever x s is normal, and where it is subnormal both quotients round to code 0, since
+// beta >= 1e-8.
+__device__ __forceinline__ uint32_t act_codes4(float x0, float x1, float x2, float x3, float beta, float y,
+                                              float m127 = 127.0f) {
+    auto code = [&](float x) {
+        const float a = x * m127;
+        const float q = a * y;
+        const float r = __builtin_fmaf(-q, beta, a);
+        const float t = __builtin_fmaf(r, y, q);
+        return __float_as_uint(t + 12582912.0f);
+    };
+    const uint32_t lo = __builtin_amdgcn_perm(code(x1), code(x0), 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(code(x3), code(x2), 0x04000c0cu);
+    return lo | hi;
+}
+
+
 template <bool VEC>
 __global__ __launch_bounds__(256) void k_quantize_act(const float* __restrict__ x, int64_t K,
                                                       int8_t* __restrict__ xq, float* __restrict__ beta) {
@@ -227,8 +250,7 @@ __global__ __launch_bounds__(256) void k_quantize_act(const float* __restrict__ 
         uint32_t* out = reinterpret_cast<uint32_t*>(xq + m * K);
         for (int64_t c = threadIdx.x; c < (K >> 2); c += 256) {
             float4 v = r4[c];
-            out[c] = act_code(v.x, b, y) | (act_code(v.y, b, y) << 8) | (act_code(v.z, b, y) << 16) |
-                     (act_code(v.w, b, y) << 24);
+            out[c] = act_codes4(v.x, v.y, v.z, v.w, b, y);
         }
     } else {
         for (int64_t c = threadIdx.x; c < K; c += 256) xq[m * K + c] = (int8_t)act_code(row[c], b, y);
@@ -268,8 +290,7 @@ __global__ __launch_bounds__(NT) void k_quantize_act_row(const float* __restrict
     for (int j = 0; j < V; ++j) {
         const int c = (int)threadIdx.x + NT * j;
         if (c < K4)
-            out[c] = act_code(v[j].x, b, y) | (act_code(v[j].y, b, y) << 8) | (act_code(v[j].z, b, y) << 16) |
-                     (act_code(v[j].w, b, y) << 24);
+            out[c] = act_codes4(v[j].x, v[j].y, v[j].z, v[j].w, b, y);
     }
 }
 
@@ -414,28 +435,6 @@ __global__ __launch_bounds__(256) void k_hadamard_rows(const float* x, int64_t K
         const int e = 4 * threadIdx.x + 1024 * q;
         if (e < len) *reinterpret_cast<float4*>(o + e) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
     }
-}
-
-// Four codes, packed little-endian, of values with |x| <= beta (true for every element of the
-// row beta was taken from).  The quotient t = fp32(127 x) / beta is formed as in act_code and
-// satisfies |t| < 127.5, so the clip of the definition never acts; adding 1.5 * 2^23 rounds t
-// half-to-even to an integer held in the low mantissa bits, whose low byte is the two's
-// complement code.  v_perm gathers the four bytes.  m127 = 127 s with s a power of two
-// (the unapplied rotation scale) gives the same codes: fp32(fp32(x s) 127) = fp32(x (127 s))
-// whenever x s is normal, and where it is subnormal both quotients round to code 0, since
-// beta >= 1e-8.
-__device__ __forceinline__ uint32_t act_codes4(float x0, float x1, float x2, float x3, float beta, float y,
-                                              float m127 = 127.0f) {
-    auto code = [&](float x) {
-        const float a = x * m127;
-        const float q = a * y;
-        const float r = __builtin_fmaf(-q, beta, a);
-        const float t = __builtin_fmaf(r, y, q);
-        return __float_as_uint(t + 12582912.0f);
-    };
-    const uint32_t lo = __builtin_amdgcn_perm(code(x1), code(x0), 0x0c0c0400u);
-    const uint32_t hi = __builtin_amdgcn_perm(code(x3), code(x2), 0x04000c0cu);
-    return lo | hi;
 }
 
 __device__ __forceinline__ void store_codes(int8_t* __restrict__ xrow, int64_t c0, int len, const float (&v)[16],
