@@ -10,8 +10,10 @@
 //     register buffers: the 16-byte loads of the next R rows are in flight while the current
 //     R rows are reduced.  A wave load is 1 KiB of one packed row (4096 weights), fully
 //     coalesced; row bases are wave-uniform (scalar) so a load costs one VGPR offset.
-//   * Activations are staged once per workgroup into LDS after the first weight loads are
-//     issued, so their latency hides under the weight latency.
+//   * Activations are staged once per workgroup into LDS; their loads are issued before the
+//     weight loads, which complete in order behind them.  The fused variant reads fp32 x in
+//     consecutive float4s (every wave load 1 KiB in whole lines, whatever the alignment of x)
+//     and transposes each 16-weight group across the four lanes of a quad with DPP.
 //   * A 16-byte load holds 64 codes c = W+1 in {0,1,2}, four per byte (weight 4b+i at bits
 //     2i).  Fields i = 0,1,2 are isolated with one AND each (the byte then holds c * 4^i),
 //     field 3 with a shift and an AND; v_dot4_i32_i8 multiplies each by four x_q bytes into
@@ -26,7 +28,8 @@
 //     y = RN(1/beta), then q + (a - q*beta)*y with two FMAs: by Markstein's theorem (the
 //     reciprocal within half an ulp, the first quotient within one ulp, the remainder exact
 //     through the FMA) this is the correctly rounded IEEE quotient, bit for bit what a
-//     division gives, at a third of the instructions.
+//     division gives, at a third of the instructions.  The code is then rne(t) by adding
+//     1.5 * 2^23 (|t| <= 127 since beta >= max |x|), its low byte gathered with v_perm.
 #include "common.hpp"
 
 namespace bitlinear {
