@@ -772,12 +772,13 @@ def cpu_baseline(workloads, budget_s=3.0, max_threads=16):
     return out
 
 
-def kernel_only(kind: str, launches: int):
+def kernel_only(kind: str, launches: int, batched_shape=(64, 4096, 11008)):
     """Run only one kernel, `launches` times, for counter collection under rocprofv3:
     gemv_fused = the roofline kernel (decode GEMV, K=4096, N=11008, weights rotating through
     64 copies so every launch reads HBM); copy = a plain 256 MiB device copy (calibrates
     FETCH_SIZE / WRITE_SIZE); gemm = the prefill GEMM (M=2048, K=4096, N=11008); batched =
-    the batched decode kernel at M=64, K=4096, N=11008 (weights rotating through 32 copies)."""
+    the batched decode kernel at `batched_shape` (M, K, N; by default M=64, K=4096, N=11008),
+    weights rotating through 32 copies."""
     import torch
     import bitlinear_matmul_absmean_amd as bl
     import workloads
@@ -815,7 +816,7 @@ def kernel_only(kind: str, launches: int):
         print(json.dumps(roof), flush=True)
         return
     if kind == "batched":
-        m, k, n = 64, 4096, 11008
+        m, k, n = batched_shape
         w = torch.from_numpy(workloads.weights(3, n, k)).to(dev)
         packed, alpha = bl.bitlinear_quantize_weights(w)
         del w
@@ -961,6 +962,8 @@ def main():
     ap.add_argument("--kernel-only", choices=["gemv_fused", "gemv_fused_graph", "copy", "gemm", "batched"],
                     help="run only this kernel (for rocprofv3 counter runs)")
     ap.add_argument("--launches", type=int, default=50)
+    ap.add_argument("--batched-shape", type=int, nargs=3, default=[64, 4096, 11008], metavar=("M", "K", "N"),
+                    help="shape of --kernel-only batched")
     ap.add_argument("--trace-summary", nargs=3, metavar=("TRACE_DIR", "PLAIN_JSON", "TRACED_JSON"),
                     help="summarise the roofline kernel's trace against its event timing")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("GEMV_FETCH", "GEMV_WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -979,7 +982,7 @@ def main():
         sys.exit(2)
 
     if args.kernel_only:
-        kernel_only(args.kernel_only, args.launches)
+        kernel_only(args.kernel_only, args.launches, tuple(args.batched_shape))
         return
 
     import torch
