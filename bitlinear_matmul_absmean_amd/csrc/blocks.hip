@@ -307,14 +307,17 @@ __global__ __launch_bounds__(BB_WAVES * 64) void k_bdec16_blocks(BlockArgs a) {
     lds_barrier();
     if (s0 < s1) {
         int s = s0;
+        // one token tile: no loads past the wave's range (16 tokens at K = 4096, N = 11008:
+        // 9.45 against 11.06 us); two token tiles keep the clamped loads, which hold fewer
+        // registers live (the skipping form spilled at three row blocks)
         for (; s + 2 <= s1; s += 2) {
             compute(0, s);
             __builtin_amdgcn_sched_barrier(0);
-            load(0, min(s + 2, last));
+            if (MT == 2 || s + 2 < s1) load(0, min(s + 2, last));
             __builtin_amdgcn_sched_barrier(0);
             compute(1, s + 1);
             __builtin_amdgcn_sched_barrier(0);
-            load(1, min(s + 3, last));
+            if (MT == 2 || s + 3 < s1) load(1, min(s + 3, last));
             __builtin_amdgcn_sched_barrier(0);
         }
         if (s < s1) compute(0, s);
@@ -358,7 +361,7 @@ static hipError_t launch_bdec16_blocks(const BlockArgs& a, hipStream_t s) {
 }
 
 // 3 to 32 tokens: the fewest row blocks per workgroup that keep the grid within 256
-// workgroups (three at N = 11008: 230 workgroups, where four left 84 CUs idle), at most 6 for
+// workgroups (three at N = 11008: 230 workgroups, where four left 84 CUs idle), at most 4 for
 // one token block and 3 for two (beyond, the fp64 accumulators spill); larger N gets more
 // workgroups.
 static hipError_t launch_bdec16_blocks_m(const BlockArgs& a, hipStream_t s) {
@@ -368,9 +371,7 @@ static hipError_t launch_bdec16_blocks_m(const BlockArgs& a, hipStream_t s) {
             case 1: return launch_bdec16_blocks<1, 1>(a, s);
             case 2: return launch_bdec16_blocks<1, 2>(a, s);
             case 3: return launch_bdec16_blocks<1, 3>(a, s);
-            case 4: return launch_bdec16_blocks<1, 4>(a, s);
-            case 5: return launch_bdec16_blocks<1, 5>(a, s);
-            default: return launch_bdec16_blocks<1, 6>(a, s);
+            default: return launch_bdec16_blocks<1, 4>(a, s);
         }
     }
     switch (rb) {

@@ -564,17 +564,18 @@ __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec64(ForwardArgs a) {
             }
         }
     };
+    // two register stages; loads past the wave's range are skipped (re-reading the last
+    // sub-step there measured 0.1-0.5 us slower)
     if (s0 < s1) {
-        const int last = s1 - 1;
         load(0, s0);
         for (int s = s0; s < s1; s += 2) {
             __builtin_amdgcn_sched_barrier(0);
-            load(1, min(s + 1, last));
+            if (s + 1 < s1) load(1, s + 1);
             __builtin_amdgcn_sched_barrier(0);
             compute(0);
             if (s + 1 < s1) {
                 __builtin_amdgcn_sched_barrier(0);
-                load(0, min(s + 2, last));
+                if (s + 2 < s1) load(0, s + 2);
                 __builtin_amdgcn_sched_barrier(0);
                 compute(1);
             }

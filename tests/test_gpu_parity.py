@@ -647,8 +647,8 @@ BLOCK_CASES = [(1, 4096, 4096), (1, 11008, 300), (2, 128, 77), (3, 4096, 1000), 
                # the largest K (alpha rows of 257 floats per row in LDS), and three row blocks at a
                # K whose alpha rows take 25 KB of LDS
                (5, 32768, 70), (4, 16384, 8300),
-               # the fewest row blocks that keep the grid within 256 workgroups: 3 to 6 with one
-               # token tile (6 also beyond 256 workgroups, with 6 x 16 alpha rows at K = 16384),
+               # the fewest row blocks that keep the grid within 256 workgroups: 3 and 4 with one
+               # token tile (4 also beyond 256 workgroups, with 4 x 16 alpha rows at K = 16384),
                # 2 and 3 with two (3 also beyond 256 workgroups)
                (6, 4096, 12000), (8, 1024, 16000), (5, 2048, 20000), (3, 16384, 23000), (7, 512, 30000),
                (24, 128, 6000), (20, 1024, 9000), (32, 640, 15000),
