@@ -363,6 +363,14 @@ static hipError_t launch_bdec16(const ForwardArgs& a, hipStream_t s) {
 // 15.5 against 13.4 / 14.4 / 16.6 / 19.9 / 20.9 us; K = 8192, N = 28672, 24 tokens 24.9 against
 // 39.0 us; K = 11008, N = 4096 and K = 28672, N = 8192 level or up to 9% faster.  Three and four
 // stages were slower on every one of these shapes except a few within 2%.
+// x_q goes through a wave-private LDS image: read straight into the operand layout, a load
+// instruction touched 16 bytes in each of 64 places (16 token rows x 4 lane groups); staged,
+// sixteen lanes read a token's 256 bytes of the sub-step in whole lines, transpose their groups
+// and store them, and the operands come back from LDS.  The token sums of x_q come from MFMAs
+// against an all-ones operand.  Measured with weights not in cache, 16 / 32 tokens: K = 11008,
+// N = 4096, 8.29 / 11.19 against 9.53 / 14.13 us; K = 8192, N = 10240, 9.89 / 12.39 against
+// 11.37 / 15.55 us; K = 28672, N = 8192, 22.0 / 29.2 against 25.4 / 36.4 us; K = 4096,
+// N = 11008, 6.90 / 8.41 against 7.16 / 9.33 us; 4 tokens level.
 template <int MT, int RB, int ST>
 __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec16w(ForwardArgs a) {
     extern __shared__ i32x4 red[];
@@ -377,18 +385,23 @@ __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec16w(ForwardArgs a) {
     const int lr = lane & 15, lg = lane >> 4;
     const int SP = (int)(K >> 8);
     const int s0 = (int)((int64_t)SP * wave / BD_WAVES), s1 = (int)((int64_t)SP * (wave + 1) / BD_WAVES);
-    const int8_t* xrow[MT];
+    // x_q of a sub-step (16 MT tokens x 256 bytes) is loaded in whole lines: instruction i
+    // covers tokens 4i .. 4i+3, sixteen lanes per token; each lane transposes its 16-byte group
+    // and stores it in a wave-private LDS image, rows padded by one unit, from which the MFMA
+    // A operands are read back
+    constexpr int XSTR = 17, XR = MT * 16 * XSTR;
+    i32x4* xs = red + wave * XR;
+    const int xg = lane & 15, xt = lane >> 4;
+    const int8_t* xrow[4 * MT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) xrow[t] = a.xq + (int64_t)min(16 * t + lr, M - 1) * K + 64 * lg;
+    for (int i = 0; i < 4 * MT; ++i) xrow[i] = a.xq + (int64_t)min(4 * i + xt, M - 1) * K + 16 * xg;
     const uint8_t* wrow[RB];
 #pragma unroll
     for (int r = 0; r < RB; ++r) wrow[r] = a.wp + min(n0 + 16 * r + lr, N - 1) * rowb + 16 * lg;
-    u32x4 xa[ST][MT][4], wb[ST][RB];
+    u32x4 xa[ST][4 * MT], wb[ST][RB];
     auto load = [&](int st, int s) {
 #pragma unroll
-        for (int t = 0; t < MT; ++t)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) xa[st][t][q] = *reinterpret_cast<const u32x4*>(xrow[t] + (int64_t)s * 256 + 16 * q);
+        for (int i = 0; i < 4 * MT; ++i) xa[st][i] = *reinterpret_cast<const u32x4*>(xrow[i] + (int64_t)s * 256);
 #pragma unroll
         for (int r = 0; r < RB; ++r) wb[st][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[r] + (int64_t)s * 64));
     };
@@ -397,22 +410,20 @@ __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec16w(ForwardArgs a) {
     for (int r = 0; r < RB; ++r)
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[r][t] = i32x4{0, 0, 0, 0};
-    int ts[MT];
+    const i32x4 ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+    i32x4 tsm[MT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) ts[t] = 0;
+    for (int t = 0; t < MT; ++t) tsm[t] = i32x4{0, 0, 0, 0};
     auto compute = [&](int st) {
+#pragma unroll
+        for (int i = 0; i < 4 * MT; ++i) xs[(4 * i + xt) * XSTR + xg] = (i32x4)transpose4x4_perm(xa[st][i]);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             i32x4 av[MT];
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
-                const u32x4 v = xa[st][t][q];
-                av[t] = (i32x4)transpose4x4_perm(v);
-                int z = ts[t];
-                z = __builtin_amdgcn_sdot4((int)v.x, 0x01010101, z, false);
-                z = __builtin_amdgcn_sdot4((int)v.y, 0x01010101, z, false);
-                z = __builtin_amdgcn_sdot4((int)v.z, 0x01010101, z, false);
-                ts[t] = __builtin_amdgcn_sdot4((int)v.w, 0x01010101, z, false);
+                av[t] = xs[(16 * t + lr) * XSTR + 4 * lg + q];
+                tsm[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[t], ones, tsm[t], 0, 0, 0);
             }
 #pragma unroll
             for (int r = 0; r < RB; ++r) {
@@ -440,12 +451,14 @@ __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec16w(ForwardArgs a) {
             }
         }
     }
+    // column 0 (lanes 0, 16, 32, 48) holds accumulator r of token 4 (lane / 16) + r
+    if (lr == 0) {
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-        int v = ts[t] + __shfl_xor(ts[t], 16, 64);
-        v += __shfl_xor(v, 32, 64);
-        if (lg == 0) tsum_w[wave][16 * t + lr] = v;
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tsum_w[wave][16 * t + 4 * lg + r] = tsm[t][r];
     }
+    __syncthreads();                               // every wave is done with its x_q image
 #pragma unroll
     for (int r = 0; r < RB; ++r)
 #pragma unroll
@@ -482,9 +495,12 @@ __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec16w(ForwardArgs a) {
 template <int MT, int RB, int ST>
 static hipError_t launch_bdec16w(const ForwardArgs& a, hipStream_t s) {
     const int64_t blocks = (a.N + 16 * RB - 1) / (16 * RB);
-    const size_t lds = (size_t)BD_WAVES * RB * MT * 64 * sizeof(i32x4);
+    const size_t tiles = (size_t)BD_WAVES * RB * MT * 64 * sizeof(i32x4);
+    const size_t stage = (size_t)BD_WAVES * MT * 16 * 17 * sizeof(i32x4);
+    const size_t lds = tiles > stage ? tiles : stage;
     return launch_with_lds(k_bdec16w<MT, RB, ST>, dim3((unsigned)blocks), dim3(BD_WAVES * 64), lds, s, a);
 }
+
 
 // 33 to 64 tokens with K % 128 == 0: the scheme of k_bdec without its K-tail selects (every
 // sub-step is whole), with plain (cached) weight loads.  A wave's 128-weight sub-steps read
@@ -652,7 +668,11 @@ static hipError_t launch_bdec16w_fill(const ForwardArgs& a, hipStream_t s) {
         case 5: return launch_bdec16w<MT, 5, 2>(a, s);
         case 6: return launch_bdec16w<MT, 6, 2>(a, s);
         case 7: return launch_bdec16w<MT, 7, 2>(a, s);
-        default: return launch_bdec16w<MT, 8, 2>(a, s);   // more than 256 workgroups from N > 32768
+        default:
+            // more than 256 workgroups from N > 32768; two 16-token tiles keep seven row blocks,
+            // where eight spill registers
+            if constexpr (MT == 2) return launch_bdec16w<MT, 7, 2>(a, s);
+            else return launch_bdec16w<MT, 8, 2>(a, s);
     }
 }
 

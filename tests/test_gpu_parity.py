@@ -188,11 +188,13 @@ FWD_CASES = [
     (5, 256, 33), (16, 4096, 4096), (9, 11008, 1000), (12, 8192, 257), (16, 768, 4095),
     (17, 11008, 700), (32, 2048, 4096), (25, 256, 64),
     # ... and 2 to 8 row blocks per workgroup (the fewest that keep the grid within 256
-    # workgroups; 8 beyond N = 32768, with more workgroups), one and two token blocks
+    # workgroups; beyond N = 32768, with more workgroups, 8 for one token block and 7 for two),
+    # one and two token blocks; token counts not a multiple of the 4 rows one x_q line load covers
     (8, 256, 9000), (8, 256, 8000), (3, 512, 12001), (12, 256, 16300), (7, 512, 20000),
     (16, 256, 24500), (10, 768, 28672), (5, 256, 40000),
     (24, 512, 8100), (32, 256, 11008), (20, 256, 16001), (28, 256, 17000), (31, 512, 21000),
     (18, 256, 25000), (32, 256, 33000), (24, 4096, 11008), (16, 8192, 10240),
+    (29, 512, 40000), (13, 1280, 3000), (19, 2304, 12000), (2, 256, 5000),
     # 33-64 tokens with whole 128-weight sub-steps (K % 128 == 0): one row block per workgroup
     # up to N = 8192, two beyond; sub-step counts not divisible by the eight waves (K = 128:
     # seven waves idle; K = 1152: 9 sub-steps), odd per-wave counts, ragged N and M
