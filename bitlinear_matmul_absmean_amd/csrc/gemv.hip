@@ -24,6 +24,9 @@
 //     x_q[k = 4j + i]) and ordered so that the 64 lanes of a wave read 1 KiB of consecutive
 //     LDS per ds_read_b128.  Wave reductions use DPP inside 16-lane rows and readlane
 //     across rows.
+//   * One token with x quantized inside: on the shapes where it is faster the dot products run
+//     on the 16x16x64 int8 MFMA instead, each lane multiplying its own codes by its own x_q
+//     on the diagonal of the product (see finish_rows).
 //   * The fused variant quantizes x with the quotient fp32(127x)/beta formed as q = a*y,
 //     y = RN(1/beta), then q + (a - q*beta)*y with two FMAs: by Markstein's theorem (the
 //     reciprocal within half an ulp, the first quotient within one ulp, the remainder exact
@@ -115,6 +118,22 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(GemvArgs g) {
     const int64_t rb = ((int64_t)blockIdx.x * WAVES + wave) * g.rows_per_wave;
     const int64_t re = rb + g.rows_per_wave < N ? rb + g.rows_per_wave : N;   // may be <= rb: no rows
     const bool tail_lane = lane + 64 * (CPL - 1) < C;   // the last chunk may be partial
+    // One token, fused, MF: the dot products run on the matrix cores (see finish_rows), G rows
+    // to an MFMA; lane l loads row rho of each group of G rows, 64-weight chunk slot mslot of
+    // each sub-step.  Kept to where it measured faster (weights not in cache, against v_dot4):
+    // four rows to an MFMA with rows of one or two chunks per lane, two with rows of two or
+    // three.  K = 11008, N = 4096: 4.79 against 5.40 us; K = 8192, N = 8192: 5.38 against
+    // 5.66 us; K = 8192, N = 28672: 12.41 against 13.17 us; K = 4096, N = 28672: 7.68 against
+    // 8.90 us.  Slower: rows of one chunk two to an MFMA (K = 4096, N = 11008: 4.71 against
+    // 4.53 us), one row to an MFMA (the trace's reduction per row), four rows of three chunks
+    // (K = 11008, N = 8000: 7.92 against 7.79 us) and rows of four chunks (K = 16384, N = 8192:
+    // 10.49 against 10.35 us).  Without the in-kernel quantization the weight stream hides the
+    // dot products: level or up to 0.09 us slower.
+    constexpr int G = R % 4 == 0 ? 4 : R % 2 == 0 ? 2 : 1;
+    constexpr bool MF = MT == 1 && FUSED && ((G == 4 && CPL <= 2) || (G == 2 && CPL >= 2 && CPL <= 3));
+    constexpr int LPR = 16 / G, CPI1 = 64 / G, NI = G * CPL;
+    const int gl = lane >> 4, il = lane & 15;
+    const int rho = il / LPR, mslot = gl * LPR + il % LPR;
 
     // ---- weight loads: rows r0 .. r0+R-1 into a register buffer -------------------------
     // Branch-free, so that the compiler can wait for exactly the loads it needs: rows past
@@ -122,6 +141,26 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(GemvArgs g) {
     // 64-weight chunk of a row re-read chunk 0: the x_q staged for those lanes is zero, so
     // their products vanish.
     auto load_rows = [&](u32x4 (&w)[R][CPL], int64_t r0) {
+        if constexpr (MF) {
+            // sub-step s of group gr: chunk s * CPI1 + mslot of row r0 + G gr + rho (chunk 0
+            // past the row end; its x_q is zero).  Issued in the order the MFMAs consume them,
+            // sub-step major, so that the first sub-steps start while later loads are in flight.
+            u32x4* wf = &w[0][0];
+            const uint8_t* base[R / G];
+#pragma unroll
+            for (int gr = 0; gr < R / G; ++gr) {
+                const int64_t row = r0 + gr * G + rho < re ? r0 + gr * G + rho : re - 1;
+                base[gr] = a.wp + row * rowb;
+            }
+#pragma unroll
+            for (int s = 0; s < NI; ++s) {
+                const int c = s * CPI1 + mslot;
+#pragma unroll
+                for (int gr = 0; gr < R / G; ++gr)
+                    wf[gr * NI + s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base[gr] + 16 * (c < C ? c : 0)));
+            }
+            return;
+        }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int64_t row = r0 + r < re ? r0 + r : re - 1;
@@ -137,6 +176,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(GemvArgs g) {
     // k = 64 c + 16 q for token t, with i = u / 256 = t * CPL + j, q = (u / 64) % 4, lane
     // l = u % 64 and c = l + 64 j: the lane that reads weight chunk c of a row finds its four
     // x_q dwords at units (i, q = 0..3, l).  Thread tid stages units tid, tid + NT, ...
+    // With MF the four dwords of each chunk are stored transposed: unit (i, f, l) holds dword
+    // f of units q = 0..3, so that one read gives the MFMA operand of field f (below).
     // The (small, cache-resident) activation loads are issued before the weight loads: a
     // wave's loads complete in order, so activations queued behind the weights would hold the
     // staging back until all of this wave's weights had arrived.  Out-of-range units load
@@ -208,17 +249,32 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(GemvArgs g) {
         float mx[MT];
 #pragma unroll
         for (int t = 0; t < MT; ++t) mx[t] = 0.0f;
+        if constexpr (MT == 1) {
+            // One token: the slots past the row re-read float4 0 of the row, which the maximum
+            // already holds, so no slot is masked.  v_max3_f32 with |.| source modifiers takes two
+            // activations per instruction; fmaxf made the compiler quiet every input first
+            // (four instructions per float4 more).  NaN inputs give unspecified codes anyway.
 #pragma unroll
-        for (int i = 0; i < FPT; ++i) {
-            int t, fl;
-            const bool valid = slot_at(i, t, fl);
-            float4 v;
-            if constexpr (KEEP) v = xv[i];
-            else v = reinterpret_cast<const float4*>(g.x)[valid ? t * k4 + fl : 0];
-            const float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+            for (int i = 0; i < FPT; ++i) {
+                float4 v;
+                if constexpr (KEEP) v = xv[i];
+                else v = reinterpret_cast<const float4*>(g.x)[tid + NT * i < k4 ? tid + NT * i : 0];
+                asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(mx[0]) : "v"(v.x), "v"(v.y), "v"(mx[0]));
+                asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(mx[0]) : "v"(v.z), "v"(v.w), "v"(mx[0]));
+            }
+        } else {
 #pragma unroll
-            for (int tt = 0; tt < MT; ++tt)
-                if (valid && tt == t) mx[tt] = fmaxf(mx[tt], m);
+            for (int i = 0; i < FPT; ++i) {
+                int t, fl;
+                const bool valid = slot_at(i, t, fl);
+                float4 v;
+                if constexpr (KEEP) v = xv[i];
+                else v = reinterpret_cast<const float4*>(g.x)[valid ? t * k4 + fl : 0];
+                const float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+#pragma unroll
+                for (int tt = 0; tt < MT; ++tt)
+                    if (valid && tt == t) mx[tt] = fmaxf(mx[tt], m);
+            }
         }
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
@@ -237,37 +293,76 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(GemvArgs g) {
         }
         const bool exporter = blockIdx.x == 0;
         uint32_t* xs32 = reinterpret_cast<uint32_t*>(xs);
+        if constexpr (MT == 1) {
+            // Slot i of thread tid is float4 f = tid + NT i: chunk c = tid / 16 + CPI i and
+            // group q = (tid / 4) % 4 of it, so its LDS dword is a per-thread base plus a
+            // compile-time offset.  Slots past the row (c >= C) store zero codes, which also
+            // clears those chunks of the image: no separate clearing pass, no per-slot index
+            // arithmetic.  With the maximum above, 12% fewer VALU instructions per wave at
+            // K = 11008; measured with weights not in cache, K = 11008, N = 4096: 5.40 against
+            // 5.78 us; K = 4096, N = 11008: 4.52 against 4.63 us; K = 28672, N = 8192: 14.04
+            // against 15.00 us.
+            constexpr int CPI = NT / 16, RPT = 64 / CPI;
+            static_assert(CPI <= 64 && 64 % CPI == 0, "a slot step covers a divisor of 64 chunks");
+            const int base = MF ? ((jj << 6) + (tid >> 4)) * 4 + ((tid >> 2) & 3)
+                                : ((((tid >> 2) & 3) << 6) + (tid >> 4)) * 4 + jj;
+            uint32_t dq[FPT];
+            int sum = 0;
 #pragma unroll
-        for (int i = 0; i < FPT; ++i) {
-            int t, fl;
-            const bool valid = slot_at(i, t, fl);
-            float4 v;
-            if constexpr (KEEP) v = xv[i];
-            else v = reinterpret_cast<const float4*>(g.x)[valid ? t * k4 + fl : 0];
-            float bt = beta_t[0], rt = rcp[0];
-#pragma unroll
-            for (int tt = 1; tt < MT; ++tt)
-                if (tt == t) { bt = beta_t[tt]; rt = rcp[tt]; }
-            // x_q of weights k = 4 fl .. 4 fl + 3 (byte i = weight 4 fl + i)
-            const uint32_t d = act_dword(v, bt, rt);
-            // quad transpose: lane jj ends with byte j = weight 4 j + jj of the group
-            const uint32_t p1 = (uint32_t)dpp_i<0xB1>((int)d);              // from lane jj ^ 1
-            const uint32_t t1 = __builtin_amdgcn_perm(p1, d, (jj & 1) ? 0x03070105u : 0x06020400u);
-            const uint32_t p2 = (uint32_t)dpp_i<0x4E>((int)t1);             // from lane jj ^ 2
-            const uint32_t t2 = __builtin_amdgcn_perm(p2, t1, (jj & 2) ? 0x03020706u : 0x05040100u);
-            if (valid) {
-                const int G = fl >> 2;                       // 16-weight group within the token
-                const int c = G >> 2, q = G & 3;
-                xs32[((((t * CPL + (c >> 6)) * 4 + q) << 6) + (c & 63)) * 4 + jj] = t2;
-                add_part(t, byte_sum(d));
-                if (exporter && g.xq_out) reinterpret_cast<uint32_t*>(g.xq_out + t * K)[fl] = d;
+            for (int i = 0; i < FPT; ++i) {
+                const bool valid = tid + NT * i < k4;
+                float4 v;
+                if constexpr (KEEP) v = xv[i];
+                else v = reinterpret_cast<const float4*>(g.x)[valid ? tid + NT * i : 0];
+                const uint32_t d = valid ? act_dword(v, beta_t[0], rcp[0]) : 0u;
+                dq[i] = d;
+                // quad transpose (a quad is valid or not as a whole: K % 64 == 0)
+                const uint32_t p1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)d, 0xB1, 0xF, 0xF, true);
+                const uint32_t t1 = __builtin_amdgcn_perm(p1, d, (jj & 1) ? 0x03070105u : 0x06020400u);
+                const uint32_t p2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)t1, 0x4E, 0xF, 0xF, true);
+                const uint32_t t2 = __builtin_amdgcn_perm(p2, t1, (jj & 2) ? 0x03020706u : 0x05040100u);
+                xs32[base + (i / RPT) * 1024 + (i % RPT) * CPI * 4] = t2;
+                sum += byte_sum(d);
             }
-        }
-        // units of chunks past the row end (and of tokens past M) hold zeros
-        for (int u = tid; u < UNITS; u += NT) {
-            const int i = u >> 8;
-            const int t = i / CPL, c = (u & 63) + 64 * (i % CPL);
-            if (c >= C || t >= M) xs[u] = u32x4{0u, 0u, 0u, 0u};
+            part[0] = sum;
+            if (exporter && g.xq_out) {
+#pragma unroll
+                for (int i = 0; i < FPT; ++i)
+                    if (tid + NT * i < k4) reinterpret_cast<uint32_t*>(g.xq_out)[tid + NT * i] = dq[i];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < FPT; ++i) {
+                int t, fl;
+                const bool valid = slot_at(i, t, fl);
+                float4 v;
+                if constexpr (KEEP) v = xv[i];
+                else v = reinterpret_cast<const float4*>(g.x)[valid ? t * k4 + fl : 0];
+                float bt = beta_t[0], rt = rcp[0];
+#pragma unroll
+                for (int tt = 1; tt < MT; ++tt)
+                    if (tt == t) { bt = beta_t[tt]; rt = rcp[tt]; }
+                // x_q of weights k = 4 fl .. 4 fl + 3 (byte i = weight 4 fl + i)
+                const uint32_t d = act_dword(v, bt, rt);
+                // quad transpose: lane jj ends with byte j = weight 4 j + jj of the group
+                const uint32_t p1 = (uint32_t)dpp_i<0xB1>((int)d);              // from lane jj ^ 1
+                const uint32_t t1 = __builtin_amdgcn_perm(p1, d, (jj & 1) ? 0x03070105u : 0x06020400u);
+                const uint32_t p2 = (uint32_t)dpp_i<0x4E>((int)t1);             // from lane jj ^ 2
+                const uint32_t t2 = __builtin_amdgcn_perm(p2, t1, (jj & 2) ? 0x03020706u : 0x05040100u);
+                if (valid) {
+                    const int G = fl >> 2;                       // 16-weight group within the token
+                    const int c = G >> 2, q = G & 3;
+                    xs32[((((t * CPL + (c >> 6)) * 4 + q) << 6) + (c & 63)) * 4 + jj] = t2;
+                    add_part(t, byte_sum(d));
+                    if (exporter && g.xq_out) reinterpret_cast<uint32_t*>(g.xq_out + t * K)[fl] = d;
+                }
+            }
+            // units of chunks past the row end (and of tokens past M) hold zeros
+            for (int u = tid; u < UNITS; u += NT) {
+                const int i = u >> 8;
+                const int t = i / CPL, c = (u & 63) + 64 * (i % CPL);
+                if (c >= C || t >= M) xs[u] = u32x4{0u, 0u, 0u, 0u};
+            }
         }
         if (exporter && g.beta_out && tid < M) {
 #pragma unroll
@@ -293,7 +388,17 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(GemvArgs g) {
                 o = transpose4x4_bytes(xr[k]);
                 add_part(t, byte_sum(xr[k].x) + byte_sum(xr[k].y) + byte_sum(xr[k].z) + byte_sum(xr[k].w));
             }
-            if (u < UNITS) xs[u] = o;
+            if constexpr (MF) {
+                if (u < UNITS) {
+                    uint32_t* xs32 = reinterpret_cast<uint32_t*>(xs);
+                    const int cc = (u & 63) + 64 * ((u >> 8) % CPL), qq = (u >> 6) & 3;
+                    const int u0 = (((cc >> 6) * 4) << 6) + (cc & 63);
+#pragma unroll
+                    for (int f = 0; f < 4; ++f) xs32[(u0 + 64 * f) * 4 + qq] = o[f];
+                }
+            } else {
+                if (u < UNITS) xs[u] = o;
+            }
         }
 #pragma unroll
         for (int t = 0; t < MT; ++t) beta_t[t] = t < M ? a.beta[t] : 0.0f;
@@ -316,6 +421,84 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(GemvArgs g) {
 
     // ---- reduce R rows held in w, finish them ------------------------------------------
     auto finish_rows = [&](const u32x4 (&w)[R][CPL], const RowAux& aux, int64_t r0) {
+        if constexpr (MF) {
+            // The 16x16x64 int8 MFMA pairs byte j of lane l's A operand with byte j of the same
+            // lane's B operand on its diagonal: C[i][i] sums the products of lanes i, i + 16,
+            // i + 32, i + 48.  So every lane puts 16 codes of its own chunk in A and the
+            // matching 16 x_q in B, and the trace of C is the wave's dot product; the lanes of
+            // row rho of a group feed diagonal entries rho * 16/G .. (rho + 1) * 16/G - 1.  The
+            // field i codes of a chunk (c, 4c or 16c in each byte after one AND; field 3 shifted
+            // down) go to four accumulators, recombined as a0 + a1/4 + a2/16 + a3 (exact).
+            // Against v_dot4: 20 instead of 36 VALU instructions per 64 weights and lane.
+            constexpr int RG = R / G;
+            const u32x4* wf = &w[0][0];
+            i32x4 acc[RG][4];
+#pragma unroll
+            for (int gr = 0; gr < RG; ++gr)
+#pragma unroll
+                for (int f = 0; f < 4; ++f) acc[gr][f] = i32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int s = 0; s < NI; ++s) {
+                // one sub-step at a time: hoisting the operands of later sub-steps ran the
+                // double-buffered kernels out of registers
+                __builtin_amdgcn_sched_barrier(0);
+                const int c = s * CPI1 + mslot;
+                const int u0 = (((c >> 6) * 4) << 6) + (c & 63);
+                i32x4 B[4];
+#pragma unroll
+                for (int f = 0; f < 4; ++f) B[f] = (i32x4)xs[u0 + 64 * f];
+#pragma unroll
+                for (int gr = 0; gr < RG; ++gr) {
+                    const u32x4 v = wf[gr * NI + s];
+                    const i32x4 A0 = (i32x4)(v & 0x03030303u), A1 = (i32x4)(v & 0x0C0C0C0Cu);
+                    const i32x4 A2 = (i32x4)(v & 0x30303030u), A3 = (i32x4)((v >> 6) & 0x03030303u);
+                    acc[gr][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, B[0], acc[gr][0], 0, 0, 0);
+                    acc[gr][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, B[1], acc[gr][1], 0, 0, 0);
+                    acc[gr][2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A2, B[2], acc[gr][2], 0, 0, 0);
+                    acc[gr][3] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A3, B[3], acc[gr][3], 0, 0, 0);
+                }
+            }
+            // register r of lane l holds C[4 (l / 16) + r][l % 16]: C[i][i] sits in lane
+            // i + 16 (i / 4), register i % 4, so lanes 0-3, 20-23, 40-43, 60-63 hold the
+            // diagonal, four entries (one quad) for each quarter of the rows of C
+            const int sel = il & 3;
+            const bool diag = (il >> 2) == gl;
+            int mine = 0;
+#pragma unroll
+            for (int gr = 0; gr < RG; ++gr) {
+                int e[4];
+#pragma unroll
+                for (int f = 0; f < 4; ++f) {
+                    const i32x4 q = acc[gr][f];
+                    e[f] = sel == 0 ? q.x : sel == 1 ? q.y : sel == 2 ? q.z : q.w;
+                }
+                int v = diag ? e[0] + e[3] + (e[1] >> 2) + (e[2] >> 4) : 0;
+                v += dpp_i<0xB1>(v);
+                v += dpp_i<0x4E>(v);
+                const int q0 = __builtin_amdgcn_readlane(v, 0), q1 = __builtin_amdgcn_readlane(v, 20);
+                const int q2 = __builtin_amdgcn_readlane(v, 40), q3 = __builtin_amdgcn_readlane(v, 60);
+                int tr[G];
+                if constexpr (G == 4) { tr[0] = q0; tr[1] = q1; tr[2] = q2; tr[3] = q3; }
+                else if constexpr (G == 2) { tr[0] = q0 + q1; tr[1] = q2 + q3; }
+                else tr[0] = q0 + q1 + q2 + q3;
+#pragma unroll
+                for (int p = 0; p < G; ++p)
+                    if (lane == gr * G + p) mine = tr[p];
+            }
+            // lane r finishes row r0 + r
+            if (lane < R) {
+                const int64_t n = r0 + lane;
+                if (n < re) {
+                    const int total = mine - xsum[0];
+                    const float sv = a.alpha_per_row ? dequant_scale(aux.al, beta_t[0]) : sc[0];
+                    float yv = (float)total * sv;
+                    if (a.bias) yv = yv + aux.bi;
+                    a.y[n] = activate(yv, a.act);
+                    if (a.acc) a.acc[n] = total;
+                }
+            }
+            return;
+        }
         int s0[R][MT], s1[R][MT], s2[R][MT], s3[R][MT];
 #pragma unroll
         for (int r = 0; r < R; ++r)

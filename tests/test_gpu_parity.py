@@ -369,7 +369,14 @@ FUSED_CASES = [(1, 64, 5), (1, 1024, 1024), (1, 4096, 4096), (1, 4096, 11008), (
                (4, 16384, 257), (4, 192, 4096),
                # several tokens in 8-wave workgroups (N >= 2048): two, three and four tokens
                (2, 8192, 3000), (3, 16384, 2500), (2, 4096, 11008),
-               (1, 12288, 4097), (1, 16384, 2048), (1, 28672, 2100), (1, 4096, 16385)]
+               (1, 12288, 4097), (1, 16384, 2048), (1, 28672, 2100), (1, 4096, 16385),
+               # one token with the dot products on MFMA: four rows to an MFMA with rows of one and
+               # two chunks per lane (four and eight rows per wave), two rows to an MFMA with six
+               # rows per wave, double-buffered steps of two rows of three chunks; a row just over
+               # one chunk per lane; waves without rows at the end of the grid; ragged N; and four
+               # rows of three chunks, which stay on v_dot4
+               (1, 8192, 7000), (1, 4096, 7000), (1, 4096, 15000), (1, 8192, 11000), (1, 8192, 15000),
+               (1, 11008, 11000), (1, 11008, 13000), (1, 4160, 9000), (1, 8192, 8193), (1, 11008, 7777)]
 
 
 @pytest.mark.parametrize("m,k,n", FUSED_CASES)
@@ -481,7 +488,7 @@ def test_forward_fused_rows_grouped(dev, m, k, ns):
     assert np.array_equal(yg, y_ref)
 
 
-@pytest.mark.parametrize("m,k,n", [(1, 4096, 4096), (1, 11008, 300), (2, 1024, 777)])
+@pytest.mark.parametrize("m,k,n", [(1, 4096, 4096), (1, 11008, 300), (2, 1024, 777), (1, 8192, 3000), (1, 11008, 8000)])
 def test_forward_fused_rows_per_row_alpha(dev, m, k, n):
     """Per-row alpha [P2 §3.1] quantization followed by the fused per-row forward."""
     torch, bl = dev
