@@ -676,6 +676,16 @@ static hipError_t launch_bdec16w_fill(const ForwardArgs& a, hipStream_t s) {
     }
 }
 
+template <int MT, int ST>
+static hipError_t launch_bdec16w_fill3(const ForwardArgs& a, hipStream_t s) {
+    const int64_t nb16 = (a.N + 15) / 16;
+    switch ((nb16 + 255) / 256) {
+        case 1: return launch_bdec16w<MT, 1, ST>(a, s);
+        case 2: return launch_bdec16w<MT, 2, ST>(a, s);
+        default: return launch_bdec16w<MT, 3, ST>(a, s);
+    }
+}
+
 hipError_t launch_decode_mfma(const ForwardArgs& a, hipStream_t s) {
     const int64_t nb16 = (a.N + 15) / 16;
     // up to 32 tokens with whole 256-weight sub-steps: 16 x 16 x 64 tiles, the grid filled
@@ -699,6 +709,18 @@ hipError_t launch_decode_mfma(const ForwardArgs& a, hipStream_t s) {
         if (nb16 <= 256) return launch_bdec16<2, 1>(a, s);
         return launch_bdec16<2, 2>(a, s);
     }
+    // 33 to 64 tokens, whole 256-weight sub-steps, matrices of up to 768 16-row blocks: k_bdec16w
+    // with three or four 16-token tiles and the fewest row blocks (up to three) that keep the
+    // grid within 256 workgroups.  Its x_q goes through LDS in whole lines, once per 16-row
+    // block of weights instead of per 32-row block of k_bdec64's, but four 16-token tiles fit
+    // the registers with one pipeline stage only (three with two).  Measured with weights not in
+    // cache, against k_bdec64: M = 64, K = 4096, N = 11008: 11.4 against 12.1 us; K = 11008,
+    // N = 4096: 16.2 against 18.1 us; K = 8192, N = 8192: 15.0 against 15.3 us; K = 16384,
+    // N = 4096: 21.4 against 23.2 us; M = 48, K = 4096, N = 11008: 10.3 against 11.9 us;
+    // M = 36: 9.9 against 11.8 us.  Wider matrices stay on k_bdec64 (M = 64, K = 8192,
+    // N = 28672: 45.8 against 37.8 us with three row blocks).
+    if (a.M <= 64 && a.K % 256 == 0 && nb16 <= 768)
+        return a.M <= 48 ? launch_bdec16w_fill3<3, 2>(a, s) : launch_bdec16w_fill3<4, 1>(a, s);
     // 33 to 64 tokens, whole 128-weight sub-steps: one 32-row block per workgroup up to 256
     // workgroups (N <= 8192), two beyond (172 workgroups at N = 11008).  Measured with weights
     // not in cache, M = 64: K = 8192, N = 8192, one block 15.8 against 18.6 us for two; K = 28672,

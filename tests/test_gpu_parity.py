@@ -195,6 +195,11 @@ FWD_CASES = [
     (24, 512, 8100), (32, 256, 11008), (20, 256, 16001), (28, 256, 17000), (31, 512, 21000),
     (18, 256, 25000), (32, 256, 33000), (24, 4096, 11008), (16, 8192, 10240),
     (29, 512, 40000), (13, 1280, 3000), (19, 2304, 12000), (2, 256, 5000),
+    # 33-64 tokens with whole 256-weight sub-steps on at most 768 16-row blocks: three 16-token
+    # tiles (33-48 tokens) and four (49-64) with one, two and three row blocks per workgroup, the
+    # largest N that takes them and the next one (back to 32x32x32 tiles)
+    (33, 256, 100), (48, 512, 4100), (40, 768, 12000), (49, 256, 1000), (64, 512, 8000),
+    (57, 1024, 12288), (64, 256, 12289),
     # 33-64 tokens with whole 128-weight sub-steps (K % 128 == 0): one row block per workgroup
     # up to N = 8192, two beyond; sub-step counts not divisible by the eight waves (K = 128:
     # seven waves idle; K = 1152: 9 sub-steps), odd per-wave counts, ragged N and M
