@@ -502,6 +502,203 @@ static hipError_t launch_bdec16w(const ForwardArgs& a, hipStream_t s) {
 }
 
 
+// Expansion of one packed dword (16 codes, weight 4b+i at bits 2i of byte b) into the
+// 16-byte MFMA operand in weight order: byte 4b+i of the result is the code of weight 4b+i.
+// Per output dword: v_perm gathers [byte b of w, byte b of w >> 2] twice, a packed 16-bit shift
+// by (0, 4) brings bits 4-5 of the upper pair down, and a mask keeps bits 0-1 of every byte.
+__device__ __forceinline__ i32x4 expand_codes_in_order(uint32_t w) {
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    const uint32_t w2 = w >> 2;
+    i32x4 r;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const uint32_t sel = (uint32_t)b | (uint32_t)(4 + b) << 8 | (uint32_t)b << 16 | (uint32_t)(4 + b) << 24;
+        u16x2 h = __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(w2, w, sel));
+        h = h >> (u16x2){0, 4};
+        r[b] = (int)(__builtin_bit_cast(uint32_t, h) & 0x03030303u);
+    }
+    return r;
+}
+
+// 16 bytes per lane from global memory straight into LDS (buffer_load_dwordx4 ... lds): lane l
+// writes its 16 bytes at lds + 16 l (lds the same for the whole wave), read from the buffer r at
+// voff (per lane) + soff (uniform).  Offsets past the buffer's size would read zeros; every
+// caller keeps them inside.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, i32x4* lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+// Buffer resource over [p, p + bytes) for raw (untyped) loads: stride 0, 32-bit data format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+
+// 17 to 64 tokens, K % 256 == 0: 16 x 16 x 64 tiles with the codes expanded in weight order, so
+// that x_q needs no transposition.  Both operands move from global memory into LDS through the
+// load unit itself (buffer_load_dwordx4 ... lds), without passing through registers: the waves
+// split K in 256-weight sub-steps as in k_bdec16w, and each wave keeps an LDS image of its
+// sub-step (x_q of 16 MT tokens x 256 bytes, then RB x 1 KiB of packed weights).  A sub-step
+// reads its image into registers, starts the fetch of the next sub-step into the same image,
+// and multiplies while that fetch is in flight.  No load in the loop writes a register, so
+// the only waits on memory are the explicit ones below.
+//   * x_q layout: token T's 16-byte unit u sits at position u ^ (T % 16) of the token's 256
+//     bytes.  A load instruction covers four tokens, sixteen lanes each; a lane quad reads one
+//     aligned 64-byte piece of a token's row (the XOR permutes units inside and between such
+//     pieces), and the sixteen lanes of an A read (16 tokens, one unit each) hit sixteen
+//     different bank groups.
+//   * weights: lane (r, g) = (l % 16, l / 16) of load instruction b reads 16 bytes (64 codes at
+//     k0 + 64 g) of row n0 + 16 b + r and reads them back from its own slot.
+//   * in MFMA q of a sub-step, lane group g holds weights 64g + 16q .. 64g + 16q + 15: packed
+//     dword q of the lane's 16 bytes, and unit 4g + q of the token's x_q.
+template <int MT, int RB>
+__global__ __launch_bounds__(BD_WAVES * 64) void k_bdec16n(ForwardArgs a) {
+    extern __shared__ i32x4 red[];
+    __shared__ int tsum_w[BD_WAVES][16 * MT];
+    __shared__ __align__(16) int tsum_t[MT * 16];
+    __shared__ __align__(16) float scale_t[MT * 16];
+    constexpr int XI = 4 * MT;                     // x_q load instructions (1 KiB each) per sub-step
+    constexpr int IMG = (XI + RB) * 64;            // 16-byte units of one wave's image
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int M = (int)a.M;
+    const int64_t K = a.K, N = a.N, rowb = K >> 2;
+    const int64_t n0 = (int64_t)blockIdx.x * (16 * RB);
+    const int lr = lane & 15, lg = lane >> 4;
+    const int SP = (int)(K >> 8);
+    const int s0 = (int)((int64_t)SP * wave / BD_WAVES), s1 = (int)((int64_t)SP * (wave + 1) / BD_WAVES);
+    i32x4* xs = red + wave * IMG;
+    i32x4* ws = xs + XI * 64;
+    // instruction i, lane (lr, lg): token 4i + lg (rows past M read row M - 1, never written),
+    // position lr, unit lr ^ ((4i + lg) % 16) = lr ^ (4 (i % 4) + lg).  Byte offsets from the
+    // sub-step's start fit 32 bits (M K < 2^31 and N K / 4 < 2^32, checked on launch), so every
+    // load is a uniform base plus one 32-bit lane offset.
+    const uint32_t Ku = (uint32_t)K, lastx = (uint32_t)(M - 1) * Ku, lgK = (uint32_t)lg * Ku;
+    uint32_t xu[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xu[j] = 16u * (uint32_t)(lr ^ (4 * j + lg));
+    uint32_t xoff[XI];
+#pragma unroll
+    for (int i = 0; i < XI; ++i) xoff[i] = min(lgK + (uint32_t)(4 * i) * Ku, lastx) + xu[i & 3];
+    uint32_t woff[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) woff[r] = (uint32_t)min(n0 + 16 * r + lr, N - 1) * (uint32_t)rowb + 16u * (uint32_t)lg;
+    const __amdgpu_buffer_rsrc_t xr = raw_buffer(a.xq, (uint32_t)(M * K));
+    const __amdgpu_buffer_rsrc_t wr = raw_buffer(a.wp, (uint32_t)(N * rowb));
+    auto fetch = [&](int s) {
+#pragma unroll
+        for (int i = 0; i < XI; ++i) load_lds16(xr, xoff[i], (uint32_t)s * 256u, xs + 64 * i);
+#pragma unroll
+        for (int r = 0; r < RB; ++r) load_lds16(wr, woff[r], (uint32_t)s * 64u, ws + 64 * r);
+    };
+    i32x4 acc[RB][MT];
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[r][t] = i32x4{0, 0, 0, 0};
+    const i32x4 ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+    i32x4 tsm[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) tsm[t] = i32x4{0, 0, 0, 0};
+    if (s0 < s1) fetch(s0);
+    for (int s = s0; s < s1; ++s) {
+        // the fetch of this sub-step has landed in the image (the only loads in flight)
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0)
+        __builtin_amdgcn_sched_barrier(0);
+        i32x4 av[MT][4];
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) av[t][q] = xs[(16 * t + lr) * 16 + ((4 * lg + q) ^ lr)];
+        u32x4 wv[RB];
+#pragma unroll
+        for (int r = 0; r < RB; ++r) wv[r] = (u32x4)ws[64 * r + lane];
+        // the next fetch rewrites the image: every read of it has to be complete first
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0)
+        __builtin_amdgcn_sched_barrier(0);
+        if (s + 1 < s1) fetch(s + 1);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int t = 0; t < MT; ++t) tsm[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[t][q], ones, tsm[t], 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const uint32_t w = q == 0 ? wv[r].x : q == 1 ? wv[r].y : q == 2 ? wv[r].z : wv[r].w;
+                const i32x4 bv = expand_codes_in_order(w);
+#pragma unroll
+                for (int t = 0; t < MT; ++t) acc[r][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[t][q], bv, acc[r][t], 0, 0, 0);
+            }
+        }
+    }
+    // column 0 (lanes 0, 16, 32, 48) holds accumulator r of token 4 (lane / 16) + r
+    if (lr == 0) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tsum_w[wave][16 * t + 4 * lg + r] = tsm[t][r];
+    }
+    __syncthreads();                               // every wave is done with its image
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) red[(wave * RB * MT + r * MT + t) * 64 + lane] = acc[r][t];
+    __syncthreads();
+    if (tid < MT * 16) {
+        int v = 0;
+#pragma unroll
+        for (int w = 0; w < BD_WAVES; ++w) v += tsum_w[w][tid];
+        tsum_t[tid] = v;
+        scale_t[tid] = (!a.alpha_per_row && tid < M) ? dequant_scale(a.alpha[0], a.beta[tid]) : 0.0f;
+    }
+    __syncthreads();
+    // element e = (tile, lane): tokens 16 t + 4 (lane / 16) + i, i < 4, of weight row
+    // n0 + 16 r + lane % 16; the four tokens' sums and scales are read as one 16-byte unit each
+    for (int e = tid; e < RB * MT * 64; e += BD_WAVES * 64) {
+        const int l = e & 63, tile = e >> 6;
+        const int r = tile / MT, t = tile % MT;
+        i32x4 sum = {0, 0, 0, 0};
+#pragma unroll
+        for (int w = 0; w < BD_WAVES; ++w) sum += red[(w * RB * MT + tile) * 64 + l];
+        const int64_t n = n0 + 16 * r + (l & 15);
+        if (n >= N) continue;
+        const int m0 = 16 * t + 4 * (l >> 4);
+        const i32x4 ts = *reinterpret_cast<const i32x4*>(&tsum_t[m0]);
+        float sc[4];
+        if (a.alpha_per_row) {
+            const float al = a.alpha[n];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc[i] = m0 + i < M ? dequant_scale(al, a.beta[m0 + i]) : 0.0f;
+        } else {
+            const float4 s4 = *reinterpret_cast<const float4*>(&scale_t[m0]);
+            sc[0] = s4.x; sc[1] = s4.y; sc[2] = s4.z; sc[3] = s4.w;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (m0 + i >= M) break;
+            const int total = sum[i] - ts[i];
+            a.y[(int64_t)(m0 + i) * N + n] = activate(dequant(total, sc[i], a.bias, n), a.act);
+            if (a.acc) a.acc[(int64_t)(m0 + i) * N + n] = total;
+        }
+    }
+}
+
+template <int MT, int RB>
+static hipError_t launch_bdec16n(const ForwardArgs& a, hipStream_t s) {
+    const int64_t blocks = (a.N + 16 * RB - 1) / (16 * RB);
+    const size_t tiles = (size_t)BD_WAVES * RB * MT * 64 * sizeof(i32x4);
+    const size_t image = (size_t)BD_WAVES * (4 * MT + RB) * 64 * sizeof(i32x4);
+    return launch_with_lds(k_bdec16n<MT, RB>, dim3((unsigned)blocks), dim3(BD_WAVES * 64), tiles > image ? tiles : image, s, a);
+}
+// Row blocks per workgroup: the fewest (up to three, the most whose images fit the LDS beside
+// four 16-token tiles) that keep the grid within 256 workgroups.
+template <int MT>
+static hipError_t launch_bdec16n_fill(const ForwardArgs& a, hipStream_t s) {
+    const int64_t nb16 = (a.N + 15) / 16;
+    if (nb16 <= 256) return launch_bdec16n<MT, 1>(a, s);
+    if (nb16 <= 512) return launch_bdec16n<MT, 2>(a, s);
+    return launch_bdec16n<MT, 3>(a, s);
+}
+
 // 33 to 64 tokens with K % 128 == 0: the scheme of k_bdec without its K-tail selects (every
 // sub-step is whole), with plain (cached) weight loads.  A wave's 128-weight sub-steps read
 // 32 bytes of each of its rows' 128-byte lines in turn; streamed past the caches, every
@@ -676,19 +873,24 @@ static hipError_t launch_bdec16w_fill(const ForwardArgs& a, hipStream_t s) {
     }
 }
 
-template <int MT, int ST>
-static hipError_t launch_bdec16w_fill3(const ForwardArgs& a, hipStream_t s) {
-    const int64_t nb16 = (a.N + 15) / 16;
-    switch ((nb16 + 255) / 256) {
-        case 1: return launch_bdec16w<MT, 1, ST>(a, s);
-        case 2: return launch_bdec16w<MT, 2, ST>(a, s);
-        default: return launch_bdec16w<MT, 3, ST>(a, s);
-    }
-}
 
 hipError_t launch_decode_mfma(const ForwardArgs& a, hipStream_t s) {
     const int64_t nb16 = (a.N + 15) / 16;
-    // up to 32 tokens with whole 256-weight sub-steps: 16 x 16 x 64 tiles, the grid filled
+    // 17 to 64 tokens, whole 256-weight sub-steps, at most 768 16-row blocks: k_bdec16n.
+    // Measured with weights not in cache, against the kernels these shapes took before
+    // (k_bdec16w), identical outputs: M = 64, K = 4096, N = 11008: 10.8 against 11.7 us;
+    // K = 11008, N = 4096: 14.6 against 17.3 us; K = 8192, N = 8192: 13.4 against 16.4 us;
+    // K = 16384, N = 4096: 18.4 against 22.9 us; M = 48, K = 4096, N = 11008: 9.7 against
+    // 10.7 us; M = 32: 8.0 against 8.4 us (K = 11008, N = 4096: 10.2 against 11.6 us); M = 17:
+    // 7.5 against 7.8 us.
+    if (a.M > 16 && a.M <= 64 && a.K % 256 == 0 && a.M * a.K < (int64_t(1) << 31) &&
+        a.N * (a.K / 4) < (int64_t(1) << 32) && nb16 <= 768) {
+        if (a.M <= 32) return launch_bdec16n_fill<2>(a, s);
+        if (a.M <= 48) return launch_bdec16n_fill<3>(a, s);
+        return launch_bdec16n_fill<4>(a, s);
+    }
+    // up to 32 tokens with whole 256-weight sub-steps (17 to 32 on wider matrices only): 16 x 16
+    // x 64 tiles, the grid filled
     if (a.M <= 32 && a.K % 256 == 0) return a.M <= 16 ? launch_bdec16w_fill<1>(a, s) : launch_bdec16w_fill<2>(a, s);
     if (a.M <= 16) {
         if (nb16 <= 256) return launch_bdec16<1, 1>(a, s);
@@ -709,18 +911,6 @@ hipError_t launch_decode_mfma(const ForwardArgs& a, hipStream_t s) {
         if (nb16 <= 256) return launch_bdec16<2, 1>(a, s);
         return launch_bdec16<2, 2>(a, s);
     }
-    // 33 to 64 tokens, whole 256-weight sub-steps, matrices of up to 768 16-row blocks: k_bdec16w
-    // with three or four 16-token tiles and the fewest row blocks (up to three) that keep the
-    // grid within 256 workgroups.  Its x_q goes through LDS in whole lines, once per 16-row
-    // block of weights instead of per 32-row block of k_bdec64's, but four 16-token tiles fit
-    // the registers with one pipeline stage only (three with two).  Measured with weights not in
-    // cache, against k_bdec64: M = 64, K = 4096, N = 11008: 11.4 against 12.1 us; K = 11008,
-    // N = 4096: 16.2 against 18.1 us; K = 8192, N = 8192: 15.0 against 15.3 us; K = 16384,
-    // N = 4096: 21.4 against 23.2 us; M = 48, K = 4096, N = 11008: 10.3 against 11.9 us;
-    // M = 36: 9.9 against 11.8 us.  Wider matrices stay on k_bdec64 (M = 64, K = 8192,
-    // N = 28672: 45.8 against 37.8 us with three row blocks).
-    if (a.M <= 64 && a.K % 256 == 0 && nb16 <= 768)
-        return a.M <= 48 ? launch_bdec16w_fill3<3, 2>(a, s) : launch_bdec16w_fill3<4, 1>(a, s);
     // 33 to 64 tokens, whole 128-weight sub-steps: one 32-row block per workgroup up to 256
     // workgroups (N <= 8192), two beyond (172 workgroups at N = 11008).  Measured with weights
     // not in cache, M = 64: K = 8192, N = 8192, one block 15.8 against 18.6 us for two; K = 28672,

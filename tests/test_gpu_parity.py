@@ -205,6 +205,13 @@ FWD_CASES = [
     # seven waves idle; K = 1152: 9 sub-steps), odd per-wave counts, ragged N and M
     (33, 128, 8193), (64, 1152, 8200), (40, 4096, 300), (64, 11008, 4100), (57, 384, 8191),
     (64, 640, 12345), (35, 2176, 33), (64, 1024, 8192), (48, 256, 30000),
+    # 17-64 tokens with whole 256-weight sub-steps on at most 768 16-row blocks (x_q and codes
+    # loaded into LDS, codes in weight order): two, three and four 16-token tiles with one, two
+    # and three row blocks per workgroup; one sub-step (seven idle waves), sub-step counts not
+    # divisible by the eight waves, token counts not a multiple of the four tokens one load
+    # instruction covers, ragged N, the largest N of each row-block count and the next one
+    (17, 256, 4096), (31, 2304, 4097), (33, 1280, 8192), (47, 512, 8193), (49, 3328, 12288),
+    (64, 2816, 12289), (62, 768, 5), (18, 4608, 300), (41, 11008, 1030), (63, 4096, 4099),
 ]
 
 
