@@ -876,6 +876,15 @@ static hipError_t launch_bdec16w_fill(const ForwardArgs& a, hipStream_t s) {
 
 hipError_t launch_decode_mfma(const ForwardArgs& a, hipStream_t s) {
     const int64_t nb16 = (a.N + 15) / 16;
+    // 4 to 16 tokens likewise, on one 16-token tile (two and three tokens stay on k_bdec16w: 6.3
+    // against 6.2 us at M = 2, K = 4096, N = 11008).  Against k_bdec16w, identical outputs, weights
+    // not in cache: M = 16, K = 8192, N = 8192: 7.8 against 9.4 us; K = 11008, N = 4096: 7.6
+    // against 8.3 us; K = 4096, N = 11008: 6.6 against 7.0 us; M = 8, K = 11008, N = 4096: 6.9
+    // against 7.4 us; M = 4: 6.5 against 6.5 us at K = 4096, N = 11008, 7.1 against 7.6 us at
+    // K = 11008, N = 4096.  One row block per workgroup (up to three workgroups per CU: 78 VGPRs,
+    // 40 KiB of LDS) was slower on the wide matrices (M = 16, K = 4096, N = 11008: 7.3 us).
+    if (a.M >= 4 && a.M <= 16 && a.K % 256 == 0 && a.N * (a.K / 4) < (int64_t(1) << 32) && nb16 <= 768)
+        return launch_bdec16n_fill<1>(a, s);
     // 17 to 64 tokens, whole 256-weight sub-steps, at most 768 16-row blocks: k_bdec16n.
     // Measured with weights not in cache, against the kernels these shapes took before
     // (k_bdec16w), identical outputs: M = 64, K = 4096, N = 11008: 10.8 against 11.7 us;

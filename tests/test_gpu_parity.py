@@ -212,6 +212,10 @@ FWD_CASES = [
     # instruction covers, ragged N, the largest N of each row-block count and the next one
     (17, 256, 4096), (31, 2304, 4097), (33, 1280, 8192), (47, 512, 8193), (49, 3328, 12288),
     (64, 2816, 12289), (62, 768, 5), (18, 4608, 300), (41, 11008, 1030), (63, 4096, 4099),
+    # ... and 4-16 tokens on one 16-token tile: one, two and three row blocks, the largest N of
+    # three (768 blocks) and the next one (back to the register-staged kernel)
+    (4, 256, 4096), (5, 2304, 4097), (11, 1280, 8192), (16, 512, 12288), (13, 768, 12289),
+    (4, 11008, 999), (15, 4096, 63),
 ]
 
 
