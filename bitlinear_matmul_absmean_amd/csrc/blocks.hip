@@ -15,8 +15,9 @@
 // One or two tokens, a GEMV: a workgroup stages the tokens' x_q in LDS (each 16-byte group
 // transposed 4x4 so that a masked dword of codes meets its activations, plus the sum of x_q
 // over each 64-weight chunk), then every wave streams its own rows, one 16-byte chunk of
-// codes per lane and load.  Three to 127 tokens run on the matrix cores (below) in slices of
-// 32; 128 and more on the block-scaled GEMM at the end of the file.
+// codes per lane and load.  Three to 127 tokens run on the matrix cores (below): with
+// K % 256 == 0, from eight tokens, in slices of up to 64 on the buffer-load kernel, otherwise in
+// slices of 32; 128 and more on the block-scaled GEMM at the end of the file.
 #include "common.hpp"
 
 namespace bitlinear {
@@ -360,6 +361,207 @@ static hipError_t launch_bdec16_blocks(const BlockArgs& a, hipStream_t s) {
                            tiles > alphas ? tiles : alphas, s, a);
 }
 
+// Batched tokens (3 to 32 per launch) with K % 256 == 0: the layout of the per-tensor kernel
+// k_bdec16n.  Codes expanded in weight order and mapped to signed bytes W_hat = c - 1 (a v_perm
+// table), so no sum of x_q is needed; x_q and the packed codes of a sub-step go from global
+// memory into a wave-private LDS image through the load unit (buffer_load_dwordx4 ... lds), the
+// next sub-step fetched while the current one is multiplied.  In MFMA q of a sub-step lane group
+// g holds weights 64 q + 16 g .. 64 q + 16 g + 15 (packed dword g of the row's 16-byte load q,
+// unit 4 q + g of the token's x_q), so MFMAs 0-1 cover the sub-step's first 128-weight block and
+// 2-3 its second: each block's int32 sums come from two MFMAs started from zero, then are scaled
+// by the block's alpha into fp64 accumulators.  The eight waves' fp64 tiles are added through
+// LDS in a fixed order and y = fp32(S * beta / 127) (+ bias).
+template <int MT, int RB>
+__global__ __launch_bounds__(BB_WAVES * 64) void k_bdec16n_blocks(BlockArgs a) {
+    // LDS: the waves' images [wave][(4 MT + RB) * 64 units], then the workgroup's alpha rows
+    // (stride KB + 1); after the K loop, the waves' fp64 tiles [wave][RB * MT][4][64]
+    extern __shared__ i32x4 img[];
+    __shared__ double bsc[16 * MT];                // beta[m] / 127 of the slice's tokens
+    constexpr int XI = 4 * MT, IMG = (XI + RB) * 64;
+    double* redd = reinterpret_cast<double*>(img);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int M = (int)a.M;
+    const int64_t K = a.K, N = a.N, rowb = K >> 2;
+    const int KB = (int)(K >> 7), KBp = KB + 1;
+    const int64_t n0 = (int64_t)blockIdx.x * (16 * RB);
+    const int rows = (int)(N - n0 < 16 * RB ? N - n0 : 16 * RB);
+    const float beta_ld = a.beta[tid < M ? tid : M - 1];
+    const float* bias_src = a.bias ? a.bias : a.alpha;
+    const int64_t nb_e = n0 + 16 * ((tid >> 6) / MT) + (tid & 15);
+    const float bias_e = bias_src[a.bias && tid < RB * MT * 64 ? (nb_e < N ? nb_e : N - 1) : 0];
+    const int lr = lane & 15, lg = lane >> 4;
+    const int SP = (int)(K >> 8);
+    const int s0 = (int)((int64_t)SP * wave / BB_WAVES), s1 = (int)((int64_t)SP * (wave + 1) / BB_WAVES);
+    i32x4* xs = img + wave * IMG;
+    const uint32_t* ws32 = reinterpret_cast<const uint32_t*>(xs + XI * 64);
+    float* as = reinterpret_cast<float*>(img + BB_WAVES * IMG);
+    // load instruction i, lane (lr, lg): token 4i + lg (rows past M read row M - 1, never
+    // written), position lr, unit lr ^ (4 (i % 4) + lg); weight load r: 16 bytes at 16 lg of
+    // row n0 + 16 r + lr's 64-byte piece of the sub-step.  Offsets fit 32 bits (checked on launch).
+    const uint32_t Ku = (uint32_t)K, lastx = (uint32_t)(M - 1) * Ku, lgK = (uint32_t)lg * Ku;
+    uint32_t xu[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xu[j] = 16u * (uint32_t)(lr ^ (4 * j + lg));
+    uint32_t xoff[XI];
+#pragma unroll
+    for (int i = 0; i < XI; ++i) xoff[i] = min(lgK + (uint32_t)(4 * i) * Ku, lastx) + xu[i & 3];
+    uint32_t woff[RB];
+    int arow[RB];                                  // LDS offset of this lane's alpha row
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        const int lrow = min(16 * r + lr, rows - 1);
+        woff[r] = (uint32_t)(n0 + lrow) * (uint32_t)rowb + 16u * (uint32_t)lg;
+        arow[r] = lrow * KBp;
+    }
+    const __amdgpu_buffer_rsrc_t xr = raw_buffer(a.xq, (uint32_t)(M * K));
+    const __amdgpu_buffer_rsrc_t wr = raw_buffer(a.wp, (uint32_t)(N * rowb));
+    auto fetch = [&](int s) {
+#pragma unroll
+        for (int i = 0; i < XI; ++i) load_lds16(xr, xoff[i], (uint32_t)s * 256u, xs + 64 * i);
+#pragma unroll
+        for (int r = 0; r < RB; ++r) load_lds16(wr, woff[r], (uint32_t)s * 64u, xs + 64 * (XI + r));
+    };
+    if (s0 < s1) fetch(s0);
+    // the workgroup's alpha rows n0 .. n0 + rows - 1: one contiguous span of rows * KB floats
+    const float* asrc = a.alpha + n0 * KB;
+    for (int e = tid; e < rows * KB; e += BB_WAVES * 64) {
+        const int row = e / KB;
+        as[row * KBp + (e - row * KB)] = asrc[e];
+    }
+    if (tid < 16 * MT) bsc[tid] = (double)beta_ld / 127.0;
+    __syncthreads();
+    double f[RB][MT][4];
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) f[r][t][i] = 0.0;
+    const i32x4 zero = {0, 0, 0, 0};
+    for (int s = s0; s < s1; ++s) {
+        // the fetch of this sub-step has landed in the image (the only loads in flight)
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0)
+        __builtin_amdgcn_sched_barrier(0);
+        i32x4 av[MT][4];
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) av[t][q] = xs[(16 * t + lr) * 16 + ((4 * q + lg) ^ lr)];
+        uint32_t wd[RB][4];
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) wd[r][q] = ws32[(64 * r + 16 * q + lr) * 4 + lg];
+        // the next fetch rewrites the image: every read of it has to be complete first
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0)
+        __builtin_amdgcn_sched_barrier(0);
+        if (s + 1 < s1) fetch(s + 1);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float al[RB];
+#pragma unroll
+            for (int r = 0; r < RB; ++r) al[r] = as[arow[r] + 2 * s + h];
+            i32x4 blk[RB][MT];
+#pragma unroll
+            for (int q = 2 * h; q < 2 * h + 2; ++q)
+#pragma unroll
+                for (int r = 0; r < RB; ++r) {
+                    const i32x4 c = expand_codes_in_order(wd[r][q]);
+                    const i32x4 bv = {(int)__builtin_amdgcn_perm(0u, 0x000100FFu, (uint32_t)c.x),
+                                      (int)__builtin_amdgcn_perm(0u, 0x000100FFu, (uint32_t)c.y),
+                                      (int)__builtin_amdgcn_perm(0u, 0x000100FFu, (uint32_t)c.z),
+                                      (int)__builtin_amdgcn_perm(0u, 0x000100FFu, (uint32_t)c.w)};
+#pragma unroll
+                    for (int t = 0; t < MT; ++t)
+                        blk[r][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[t][q], bv, q == 2 * h ? zero : blk[r][t], 0, 0, 0);
+                }
+            // column l % 16 of a tile is this lane's row: scale its block sums by the row's alpha
+#pragma unroll
+            for (int r = 0; r < RB; ++r)
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        f[r][t][i] = __builtin_fma((double)al[r], (double)blk[r][t][i], f[r][t][i]);
+        }
+    }
+    __syncthreads();                               // images and alpha rows no longer read
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) redd[(((wave * RB * MT) + r * MT + t) * 4 + i) * 64 + lane] = f[r][t][i];
+    __syncthreads();
+    static_assert(RB * MT * 64 <= BB_WAVES * 64, "one epilogue element per thread");
+    if (tid < RB * MT * 64) {
+        const int l = tid & 63, tile = tid >> 6;
+        const int r = tile / MT, t = tile % MT;
+        const int64_t n = n0 + 16 * r + (l & 15);
+        if (n < N) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 16 * t + 4 * (l >> 4) + i;
+                if (m >= M) continue;
+                double sum = 0.0;
+#pragma unroll
+                for (int w = 0; w < BB_WAVES; ++w) sum += redd[((w * RB * MT + tile) * 4 + i) * 64 + l];
+                float v = (float)(sum * bsc[m]);
+                if (a.bias) v = v + bias_e;
+                a.y[(int64_t)m * N + n] = v;
+            }
+        }
+    }
+}
+
+template <int MT, int RB>
+static size_t bdec16n_blocks_lds(int64_t K) {
+    const size_t images = (size_t)BB_WAVES * (4 * MT + RB) * 64 * sizeof(i32x4) + (size_t)16 * RB * (K / 128 + 1) * sizeof(float);
+    const size_t tiles = (size_t)BB_WAVES * RB * MT * 4 * 64 * sizeof(double);
+    return images > tiles ? images : tiles;
+}
+template <int MT, int RB>
+static hipError_t launch_bdec16n_blocks(const BlockArgs& a, hipStream_t s) {
+    const int64_t wgs = (a.N + 16 * RB - 1) / (16 * RB);
+    return launch_with_lds(k_bdec16n_blocks<MT, RB>, dim3((unsigned)wgs), dim3(BB_WAVES * 64), bdec16n_blocks_lds<MT, RB>(a.K), s, a);
+}
+// Measured with weights not in cache, outputs identical to the earlier kernel (32-token slices
+// of k_bdec16_blocks, in brackets): K = 4096, N = 11008: M = 8 / 16 / 32 / 64: 8.1 / 8.3 / 9.9 /
+// 17.5 us (8.2 / 8.8 / 13.8 / 27.2); K = 11008, N = 4096: M = 16 / 32 / 64: 8.7 / 10.9 / 15.4 us
+// (10.2 / 16.7 / 32.9); K = 8192, N = 8192, M = 64: 15.4 us (22.7 as two 32-token slices of this
+// kernel).  Three and four tokens stay on the earlier kernel (M = 3: 7.8 against 8.2 us).
+// One slice of up to 64 tokens: MT = ceil(M / 16) token tiles and the fewest row blocks per
+// workgroup that keep the grid within 256 workgroups, up to three for one or two tiles and two
+// for three or four (the fp64 accumulators and the one-element-per-thread epilogue); false
+// when the shape is not one this kernel takes (K % 256 != 0, more than 768 16-row blocks,
+// offsets past 32 bits, images and alpha rows past the LDS).
+template <int MT, int RB>
+static bool bdec16n_blocks_try(const BlockArgs& a, hipStream_t s, hipError_t* e) {
+    if (bdec16n_blocks_lds<MT, RB>(a.K) + 16 * MT * sizeof(double) > 160 * 1024) return false;
+    *e = launch_bdec16n_blocks<MT, RB>(a, s);
+    return true;
+}
+template <int MT>
+static bool bdec16n_blocks_rb(const BlockArgs& a, int64_t nb16, hipStream_t s, hipError_t* e) {
+    if (nb16 <= 256) return bdec16n_blocks_try<MT, 1>(a, s, e);
+    if (nb16 <= 512 || MT > 2) return bdec16n_blocks_try<MT, 2>(a, s, e);
+    if constexpr (MT <= 2) return bdec16n_blocks_try<MT, 3>(a, s, e);
+    return false;
+}
+static bool bdec16n_blocks_launch(const BlockArgs& a, hipStream_t s, hipError_t* e) {
+    const int64_t nb16 = (a.N + 15) / 16;
+    if (a.M > 64 || a.K % 256 != 0 || nb16 > 768 || a.M * a.K >= (int64_t(1) << 31) ||
+        a.N * (a.K / 4) >= (int64_t(1) << 32))
+        return false;
+    if (a.M <= 16) return bdec16n_blocks_rb<1>(a, nb16, s, e);
+    if (a.M <= 32) return bdec16n_blocks_rb<2>(a, nb16, s, e);
+    if (a.M <= 48) return bdec16n_blocks_rb<3>(a, nb16, s, e);
+    return bdec16n_blocks_rb<4>(a, nb16, s, e);
+}
+
 // 3 to 32 tokens: the fewest row blocks per workgroup that keep the grid within 256
 // workgroups (three at N = 11008: 230 workgroups, where four left 84 CUs idle), at most 4 for
 // one token block and 3 for two (beyond, the fp64 accumulators spill); larger N gets more
@@ -595,14 +797,19 @@ hipError_t launch_forward_blocks(const int8_t* xq, const float* beta, int64_t M,
     // decode kernel (measured at M = 64, K = 4096, N = 11008, weights not in cache: two slices
     // 43.3 us, the GEMM's 86 workgroups 46.0 us)
     if (M >= 128) return launch_gemm_blocks<2>(a, s);
-    for (int64_t m0 = 0; m0 < M; m0 += 32) {
+    for (int64_t m0 = 0; m0 < M;) {
         BlockArgs sl = a;
-        sl.M = M - m0 < 32 ? M - m0 : 32;
         sl.xq = xq + m0 * K;
         sl.beta = beta + m0;
         sl.y = y + m0 * N;
-        hipError_t e = launch_bdec16_blocks_m(sl, s);
+        hipError_t e = hipSuccess;
+        sl.M = M - m0 < 64 ? M - m0 : 64;
+        if (sl.M < 8 || !bdec16n_blocks_launch(sl, s, &e)) {
+            sl.M = M - m0 < 32 ? M - m0 : 32;
+            e = launch_bdec16_blocks_m(sl, s);
+        }
         if (e != hipSuccess) return e;
+        m0 += sl.M;
     }
     return hipSuccess;
 }

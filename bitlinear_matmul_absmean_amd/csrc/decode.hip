@@ -502,36 +502,6 @@ static hipError_t launch_bdec16w(const ForwardArgs& a, hipStream_t s) {
 }
 
 
-// Expansion of one packed dword (16 codes, weight 4b+i at bits 2i of byte b) into the
-// 16-byte MFMA operand in weight order: byte 4b+i of the result is the code of weight 4b+i.
-// Per output dword: v_perm gathers [byte b of w, byte b of w >> 2] twice, a packed 16-bit shift
-// by (0, 4) brings bits 4-5 of the upper pair down, and a mask keeps bits 0-1 of every byte.
-__device__ __forceinline__ i32x4 expand_codes_in_order(uint32_t w) {
-    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-    const uint32_t w2 = w >> 2;
-    i32x4 r;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const uint32_t sel = (uint32_t)b | (uint32_t)(4 + b) << 8 | (uint32_t)b << 16 | (uint32_t)(4 + b) << 24;
-        u16x2 h = __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(w2, w, sel));
-        h = h >> (u16x2){0, 4};
-        r[b] = (int)(__builtin_bit_cast(uint32_t, h) & 0x03030303u);
-    }
-    return r;
-}
-
-// 16 bytes per lane from global memory straight into LDS (buffer_load_dwordx4 ... lds): lane l
-// writes its 16 bytes at lds + 16 l (lds the same for the whole wave), read from the buffer r at
-// voff (per lane) + soff (uniform).  Offsets past the buffer's size would read zeros; every
-// caller keeps them inside.
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, i32x4* lds) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
-}
-// Buffer resource over [p, p + bytes) for raw (untyped) loads: stride 0, 32-bit data format.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* p, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
-}
-
 // 17 to 64 tokens, K % 256 == 0: 16 x 16 x 64 tiles with the codes expanded in weight order, so
 // that x_q needs no transposition.  Both operands move from global memory into LDS through the
 // load unit itself (buffer_load_dwordx4 ... lds), without passing through registers: the waves
