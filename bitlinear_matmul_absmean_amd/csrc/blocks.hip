@@ -469,11 +469,7 @@ __global__ __launch_bounds__(BB_WAVES * 64) void k_bdec16n_blocks(BlockArgs a) {
             for (int q = 2 * h; q < 2 * h + 2; ++q)
 #pragma unroll
                 for (int r = 0; r < RB; ++r) {
-                    const i32x4 c = expand_codes_in_order(wd[r][q]);
-                    const i32x4 bv = {(int)__builtin_amdgcn_perm(0u, 0x000100FFu, (uint32_t)c.x),
-                                      (int)__builtin_amdgcn_perm(0u, 0x000100FFu, (uint32_t)c.y),
-                                      (int)__builtin_amdgcn_perm(0u, 0x000100FFu, (uint32_t)c.z),
-                                      (int)__builtin_amdgcn_perm(0u, 0x000100FFu, (uint32_t)c.w)};
+                    const i32x4 bv = expand_signed_in_order(wd[r][q]);
 #pragma unroll
                     for (int t = 0; t < MT; ++t)
                         blk[r][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[t][q], bv, q == 2 * h ? zero : blk[r][t], 0, 0, 0);

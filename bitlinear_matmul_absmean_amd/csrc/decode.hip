@@ -502,8 +502,8 @@ static hipError_t launch_bdec16w(const ForwardArgs& a, hipStream_t s) {
 }
 
 
-// 17 to 64 tokens, K % 256 == 0: 16 x 16 x 64 tiles with the codes expanded in weight order, so
-// that x_q needs no transposition.  Both operands move from global memory into LDS through the
+// 4 to 64 tokens, K % 256 == 0: 16 x 16 x 64 tiles with the codes expanded in weight order, so
+// that x_q needs no transposition, as signed bytes W_hat = c - 1, so that no sum of x_q is needed.  Both operands move from global memory into LDS through the
 // load unit itself (buffer_load_dwordx4 ... lds), without passing through registers: the waves
 // split K in 256-weight sub-steps as in k_bdec16w, and each wave keeps an LDS image of its
 // sub-step (x_q of 16 MT tokens x 256 bytes, then RB x 1 KiB of packed weights).  A sub-step
@@ -519,11 +519,12 @@ static hipError_t launch_bdec16w(const ForwardArgs& a, hipStream_t s) {
 //     k0 + 64 g) of row n0 + 16 b + r and reads them back from its own slot.
 //   * in MFMA q of a sub-step, lane group g holds weights 64g + 16q .. 64g + 16q + 15: packed
 //     dword q of the lane's 16 bytes, and unit 4g + q of the token's x_q.
+//   * signed codes cost four VALU instructions per 16 codes; the unsigned codes with token sums
+//     from MFMAs against an all-ones operand cost one MFMA per token tile and 64 weights, half
+//     of all MFMAs with one row block per workgroup.
 template <int MT, int RB>
 __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec16n(ForwardArgs a) {
     extern __shared__ i32x4 red[];
-    __shared__ int tsum_w[BD_WAVES][16 * MT];
-    __shared__ __align__(16) int tsum_t[MT * 16];
     __shared__ __align__(16) float scale_t[MT * 16];
     constexpr int XI = 4 * MT;                     // x_q load instructions (1 KiB each) per sub-step
     constexpr int IMG = (XI + RB) * 64;            // 16-byte units of one wave's image
@@ -564,10 +565,6 @@ __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec16n(ForwardArgs a) {
     for (int r = 0; r < RB; ++r)
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[r][t] = i32x4{0, 0, 0, 0};
-    const i32x4 ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
-    i32x4 tsm[MT];
-#pragma unroll
-    for (int t = 0; t < MT; ++t) tsm[t] = i32x4{0, 0, 0, 0};
     if (s0 < s1) fetch(s0);
     for (int s = s0; s < s1; ++s) {
         // the fetch of this sub-step has landed in the image (the only loads in flight)
@@ -590,22 +587,13 @@ __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec16n(ForwardArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
 #pragma unroll
-            for (int t = 0; t < MT; ++t) tsm[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[t][q], ones, tsm[t], 0, 0, 0);
-#pragma unroll
             for (int r = 0; r < RB; ++r) {
                 const uint32_t w = q == 0 ? wv[r].x : q == 1 ? wv[r].y : q == 2 ? wv[r].z : wv[r].w;
-                const i32x4 bv = expand_codes_in_order(w);
+                const i32x4 bv = expand_signed_in_order(w);
 #pragma unroll
                 for (int t = 0; t < MT; ++t) acc[r][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[t][q], bv, acc[r][t], 0, 0, 0);
             }
         }
-    }
-    // column 0 (lanes 0, 16, 32, 48) holds accumulator r of token 4 (lane / 16) + r
-    if (lr == 0) {
-#pragma unroll
-        for (int t = 0; t < MT; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) tsum_w[wave][16 * t + 4 * lg + r] = tsm[t][r];
     }
     __syncthreads();                               // every wave is done with its image
 #pragma unroll
@@ -614,15 +602,11 @@ __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec16n(ForwardArgs a) {
         for (int t = 0; t < MT; ++t) red[(wave * RB * MT + r * MT + t) * 64 + lane] = acc[r][t];
     __syncthreads();
     if (tid < MT * 16) {
-        int v = 0;
-#pragma unroll
-        for (int w = 0; w < BD_WAVES; ++w) v += tsum_w[w][tid];
-        tsum_t[tid] = v;
         scale_t[tid] = (!a.alpha_per_row && tid < M) ? dequant_scale(a.alpha[0], a.beta[tid]) : 0.0f;
     }
     __syncthreads();
     // element e = (tile, lane): tokens 16 t + 4 (lane / 16) + i, i < 4, of weight row
-    // n0 + 16 r + lane % 16; the four tokens' sums and scales are read as one 16-byte unit each
+    // n0 + 16 r + lane % 16; the four tokens' scales are read as one 16-byte unit
     for (int e = tid; e < RB * MT * 64; e += BD_WAVES * 64) {
         const int l = e & 63, tile = e >> 6;
         const int r = tile / MT, t = tile % MT;
@@ -632,7 +616,6 @@ __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec16n(ForwardArgs a) {
         const int64_t n = n0 + 16 * r + (l & 15);
         if (n >= N) continue;
         const int m0 = 16 * t + 4 * (l >> 4);
-        const i32x4 ts = *reinterpret_cast<const i32x4*>(&tsum_t[m0]);
         float sc[4];
         if (a.alpha_per_row) {
             const float al = a.alpha[n];
@@ -645,7 +628,7 @@ __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec16n(ForwardArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if (m0 + i >= M) break;
-            const int total = sum[i] - ts[i];
+            const int total = sum[i];
             a.y[(int64_t)(m0 + i) * N + n] = activate(dequant(total, sc[i], a.bias, n), a.act);
             if (a.acc) a.acc[(int64_t)(m0 + i) * N + n] = total;
         }
