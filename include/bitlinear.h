@@ -253,8 +253,9 @@ int bitlinear_quantize_weights_blocks(const float* W, int64_t N, int64_t K, uint
  *   x_q [M, K] int8, beta [M] fp32 (from bitlinear_quantize_act); W_packed [N, K/4] uint8 and
  *   alpha_blocks [N, K/128] fp32 (from bitlinear_quantize_weights_blocks); bias [N] or NULL;
  *   y [M, N] fp32 (out).  x_q and W_packed 16-byte aligned, alpha_blocks 4-byte aligned.
- * K % 128 == 0, K <= 32768 and M <= 262140.  One or two tokens run a GEMV; more run an int8
- * MFMA kernel over slices of 32 tokens, each slice reading the codes once.
+ * K % 128 == 0, K <= 32768 and M <= 262140.  One or two tokens run a GEMV; 3 to 127 run an
+ * int8 MFMA kernel over slices of up to 64 tokens (32 when K % 256 != 0 or below 8 tokens),
+ * each slice reading the codes once; 128 and more an int8 MFMA GEMM.
  * Errors: INVALID_ARG, SHAPE, ALIGNMENT, HIP.
  */
 int bitlinear_forward_blocks(const int8_t* x_q, const float* beta, int64_t M, int64_t K,
