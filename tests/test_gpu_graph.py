@@ -40,6 +40,7 @@ def test_graph_replays_match_eager(dev):
     w_b64 = workloads.weights(100, 9000, 1024)           # batched decode, 64 tokens, whole sub-steps
     w_b16 = workloads.weights(101, 700, 2048)            # batched decode, 12 tokens, one row block per workgroup
     w_bg = workloads.weights(102, 300, 640)              # block-scaled GEMM, 160 tokens
+    w_bb = workloads.weights(103, 900, 1024)             # block scales, 40 tokens (x_q and codes through LDS loads)
     p_dec, a_dec = bl.bitlinear_quantize_weights(t(w_dec))
     p_gemm, a_gemm = bl.bitlinear_quantize_weights(t(w_gemm))
     p_bat, a_bat = bl.bitlinear_quantize_weights(t(w_bat))
@@ -52,6 +53,7 @@ def test_graph_replays_match_eager(dev):
     p_b64, a_b64 = bl.bitlinear_quantize_weights(t(w_b64))
     p_b16, a_b16 = bl.bitlinear_quantize_weights(t(w_b16))
     p_bg, a_bg = bl.bitlinear_quantize_weights_blocks(t(w_bg))
+    p_bb, a_bb = bl.bitlinear_quantize_weights_blocks(t(w_bb))
     # activations and static outputs
     x_dec = t(workloads.activations_with_outliers(90, 1, 4096))
     x_gemm = t(workloads.activations_with_outliers(91, 200, 512))
@@ -63,6 +65,7 @@ def test_graph_replays_match_eager(dev):
     x_b64 = t(workloads.activations_with_outliers(100, 64, 1024))
     x_b16 = t(workloads.activations_with_outliers(101, 12, 2048))
     x_bg = t(workloads.activations_with_outliers(102, 160, 640))
+    x_bb = t(workloads.activations_with_outliers(103, 40, 1024))
     bias = t(workloads.activations(98, 1, 9000)[0])
     out = {
         "dec": torch.empty((1, 1000), **f32), "gemm": torch.empty((200, 700), **f32),
@@ -70,7 +73,7 @@ def test_graph_replays_match_eager(dev):
         "mlp_g": torch.empty((130, 1000), **f32), "had": torch.empty((1, 300), **f32),
         "blk": torch.empty((4, 500), **f32), "t5": torch.empty((1, 300), **f32),
         "b64": torch.empty((64, 9000), **f32), "b16": torch.empty((12, 700), **f32),
-        "bg": torch.empty((160, 300), **f32),
+        "bg": torch.empty((160, 300), **f32), "bb": torch.empty((40, 900), **f32),
     }
     xq_b64 = torch.empty((64, 1024), dtype=torch.int8, device="cuda")
     b_b64 = torch.empty(64, **f32)
@@ -78,6 +81,8 @@ def test_graph_replays_match_eager(dev):
     b_b16 = torch.empty(12, **f32)
     xq_bg = torch.empty((160, 640), dtype=torch.int8, device="cuda")
     b_bg = torch.empty(160, **f32)
+    xq_bb = torch.empty((40, 1024), dtype=torch.int8, device="cuda")
+    b_bb = torch.empty(40, **f32)
     xq_gemm = torch.empty((200, 512), dtype=torch.int8, device="cuda")
     b_gemm = torch.empty(200, **f32)
     xq_bat = torch.empty((24, 1024), dtype=torch.int8, device="cuda")
@@ -110,6 +115,8 @@ def test_graph_replays_match_eager(dev):
         bl.bitlinear_forward(xq_b16, b_b16, p_b16, a_b16, y=out["b16"])
         bl.bitlinear_quantize_act(x_bg, x_q=xq_bg, beta=b_bg)
         bl.bitlinear_forward_blocks(xq_bg, b_bg, p_bg, a_bg, bias=bias[:300], y=out["bg"])
+        bl.bitlinear_quantize_act(x_bb, x_q=xq_bb, beta=b_bb)
+        bl.bitlinear_forward_blocks(xq_bb, b_bb, p_bb, a_bb, bias=bias[:900], y=out["bb"])
 
     _say("graph: eager reference")
     calls()
