@@ -391,8 +391,8 @@ __global__ __launch_bounds__(BB_WAVES * 64) void k_bdec16n_blocks(BlockArgs a) {
     const int64_t nb_e = n0 + 16 * ((tid >> 6) / MT) + (tid & 15);
     const float bias_e = bias_src[a.bias && tid < RB * MT * 64 ? (nb_e < N ? nb_e : N - 1) : 0];
     const int lr = lane & 15, lg = lane >> 4;
+    // sub-steps interleaved over the waves (wave w takes w, w + 8, ...), as in k_bdec16n
     const int SP = (int)(K >> 8);
-    const int s0 = (int)((int64_t)SP * wave / BB_WAVES), s1 = (int)((int64_t)SP * (wave + 1) / BB_WAVES);
     i32x4* xs = img + wave * IMG;
     const uint32_t* ws32 = reinterpret_cast<const uint32_t*>(xs + XI * 64);
     float* as = reinterpret_cast<float*>(img + BB_WAVES * IMG);
@@ -422,7 +422,7 @@ __global__ __launch_bounds__(BB_WAVES * 64) void k_bdec16n_blocks(BlockArgs a) {
 #pragma unroll
         for (int r = 0; r < RB; ++r) load_lds16(wr, woff[r], (uint32_t)s * 64u, xs + 64 * (XI + r));
     };
-    if (s0 < s1) fetch(s0);
+    if (wave < SP) fetch(wave);
     // the workgroup's alpha rows n0 .. n0 + rows - 1: one contiguous span of rows * KB floats
     const float* asrc = a.alpha + n0 * KB;
     for (int e = tid; e < rows * KB; e += BB_WAVES * 64) {
@@ -439,7 +439,7 @@ __global__ __launch_bounds__(BB_WAVES * 64) void k_bdec16n_blocks(BlockArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) f[r][t][i] = 0.0;
     const i32x4 zero = {0, 0, 0, 0};
-    for (int s = s0; s < s1; ++s) {
+    for (int s = wave; s < SP; s += BB_WAVES) {
         // the fetch of this sub-step has landed in the image (the only loads in flight)
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0)
@@ -458,7 +458,7 @@ __global__ __launch_bounds__(BB_WAVES * 64) void k_bdec16n_blocks(BlockArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0)
         __builtin_amdgcn_sched_barrier(0);
-        if (s + 1 < s1) fetch(s + 1);
+        if (s + BB_WAVES < SP) fetch(s + BB_WAVES);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             float al[RB];
@@ -529,6 +529,8 @@ static hipError_t launch_bdec16n_blocks(const BlockArgs& a, hipStream_t s) {
 // 17.5 us (8.2 / 8.8 / 13.8 / 27.2); K = 11008, N = 4096: M = 16 / 32 / 64: 8.7 / 10.9 / 15.4 us
 // (10.2 / 16.7 / 32.9); K = 8192, N = 8192, M = 64: 15.4 us (22.7 as two 32-token slices of this
 // kernel).  Three and four tokens stay on the earlier kernel (M = 3: 7.8 against 8.2 us).
+// Sub-steps interleaved over the waves then took M = 16 to 7.7 us (8.5), M = 32 to 9.4 (10.1),
+// K = 8192, N = 8192, M = 64 to 15.6 (16.7); M = 64, K = 4096, N = 11008 level.
 // One slice of up to 64 tokens: MT = ceil(M / 16) token tiles and the fewest row blocks per
 // workgroup that keep the grid within 256 workgroups, up to three for one or two tiles and two
 // for three or four (the fp64 accumulators and the one-element-per-thread epilogue); false
