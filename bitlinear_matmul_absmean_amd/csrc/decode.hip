@@ -384,7 +384,8 @@ __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec16w(ForwardArgs a) {
     const int64_t n0 = (int64_t)blockIdx.x * (16 * RB);
     const int lr = lane & 15, lg = lane >> 4;
     const int SP = (int)(K >> 8);
-    const int s0 = (int)((int64_t)SP * wave / BD_WAVES), s1 = (int)((int64_t)SP * (wave + 1) / BD_WAVES);
+    // the wave's i-th sub-step is wave + 8 i (interleaved over the waves)
+    const int s0 = 0, s1 = wave < SP ? (SP - wave + BD_WAVES - 1) / BD_WAVES : 0;
     // x_q of a sub-step (16 MT tokens x 256 bytes) is loaded in whole lines: instruction i
     // covers tokens 4i .. 4i+3, sixteen lanes per token; each lane transposes its 16-byte group
     // and stores it in a wave-private LDS image, rows padded by one unit, from which the MFMA
@@ -401,9 +402,9 @@ __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec16w(ForwardArgs a) {
     u32x4 xa[ST][4 * MT], wb[ST][RB];
     auto load = [&](int st, int s) {
 #pragma unroll
-        for (int i = 0; i < 4 * MT; ++i) xa[st][i] = *reinterpret_cast<const u32x4*>(xrow[i] + (int64_t)s * 256);
+        for (int i = 0; i < 4 * MT; ++i) xa[st][i] = *reinterpret_cast<const u32x4*>(xrow[i] + (int64_t)(wave + BD_WAVES * s) * 256);
 #pragma unroll
-        for (int r = 0; r < RB; ++r) wb[st][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[r] + (int64_t)s * 64));
+        for (int r = 0; r < RB; ++r) wb[st][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[r] + (int64_t)(wave + BD_WAVES * s) * 64));
     };
     i32x4 acc[RB][MT];
 #pragma unroll
@@ -678,7 +679,8 @@ __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec64(ForwardArgs a) {
     const int lr = lane & 31, lg = lane >> 5;
     i32x4* xs = red + wave * XR;
     const int SP = (int)(K >> 7);
-    const int s0 = (int)((int64_t)SP * wave / BD_WAVES), s1 = (int)((int64_t)SP * (wave + 1) / BD_WAVES);
+    // the wave's i-th sub-step is wave + 8 i (interleaved over the waves)
+    const int s0 = 0, s1 = wave < SP ? (SP - wave + BD_WAVES - 1) / BD_WAVES : 0;
     // x_q: instruction i covers tokens 8i + lane/8, 16 bytes at k0 + 16 (lane % 8); weights:
     // lane (lr, lg) reads 16 bytes (64 codes at k0 + 64 lg) of row n0 + 32r + lr.  Rows past M
     // or N are clamped (never written).
@@ -692,9 +694,9 @@ __global__ __launch_bounds__(BD_WAVES * 64) void k_bdec64(ForwardArgs a) {
     u32x4 xa[2][MT * 4], wb[2][RB];
     auto load = [&](int st, int s) {
 #pragma unroll
-        for (int i = 0; i < MT * 4; ++i) xa[st][i] = *reinterpret_cast<const u32x4*>(xrow[i] + (int64_t)s * 128);
+        for (int i = 0; i < MT * 4; ++i) xa[st][i] = *reinterpret_cast<const u32x4*>(xrow[i] + (int64_t)(wave + BD_WAVES * s) * 128);
 #pragma unroll
-        for (int r = 0; r < RB; ++r) wb[st][r] = *reinterpret_cast<const u32x4*>(wrow[r] + (int64_t)s * 32);
+        for (int r = 0; r < RB; ++r) wb[st][r] = *reinterpret_cast<const u32x4*>(wrow[r] + (int64_t)(wave + BD_WAVES * s) * 32);
     };
     i32x16 acc[RB][MT];
 #pragma unroll
@@ -830,19 +832,19 @@ static hipError_t launch_bdec16w_fill(const ForwardArgs& a, hipStream_t s) {
 
 hipError_t launch_decode_mfma(const ForwardArgs& a, hipStream_t s) {
     const int64_t nb16 = (a.N + 15) / 16;
-    // 4 to 16 tokens likewise, on one 16-token tile (two and three tokens stay on k_bdec16w: 6.3
-    // against 6.2 us at M = 2, K = 4096, N = 11008).  Against k_bdec16w, identical outputs, weights
+    // 2 to 16 tokens likewise, on one 16-token tile.  Against k_bdec16w, identical outputs, weights
     // not in cache: M = 16, K = 8192, N = 8192: 7.8 against 9.4 us; K = 11008, N = 4096: 7.6
     // against 8.3 us; K = 4096, N = 11008: 6.6 against 7.0 us; M = 8, K = 11008, N = 4096: 6.9
     // against 7.4 us; M = 4: 6.5 against 6.5 us at K = 4096, N = 11008, 7.1 against 7.6 us at
     // K = 11008, N = 4096.  One row block per workgroup (up to three workgroups per CU: 78 VGPRs,
     // 40 KiB of LDS) was slower on the wide matrices (M = 16, K = 4096, N = 11008: 7.3 us).
-    if (a.M >= 4 && a.M <= 16 && a.K % 256 == 0 && a.N * (a.K / 4) < (int64_t(1) << 32) && nb16 <= 768)
+    if (a.M >= 2 && a.M <= 16 && a.K % 256 == 0 && a.N * (a.K / 4) < (int64_t(1) << 32) && nb16 <= 768)
         return launch_bdec16n_fill<1>(a, s);
     // Sub-steps interleaved over the waves rather than a contiguous range per wave, same
     // outputs, weights not in cache: M = 4, K = 4096, N = 11008: 5.9 against 6.6 us; M = 16:
     // 6.5 against 6.7 us (K = 11008, N = 4096: 7.3 against 7.7 us); M = 32: 7.7 against 8.0 us;
-    // M = 64 level.
+    // M = 64 level.  Two and three tokens then left k_bdec16w too (M = 2 / 3, K = 4096,
+    // N = 11008: 5.8 / 5.9 against 6.2 / 6.3 us; M = 3, K = 11008, N = 4096: 6.9 against 7.5).
     // 17 to 64 tokens, whole 256-weight sub-steps, at most 768 16-row blocks: k_bdec16n.
     // Measured with weights not in cache, against the kernels these shapes took before
     // (k_bdec16w), identical outputs: M = 64, K = 4096, N = 11008: 10.8 against 11.7 us;
