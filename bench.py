@@ -461,7 +461,7 @@ def blocks_bench(torch, bl, workloads, dev, ms_plain_step):
         ms, _ = _graph_time(torch, lambda i: bl.bitlinear_forward_blocks(xq, beta, *pool[i % copies], y=y), 96)
         out["batched"].append({"M": m, "K": k, "N": n, "us": round(ms * 1e3, 2),
                                "kernel": "16x16x64 int8 MFMA tiles, int32 sums per block scaled in fp64" +
-                                         (", x_q and codes loaded into LDS" if m >= 8 and k % 256 == 0 else "") +
+                                         (", x_q and codes loaded into LDS" if m >= 3 and k % 256 == 0 else "") +
                                          ("" if m <= 64 else f", {(m + 63) // 64} slices of up to 64 tokens")})
     del pool
     # prefill with block scales: M = 2048 (int8 ops 2MNK) beside the per-tensor GEMM of the same shape

@@ -16,7 +16,7 @@
 // transposed 4x4 so that a masked dword of codes meets its activations, plus the sum of x_q
 // over each 64-weight chunk), then every wave streams its own rows, one 16-byte chunk of
 // codes per lane and load.  Three to 127 tokens run on the matrix cores (below): with
-// K % 256 == 0, from eight tokens, in slices of up to 64 on the buffer-load kernel, otherwise in
+// K % 256 == 0 in slices of up to 64 on the buffer-load kernel, otherwise in
 // slices of 32; 128 and more on the block-scaled GEMM at the end of the file.
 #include "common.hpp"
 
@@ -528,9 +528,11 @@ static hipError_t launch_bdec16n_blocks(const BlockArgs& a, hipStream_t s) {
 // of k_bdec16_blocks, in brackets): K = 4096, N = 11008: M = 8 / 16 / 32 / 64: 8.1 / 8.3 / 9.9 /
 // 17.5 us (8.2 / 8.8 / 13.8 / 27.2); K = 11008, N = 4096: M = 16 / 32 / 64: 8.7 / 10.9 / 15.4 us
 // (10.2 / 16.7 / 32.9); K = 8192, N = 8192, M = 64: 15.4 us (22.7 as two 32-token slices of this
-// kernel).  Three and four tokens stay on the earlier kernel (M = 3: 7.8 against 8.2 us).
+// kernel).
 // Sub-steps interleaved over the waves then took M = 16 to 7.7 us (8.5), M = 32 to 9.4 (10.1),
-// K = 8192, N = 8192, M = 64 to 15.6 (16.7); M = 64, K = 4096, N = 11008 level.
+// K = 8192, N = 8192, M = 64 to 15.6 (16.7); M = 64, K = 4096, N = 11008 level.  With them it
+// also beats the earlier kernel from three tokens: M = 3 / 4 / 7, K = 4096, N = 11008: 7.5 /
+// 7.5 / 7.4 us (7.9 / 8.1 / 8.1); M = 4, K = 11008, N = 4096: 7.7 us (9.0).
 // One slice of up to 64 tokens: MT = ceil(M / 16) token tiles and the fewest row blocks per
 // workgroup that keep the grid within 256 workgroups, up to three for one or two tiles and two
 // for three or four (the fp64 accumulators and the one-element-per-thread epilogue); false
@@ -802,7 +804,7 @@ hipError_t launch_forward_blocks(const int8_t* xq, const float* beta, int64_t M,
         sl.y = y + m0 * N;
         hipError_t e = hipSuccess;
         sl.M = M - m0 < 64 ? M - m0 : 64;
-        if (sl.M < 8 || !bdec16n_blocks_launch(sl, s, &e)) {
+        if (sl.M < 3 || !bdec16n_blocks_launch(sl, s, &e)) {
             sl.M = M - m0 < 32 ? M - m0 : 32;
             e = launch_bdec16_blocks_m(sl, s);
         }

@@ -254,7 +254,7 @@ int bitlinear_quantize_weights_blocks(const float* W, int64_t N, int64_t K, uint
  *   alpha_blocks [N, K/128] fp32 (from bitlinear_quantize_weights_blocks); bias [N] or NULL;
  *   y [M, N] fp32 (out).  x_q and W_packed 16-byte aligned, alpha_blocks 4-byte aligned.
  * K % 128 == 0, K <= 32768 and M <= 262140.  One or two tokens run a GEMV; 3 to 127 run an
- * int8 MFMA kernel over slices of up to 64 tokens (32 when K % 256 != 0 or below 8 tokens),
+ * int8 MFMA kernel over slices of up to 64 tokens (32 when K % 256 != 0),
  * each slice reading the codes once; 128 and more an int8 MFMA GEMM.
  * Errors: INVALID_ARG, SHAPE, ALIGNMENT, HIP.
  */

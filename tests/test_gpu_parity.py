@@ -679,7 +679,7 @@ BLOCK_CASES = [(1, 4096, 4096), (1, 11008, 300), (2, 128, 77), (3, 4096, 1000), 
                (24, 128, 6000), (20, 1024, 9000), (32, 640, 15000),
                # 33-127 tokens: three and four slices of 32, the last ragged
                (65, 4224, 4100), (127, 256, 129),
-               # K % 256 == 0 from 8 tokens: the buffer-load kernel (codes in weight order, one
+               # K % 256 == 0 from 3 tokens: the buffer-load kernel (codes in weight order, one
                # 128-weight block per pair of MFMAs) in slices of up to 64 tokens, one to four
                # token tiles, one to three row blocks (two at most with three or four tiles, also
                # beyond 256 workgroups), one sub-step (seven idle waves), sub-step counts not
@@ -688,7 +688,8 @@ BLOCK_CASES = [(1, 4096, 4096), (1, 11008, 300), (2, 128, 77), (3, 4096, 1000), 
                # kernel and 36 on this one
                (8, 256, 4096), (13, 2304, 4097), (17, 1280, 8193), (31, 512, 12288),
                (33, 4096, 300), (47, 768, 4100), (48, 3328, 8192), (49, 256, 4096), (60, 2816, 8193),
-               (64, 4096, 12288), (64, 16384, 1000), (66, 1024, 700), (100, 4608, 513)]
+               (64, 4096, 12288), (64, 16384, 1000), (66, 1024, 700), (100, 4608, 513),
+               (3, 256, 4096), (7, 2304, 8193), (4, 11008, 300)]
 
 
 @pytest.mark.parametrize("m,k,n", BLOCK_CASES)
