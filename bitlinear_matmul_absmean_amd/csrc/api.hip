@@ -41,17 +41,20 @@ int check_forward(const int8_t* x_q, const float* beta, int64_t M, int64_t K, co
 
 enum class Path { Gemv, Decode, Gemm, Generic };
 
-// One token: the VALU GEMV.  Two to four tokens: the GEMV for matrices of 2^26 weights or
-// more, and for two tokens with K >= 8192, where it streams the codes faster; else the MFMA
-// decode kernel (measured with weights not in cache: M = 4, 7.2 vs 9.6 us at K = 4096,
-// N = 11008; M = 2, 4.2 vs 4.9 us at K = N = 4096, 5.9 vs 6.8 us at K = 11008, N = 4096;
-// 13.8 vs 23.7 us at K = 8192, N = 28672).  Up to 64 tokens: the MFMA decode kernel; more:
-// the MFMA GEMM.  Every fast path needs K % 64 == 0 and 16-byte aligned rows; other calls take
-// the generic kernel.
+// One token: the VALU GEMV.  Two tokens: the GEMV for matrices of 2^26 weights or more and
+// for K >= 8192, where it streams the codes faster; else the MFMA decode kernel (measured with
+// weights not in cache, GEMV against decode kernel: 6.1 vs 6.7 us at K = 11008, N = 4096; 6.5
+// vs 7.3 us at K = N = 8192; 14.9 vs 16.0 us at K = 8192, N = 28672; 6.9 vs 8.7 us at K = 16384,
+// N = 4096).  Three to 64 tokens: the MFMA decode kernel (the GEMV only where that kernel does
+// not apply), which beat the GEMV for three and four tokens on every shape measured, also on
+// large matrices: M = 3, K = 8192, N = 28672: 16.1 vs 18.9 us; M = 4: 16.3 vs 21.6 us; M = 4,
+// K = 16384, N = 8192: 10.7 vs 19.4 us; M = 4, K = 4096, N = 16384: 7.9 vs 10.3 us.  More than
+// 64 tokens: the MFMA GEMM.  Every fast path needs K % 64 == 0 and 16-byte aligned rows; other
+// calls take the generic kernel.
 constexpr int64_t GEMV_BATCH_MIN_WEIGHTS = (int64_t)1 << 26;
 Path choose_path(int64_t M, int64_t K, int64_t N, const int8_t* xq, const uint8_t* wp) {
     if (!fast_forward_ok(K, xq, wp)) return Path::Generic;
-    if (gemv_supports(M, K) && (M == 1 || (M == 2 && K >= 8192) || N * K >= GEMV_BATCH_MIN_WEIGHTS ||
+    if (gemv_supports(M, K) && (M == 1 || (M == 2 && (K >= 8192 || N * K >= GEMV_BATCH_MIN_WEIGHTS)) ||
                                 !decode_mfma_supports(M, K)))
         return Path::Gemv;
     if (decode_mfma_supports(M, K)) return Path::Decode;

@@ -172,7 +172,8 @@ FWD_CASES = [
     # ragged N
     (1, 4096, 4096), (1, 4096, 11008), (1, 12288, 4097), (1, 4096, 16385), (1, 16384, 2048),
     (1, 28672, 2100), (1, 8192, 2048),
-    # two to four tokens on the GEMV (matrices of 2^26 weights or more; two tokens with K >= 8192)
+    # two to four tokens: two on the GEMV (matrices of 2^26 weights or more, or K >= 8192), three
+    # and four on the MFMA decode kernel
     (2, 16384, 4100), (4, 8192, 8200), (3, 4096, 16400), (2, 8192, 1000), (2, 11008, 4099), (3, 16384, 4200),
     # batched decode with K % 256 != 0: 16x16x64 tiles with 1/2/4/8 row blocks per workgroup and
     # one or two token blocks, 32x32x32 tiles with 1/2; K % 256 = 64 and K % 128 = 64 tails;
