@@ -217,6 +217,9 @@ FWD_CASES = [
     # three (768 blocks) and the next one (back to the register-staged kernel)
     (4, 256, 4096), (5, 2304, 4097), (11, 1280, 8192), (16, 512, 12288), (13, 768, 12289),
     (4, 11008, 999), (15, 4096, 63),
+    # ... and 33-64 tokens on at most 256 16-row blocks as two 32-token halves of the grid: one
+    # and two row blocks per workgroup, a second half of one token, ragged N
+    (64, 4096, 4096), (35, 2304, 2049), (33, 11008, 2048), (57, 512, 4000), (48, 1280, 4095),
 ]
 
 
