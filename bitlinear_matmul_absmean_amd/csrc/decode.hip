@@ -653,20 +653,21 @@ static hipError_t launch_bdec16n(const ForwardArgs& a, hipStream_t s) {
     const size_t image = (size_t)BD_WAVES * (4 * MT + RB) * 64 * sizeof(i32x4);
     return launch_with_lds(k_bdec16n<MT, RB>, dim3((unsigned)blocks), dim3(BD_WAVES * 64), tiles > image ? tiles : image, s, a);
 }
-// 33 to 64 tokens as two 32-token halves in one launch (a second grid dimension), each
-// workgroup reading half of x_q: RB row blocks per workgroup.
-template <int RB>
+// Two halves of the tokens in one launch (a second grid dimension), MT 16-token tiles each, every
+// workgroup reading its half of x_q: RB row blocks per workgroup.
+template <int MT, int RB>
 static hipError_t launch_bdec16n_halves(const ForwardArgs& a, hipStream_t s) {
     const int64_t blocks = (a.N + 16 * RB - 1) / (16 * RB);
-    const size_t tiles = (size_t)BD_WAVES * RB * 2 * 64 * sizeof(i32x4);
-    const size_t image = (size_t)BD_WAVES * (8 + RB) * 64 * sizeof(i32x4);
-    return launch_with_lds(k_bdec16n<2, RB>, dim3((unsigned)blocks, (unsigned)((a.M + 31) / 32)), dim3(BD_WAVES * 64),
-                           tiles > image ? tiles : image, s, a);
+    const size_t tiles = (size_t)BD_WAVES * RB * MT * 64 * sizeof(i32x4);
+    const size_t image = (size_t)BD_WAVES * (4 * MT + RB) * 64 * sizeof(i32x4);
+    return launch_with_lds(k_bdec16n<MT, RB>, dim3((unsigned)blocks, (unsigned)((a.M + 16 * MT - 1) / (16 * MT))),
+                           dim3(BD_WAVES * 64), tiles > image ? tiles : image, s, a);
 }
 // (at most 256 16-row blocks: one or two per workgroup keep the grid within 256 workgroups)
+template <int MT>
 static hipError_t launch_bdec16n_halves_fill(const ForwardArgs& a, hipStream_t s) {
     const int64_t nb16 = (a.N + 15) / 16;
-    return nb16 <= 128 ? launch_bdec16n_halves<1>(a, s) : launch_bdec16n_halves<2>(a, s);
+    return nb16 <= 128 ? launch_bdec16n_halves<MT, 1>(a, s) : launch_bdec16n_halves<MT, 2>(a, s);
 }
 
 // Row blocks per workgroup: the fewest (up to three, the most whose images fit the LDS beside
@@ -879,7 +880,10 @@ hipError_t launch_decode_mfma(const ForwardArgs& a, hipStream_t s) {
     // 7.5 against 7.8 us.
     if (a.M > 16 && a.M <= 64 && a.K % 256 == 0 && a.M * a.K < (int64_t(1) << 31) &&
         a.N * (a.K / 4) < (int64_t(1) << 32) && nb16 <= 768) {
-        if (a.M <= 32) return launch_bdec16n_fill<2>(a, s);
+        // 17 to 32 tokens on at most 256 16-row blocks likewise in two 16-token halves (M = 32,
+        // K = 11008, N = 4096: 8.6 against 9.8 us; M = 24: 7.6 against 8.9 us; M = 32, K = 4096,
+        // N = 4096: 5.3 against 5.8 us)
+        if (a.M <= 32) return nb16 <= 256 ? launch_bdec16n_halves_fill<1>(a, s) : launch_bdec16n_fill<2>(a, s);
         // 33 to 64 tokens on at most 256 16-row blocks: two 32-token halves, each workgroup
         // reading half of x_q for twice the rows (measured with weights not in cache, same
         // outputs: M = 64, K = 11008, N = 4096: 10.9 against 14.3 us; K = 16384: 14.8 against
@@ -887,7 +891,7 @@ hipError_t launch_decode_mfma(const ForwardArgs& a, hipStream_t s) {
         // matrices keep all tokens in a workgroup (M = 64, K = 4096, N = 11008: 10.9 against
         // 11.6 us in halves; M = 48: 9.5 against 11.1 us; K = N = 8192: M = 64 13.8 against
         // 13.1 us, M = 40 11.2 against 11.7 us).
-        if (nb16 <= 256) return launch_bdec16n_halves_fill(a, s);
+        if (nb16 <= 256) return launch_bdec16n_halves_fill<2>(a, s);
         if (a.M <= 48) return launch_bdec16n_fill<3>(a, s);
         return launch_bdec16n_fill<4>(a, s);
     }
