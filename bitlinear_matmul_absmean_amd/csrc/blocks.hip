@@ -381,6 +381,14 @@ __global__ __launch_bounds__(BB_WAVES * 64) void k_bdec16n_blocks(BlockArgs a) {
     double* redd = reinterpret_cast<double*>(img);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // a second grid dimension splits the tokens: workgroup row y takes tokens 16 MT y onwards
+    if (gridDim.y > 1) {
+        const int64_t m0 = (int64_t)blockIdx.y * (16 * MT);
+        a.xq += m0 * a.K;
+        a.beta += m0;
+        a.y += m0 * a.N;
+        a.M = a.M - m0 < 16 * MT ? a.M - m0 : 16 * MT;
+    }
     const int M = (int)a.M;
     const int64_t K = a.K, N = a.N, rowb = K >> 2;
     const int KB = (int)(K >> 7), KBp = KB + 1;
@@ -519,10 +527,12 @@ static size_t bdec16n_blocks_lds(int64_t K) {
     const size_t tiles = (size_t)BB_WAVES * RB * MT * 4 * 64 * sizeof(double);
     return images > tiles ? images : tiles;
 }
+// halves: the tokens in two halves of MT tiles each on a second grid dimension
 template <int MT, int RB>
-static hipError_t launch_bdec16n_blocks(const BlockArgs& a, hipStream_t s) {
+static hipError_t launch_bdec16n_blocks(const BlockArgs& a, hipStream_t s, bool halves = false) {
     const int64_t wgs = (a.N + 16 * RB - 1) / (16 * RB);
-    return launch_with_lds(k_bdec16n_blocks<MT, RB>, dim3((unsigned)wgs), dim3(BB_WAVES * 64), bdec16n_blocks_lds<MT, RB>(a.K), s, a);
+    const unsigned ty = halves ? (unsigned)((a.M + 16 * MT - 1) / (16 * MT)) : 1u;
+    return launch_with_lds(k_bdec16n_blocks<MT, RB>, dim3((unsigned)wgs, ty), dim3(BB_WAVES * 64), bdec16n_blocks_lds<MT, RB>(a.K), s, a);
 }
 // Measured with weights not in cache, outputs identical to the earlier kernel (32-token slices
 // of k_bdec16_blocks, in brackets): K = 4096, N = 11008: M = 8 / 16 / 32 / 64: 8.1 / 8.3 / 9.9 /
@@ -539,9 +549,9 @@ static hipError_t launch_bdec16n_blocks(const BlockArgs& a, hipStream_t s) {
 // when the shape is not one this kernel takes (K % 256 != 0, more than 768 16-row blocks,
 // offsets past 32 bits, images and alpha rows past the LDS).
 template <int MT, int RB>
-static bool bdec16n_blocks_try(const BlockArgs& a, hipStream_t s, hipError_t* e) {
+static bool bdec16n_blocks_try(const BlockArgs& a, hipStream_t s, hipError_t* e, bool halves = false) {
     if (bdec16n_blocks_lds<MT, RB>(a.K) + 16 * MT * sizeof(double) > 160 * 1024) return false;
-    *e = launch_bdec16n_blocks<MT, RB>(a, s);
+    *e = launch_bdec16n_blocks<MT, RB>(a, s, halves);
     return true;
 }
 template <int MT>
@@ -557,6 +567,14 @@ static bool bdec16n_blocks_launch(const BlockArgs& a, hipStream_t s, hipError_t*
         a.N * (a.K / 4) >= (int64_t(1) << 32))
         return false;
     if (a.M <= 16) return bdec16n_blocks_rb<1>(a, nb16, s, e);
+    // at most 256 16-row blocks: the tokens in two halves, each workgroup reading half of x_q
+    // for twice the rows, as in the per-tensor kernel (same outputs; M = 64, K = 11008,
+    // N = 4096: 13.3 against 16.1 us; K = 16384: 17.6 against 20.6 us; M = 32, K = 11008:
+    // 10.0 against 10.8 us)
+    if (nb16 <= 256) {
+        if (a.M <= 32) return nb16 <= 128 ? bdec16n_blocks_try<1, 1>(a, s, e, true) : bdec16n_blocks_try<1, 2>(a, s, e, true);
+        return nb16 <= 128 ? bdec16n_blocks_try<2, 1>(a, s, e, true) : bdec16n_blocks_try<2, 2>(a, s, e, true);
+    }
     if (a.M <= 32) return bdec16n_blocks_rb<2>(a, nb16, s, e);
     if (a.M <= 48) return bdec16n_blocks_rb<3>(a, nb16, s, e);
     return bdec16n_blocks_rb<4>(a, nb16, s, e);

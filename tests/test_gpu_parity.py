@@ -693,7 +693,10 @@ BLOCK_CASES = [(1, 4096, 4096), (1, 11008, 300), (2, 128, 77), (3, 4096, 1000), 
                (8, 256, 4096), (13, 2304, 4097), (17, 1280, 8193), (31, 512, 12288),
                (33, 4096, 300), (47, 768, 4100), (48, 3328, 8192), (49, 256, 4096), (60, 2816, 8193),
                (64, 4096, 12288), (64, 16384, 1000), (66, 1024, 700), (100, 4608, 513),
-               (3, 256, 4096), (7, 2304, 8193), (4, 11008, 300)]
+               (3, 256, 4096), (7, 2304, 8193), (4, 11008, 300),
+               # at most 256 16-row blocks from 17 tokens: two halves of the tokens on a second grid
+               # dimension, one and two row blocks, one or two tiles per half, a one-token half
+               (64, 4096, 4096), (33, 2304, 2049), (20, 1024, 500), (47, 11008, 1000)]
 
 
 @pytest.mark.parametrize("m,k,n", BLOCK_CASES)
