@@ -458,7 +458,7 @@ def blocks_bench(torch, bl, workloads, dev, ms_plain_step):
         x = torch.from_numpy(workloads.activations(3, m, k)).to(dev)
         xq, beta = bl.bitlinear_quantize_act(x)
         y = torch.empty((m, n), dtype=torch.float32, device=dev)
-        ms, _ = _graph_time(torch, lambda i: bl.bitlinear_forward_blocks(xq, beta, *pool[i % copies], y=y), 96)
+        ms, _ = _graph_time(torch, lambda i: bl.bitlinear_forward_blocks(xq, beta, *pool[i % copies], y=y), 96, trials=5)
         out["batched"].append({"M": m, "K": k, "N": n, "us": round(ms * 1e3, 2),
                                "kernel": "16x16x64 int8 MFMA tiles, int32 sums per block scaled in fp64" +
                                          (", x_q and codes loaded into LDS" if m >= 3 and k % 256 == 0 else "") +
@@ -567,7 +567,8 @@ def batched_bench(torch, bl, workloads, dev, reps=96):
             x = torch.from_numpy(workloads.activations(3, m, k)).to(dev)
             xq, beta = bl.bitlinear_quantize_act(x)
             y = torch.empty((m, n), dtype=torch.float32, device=dev)
-            ms, _ = _graph_time(torch, lambda i: bl.bitlinear_forward(xq, beta, pool[i % copies], alpha, y=y), reps)
+            ms, _ = _graph_time(torch, lambda i: bl.bitlinear_forward(xq, beta, pool[i % copies], alpha, y=y), reps,
+                                trials=5)
             gbs = n * k / 4 / (ms * 1e-3) / 1e9
             out.append(dict(M=m, K=k, N=n, kernel=bl.bitlinear_forward_kernel(m, k, n, xq, packed),
                             us=round(ms * 1e3, 2), weight_gbs=round(gbs, 1),
