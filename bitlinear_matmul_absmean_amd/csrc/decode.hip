@@ -503,14 +503,16 @@ static hipError_t launch_bdec16w(const ForwardArgs& a, hipStream_t s) {
 }
 
 
-// 4 to 64 tokens, K % 256 == 0: 16 x 16 x 64 tiles with the codes expanded in weight order, so
-// that x_q needs no transposition, as signed bytes W_hat = c - 1, so that no sum of x_q is needed.  Both operands move from global memory into LDS through the
-// load unit itself (buffer_load_dwordx4 ... lds), without passing through registers: the waves
-// split K in 256-weight sub-steps as in k_bdec16w, and each wave keeps an LDS image of its
-// sub-step (x_q of 16 MT tokens x 256 bytes, then RB x 1 KiB of packed weights).  A sub-step
-// reads its image into registers, starts the fetch of the next sub-step into the same image,
-// and multiplies while that fetch is in flight.  No load in the loop writes a register, so
-// the only waits on memory are the explicit ones below.
+// 2 to 64 tokens, K % 256 == 0: 16 x 16 x 64 tiles with the codes expanded in weight order, so
+// that x_q needs no transposition, as signed bytes W_hat = c - 1, so that no sum of x_q is
+// needed.  Both operands move from global memory into LDS through the load unit itself
+// (buffer_load_dwordx4 ... lds), without passing through registers: the waves take the
+// 256-weight sub-steps in turn (wave w: w, w + 8, ...), and each wave keeps an LDS image of its
+// sub-step (x_q of 4 XG tokens x 256 bytes, then RB x 1 KiB of packed weights).  A sub-step
+// reads its image into registers, starts the fetch of the wave's next sub-step into the same
+// image, and multiplies while that fetch is in flight.  No load in the loop writes a register,
+// so the only waits on memory are the explicit ones below.  A second grid dimension, when
+// there is one, splits the tokens into slices of 16 MT.
 //   * x_q layout: token T's 16-byte unit u sits at position u ^ (T % 16) of the token's 256
 //     bytes.  A load instruction covers four tokens, sixteen lanes each; a lane quad reads one
 //     aligned 64-byte piece of a token's row (the XOR permutes units inside and between such
