@@ -361,7 +361,7 @@ static hipError_t launch_bdec16_blocks(const BlockArgs& a, hipStream_t s) {
                            tiles > alphas ? tiles : alphas, s, a);
 }
 
-// Batched tokens (3 to 32 per launch) with K % 256 == 0: the layout of the per-tensor kernel
+// Batched tokens (3 to 64 per launch) with K % 256 == 0: the layout of the per-tensor kernel
 // k_bdec16n.  Codes expanded in weight order and mapped to signed bytes W_hat = c - 1 (a v_perm
 // table), so no sum of x_q is needed; x_q and the packed codes of a sub-step go from global
 // memory into a wave-private LDS image through the load unit (buffer_load_dwordx4 ... lds), the
