@@ -803,9 +803,9 @@ static hipError_t launch_blocks_cpl(const BlockArgs& a, int64_t groups, hipStrea
     }
 }
 
-// One or two tokens: the GEMV; more: the MFMA kernel over slices of 32 tokens (measured at
-// three tokens, weights not in cache: 10.9 vs 12.8 us at K=4096, N=11008; 21.0 vs 31.7 us at
-// K=28672, N=8192).
+// One or two tokens: the GEMV; 3 to 127: MFMA kernels over slices of up to 64 tokens (32 on the
+// earlier kernel when K % 256 != 0; that kernel against the GEMV at three tokens, weights not in
+// cache: 10.9 vs 12.8 us at K=4096, N=11008; 21.0 vs 31.7 us at K=28672, N=8192).
 hipError_t launch_forward_blocks(const int8_t* xq, const float* beta, int64_t M, int64_t K, const uint8_t* wp,
                                  const float* alpha, int64_t N, const float* bias, float* y, hipStream_t s) {
     const BlockArgs a{xq, beta, M, K, N, wp, alpha, bias, y, 0};
