@@ -55,7 +55,7 @@ __device__ __forceinline__ i32x4 unpack16(uint32_t v) {
 #define MF(i, j, av, bv) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, acc[i][j], 0, 0, 0)
 
 constexpr int GEMM_BM = 128, GEMM_BN = 256, GEMM_BK = 64;
-constexpr int64_t GEMM_SMALL_GRID = 128;
+constexpr int64_t GEMM_SMALL_GRID = 192;      // tiles of 128 x 256 up to which 64-token tiles run
 
 // GELU: the BitMLP activation in the epilogue, fixed at compile time so that the plain
 // kernel carries no call.  FM: 32-token blocks per tile, 4 (128 x 256 tiles) or 2 (64 x 256,
@@ -318,12 +318,16 @@ static hipError_t launch_gemm_fm(const ForwardArgs& a, hipStream_t s) {
 
 // 128 x 256 tiles, or 64 x 256 for grids of at most 128 such tiles (a quarter of the 512
 // workgroup slots).  Measured: M = 1024, K = N = 4096: 34.3 vs 45.6 us; M = 512: 31.0 vs
-// 44.7 us; M = 128, N = 11008: 30.0 vs 43.2 us.  With more tiles the 128-token tiles win even
-// at half the slots, since a 64-token tile reads the weights twice as often (M = 2048,
-// K = 11008, N = 4096: 100 vs 126 us; M = 512, N = 11008, 172 tiles: level).
+// 44.7 us; M = 128, N = 11008: 30.0 vs 43.2 us.  With more tiles the 128-token tiles win or tie
+// at long K, since a 64-token tile reads the weights twice as often (M = 2048, K = 11008,
+// N = 4096: 100 vs 126 us; K = 4096: 48.9 vs 49.1 us; M = 512, N = 11008, 172 tiles: level),
+// but up to 192 tiles, and up to 256 with K <= 2048, the 64-token tiles that fill the slots
+// were faster (M = 1536, K = N = 4096: 42.0 vs 46.2 us; M = 2048, K = 2048, N = 4096: 28.8 vs
+// 32.2 us).
 hipError_t launch_gemm_mfma(const ForwardArgs& a, hipStream_t s) {
     const int64_t tiles128 = ((a.M + GEMM_BM - 1) / GEMM_BM) * ((a.N + GEMM_BN - 1) / GEMM_BN);
-    return tiles128 <= GEMM_SMALL_GRID ? launch_gemm_fm<2>(a, s) : launch_gemm_fm<4>(a, s);
+    const bool small = tiles128 <= GEMM_SMALL_GRID || (tiles128 <= 256 && a.K <= 2048);
+    return small ? launch_gemm_fm<2>(a, s) : launch_gemm_fm<4>(a, s);
 }
 
 // ---------------------------------------------------------------------------------------
